@@ -1,0 +1,188 @@
+// C ABI of libsala: argument validation (nothing is enqueued unless every check passes),
+// workspace sizing and dispatch to the gfx950 kernels. The method, layouts and error rules of
+// each entry point are documented in sala.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "sala.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sala_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SALA_OK;
+  g_last_hip_error = (int)e;
+  return SALA_ERR_HIP;
+}
+
+sala_status check_linear(const sala_linear_desc* d) {
+  if (!d) return SALA_ERR_NULL;
+  if (d->batch < 1 || d->seq_len < 0 || d->n_heads < 1 || d->n_kv_heads < 1 || d->pos0 < 0)
+    return SALA_ERR_INVALID;
+  if (d->head_dim != 64 && d->head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (d->dtype != SALA_F32 && d->dtype != SALA_BF16) return SALA_ERR_INVALID;
+  if (!(d->rope_base > 0.f) || !isfinite(d->rope_base)) return SALA_ERR_INVALID;
+  if (!(d->norm_eps >= 0.f) || !isfinite(d->norm_eps)) return SALA_ERR_INVALID;
+  if (d->n_heads % d->n_kv_heads != 0) return SALA_ERR_INVALID;
+  if (d->n_kv_heads != d->n_heads) return SALA_ERR_UNSUPPORTED;  // GQA linear layers: not built
+  // sizes must stay within 64-bit element offsets and 32-bit grid dimensions
+  const double elems = (double)d->batch * d->seq_len * d->n_heads * d->head_dim;
+  if (elems > 9.0e15 || (double)d->batch * d->seq_len * d->n_heads > 2.0e9) return SALA_ERR_INVALID;
+  return SALA_OK;
+}
+
+sala_status check_sparse(const sala_sparse_desc* d) {
+  if (!d) return SALA_ERR_NULL;
+  if (d->batch < 1 || d->n_q < 1 || d->n_heads < 1 || d->n_kv_heads < 1) return SALA_ERR_INVALID;
+  if (d->n_heads % d->n_kv_heads != 0) return SALA_ERR_INVALID;
+  if (d->head_dim != 64 && d->head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (d->dtype != SALA_F32 && d->dtype != SALA_BF16) return SALA_ERR_INVALID;
+  if (d->block != 64) return SALA_ERR_UNSUPPORTED;
+  if (d->n_local != 1 && d->n_local != 2) return SALA_ERR_UNSUPPORTED;
+  if (d->topk < 1 + d->n_local || d->topk > 256) return SALA_ERR_INVALID;
+  if (!(d->norm_eps >= 0.f) || !isfinite(d->norm_eps)) return SALA_ERR_INVALID;
+  if (!(d->scale >= 0.f) || !isfinite(d->scale)) return SALA_ERR_INVALID;
+  if (d->kv_len < d->n_q || d->kv_capacity < d->kv_len || d->kv_capacity % 64 != 0)
+    return SALA_ERR_INVALID;
+  if (d->n_q > 1 && (d->kv_len - d->n_q) % 64 != 0) return SALA_ERR_INVALID;
+  if (d->n_heads > 64) return SALA_ERR_UNSUPPORTED;
+  if ((double)d->batch * d->n_kv_heads * (d->kv_capacity / 64) > 2.0e9) return SALA_ERR_INVALID;
+  return SALA_OK;
+}
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sala_abi_version(void) { return SALA_ABI_VERSION; }
+
+int sala_last_hip_error(void) { return g_last_hip_error; }
+
+const char* sala_status_str(sala_status s) {
+  switch (s) {
+    case SALA_OK: return "ok";
+    case SALA_ERR_NULL: return "a required pointer is NULL";
+    case SALA_ERR_INVALID: return "invalid sizes, parameters or alignment";
+    case SALA_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case SALA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SALA_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t sala_workspace_bytes(int op, const void* desc) {
+  switch (op) {
+    case SALA_OP_LINEAR_PREFILL: {
+      const sala_linear_desc* d = static_cast<const sala_linear_desc*>(desc);
+      if (check_linear(d) != SALA_OK) return SIZE_MAX;
+      return sala::linear_prefill_workspace(*d);
+    }
+    case SALA_OP_BLOCK_SELECT: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse(d) != SALA_OK) return SIZE_MAX;
+      return sala::block_select_workspace(*d);
+    }
+    case SALA_OP_SPARSE_ATTN: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse(d) != SALA_OK) return SIZE_MAX;
+      return sala::sparse_attn_workspace(*d);
+    }
+    default: return SIZE_MAX;
+  }
+}
+
+sala_status sala_linear_prefill(const sala_linear_desc* desc, const void* q, const void* k,
+                                const void* v, const void* gate, const float* q_norm_w,
+                                const float* k_norm_w, const float* state_in, float* state_out,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  sala_status s = check_linear(desc);
+  if (s != SALA_OK) return s;
+  const sala_linear_desc& d = *desc;
+  if (d.dtype == SALA_BF16 && d.head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (d.seq_len > 0 && (!q || !k || !v || !gate || !out)) return SALA_ERR_NULL;
+  if (!all_aligned({q, k, v, gate, out, q_norm_w, k_norm_w, state_in, state_out, workspace}))
+    return SALA_ERR_INVALID;
+  const size_t need = sala::linear_prefill_workspace(d);
+  if (d.seq_len > 0 && need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_linear_prefill(d, q, k, v, gate, q_norm_w, k_norm_w, state_in,
+                                                state_out, out, workspace, (hipStream_t)stream));
+}
+
+sala_status sala_linear_decode_step(const sala_linear_desc* desc, const void* q, const void* k,
+                                    const void* v, const void* gate, const float* q_norm_w,
+                                    const float* k_norm_w, float* state, void* out, void* stream) {
+  sala_status s = check_linear(desc);
+  if (s != SALA_OK) return s;
+  if (desc->seq_len != 1) return SALA_ERR_INVALID;
+  if (!q || !k || !v || !gate || !state || !out) return SALA_ERR_NULL;
+  if (!all_aligned({q, k, v, gate, out, q_norm_w, k_norm_w, state})) return SALA_ERR_INVALID;
+  return hip_status(sala::launch_linear_decode(*desc, q, k, v, gate, q_norm_w, k_norm_w, state, out,
+                                               (hipStream_t)stream));
+}
+
+sala_status sala_kv_append(const sala_sparse_desc* desc, const void* k_new, const void* v_new,
+                           const float* k_norm_w, void* k_cache, void* v_cache, float* k_pool,
+                           void* stream) {
+  sala_status s = check_sparse(desc);
+  if (s != SALA_OK) return s;
+  if (!k_new || !v_new || !k_cache || !v_cache || !k_pool) return SALA_ERR_NULL;
+  if (!all_aligned({k_new, v_new, k_norm_w, k_cache, v_cache, k_pool})) return SALA_ERR_INVALID;
+  return hip_status(sala::launch_kv_append(*desc, k_new, v_new, k_norm_w, k_cache, v_cache, k_pool,
+                                           (hipStream_t)stream));
+}
+
+sala_status sala_kv_pool(const sala_sparse_desc* desc, const void* k_cache, float* k_pool,
+                         int64_t block_begin, int64_t block_end, void* stream) {
+  sala_status s = check_sparse(desc);
+  if (s != SALA_OK) return s;
+  if (!k_cache || !k_pool) return SALA_ERR_NULL;
+  if (block_begin < 0 || block_end < block_begin || block_end * 64 > desc->kv_len ||
+      block_end - block_begin > 2000000000LL)
+    return SALA_ERR_INVALID;
+  if (!all_aligned({k_cache, k_pool})) return SALA_ERR_INVALID;
+  return hip_status(sala::launch_kv_pool(*desc, k_cache, k_pool, block_begin, block_end,
+                                         (hipStream_t)stream));
+}
+
+sala_status sala_block_select(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                              const float* k_pool, int32_t* sel, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  sala_status s = check_sparse(desc);
+  if (s != SALA_OK) return s;
+  if (!q || !k_pool || !sel) return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_pool, sel, workspace})) return SALA_ERR_INVALID;
+  const size_t need = sala::block_select_workspace(*desc);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_block_select(*desc, q, q_norm_w, k_pool, sel, workspace,
+                                              (hipStream_t)stream));
+}
+
+sala_status sala_sparse_attn(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                             const void* k_cache, const void* v_cache, const void* gate,
+                             const int32_t* sel, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  sala_status s = check_sparse(desc);
+  if (s != SALA_OK) return s;
+  const sala_sparse_desc& d = *desc;
+  if (d.dtype == SALA_BF16 && d.head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (d.dtype == SALA_BF16 && d.n_q == 1 && d.n_heads / d.n_kv_heads > 16) return SALA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !gate || !sel || !out) return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, sel, out, workspace})) return SALA_ERR_INVALID;
+  const size_t need = sala::sparse_attn_workspace(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_sparse_attn(d, q, q_norm_w, k_cache, v_cache, gate, sel, out,
+                                             workspace, (hipStream_t)stream));
+}
+
+}  // extern "C"

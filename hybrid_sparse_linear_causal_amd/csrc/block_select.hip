@@ -1,0 +1,320 @@
+// Block selection for the sparse layer: query-block representatives, block scores against the
+// pooled keys, and forced + top-k selection with lowest-index ties.
+//
+// Pages: "面壁智能发布MiniCPM-SALA：稀疏-线性混合架构，9B模型端侧跑通百万上下文，速度飙升3.5倍", section
+// "SALA混合架构：黄金配比破解瓶颈" — a fine block-selection mechanism lets each query attend to only
+// a small set of key/value pairs; "MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模" §1 —
+// sliding-window and global-anchor sparsity (here: forced local blocks and forced block 0).
+// Reading implemented: q~[g,i] = sum over the group's heads of the mean of the normalised
+// queries of block i (decode: the single token); score[j] = q~ . k_pool[j] in fp32; keep the
+// topk - |forced| best candidates j in [1, i - n_local], ties to the lowest index.
+//
+// Kernels: (1) qtilde_kernel — one pass over q; (2) score_tile_kernel (prefill, 64x64 fp32
+// tiles of q~ k_pool^T) or score_row_kernel (one query block: streams the pooled keys);
+// (3) select_kernel — per row an exact radix select on monotone uint32 keys of the scores,
+// then ordered compaction so the output is ascending and deterministic.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sala {
+
+namespace {
+
+constexpr int NT = 256;
+
+// grid (B, nqb); q~[b][g][r][DD] (fp32) = sum_{h in g} mean_t RMSNorm(q[t, h]) * w
+template <typename T, int DD>
+__global__ void __launch_bounds__(NT)
+qtilde_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __restrict__ qt,
+              int n_q, int Hq, int Hkv, long q0, float eps) {
+  constexpr int EPL = 16 / (int)sizeof(T), LPR = DD / EPL, RPP = NT / LPR;
+  __shared__ float hsum[64][DD];  // per-head sums for up to 64 heads
+  const int b = blockIdx.x, r = blockIdx.y;
+  const int j = threadIdx.x, hr = j / LPR, seg = j % LPR;
+  // tokens of this query block inside the call: positions [64*(q0/64 + r), +64) clipped
+  const long blk = q0 / 64 + r;
+  const long p_lo = max(q0, blk * 64), p_hi = min(q0 + n_q, blk * 64 + 64);
+  const float inv_cnt = 1.0f / (float)(p_hi - p_lo);
+  for (int h0 = 0; h0 < Hq; h0 += RPP) {
+    const int h = h0 + hr;
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    if (h < Hq) {
+      for (long p = p_lo; p < p_hi; ++p) {
+        const T* src = q + (((long)b * n_q + (p - q0)) * Hq + h) * DD + seg * EPL;
+        float x[EPL];
+        if constexpr (sizeof(T) == 2) {
+          unpack8(*reinterpret_cast<const uint4*>(src), x);
+        } else {
+          const float4 u = *reinterpret_cast<const float4*>(src);
+          x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+        ss = group_sum<LPR>(ss);
+        const float inv = 1.0f / sqrtf(ss / DD + eps);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += x[e] * inv;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        hsum[h][seg * EPL + e] = acc[e] * inv_cnt * (qw ? qw[seg * EPL + e] : 1.0f);
+    }
+  }
+  __syncthreads();
+  const int G = Hq / Hkv;
+  for (int idx = j; idx < Hkv * DD; idx += NT) {
+    const int g = idx / DD, dd = idx % DD;
+    float s = 0.f;
+    for (int hh = 0; hh < G; ++hh) s += hsum[g * G + hh][dd];
+    qt[(((long)b * Hkv + g) * gridDim.y + r) * DD + dd] = s;
+  }
+}
+
+// Prefill scores: grid (B*Hkv, ceil(nqb/64), ceil(RL/64)); 64x64 tile, 4x4 per thread.
+// sc[bg][r][j] = q~[bg][r] . k_pool[bg][j] for j <= qb0 + r - n_local (others untouched).
+template <int DD>
+__global__ void __launch_bounds__(NT)
+score_tile_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
+                  float* __restrict__ sc, int nqb, long qb0, int RL, long nblk_cap, int n_local) {
+  __shared__ float sq[64][DD + 1];
+  __shared__ float sk[64][DD + 1];
+  const int bg = blockIdx.x;
+  const int r0 = blockIdx.y * 64, j0 = blockIdx.z * 64;
+  const long i_max = qb0 + min(nqb, r0 + 64) - 1;
+  if (j0 > i_max - n_local) return;  // whole tile above the candidate range
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < 64 * DD; idx += NT) {
+    const int rr = idx / DD, dd = idx % DD;
+    sq[rr][dd] = (r0 + rr < nqb) ? qt[((long)bg * nqb + r0 + rr) * DD + dd] : 0.f;
+    sk[rr][dd] = (j0 + rr < RL) ? kpool[((long)bg * nblk_cap + j0 + rr) * DD + dd] : 0.f;
+  }
+  __syncthreads();
+  const int ty = tid / 16, tx = tid % 16;
+  float acc[4][4] = {};
+  for (int dd = 0; dd < DD; ++dd) {
+    float a[4], c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { a[u] = sq[ty * 4 + u][dd]; c[u] = sk[tx * 4 + u][dd]; }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc[u][w] += a[u] * c[w];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = r0 + ty * 4 + u;
+    if (r >= nqb) continue;
+    const long lim = qb0 + r - n_local;  // last candidate block of row r
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int jj = j0 + tx * 4 + w;
+      if (jj <= lim) sc[((long)bg * nqb + r) * RL + jj] = acc[u][w];
+    }
+  }
+}
+
+// One query block (decode): grid (B*Hkv, ceil(ncand/256)); 8 lanes per pooled key row.
+template <int DD>
+__global__ void __launch_bounds__(NT)
+score_row_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
+                 float* __restrict__ sc, int RL, long nblk_cap, long ncand_end) {
+  constexpr int LPB = 8;              // lanes per pooled row
+  constexpr int FPL = DD / LPB;       // floats per lane (16 or 8)
+  const int bg = blockIdx.x;
+  const int tid = threadIdx.x, sub = tid / LPB, part = tid % LPB;
+  float qv[FPL];
+#pragma unroll
+  for (int e = 0; e < FPL; ++e) qv[e] = qt[(long)bg * DD + part * FPL + e];
+  const long jbase = (long)blockIdx.y * 256;
+  for (int it = 0; it < 256 / (NT / LPB); ++it) {
+    const long jj = jbase + it * (NT / LPB) + sub;
+    float s = 0.f;
+    if (jj < ncand_end) {
+      const float* row = kpool + ((long)bg * nblk_cap + jj) * DD + part * FPL;
+#pragma unroll
+      for (int e = 0; e < FPL; e += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(row + e);
+        s += u.x * qv[e] + u.y * qv[e + 1] + u.z * qv[e + 2] + u.w * qv[e + 3];
+      }
+    }
+    s = group_sum<LPB>(s);
+    if (part == 0 && jj < ncand_end) sc[(long)bg * RL + jj] = s;
+  }
+}
+
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < NT / 64; ++w) { const int t = tmp[w]; tmp[w] = acc; acc += t; }
+    tmp[NT / 64] = acc;
+  }
+  __syncthreads();
+  const int res = x - v + tmp[wave];
+  *total = tmp[NT / 64];
+  __syncthreads();
+  return res;
+}
+
+// grid (B*Hkv*nqb); row (bg, r) with i = qb0 + r. Exact top-r over candidate keys
+// (score desc, index asc) by MSB-first radix select on 32-bit monotone keys, then an ordered
+// walk over blocks 0..i that emits forced and chosen blocks ascending; -1 pads to topk.
+__global__ void __launch_bounds__(NT)
+select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, long qb0, int RL,
+              int topk, int n_local) {
+  __shared__ int hist[256];
+  __shared__ int scan_tmp[NT / 64 + 1];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const long row = blockIdx.x;
+  const int r = (int)(row % nqb);
+  const long i = qb0 + r;
+  const float* srow = sc + row * RL;
+  int32_t* out = sel + row * topk;
+  const int tid = threadIdx.x;
+  const long nc = i - n_local > 0 ? i - n_local : 0;             // candidates j = 1..nc
+  const long f_lo = i - n_local + 1 > 0 ? i - n_local + 1 : 0;   // forced local range [f_lo, i]
+  const int n_forced = (int)(i - f_lo + 1) + (f_lo > 0 ? 1 : 0);
+  const int rsel = topk - n_forced;
+  const bool take_all = nc <= rsel;
+
+  uint32_t T = 0;
+  int need = 0;
+  if (!take_all) {
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = rsel;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      hist[tid] = 0;
+      __syncthreads();
+      for (long jj = 1 + tid; jj <= nc; jj += NT) {
+        const uint32_t key = score_key(srow[jj]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0, dgt = 255;
+        for (; dgt > 0; --dgt) {
+          if (cum + hist[dgt] >= remaining) break;
+          cum += hist[dgt];
+        }
+        s_prefix = prefix | ((uint32_t)dgt << shift);
+        s_need = remaining - cum;
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      remaining = s_need;
+      pmask |= 255u << shift;
+    }
+    T = prefix;
+    need = remaining;  // how many candidates with key == T to keep (lowest indices first)
+  }
+
+  // ordered pass over blocks 0..i: each thread owns a contiguous index range
+  const long nall = i + 1;
+  const long per = (nall + NT - 1) / NT;
+  const long a = tid * per, e_end = min(nall, a + per);
+  // (1) equal-key counts in index order
+  int eq = 0;
+  if (!take_all)
+    for (long jj = max(a, 1L); jj < e_end && jj <= nc; ++jj) eq += (score_key(srow[jj]) == T);
+  int eq_total;
+  int eq_before = block_excl_scan(eq, scan_tmp, &eq_total);
+  // (2) count selected blocks in the range
+  auto picked = [&](long jj, int& eqb) -> bool {
+    if (jj == 0 || jj >= f_lo) return true;  // forced
+    if (take_all) return true;              // 1 <= jj <= nc
+    const uint32_t key = score_key(srow[jj]);
+    if (key > T) return true;
+    if (key == T) return (eqb++) < need;
+    return false;
+  };
+  int cnt = 0;
+  {
+    int eqb = eq_before;
+    for (long jj = a; jj < e_end; ++jj) cnt += picked(jj, eqb);
+  }
+  int total;
+  int pos = block_excl_scan(cnt, scan_tmp, &total);
+  {
+    int eqb = eq_before;
+    for (long jj = a; jj < e_end; ++jj)
+      if (picked(jj, eqb)) {
+        if (pos < topk) out[pos] = (int32_t)jj;  // bounded even if the count were off
+        ++pos;
+      }
+  }
+  for (int k = total + tid; k < topk; k += NT) out[k] = -1;
+}
+
+}  // namespace
+
+static long select_row_len(const sala_sparse_desc& d) {
+  const SparseGeom g = sparse_geom(d);
+  return g.qb0 + g.nqb;  // blocks 0 .. i_max
+}
+
+size_t block_select_workspace(const sala_sparse_desc& d) {
+  const SparseGeom g = sparse_geom(d);
+  const size_t bg = (size_t)d.batch * d.n_kv_heads;
+  const size_t qt = bg * g.nqb * d.head_dim * sizeof(float);
+  const size_t sc = bg * g.nqb * select_row_len(d) * sizeof(float);
+  return ((qt + 255) & ~(size_t)255) + sc;
+}
+
+hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
+                               const float* k_pool, int32_t* sel, void* ws, hipStream_t st) {
+  const SparseGeom g = sparse_geom(d);
+  const int BG = d.batch * d.n_kv_heads;
+  const long RL = select_row_len(d);
+  float* qt = static_cast<float*>(ws);
+  const size_t qt_bytes = (size_t)BG * g.nqb * d.head_dim * sizeof(float);
+  float* sc = reinterpret_cast<float*>(static_cast<char*>(ws) + ((qt_bytes + 255) & ~(size_t)255));
+  const dim3 gq(d.batch, (unsigned)g.nqb);
+#define SALA_QT(T, DD)                                                                             \
+  hipLaunchKernelGGL((qtilde_kernel<T, DD>), gq, dim3(NT), 0, st, (const T*)q, qw, qt, d.n_q,      \
+                     d.n_heads, d.n_kv_heads, (long)g.q0, d.norm_eps)
+  if (d.dtype == SALA_BF16) {
+    if (d.head_dim == 128) SALA_QT(bf16_t, 128); else SALA_QT(bf16_t, 64);
+  } else {
+    if (d.head_dim == 128) SALA_QT(float, 128); else SALA_QT(float, 64);
+  }
+#undef SALA_QT
+  const long i_max = g.qb0 + g.nqb - 1;
+  if (i_max - d.n_local >= 1) {
+    if (g.nqb == 1) {
+      const long ncand_end = i_max - d.n_local + 1;  // score blocks 0 .. i - n_local
+      const dim3 gs(BG, (unsigned)((ncand_end + 255) / 256));
+      if (d.head_dim == 128)
+        hipLaunchKernelGGL(score_row_kernel<128>, gs, dim3(NT), 0, st, qt, k_pool, sc, (int)RL,
+                           (long)g.nblk_cap, ncand_end);
+      else
+        hipLaunchKernelGGL(score_row_kernel<64>, gs, dim3(NT), 0, st, qt, k_pool, sc, (int)RL,
+                           (long)g.nblk_cap, ncand_end);
+    } else {
+      const dim3 gs(BG, (unsigned)((g.nqb + 63) / 64), (unsigned)((RL + 63) / 64));
+      if (d.head_dim == 128)
+        hipLaunchKernelGGL(score_tile_kernel<128>, gs, dim3(NT), 0, st, qt, k_pool, sc, (int)g.nqb,
+                           (long)g.qb0, (int)RL, (long)g.nblk_cap, d.n_local);
+      else
+        hipLaunchKernelGGL(score_tile_kernel<64>, gs, dim3(NT), 0, st, qt, k_pool, sc, (int)g.nqb,
+                           (long)g.qb0, (int)RL, (long)g.nblk_cap, d.n_local);
+    }
+  }
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(BG * g.nqb)), dim3(NT), 0, st, sc, sel,
+                     (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
+  return hipGetLastError();
+}
+
+}  // namespace sala

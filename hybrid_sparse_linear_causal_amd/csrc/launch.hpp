@@ -1,0 +1,70 @@
+// Internal launcher declarations shared by the kernel files and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sala.h"
+
+namespace sala {
+
+typedef uint16_t bf16_t;
+
+// RoPE frequencies in revolutions per position, f_i = base^(-2i/d) / (2 pi), i < d/2,
+// computed on the host in double precision and passed by value to the kernels.
+struct RopeFreqs {
+  double f[64];
+};
+
+inline RopeFreqs make_rope_freqs(int d, float base) {
+  RopeFreqs r;
+  for (int i = 0; i < 64; ++i)
+    r.f[i] = (i < d / 2) ? pow((double)base, -2.0 * i / d) / 6.283185307179586476925286766559 : 0.0;
+  return r;
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// ---- linear layer
+int linear_segment_len(const sala_linear_desc& d);
+size_t linear_prefill_workspace(const sala_linear_desc& d);
+hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const void* k,
+                                 const void* v, const void* g, const float* qw, const float* kw,
+                                 const float* state_in, float* state_out, void* out, void* ws,
+                                 hipStream_t st);
+hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const void* k,
+                                const void* v, const void* g, const float* qw, const float* kw,
+                                float* state, void* out, hipStream_t st);
+
+// ---- sparse layer
+struct SparseGeom {
+  int64_t q0;       // position of the first query token
+  int64_t qb0;      // first query block
+  int64_t nqb;      // query blocks covered by the call
+  int64_t nblk_cap; // pooled-key rows per (b, g) = kv_capacity / 64
+  float scale;      // resolved softmax scale
+};
+SparseGeom sparse_geom(const sala_sparse_desc& d);
+
+hipError_t launch_kv_append(const sala_sparse_desc& d, const void* k_new, const void* v_new,
+                            const float* kw, void* k_cache, void* v_cache, float* k_pool,
+                            hipStream_t st);
+hipError_t launch_kv_pool(const sala_sparse_desc& d, const void* k_cache, float* k_pool,
+                          int64_t blk_begin, int64_t blk_end, hipStream_t st);
+size_t block_select_workspace(const sala_sparse_desc& d);
+hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
+                               const float* k_pool, int32_t* sel, void* ws, hipStream_t st);
+size_t sparse_attn_workspace(const sala_sparse_desc& d);
+hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
+                              const void* k_cache, const void* v_cache, const void* g,
+                              const int32_t* sel, void* out, void* ws, hipStream_t st);
+
+}  // namespace sala

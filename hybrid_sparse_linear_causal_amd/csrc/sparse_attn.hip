@@ -1,0 +1,530 @@
+// Block-sparse softmax attention with output gate for the sparse layer.
+//
+// Pages: "面壁智能发布MiniCPM-SALA：稀疏-线性混合架构，9B模型端侧跑通百万上下文，速度飙升3.5倍", section
+// "SALA混合架构：黄金配比破解瓶颈" — each query attends only to the key/value pairs of the blocks
+// the selection picked; no positional encoding in this layer. "MiniCPM-SALA：融合稀疏与线性注意力
+// 实现高效长上下文建模" opening summary — QK normalisation in every layer, an output gate after
+// every attention block. For query t at position p in block i, head h of KV group g:
+//   out[t, h] = softmax_s(scale * q^ . k_s) . v_s * sigmoid(gate[t, h]),
+//   s ranging over tokens s <= p of the blocks in sel[g, i].
+//
+// bf16 prefill (d = 128): one workgroup per (b, g, query block, 4 query heads); each wave owns
+// one head's 64 query rows. For every selected block the 64x128 K tile and the transposed V
+// tile are staged once in LDS for the 4 waves. Per wave and block:
+//   S^T = K Q^T   (16 MFMA 16x16x32 tiles x 4 k-steps; queries are the MFMA columns)
+//   online softmax on S^T in fp32 (exp2 with scale*log2(e) folded into q; rescaling of the
+//                 running output only when a row maximum grows by more than 2^8)
+//   O^T += V^T P^T (P^T comes straight from the S^T accumulators: the 16x16x32 k-index is
+//                 permuted consistently for both operands, so no cross-lane moves)
+// bf16 decode (n_q = 1): split over the selected blocks (one block per wave), the query
+// heads of the GQA group are the 16 MFMA columns; partial (max, sum, output) are combined by
+// a second kernel that also applies the gate.
+// f32 (any shape, correctness-scale inputs): one thread per query row, keys from LDS.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sala {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int KS = D + 8;    // K tile row stride (bf16): 272 B
+constexpr int VS = 64 + 8;   // V^T tile row stride (bf16): 144 B
+constexpr float RESCALE_TH = 8.0f;  // log2 units
+constexpr int DEC_SPLIT = 16;       // decode workgroups per (b, g)
+
+struct AttnLds {
+  bf16_t k[64 * KS];
+  bf16_t vt[D * VS];
+};
+
+__device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
+  const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Stage one 64-key block: K rows as-is, V transposed to [dv][key]. Thread j: K rows j/16+16m,
+// V keys 4*(j/16)+u, 16-byte segment j%16 (8 dims). Rows at or beyond kv_len are zero.
+struct BlockRegs {
+  uint4 k[4], v[4];
+};
+__device__ __forceinline__ void load_block(BlockRegs& r, const bf16_t* kc, const bf16_t* vc,
+                                           long row_base, long blk, long kv_len) {
+  const int j = threadIdx.x, seg = j & 15, kg = j >> 4;
+  const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const long pk = blk * 64 + kg + 16 * m;
+    r.k[m] = pk < kv_len ? *reinterpret_cast<const uint4*>(kc + (row_base + pk) * D + 8 * seg) : z;
+    const long pv = blk * 64 + 4 * kg + m;
+    r.v[m] = pv < kv_len ? *reinterpret_cast<const uint4*>(vc + (row_base + pv) * D + 8 * seg) : z;
+  }
+}
+__device__ __forceinline__ void store_block(const BlockRegs& r, AttnLds& L) {
+  const int j = threadIdx.x, seg = j & 15, kg = j >> 4;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) *reinterpret_cast<uint4*>(&L.k[(kg + 16 * m) * KS + 8 * seg]) = r.k[m];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint2 w;
+    w.x = bf_half(r.v[0], e) | (bf_half(r.v[1], e) << 16);
+    w.y = bf_half(r.v[2], e) | (bf_half(r.v[3], e) << 16);
+    *reinterpret_cast<uint2*>(&L.vt[(8 * seg + e) * VS + 4 * kg]) = w;
+  }
+}
+
+// grid: B*Hkv*nqb*ceil(G/4) workgroups of 256 threads
+__global__ void __launch_bounds__(256)
+sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
+                           const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+                           const bf16_t* __restrict__ g, const int32_t* __restrict__ sel,
+                           bf16_t* __restrict__ out, int n_q, int Hq, int Hkv, long q0, long qb0,
+                           int nqb, long kv_len, long cap, int topk, float eps, float qscale) {
+  __shared__ __align__(16) AttnLds L;
+  const int G = Hq / Hkv, nhq = (G + 3) / 4;
+  // XCD-aware order: workgroup x runs on XCD x % 8; give each XCD a contiguous run of work
+  const unsigned nwg = gridDim.x;
+  unsigned w = blockIdx.x;
+  if ((nwg & 7u) == 0) w = (blockIdx.x & 7u) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int hq = w % nhq;
+  unsigned rest = w / nhq;
+  const int r = rest % nqb;
+  rest /= nqb;
+  const int gk = rest % Hkv, b = rest / Hkv;
+
+  const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
+  const int hl = 4 * hq + wave;
+  const bool head_ok = hl < G;
+  const int h = gk * G + (head_ok ? hl : 0);
+  const long i = qb0 + r;
+  const long row_base = ((long)b * Hkv + gk) * cap;
+  const int32_t* srow = sel + (((long)b * Hkv + gk) * nqb + r) * topk;
+
+  // ---- Q^T fragments (B operand: k = dim, n = query); normalised, scaled by scale*log2(e)
+  bf16x8 qf[4][4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const long t = i * 64 + 16 * qt + l16 - q0;
+    const bool ok = head_ok && t < n_q;
+    float x[4][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (ok) u = *reinterpret_cast<const uint4*>(q + ((long)(b * (long)n_q + t) * Hq + h) * D + 32 * ks + 8 * lq);
+      unpack8(u, x[ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = qscale / sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = x[ks][e] * inv * (qw ? qw[32 * ks + 8 * lq + e] : 1.0f);
+      qf[qt][ks] = as_bf16x8(pack8(y));
+    }
+  }
+
+  int nsel = 0;
+  while (nsel < topk && srow[nsel] >= 0) ++nsel;
+
+  float m[4], lp[4];
+  f32x4 OT[8][4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) { m[qt] = -INFINITY; lp[qt] = 0.f; }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) OT[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  BlockRegs br;
+  if (nsel > 0) load_block(br, kc, vc, row_base, srow[0], kv_len);
+  for (int e = 0; e < nsel; ++e) {
+    const long blk = srow[e];
+    __syncthreads();
+    store_block(br, L);
+    __syncthreads();
+    if (e + 1 < nsel) load_block(br, kc, vc, row_base, srow[e + 1], kv_len);
+    if (!head_ok) continue;
+
+    // S^T[kt][qt] = K[kt] Q^T[qt]
+    f32x4 ST[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) ST[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&L.k[(16 * kt + l16) * KS + 32 * ks + 8 * lq]));
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ST[kt][qt]);
+      }
+    }
+    if (blk == i) {  // diagonal block: key after query is masked
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (16 * kt + 4 * lq + c > 16 * qt + l16) ST[kt][qt][c] = -INFINITY;
+    }
+    // online softmax with lazy rescaling
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      float mx = ST[0][qt][0];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, ST[kt][qt][c]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const bool need = mx > m[qt] + RESCALE_TH;
+      if (__any(need)) {
+        const float mn = need ? mx : m[qt];
+        const float alpha = exp2f(m[qt] - mn);
+        lp[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) OT[dt][qt] *= alpha;
+        m[qt] = mn;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 pf[4];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        float p[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          p[u] = exp2f(ST[2 * c][qt][u] - m[qt]);
+          p[4 + u] = exp2f(ST[2 * c + 1][qt][u] - m[qt]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) lp[qt] += p[u];
+        pf[qt] = as_bf16x8(pack8(p));
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16_t* vr = &L.vt[(16 * dt + l16) * VS + 32 * c + 4 * lq];
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + 16));
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) OT[dt][qt] = mfma16x16x32(a, pf[qt], OT[dt][qt]);
+      }
+    }
+  }
+  if (!head_ok) return;
+
+  // ---- normalise, gate, store (lane: query 16qt + l16, dims 16dt + 4lq .. +3)
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    float l = lp[qt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float il = 1.0f / l;
+    const long t = i * 64 + 16 * qt + l16 - q0;
+    if (t >= n_q) continue;
+    const long base = ((long)(b * (long)n_q + t) * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const long off = base + 16 * dt + 4 * lq;
+      const uint2 gv = *reinterpret_cast<const uint2*>(g + off);
+      const float g0 = __uint_as_float(gv.x << 16), g1 = __uint_as_float(gv.x & 0xffff0000u);
+      const float g2 = __uint_as_float(gv.y << 16), g3 = __uint_as_float(gv.y & 0xffff0000u);
+      uint2 o;
+      o.x = pack_bf16x2(OT[dt][qt][0] * il * sigmoidf_(g0), OT[dt][qt][1] * il * sigmoidf_(g1));
+      o.y = pack_bf16x2(OT[dt][qt][2] * il * sigmoidf_(g2), OT[dt][qt][3] * il * sigmoidf_(g3));
+      *reinterpret_cast<uint2*>(out + off) = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode (n_q = 1)
+
+// grid (B*Hkv, DEC_SPLIT); wave-global index wi = split*4 + wave takes sel entries
+// wi, wi + 4*DEC_SPLIT, ... Partial per workgroup: m[16], l[16], O[16][D] (fp32).
+__global__ void __launch_bounds__(256)
+sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
+                          const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+                          const int32_t* __restrict__ sel, float* __restrict__ part, int Hq,
+                          int Hkv, long kv_len, long cap, int topk, float eps, float qscale) {
+  __shared__ __align__(16) bf16_t vts[4][D * VS];
+  __shared__ float cm[4][16], cl[4][16];
+  const int bg = blockIdx.x, split = blockIdx.y;
+  const int b = bg / Hkv, gk = bg % Hkv, G = Hq / Hkv;
+  const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
+  const long p = kv_len - 1;
+  const long row_base = (long)bg * cap;
+  const int32_t* srow = sel + (long)bg * topk;
+  int nsel = 0;
+  while (nsel < topk && srow[nsel] >= 0) ++nsel;
+
+  // Q^T fragments: column l16 = head gk*G + l16 (zero beyond the group)
+  bf16x8 qf[4];
+  {
+    const bool ok = l16 < G;
+    float x[4][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (ok) u = *reinterpret_cast<const uint4*>(q + ((long)b * Hq + gk * G + l16) * D + 32 * ks + 8 * lq);
+      unpack8(u, x[ks]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = qscale / sqrtf(ss * (1.0f / D) + eps);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = x[ks][e] * inv * (qw ? qw[32 * ks + 8 * lq + e] : 1.0f);
+      qf[ks] = as_bf16x8(pack8(y));
+    }
+  }
+
+  float m = -INFINITY, lp = 0.f;
+  f32x4 OT[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) OT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int stride = 4 * DEC_SPLIT;
+  const int iters = (nsel + stride - 1) / stride;
+  bf16_t* vt = vts[wave];
+  for (int it = 0; it < iters; ++it) {
+    const int e = it * stride + split * 4 + wave;
+    const bool act = e < nsel;
+    const long blk = act ? srow[e] : 0;
+    // stage V^T of this wave's block: lane handles keys 4*(lane/16)+u+16m..., dims 8*(lane%16)
+    if (act) {
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        uint4 vv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const long pk = blk * 64 + 16 * mm + 4 * lq + u;
+          vv[u] = pk < kv_len ? *reinterpret_cast<const uint4*>(vc + (row_base + pk) * D + 8 * l16)
+                              : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) {
+          uint2 w;
+          w.x = bf_half(vv[0], ee) | (bf_half(vv[1], ee) << 16);
+          w.y = bf_half(vv[2], ee) | (bf_half(vv[3], ee) << 16);
+          *reinterpret_cast<uint2*>(&vt[(8 * l16 + ee) * VS + 16 * mm + 4 * lq]) = w;
+        }
+      }
+    }
+    __syncthreads();
+    if (act) {
+      f32x4 ST[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        ST[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const long pk = blk * 64 + 16 * kt + l16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          uint4 u = make_uint4(0, 0, 0, 0);
+          if (pk < kv_len) u = *reinterpret_cast<const uint4*>(kc + (row_base + pk) * D + 32 * ks + 8 * lq);
+          ST[kt] = mfma16x16x32(as_bf16x8(u), qf[ks], ST[kt]);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (blk * 64 + 16 * kt + 4 * lq + c > p) ST[kt][c] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, ST[kt][c]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2f(m - mn);
+      lp *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) OT[dt] *= alpha;
+      m = mn;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float pr[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pr[u] = exp2f(ST[2 * c][u] - m);
+          pr[4 + u] = exp2f(ST[2 * c + 1][u] - m);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) lp += pr[u];
+        const bf16x8 pf = as_bf16x8(pack8(pr));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const bf16_t* vr = &vt[(16 * dt + l16) * VS + 32 * c + 4 * lq];
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + 16));
+          OT[dt] = mfma16x16x32(a, pf, OT[dt]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // combine the 4 waves: O staged in the (now free) V^T area as fp32 [wave][head][D]
+  lp += __shfl_xor(lp, 16, 64);
+  lp += __shfl_xor(lp, 32, 64);
+  if (lq == 0) { cm[wave][l16] = m; cl[wave][l16] = lp; }
+  float* ost = reinterpret_cast<float*>(&vts[0][0]);  // 4*16*128 floats = 32 KB <= sizeof(vts)
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ost[(wave * 16 + l16) * D + 16 * dt + 4 * lq + c] = OT[dt][c];
+  __syncthreads();
+  float* dst = part + ((long)bg * DEC_SPLIT + split) * 16 * (D + 2);
+  for (int idx = j; idx < 16 * D; idx += 256) {
+    const int hh = idx / D, dd = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, cm[wv][hh]);
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) {
+      const float sc = (cm[wv][hh] == -INFINITY) ? 0.f : exp2f(cm[wv][hh] - M);
+      o += ost[(wv * 16 + hh) * D + dd] * sc;
+      l += cl[wv][hh] * sc;
+    }
+    dst[hh * (D + 2) + 2 + dd] = o;
+    if (dd == 0) { dst[hh * (D + 2)] = M; dst[hh * (D + 2) + 1] = l; }
+  }
+}
+
+// grid (B*Hkv); combine DEC_SPLIT partials, normalise, gate, store out[b, h, :]
+__global__ void __launch_bounds__(256)
+sparse_decode_combine_kernel(const float* __restrict__ part, const bf16_t* __restrict__ g,
+                             bf16_t* __restrict__ out, int Hq, int Hkv) {
+  const int bg = blockIdx.x, b = bg / Hkv, gk = bg % Hkv, G = Hq / Hkv;
+  const float* src = part + (long)bg * DEC_SPLIT * 16 * (D + 2);
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int hh = idx / D, dd = idx % D;
+    float M = -INFINITY;
+    for (int s = 0; s < DEC_SPLIT; ++s) M = fmaxf(M, src[(s * 16 + hh) * (D + 2)]);
+    float o = 0.f, l = 0.f;
+    for (int s = 0; s < DEC_SPLIT; ++s) {
+      const float* ps = src + (s * 16 + hh) * (D + 2);
+      const float sc = (ps[0] == -INFINITY) ? 0.f : exp2f(ps[0] - M);
+      o += ps[2 + dd] * sc;
+      l += ps[1] * sc;
+    }
+    const long off = ((long)b * Hq + gk * G + hh) * D + dd;
+    out[off] = f2bf(o / l * sigmoidf_(bf2f(g[off])));
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+
+// grid (B*Hq, nqb); 64 threads, thread = query row of the block; keys staged in LDS.
+template <int DD>
+__global__ void __launch_bounds__(64)
+sparse_attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ qw,
+                       const float* __restrict__ kc, const float* __restrict__ vc,
+                       const float* __restrict__ g, const int32_t* __restrict__ sel,
+                       float* __restrict__ out, int n_q, int Hq, int Hkv, long q0, long qb0,
+                       int nqb, long kv_len, long cap, int topk, float eps, float scale) {
+  __shared__ float ks[64][DD], vs[64][DD];
+  const int bh = blockIdx.x, r = blockIdx.y, b = bh / Hq, h = bh % Hq, G = Hq / Hkv, gk = h / G;
+  const int lane = threadIdx.x;
+  const long i = qb0 + r;
+  const long pos = i * 64 + lane, t = pos - q0;
+  const bool ok = t >= 0 && t < n_q;
+  float qv[DD], acc[DD];
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < DD; ++d) {
+    qv[d] = ok ? q[(((long)b * n_q + t) * Hq + h) * DD + d] : 0.f;
+    ss += qv[d] * qv[d];
+    acc[d] = 0.f;
+  }
+  const float inv = scale / sqrtf(ss / DD + eps);
+#pragma unroll
+  for (int d = 0; d < DD; ++d) qv[d] *= inv * (qw ? qw[d] : 1.0f);
+  float m = -INFINITY, l = 0.f;
+  const int32_t* srow = sel + (((long)b * Hkv + gk) * nqb + r) * topk;
+  const long row_base = ((long)b * Hkv + gk) * cap;
+  for (int e = 0; e < topk; ++e) {
+    const long blk = srow[e];
+    if (blk < 0) break;
+    __syncthreads();
+    for (int idx = lane; idx < 64 * DD; idx += 64) {
+      const int kk = idx / DD, dd = idx % DD;
+      const long pk = blk * 64 + kk;
+      ks[kk][dd] = pk < kv_len ? kc[(row_base + pk) * DD + dd] : 0.f;
+      vs[kk][dd] = pk < kv_len ? vc[(row_base + pk) * DD + dd] : 0.f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < 64; ++kk) {
+      const long pk = blk * 64 + kk;
+      if (pk > pos || pk >= kv_len) continue;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < DD; ++d) s += qv[d] * ks[kk][d];
+      const float mn = fmaxf(m, s);
+      const float alpha = expf(m - mn), pw = expf(s - mn);
+      l = l * alpha + pw;
+#pragma unroll
+      for (int d = 0; d < DD; ++d) acc[d] = acc[d] * alpha + pw * vs[kk][d];
+      m = mn;
+    }
+  }
+  if (!ok) return;
+  const long base = (((long)b * n_q + t) * Hq + h) * DD;
+#pragma unroll
+  for (int d = 0; d < DD; ++d) out[base + d] = acc[d] / l / (1.0f + expf(-g[base + d]));
+}
+
+}  // namespace
+
+size_t sparse_attn_workspace(const sala_sparse_desc& d) {
+  if (d.dtype == SALA_BF16 && d.n_q == 1)
+    return (size_t)d.batch * d.n_kv_heads * DEC_SPLIT * 16 * (D + 2) * sizeof(float);
+  return 0;
+}
+
+hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
+                              const void* k_cache, const void* v_cache, const void* g,
+                              const int32_t* sel, void* out, void* ws, hipStream_t st) {
+  const SparseGeom gm = sparse_geom(d);
+  const int G = d.n_heads / d.n_kv_heads;
+  if (d.dtype == SALA_F32) {
+    const dim3 grid(d.batch * d.n_heads, (unsigned)gm.nqb);
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL(sparse_attn_f32_kernel<128>, grid, dim3(64), 0, st, (const float*)q, qw,
+                         (const float*)k_cache, (const float*)v_cache, (const float*)g, sel, (float*)out,
+                         d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0, (int)gm.nqb,
+                         (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, gm.scale);
+    else
+      hipLaunchKernelGGL(sparse_attn_f32_kernel<64>, grid, dim3(64), 0, st, (const float*)q, qw,
+                         (const float*)k_cache, (const float*)v_cache, (const float*)g, sel, (float*)out,
+                         d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0, (int)gm.nqb,
+                         (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, gm.scale);
+    return hipGetLastError();
+  }
+  const float qscale = gm.scale * 1.4426950408889634f;  // exp -> exp2
+  if (d.n_q == 1) {
+    float* part = static_cast<float*>(ws);
+    hipLaunchKernelGGL(sparse_decode_bf16_kernel, dim3(d.batch * d.n_kv_heads, DEC_SPLIT), dim3(256), 0,
+                       st, (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, sel,
+                       part, d.n_heads, d.n_kv_heads, (long)d.kv_len, (long)d.kv_capacity, d.topk,
+                       d.norm_eps, qscale);
+    hipLaunchKernelGGL(sparse_decode_combine_kernel, dim3(d.batch * d.n_kv_heads), dim3(256), 0, st,
+                       part, (const bf16_t*)g, (bf16_t*)out, d.n_heads, d.n_kv_heads);
+    return hipGetLastError();
+  }
+  const long nwg = (long)d.batch * d.n_kv_heads * gm.nqb * ((G + 3) / 4);
+  hipLaunchKernelGGL(sparse_prefill_bf16_kernel, dim3((unsigned)nwg), dim3(256), 0, st, (const bf16_t*)q,
+                     qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
+                     (bf16_t*)out, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0,
+                     (int)gm.nqb, (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, qscale);
+  return hipGetLastError();
+}
+
+}  // namespace sala

@@ -1,0 +1,177 @@
+// Sparse-layer KV cache maintenance: append (QK-norm of the new keys, cache write) and block
+// pooling (mean key of each complete 64-token block).
+//
+// Pages: "面壁智能发布MiniCPM-SALA：稀疏-线性混合架构，9B模型端侧跑通百万上下文，速度飙升3.5倍", section
+// "SALA混合架构：黄金配比破解瓶颈" — the sparse layers (InfLLM-V2) select key blocks per query
+// and keep no positional encoding, so cached keys are position-free; "MiniCPM-SALA：融合稀疏与线性
+// 注意力实现高效长上下文建模" §1 — sparse attention still keeps the full KV cache. The pooled
+// (mean) key per block is the block representative the selection scores against.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sala {
+
+SparseGeom sparse_geom(const sala_sparse_desc& d) {
+  SparseGeom g;
+  g.q0 = d.kv_len - d.n_q;
+  g.qb0 = g.q0 / 64;
+  g.nqb = (d.kv_len - 1) / 64 - g.qb0 + 1;
+  g.nblk_cap = d.kv_capacity / 64;
+  g.scale = d.scale > 0.f ? d.scale : (float)(1.0 / sqrt((double)d.head_dim));
+  return g;
+}
+
+namespace {
+
+// Elements a lane moves per 16-byte access and lanes per head row.
+template <typename T, int DD> struct RowGeom {
+  static constexpr int EPL = 16 / (int)sizeof(T);
+  static constexpr int LPR = DD / EPL;  // lanes per row (<= 64)
+  static constexpr int RPP = 256 / LPR; // rows per 256-thread pass
+};
+
+template <typename T>
+__device__ __forceinline__ void load_row_part(const T* p, float* f);
+template <>
+__device__ __forceinline__ void load_row_part<bf16_t>(const bf16_t* p, float* f) {
+  unpack8(*reinterpret_cast<const uint4*>(p), f);
+}
+template <>
+__device__ __forceinline__ void load_row_part<float>(const float* p, float* f) {
+  const float4 u = *reinterpret_cast<const float4*>(p);
+  f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+}
+template <typename T>
+__device__ __forceinline__ void store_row_part(T* p, const float* f);
+template <>
+__device__ __forceinline__ void store_row_part<bf16_t>(bf16_t* p, const float* f) {
+  *reinterpret_cast<uint4*>(p) = pack8(f);
+}
+template <>
+__device__ __forceinline__ void store_row_part<float>(float* p, const float* f) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+}
+
+// grid (B*Hkv, blocks touched by the new tokens); 256 threads.
+template <typename T, int DD>
+__global__ void __launch_bounds__(256)
+kv_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
+                 const float* __restrict__ kw, T* __restrict__ k_cache, T* __restrict__ v_cache,
+                 float* __restrict__ k_pool, int n_q, int Hkv, long kv_len, long cap, float eps) {
+  using G = RowGeom<T, DD>;
+  constexpr int EPL = G::EPL, LPR = G::LPR, RPP = G::RPP;
+  __shared__ float psum[RPP][DD];
+  const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
+  const long q0 = kv_len - n_q;
+  const long blk = q0 / 64 + blockIdx.y;
+  const int j = threadIdx.x, r = j / LPR, seg = j % LPR;
+  const long row_base = ((long)b * Hkv + g) * cap;  // cache row of (b, g, position 0)
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int t = r; t < 64; t += RPP) {
+    const long p = blk * 64 + t;
+    float x[EPL];
+    if (p >= q0 && p < kv_len) {
+      const long src = (((long)b * n_q + (p - q0)) * Hkv + g) * DD + seg * EPL;
+      load_row_part<T>(k_new + src, x);
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+      ss = group_sum<LPR>(ss);
+      const float inv = 1.0f / sqrtf(ss / DD + eps);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] *= inv * (kw ? kw[seg * EPL + e] : 1.0f);
+      store_row_part<T>(k_cache + (row_base + p) * DD + seg * EPL, x);
+      float vv[EPL];
+      load_row_part<T>(v_new + src, vv);
+      store_row_part<T>(v_cache + (row_base + p) * DD + seg * EPL, vv);
+    } else if (p < q0) {
+      load_row_part<T>(k_cache + (row_base + p) * DD + seg * EPL, x);  // already cached
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+  }
+  if ((blk + 1) * 64 > kv_len) return;  // block still incomplete: nothing to pool (uniform)
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) psum[r][seg * EPL + e] = acc[e];
+  __syncthreads();
+  for (int dd = j; dd < DD; dd += 256) {
+    float s = 0.f;
+    for (int rr = 0; rr < RPP; ++rr) s += psum[rr][dd];
+    k_pool[(((long)b * Hkv + g) * (cap / 64) + blk) * DD + dd] = s * (1.0f / 64.0f);
+  }
+}
+
+// grid (B*Hkv, blk_end - blk_begin); mean of the 64 cached keys of each block
+template <typename T, int DD>
+__global__ void __launch_bounds__(256)
+kv_pool_kernel(const T* __restrict__ k_cache, float* __restrict__ k_pool, int Hkv, long cap,
+               long blk_begin) {
+  using G = RowGeom<T, DD>;
+  constexpr int EPL = G::EPL, LPR = G::LPR, RPP = G::RPP;
+  __shared__ float psum[RPP][DD];
+  const int bg = blockIdx.x;
+  const long blk = blk_begin + blockIdx.y;
+  const int j = threadIdx.x, r = j / LPR, seg = j % LPR;
+  const long row_base = (long)bg * cap;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int t = r; t < 64; t += RPP) {
+    float x[EPL];
+    load_row_part<T>(k_cache + (row_base + blk * 64 + t) * DD + seg * EPL, x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += x[e];
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) psum[r][seg * EPL + e] = acc[e];
+  __syncthreads();
+  for (int dd = j; dd < DD; dd += 256) {
+    float s = 0.f;
+    for (int rr = 0; rr < RPP; ++rr) s += psum[rr][dd];
+    k_pool[((long)bg * (cap / 64) + blk) * DD + dd] = s * (1.0f / 64.0f);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const sala_sparse_desc& d, const void* k_new, const void* v_new,
+                            const float* kw, void* k_cache, void* v_cache, float* k_pool,
+                            hipStream_t st) {
+  const long q0 = d.kv_len - d.n_q;
+  const long nblk = (d.kv_len - 1) / 64 - q0 / 64 + 1;
+  const dim3 grid(d.batch * d.n_kv_heads, (unsigned)nblk);
+#define SALA_APPEND(T, DD)                                                                        \
+  hipLaunchKernelGGL((kv_append_kernel<T, DD>), grid, dim3(256), 0, st, (const T*)k_new,          \
+                     (const T*)v_new, kw, (T*)k_cache, (T*)v_cache, k_pool, d.n_q, d.n_kv_heads,  \
+                     (long)d.kv_len, (long)d.kv_capacity, d.norm_eps)
+  if (d.dtype == SALA_BF16) {
+    if (d.head_dim == 128) SALA_APPEND(bf16_t, 128); else SALA_APPEND(bf16_t, 64);
+  } else {
+    if (d.head_dim == 128) SALA_APPEND(float, 128); else SALA_APPEND(float, 64);
+  }
+#undef SALA_APPEND
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_pool(const sala_sparse_desc& d, const void* k_cache, float* k_pool,
+                          int64_t blk_begin, int64_t blk_end, hipStream_t st) {
+  if (blk_end <= blk_begin) return hipSuccess;
+  const dim3 grid(d.batch * d.n_kv_heads, (unsigned)(blk_end - blk_begin));
+#define SALA_POOL(T, DD)                                                                          \
+  hipLaunchKernelGGL((kv_pool_kernel<T, DD>), grid, dim3(256), 0, st, (const T*)k_cache, k_pool,  \
+                     d.n_kv_heads, (long)d.kv_capacity, (long)blk_begin)
+  if (d.dtype == SALA_BF16) {
+    if (d.head_dim == 128) SALA_POOL(bf16_t, 128); else SALA_POOL(bf16_t, 64);
+  } else {
+    if (d.head_dim == 128) SALA_POOL(float, 128); else SALA_POOL(float, 64);
+  }
+#undef SALA_POOL
+  return hipGetLastError();
+}
+
+}  // namespace sala

@@ -1,0 +1,242 @@
+"""Python binding of libsala: argument marshalling only.
+
+Every step of the hot path runs in libsala's HIP kernels; this module only turns torch tensors
+into pointers and sizes, allocates workspace through torch, passes torch's current stream and
+raises on a non-OK status. It fails loudly (SalaError at import of the library) when
+libsala.so is missing: there is no CPU fallback.
+
+Entry points mirror include/sala.h: linear_prefill, linear_decode_step, kv_append, kv_pool,
+block_select, sparse_attn (+ workspace_bytes, abi_version).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsala.so")
+
+SALA_F32, SALA_BF16 = 0, 1
+OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN = 1, 2, 3
+STATUS = {0: "ok", 1: "null pointer", 2: "invalid", 3: "unsupported", 4: "workspace", 5: "hip"}
+
+
+class SalaError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"libsala {what}: status {status} ({STATUS.get(status, '?')})")
+
+
+class LinearDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("pos0", ctypes.c_int64), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+
+class SparseDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("topk", ctypes.c_int32), ("n_local", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float), ("scale", ctypes.c_float), ("reserved_", ctypes.c_int32),
+                ("kv_len", ctypes.c_int64), ("kv_capacity", ctypes.c_int64)]
+
+
+_VP = ctypes.c_void_p
+_lib = None
+
+
+def lib():
+    """Load libsala.so once (raises SalaError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SalaError(-1, f"library not built: {LIB_PATH} missing (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sala_linear_prefill.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 10 + [ctypes.c_size_t, _VP]
+        L.sala_linear_decode_step.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 9
+        L.sala_kv_append.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7
+        L.sala_kv_pool.argtypes = [ctypes.POINTER(SparseDesc), _VP, _VP, ctypes.c_int64, ctypes.c_int64, _VP]
+        L.sala_block_select.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 5 + [ctypes.c_size_t, _VP]
+        L.sala_sparse_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 8 + [ctypes.c_size_t, _VP]
+        L.sala_workspace_bytes.argtypes = [ctypes.c_int, _VP]
+        L.sala_workspace_bytes.restype = ctypes.c_size_t
+        L.sala_status_str.argtypes = [ctypes.c_int]
+        L.sala_status_str.restype = ctypes.c_char_p
+        for name in ("sala_linear_prefill", "sala_linear_decode_step", "sala_kv_append", "sala_kv_pool",
+                     "sala_block_select", "sala_sparse_attn", "sala_abi_version", "sala_last_hip_error"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def abi_version():
+    return lib().sala_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SALA_BF16
+    if t.dtype == torch.float32:
+        return SALA_F32
+    raise SalaError(2, f"dtype {t.dtype} (need bfloat16 or float32)")
+
+
+def _check(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise SalaError(2, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise SalaError(2, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise SalaError(2, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _call(fn, *args, what=""):
+    st = fn(*args)
+    if st != 0:
+        raise SalaError(st, what)
+
+
+def workspace_bytes(op, desc):
+    n = lib().sala_workspace_bytes(op, ctypes.byref(desc))
+    if n == ctypes.c_size_t(-1).value:
+        raise SalaError(2, "workspace_bytes: invalid descriptor")
+    return n
+
+
+def _workspace(op, desc, device, workspace):
+    need = workspace_bytes(op, desc)
+    if need == 0:
+        return None, 0
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(need, dtype=torch.uint8, device=device), need
+
+
+def linear_desc(q, pos0, rope_base, eps):
+    B, N, H, d = q.shape
+    return LinearDesc(B, N, H, H, d, _dtype_code(q), int(pos0), float(rope_base), float(eps))
+
+
+def linear_prefill(q, k, v, g, *, pos0=0, rope_base=10000.0, eps=1e-6, state_in=None,
+                   state_out=None, q_norm_w=None, k_norm_w=None, out=None, workspace=None,
+                   stream=None):
+    """q, k, v, g: [B, N, H, d] (bf16 or f32); returns (out, state_out [B, H, d, d] f32)."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, q.dtype)
+    B, N, H, d = q.shape
+    for n, t in (("k", k), ("v", v), ("g", g)):
+        if tuple(t.shape) != (B, N, H, d):
+            raise SalaError(2, f"{n} shape {tuple(t.shape)} != {(B, N, H, d)}")
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None:
+        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    for n, t in (("state_in", state_in), ("state_out", state_out), ("q_norm_w", q_norm_w),
+                 ("k_norm_w", k_norm_w)):
+        _check(t, n, torch.float32)
+    desc = linear_desc(q, pos0, rope_base, eps)
+    ws, ws_bytes = _workspace(OP_LINEAR_PREFILL, desc, q.device, workspace)
+    _call(lib().sala_linear_prefill, ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+          _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(ws),
+          ws_bytes, _stream(stream), what="linear_prefill")
+    return out, state_out
+
+
+def linear_decode_step(q, k, v, g, state, pos, *, rope_base=10000.0, eps=1e-6, q_norm_w=None,
+                       k_norm_w=None, out=None, stream=None):
+    """q, k, v, g: [B, H, d]; state [B, H, d, d] f32 updated in place; returns out [B, H, d]."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, q.dtype)
+    _check(state, "state", torch.float32)
+    B, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    desc = LinearDesc(B, 1, H, H, d, _dtype_code(q), int(pos), float(rope_base), float(eps))
+    _call(lib().sala_linear_decode_step, ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+          _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state), _ptr(out), _stream(stream),
+          what="linear_decode_step")
+    return out
+
+
+def sparse_desc(*, batch, n_q, n_heads, n_kv_heads, head_dim, dtype, kv_len, kv_capacity, topk=64,
+                n_local=2, eps=1e-6, scale=0.0, block=64):
+    code = dtype if isinstance(dtype, int) else (SALA_BF16 if dtype == torch.bfloat16 else SALA_F32)
+    return SparseDesc(batch, n_q, n_heads, n_kv_heads, head_dim, code, block, topk, n_local,
+                      float(eps), float(scale), 0, int(kv_len), int(kv_capacity))
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, k_pool, kv_len, *, eps=1e-6, k_norm_w=None,
+              n_heads=None, stream=None):
+    """k_new, v_new [B, n_q, Hkv, d]; caches [B, Hkv, cap, d]; k_pool [B, Hkv, cap/64, d] f32.
+    kv_len = tokens in the cache after the append."""
+    B, nq, Hkv, d = k_new.shape
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, n, k_new.dtype)
+    _check(k_pool, "k_pool", torch.float32)
+    desc = sparse_desc(batch=B, n_q=nq, n_heads=n_heads or Hkv, n_kv_heads=Hkv, head_dim=d,
+                       dtype=k_new.dtype, kv_len=kv_len, kv_capacity=k_cache.shape[2], topk=3,
+                       n_local=2, eps=eps)
+    _call(lib().sala_kv_append, ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(k_norm_w),
+          _ptr(k_cache), _ptr(v_cache), _ptr(k_pool), _stream(stream), what="kv_append")
+
+
+def kv_pool(k_cache, k_pool, kv_len, blk_begin, blk_end, *, stream=None):
+    B, Hkv, cap, d = k_cache.shape
+    _check(k_cache, "k_cache")
+    _check(k_pool, "k_pool", torch.float32)
+    desc = sparse_desc(batch=B, n_q=1, n_heads=Hkv, n_kv_heads=Hkv, head_dim=d, dtype=k_cache.dtype,
+                       kv_len=kv_len, kv_capacity=cap, topk=3, n_local=2)
+    _call(lib().sala_kv_pool, ctypes.byref(desc), _ptr(k_cache), _ptr(k_pool), int(blk_begin),
+          int(blk_end), _stream(stream), what="kv_pool")
+
+
+def block_select(q, k_pool, kv_len, kv_capacity, *, n_kv_heads, topk=64, n_local=2, eps=1e-6,
+                 q_norm_w=None, sel=None, workspace=None, stream=None):
+    """q [B, n_q, Hq, d]; returns sel [B, Hkv, nqb, topk] int32."""
+    _check(q, "q")
+    _check(k_pool, "k_pool", torch.float32)
+    B, nq, Hq, d = q.shape
+    desc = sparse_desc(batch=B, n_q=nq, n_heads=Hq, n_kv_heads=n_kv_heads, head_dim=d, dtype=q.dtype,
+                       kv_len=kv_len, kv_capacity=kv_capacity, topk=topk, n_local=n_local, eps=eps)
+    q0 = kv_len - nq
+    nqb = (kv_len - 1) // 64 - q0 // 64 + 1
+    if sel is None:
+        sel = torch.empty((B, n_kv_heads, nqb, topk), dtype=torch.int32, device=q.device)
+    ws, ws_bytes = _workspace(OP_BLOCK_SELECT, desc, q.device, workspace)
+    _call(lib().sala_block_select, ctypes.byref(desc), _ptr(q), _ptr(q_norm_w), _ptr(k_pool),
+          _ptr(sel), _ptr(ws), ws_bytes, _stream(stream), what="block_select")
+    return sel
+
+
+def sparse_attn(q, k_cache, v_cache, g, sel, kv_len, *, topk=None, n_local=2, eps=1e-6, scale=0.0,
+                q_norm_w=None, out=None, workspace=None, stream=None):
+    """q, g [B, n_q, Hq, d]; caches [B, Hkv, cap, d]; sel from block_select. Returns out."""
+    for n, t in (("q", q), ("g", g), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, n, q.dtype)
+    _check(sel, "sel", torch.int32)
+    B, nq, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    desc = sparse_desc(batch=B, n_q=nq, n_heads=Hq, n_kv_heads=Hkv, head_dim=d, dtype=q.dtype,
+                       kv_len=kv_len, kv_capacity=cap, topk=topk or sel.shape[-1], n_local=n_local,
+                       eps=eps, scale=scale)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, ws_bytes = _workspace(OP_SPARSE_ATTN, desc, q.device, workspace)
+    _call(lib().sala_sparse_attn, ctypes.byref(desc), _ptr(q), _ptr(q_norm_w), _ptr(k_cache),
+          _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(out), _ptr(ws), ws_bytes, _stream(stream),
+          what="sparse_attn")
+    return out

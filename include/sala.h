@@ -1,0 +1,197 @@
+/*
+ * libsala — the SALA hybrid attention hot path (linear layers + block-sparse layers) for
+ * AMD MI355X (gfx950). C ABI: plain pointers and sizes, no framework types.
+ *
+ * The method: a hybrid decoder whose attention layers are 75% linear attention (Lightning
+ * style) and 25% block-sparse softmax attention (InfLLM-V2 style); QK normalisation in every
+ * layer; RoPE only in the linear layers (the sparse layers use no positional encoding, so
+ * their KV cache is position-free); an output gate after every attention block.
+ * Pages: "MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模" (opening summary; §1
+ * Introduction; §2.1 Model architecture) and "面壁智能发布MiniCPM-SALA：稀疏-线性混合架构，9B模型端侧
+ * 跑通百万上下文，速度飙升3.5倍" (section "SALA混合架构：黄金配比破解瓶颈").
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Memory: every tensor pointer is DEVICE memory owned by the caller; the library never
+ *   allocates, frees or synchronises. Scratch memory, where needed, is a caller-provided
+ *   device `workspace` of at least sala_workspace_bytes(op, desc) bytes. Pointers must be
+ *   16-byte aligned; tensors are dense and contiguous in the layouts stated below.
+ * - dtype: SALA_BF16 tensors hold bf16 bit patterns (uint16); SALA_F32 tensors hold float.
+ *   The linear state, norm weights and pooled keys are always float32.
+ * - Stream: `stream` is a hipStream_t (NULL = the default stream). Work is enqueued in
+ *   stream order and runs asynchronously; results are valid once the stream is synchronised.
+ * - Errors: arguments are checked before anything is enqueued. On any non-OK status nothing
+ *   has been enqueued, except SALA_ERR_HIP, which reports a failed launch (the HIP error code
+ *   is kept per thread, see sala_last_hip_error). Device faults surface at the caller's next
+ *   synchronisation. No C++ exception crosses this interface.
+ * - Aliasing: outputs must not overlap inputs, except where an entry point says otherwise.
+ */
+#ifndef SALA_H_
+#define SALA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SALA_ABI_VERSION 1
+
+typedef enum {
+  SALA_OK = 0,
+  SALA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SALA_ERR_INVALID = 2,     /* inconsistent or out-of-range sizes / parameters / alignment */
+  SALA_ERR_UNSUPPORTED = 3, /* valid, but not a shape or dtype this build implements */
+  SALA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than sala_workspace_bytes() */
+  SALA_ERR_HIP = 5          /* a kernel launch failed */
+} sala_status;
+
+typedef enum { SALA_F32 = 0, SALA_BF16 = 1 } sala_dtype;
+
+typedef enum { SALA_OP_LINEAR_PREFILL = 1, SALA_OP_BLOCK_SELECT = 2, SALA_OP_SPARSE_ATTN = 3 } sala_op;
+
+/* Linear-attention layer shape.
+ *   batch      B >= 1
+ *   seq_len    N tokens in this call (prefill: N >= 0; decode: must be 1)
+ *   n_heads    H query heads; n_kv_heads must equal n_heads in this build
+ *   head_dim   d: 64 or 128 (bf16 prefill needs 128)
+ *   dtype      sala_dtype of q, k, v, gate and out
+ *   pos0       position of the first token of the call (>= 0); RoPE uses p = pos0 + t
+ *   rope_base  RoPE base (theta_i = rope_base^(-2i/d)), > 0
+ *   norm_eps   QK-norm epsilon, >= 0 */
+typedef struct {
+  int32_t batch;
+  int32_t seq_len;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int64_t pos0;
+  float rope_base;
+  float norm_eps;
+} sala_linear_desc;
+
+/* Block-sparse layer shape.
+ *   batch       B >= 1
+ *   n_q         query tokens in this call (prefill: >= 1; decode: 1). The queries are the
+ *               tokens at positions [kv_len - n_q, kv_len); when n_q > 1 the first of them
+ *               must start a block ((kv_len - n_q) % block == 0).
+ *   n_heads     Hq query heads; n_kv_heads Hkv divides Hq (GQA group = Hq / Hkv heads)
+ *   head_dim    d: 64 or 128 (bf16 needs 128)
+ *   dtype       sala_dtype of q, gate, out, k/v caches and new k/v
+ *   block       tokens per key block and per query block: must be 64
+ *   topk        blocks kept per query block, forced blocks included: 1 + n_local .. 256
+ *   n_local     local blocks forced (the query's own block, and block i-1 when 2): 1 or 2
+ *   norm_eps    QK-norm epsilon, >= 0
+ *   scale       softmax scale; 0 selects 1/sqrt(d)
+ *   kv_len      tokens in the cache once this call's tokens are in it (>= n_q)
+ *   kv_capacity token capacity of each cache row: >= kv_len, multiple of 64 */
+typedef struct {
+  int32_t batch;
+  int32_t n_q;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t block;
+  int32_t topk;
+  int32_t n_local;
+  float norm_eps;
+  float scale;
+  int32_t reserved_;
+  int64_t kv_len;
+  int64_t kv_capacity;
+} sala_sparse_desc;
+
+/* Linear layer prefill: causal linear attention over the N tokens of the call, carrying the
+ * per-head d x d state (pages: "MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模" §1 and
+ * §2.1 — O(N) recurrent linear attention with constant per-token memory; opening summary —
+ * QK-norm, RoPE and output gate). Per token t at position p = pos0 + t:
+ *   q^ = RoPE_p(RMSNorm(q_t) * q_norm_w), k^ = RoPE_p(RMSNorm(k_t) * k_norm_w)
+ *   S  <- S + k^^T v_t           (S[i][j] += k^[i] v[j])
+ *   out_t = (q^ S) * sigmoid(g_t)
+ * Inputs  q, k, v, gate, out: [B, N, H, d] (token-major, dtype);
+ *         q_norm_w, k_norm_w: [d] float or NULL (= all ones);
+ *         state_in: [B, H, d, d] float (S[i][j], row i = key dim) or NULL (= zeros).
+ * Outputs out: [B, N, H, d]; state_out: [B, H, d, d] float, or NULL to skip. state_out may
+ *         alias state_in. The bf16 path evaluates the recurrence in 64-token chunks on MFMA
+ *         (bf16 operands, fp32 accumulation, fp32 state); the f32 path is a plain fp32 scan.
+ * Workspace: sala_workspace_bytes(SALA_OP_LINEAR_PREFILL, desc) bytes (may be 0). */
+sala_status sala_linear_prefill(const sala_linear_desc* desc, const void* q, const void* k,
+                                const void* v, const void* gate, const float* q_norm_w,
+                                const float* k_norm_w, const float* state_in, float* state_out,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Linear layer decode step: one token per sequence at position desc->pos0 (same pages).
+ * desc->seq_len must be 1. q, k, v, gate, out: [B, H, d]; state: [B, H, d, d] float, updated
+ * in place (S <- S + k^^T v, then out = (q^ S) * sigmoid(g)). */
+sala_status sala_linear_decode_step(const sala_linear_desc* desc, const void* q, const void* k,
+                                    const void* v, const void* gate, const float* q_norm_w,
+                                    const float* k_norm_w, float* state, void* out, void* stream);
+
+/* Sparse layer KV append (pages: "面壁智能发布MiniCPM-SALA…" section "SALA混合架构…" — the sparse
+ * layers keep the full KV cache without positional encoding; the block-selection mechanism
+ * works on whole key blocks). Writes the n_q new tokens at positions [kv_len - n_q, kv_len):
+ *   k_cache[b, g, p, :] = RMSNorm(k_new[b, t, g, :]) * k_norm_w   (bf16/f32 as dtype)
+ *   v_cache[b, g, p, :] = v_new[b, t, g, :]
+ * and, for every key block that this call completes, the pooled key
+ *   k_pool[b, g, j, :] = mean of the block's 64 normalised keys (float; new keys contribute
+ *   their float value before rounding to the cache dtype, keys already cached their stored
+ *   value).
+ * k_new, v_new: [B, n_q, Hkv, d]; k_cache, v_cache: [B, Hkv, kv_capacity, d];
+ * k_pool: [B, Hkv, kv_capacity / 64, d] float; k_norm_w: [d] float or NULL. */
+sala_status sala_kv_append(const sala_sparse_desc* desc, const void* k_new, const void* v_new,
+                           const float* k_norm_w, void* k_cache, void* v_cache, float* k_pool,
+                           void* stream);
+
+/* Rebuild pooled keys from the cache contents: k_pool[b, g, j, :] = mean over the block's 64
+ * cached keys, for blocks j in [block_begin, block_end), all of which must be complete
+ * (block_end * 64 <= kv_len). For caches filled outside sala_kv_append (restored state). */
+sala_status sala_kv_pool(const sala_sparse_desc* desc, const void* k_cache, float* k_pool,
+                         int64_t block_begin, int64_t block_end, void* stream);
+
+/* Block selection for the sparse layer (same pages; sliding-window and global-anchor patterns
+ * from "MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模" §1). For each query block i covered by
+ * the call (decode: the block of the single query) and KV group g:
+ *   q~[g, i] = sum over the group's heads h of mean over the block's query tokens of
+ *              RMSNorm(q[t, h]) * q_norm_w          (decode: the single token, no mean)
+ *   score[j] = q~[g, i] . k_pool[g, j] for candidate blocks j in [1, i - n_local]
+ *   forced   = {0} U {i - n_local + 1 .. i}; keep the topk - |forced| best candidates,
+ *              ranked by score descending then block index ascending (ties: lowest index).
+ * Output sel: [B, Hkv, nqb, topk] int32, ascending block indices, padded with -1, where
+ * nqb = (kv_len - 1) / 64 - (kv_len - n_q) / 64 + 1 (row r is query block
+ * (kv_len - n_q) / 64 + r). Scores are fp32. q: [B, n_q, Hq, d]; k_pool as in sala_kv_append.
+ * Workspace: sala_workspace_bytes(SALA_OP_BLOCK_SELECT, desc). */
+sala_status sala_block_select(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                              const float* k_pool, int32_t* sel, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Block-sparse softmax attention with output gate (same pages). For each query token t (at
+ * position p) and head h in KV group g, with i = p / 64:
+ *   keys    = tokens s <= p of the blocks listed in sel[b, g, i - first_block, :] (-1 ignored)
+ *   out[t,h] = softmax_s(scale * q^ . k_cache[s]) . v_cache[s] * sigmoid(gate[t, h])
+ * where q^ = RMSNorm(q) * q_norm_w and the cache holds already-normalised keys. The bf16 path
+ * uses MFMA (bf16 operands, fp32 accumulation and fp32 online softmax).
+ * q, gate, out: [B, n_q, Hq, d]; caches as in sala_kv_append; sel as from sala_block_select.
+ * Workspace: sala_workspace_bytes(SALA_OP_SPARSE_ATTN, desc). */
+sala_status sala_sparse_attn(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                             const void* k_cache, const void* v_cache, const void* gate,
+                             const int32_t* sel, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Workspace bytes an operation needs for this descriptor (0 if none; SIZE_MAX if the
+ * descriptor is invalid). `desc` points to a sala_linear_desc for SALA_OP_LINEAR_PREFILL and
+ * to a sala_sparse_desc otherwise. */
+size_t sala_workspace_bytes(int op, const void* desc);
+
+const char* sala_status_str(sala_status status);
+int sala_abi_version(void);
+/* hipError_t of the last SALA_ERR_HIP on the calling thread (0 if none). */
+int sala_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SALA_H_ */

@@ -1,0 +1,68 @@
+"""Helpers shared by the GPU parity tests: device transfer, the tolerance rule and the
+selection margin rule. Holds no arithmetic of the method."""
+
+import numpy as np
+
+import oracle as O
+
+MARGIN = 1e-3
+
+
+def dev(x, dtype):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def host(t):
+    import torch
+
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def assert_rel(gpu, ref, tol, what=""):
+    """max |gpu - ref| <= tol * max |ref| (the acceptance rule for floating point)."""
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite values"
+    err = np.max(np.abs(gpu - ref)) if ref.size else 0.0
+    scale = np.max(np.abs(ref)) if ref.size else 0.0
+    assert err <= tol * scale, f"{what}: max err {err:.3e} > {tol} * {scale:.3e}"
+    return err / max(scale, 1e-300)
+
+
+def check_selection(gpu_sel, ref_sel, scores_fn, topk, n_local, first_block=0):
+    """Bit-exact selection, except rows whose r-th / (r+1)-th candidate scores are closer than
+    MARGIN: there every GPU-chosen candidate must score >= s_r - MARGIN and the forced blocks,
+    ordering and padding must still be exact. scores_fn(b, g, i) -> oracle candidate scores
+    (index j -> score) for query block i. Returns the number of rows accepted by the margin rule.
+    """
+    gpu_sel = np.asarray(gpu_sel)
+    ref_sel = np.asarray(ref_sel)
+    assert gpu_sel.shape == ref_sel.shape
+    B, G, R, K = gpu_sel.shape
+    by_margin = 0
+    for b in range(B):
+        for g in range(G):
+            for r in range(R):
+                a, e = gpu_sel[b, g, r].tolist(), ref_sel[b, g, r].tolist()
+                if a == e:
+                    continue
+                i = first_block + r
+                # structure: ascending, forced present, same count, -1 padded
+                va = [x for x in a if x >= 0]
+                assert va == sorted(set(va)) and a[len(va):] == [-1] * (K - len(va)), (b, g, i, a)
+                assert len(va) == len([x for x in e if x >= 0]), (b, g, i, a, e)
+                forced = {0} | set(range(max(0, i - n_local + 1), i + 1))
+                assert forced <= set(va), (b, g, i, a)
+                sc = scores_fn(b, g, i)
+                cands = list(range(1, i - n_local + 1))
+                ranked = sorted(cands, key=lambda j: (-sc[j], j))
+                rr = topk - len(forced)
+                s_r, s_r1 = sc[ranked[rr - 1]], sc[ranked[rr]]
+                assert s_r - s_r1 < MARGIN, f"row {(b, g, i)}: selections differ with margin {s_r - s_r1}"
+                for j in set(va) - forced:
+                    assert sc[j] >= s_r - MARGIN, (b, g, i, j, sc[j], s_r)
+                by_margin += 1
+    return by_margin

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point declared in
+include/sala.h, and rejects bad arguments before anything is enqueued (these paths make no
+HIP call, so they run on a CPU-only host)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+LIB = os.path.join(ROOT, "hybrid_sparse_linear_causal_amd", "libsala.so")
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsala.so not built")
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "sala.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sala_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    names = declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    assert L.sala_abi_version() == 1
+    for code in range(6):
+        assert L.sala_status_str(code)
+    assert L.sala_last_hip_error() == 0
+
+
+def _lin(**kw):
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    base = dict(batch=1, seq_len=128, n_heads=2, n_kv_heads=2, head_dim=128, dtype=S.SALA_BF16,
+                pos0=0, rope_base=10000.0, norm_eps=1e-6)
+    base.update(kw)
+    return S.LinearDesc(**base)
+
+
+def _sp(**kw):
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    base = dict(batch=1, n_q=128, n_heads=4, n_kv_heads=2, head_dim=128, dtype=S.SALA_BF16, block=64,
+                topk=8, n_local=2, norm_eps=1e-6, scale=0.0, reserved_=0, kv_len=128, kv_capacity=128)
+    base.update(kw)
+    return S.SparseDesc(**base)
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(batch=0), 2), (dict(seq_len=-1), 2), (dict(head_dim=96), 3), (dict(dtype=7), 2),
+    (dict(n_kv_heads=1), 3), (dict(n_kv_heads=3), 2), (dict(rope_base=0.0), 2),
+    (dict(norm_eps=-1.0), 2), (dict(pos0=-5), 2), (dict(head_dim=64), 3),
+])
+def test_linear_prefill_rejects(kw, expect):
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    d = _lin(**kw)
+    st = S.lib().sala_linear_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, None,
+                                     FAKE, FAKE, 1 << 30, None)
+    assert st == expect
+
+
+def test_linear_prefill_null_and_alignment_and_workspace():
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = _lin(seq_len=1 << 16, n_heads=32, n_kv_heads=32)
+    assert L.sala_linear_prefill(None, FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE, FAKE, 0, None) == 1
+    assert L.sala_linear_prefill(ctypes.byref(d), None, FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                 FAKE, 1 << 40, None) == 1
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert L.sala_linear_prefill(ctypes.byref(d), odd, FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                 FAKE, 1 << 40, None) == 2
+    need = S.workspace_bytes(S.OP_LINEAR_PREFILL, d)
+    assert need > 0
+    assert L.sala_linear_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                 FAKE, need - 1, None) == 4
+    assert L.sala_linear_prefill(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                 None, need, None) == 4
+
+
+def test_linear_decode_rejects():
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = _lin(seq_len=2)
+    assert L.sala_linear_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None) == 2
+    d = _lin(seq_len=1)
+    assert L.sala_linear_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(block=32), 3), (dict(n_local=3), 3), (dict(topk=2), 2), (dict(topk=257), 2),
+    (dict(n_heads=3), 2), (dict(kv_len=100, n_q=128), 2), (dict(kv_capacity=100, kv_len=100, n_q=100), 2),
+    (dict(kv_capacity=192, kv_len=160, n_q=128), 2), (dict(head_dim=80), 3), (dict(scale=-1.0), 2),
+    (dict(n_heads=128, n_kv_heads=2), 3), (dict(n_q=0), 2),
+])
+def test_sparse_rejects(kw, expect):
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = _sp(**kw)
+    assert L.sala_kv_append(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == expect
+    assert L.sala_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == expect
+    assert L.sala_sparse_attn(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                              None) == expect
+    assert L.sala_workspace_bytes(S.OP_BLOCK_SELECT, ctypes.byref(d)) == ctypes.c_size_t(-1).value
+
+
+def test_sparse_null_workspace_and_pool_range():
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = _sp()
+    assert L.sala_block_select(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    need = S.workspace_bytes(S.OP_BLOCK_SELECT, d)
+    assert need > 0
+    assert L.sala_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == 4
+    assert L.sala_kv_pool(ctypes.byref(d), FAKE, FAKE, 0, 3, None) == 2  # 3*64 > kv_len
+    assert L.sala_kv_pool(ctypes.byref(d), FAKE, FAKE, 2, 1, None) == 2
+    assert L.sala_kv_pool(ctypes.byref(d), None, FAKE, 0, 1, None) == 1
+    dd = _sp(n_q=1, kv_len=1000, kv_capacity=1024, n_heads=64, n_kv_heads=2)  # bf16 decode, group 32
+    assert L.sala_sparse_attn(ctypes.byref(dd), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                              None) == 3
+    assert S.workspace_bytes(S.OP_SPARSE_ATTN, _sp(n_q=1, kv_len=1000, kv_capacity=1024)) > 0
