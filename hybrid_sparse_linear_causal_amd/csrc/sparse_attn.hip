@@ -33,54 +33,165 @@ constexpr int VS = 64 + 8;   // V^T tile row stride (bf16): 144 B
 constexpr float RESCALE_TH = 8.0f;  // log2 units
 constexpr int DEC_SPLIT = 16;       // decode workgroups per (b, g)
 
-struct AttnLds {
-  bf16_t k[64 * KS];
-  bf16_t vt[D * VS];
-};
+// LDS tile of one 64-key block: 64 rows x 256 B, 16-byte chunk c of row r stored at chunk
+// position c ^ (r & 15) so that 16 rows read at the same column hit 16 different bank groups.
+constexpr int TILE = 64 * 128;  // bf16 elements per tile
+constexpr int NSTAGE = 3;       // LDS ring depth (blocks in flight)
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + 8 * (chunk ^ (row & 15)); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16 lanes, lane i
+// supplies the address of 4 consecutive bf16; lane j receives element j%4 of the chunks of
+// lanes j/4 + 4e, e = 0..3. With lane i pointing at row k0 + i/4, columns c0 + 4*(i%4), lane j
+// receives column c0 + j of rows k0 .. k0+3: four consecutive-k values of one MFMA column.
+__device__ __forceinline__ uint2 ds_read_tr(const bf16_t* p) {
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  return __builtin_bit_cast(uint2, r);
+}
 
 __device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
   const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// Stage one 64-key block: K rows as-is, V transposed to [dv][key]. Thread j: K rows j/16+16m,
-// V keys 4*(j/16)+u, 16-byte segment j%16 (8 dims). Rows at or beyond kv_len are zero.
-struct BlockRegs {
-  uint4 k[4], v[4];
-};
-__device__ __forceinline__ void load_block(BlockRegs& r, const bf16_t* kc, const bf16_t* vc,
-                                           long row_base, long blk, long kv_len) {
-  const int j = threadIdx.x, seg = j & 15, kg = j >> 4;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const long pk = blk * 64 + kg + 16 * m;
-    r.k[m] = pk < kv_len ? *reinterpret_cast<const uint4*>(kc + (row_base + pk) * D + 8 * seg) : z;
-    const long pv = blk * 64 + 4 * kg + m;
-    r.v[m] = pv < kv_len ? *reinterpret_cast<const uint4*>(vc + (row_base + pv) * D + 8 * seg) : z;
-  }
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane l's
+// chunk lands at LDS byte address lds_addr + 16 * l. Issued from inline assembly so that the
+// compiler does not serialise it with unrelated LDS reads; it has no register outputs, and
+// completion is awaited explicitly with s_waitcnt vmcnt before the barrier that publishes it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
+               : "memory", "m0");
 }
-__device__ __forceinline__ void store_block(const BlockRegs& r, AttnLds& L) {
-  const int j = threadIdx.x, seg = j & 15, kg = j >> 4;
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Issue the DMA of one 64-key block (K and V tiles, 16 KB each = 16 pieces of 1 KB) into a
+// stage. With 8 waves each wave moves pieces 2w and 2w+1 (rows 8w .. 8w+7) of both tiles:
+// DMA_PER_WAVE instructions. Rows at or beyond kv_len are clamped to the last valid row: they
+// are causally masked (K) or weighted 0 (V).
+constexpr int DMA_PER_WAVE = 4;
+__device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, long row_base,
+                                          long blk, long kv_len, bf16_t* Ks, bf16_t* Vs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) *reinterpret_cast<uint4*>(&L.k[(kg + 16 * m) * KS + 8 * seg]) = r.k[m];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint2 w;
-    w.x = bf_half(r.v[0], e) | (bf_half(r.v[1], e) << 16);
-    w.y = bf_half(r.v[2], e) | (bf_half(r.v[3], e) << 16);
-    *reinterpret_cast<uint2*>(&L.vt[(8 * seg + e) * VS + 4 * kg]) = w;
+  for (int m = 0; m < 2; ++m) {
+    const int I = 2 * wave + m;                 // 1 KB piece: rows 4I .. 4I+3
+    const int row = 4 * I + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);    // source chunk stored at swizzled position
+    long p = blk * 64 + row;
+    if (p >= kv_len) p = kv_len - 1;
+    const long off = (row_base + p) * D + 8 * ch;
+    dma16(kc + off, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Ks + I * 512)));
+    dma16(vc + off, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Vs + I * 512)));
   }
 }
 
-// grid: B*Hkv*nqb*ceil(G/4) workgroups of 256 threads
-__global__ void __launch_bounds__(256)
+// A operand V^T (rows dv = 16*dt + l16, k = keys in the permuted order of the P^T fragments:
+// slots 0..3 = keys kb + 4*lq + e, slots 4..7 = keys kb + 16 + 4*lq + e) via two
+// transposing reads. Source lane (i = l16) points at key row kb(+16) + 4*lq + i/4, columns
+// 16*dt + 4*(i%4).
+__device__ __forceinline__ bf16x8 vt_frag(const bf16_t* Vs, int kb, int dt, int l16, int lq) {
+  const int row0 = kb + 4 * lq + (l16 >> 2);
+  const int col = 16 * dt + 4 * (l16 & 3);          // element column; chunk = col / 8
+  const int ch = col >> 3, sub = col & 7;
+  const uint2 a = ds_read_tr(Vs + swz(row0, ch) + sub);
+  const uint2 b = ds_read_tr(Vs + swz(row0 + 16, ch) + sub);
+  return as_bf16x8(a, b);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One wave's work on one staged 64-key block for its QT x 16 query rows (rows qrow0 + 16*qt
+// + l16 of the query block): S^T = K Q^T, online softmax (lazy rescale), O^T += V^T P^T.
+// diag masks keys after the query (the query's own block).
+template <int QT>
+__device__ __forceinline__ void attend_block(const bf16_t* Ks, const bf16_t* Vs, const bf16x8 (&qf)[QT][4],
+                                             f32x4 (&OT)[8][QT], float (&m)[QT], float (&lp)[QT],
+                                             int l16, int lq, int qrow0, bool diag) {
+  f32x4 ST[4][QT];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + swz(16 * kt + l16, 4 * ks + lq)));
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ST[kt][qt]);
+    }
+  }
+  if (diag) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (16 * kt + 4 * lq + c > qrow0 + 16 * qt + l16) ST[kt][qt][c] = -INFINITY;
+  }
+  // the running maximum moves only when a row maximum exceeds it by more than RESCALE_TH
+  // (log2 units), so exp2 arguments stay <= RESCALE_TH and the output is rarely rescaled
+  bool any_need = false;
+  float mn[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float mx = fmaxf(fmaxf(ST[0][qt][0], ST[0][qt][1]), fmaxf(ST[0][qt][2], ST[0][qt][3]));
+#pragma unroll
+    for (int kt = 1; kt < 4; ++kt)
+      mx = fmaxf(mx, fmaxf(fmaxf(ST[kt][qt][0], ST[kt][qt][1]), fmaxf(ST[kt][qt][2], ST[kt][qt][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool need = mx > m[qt] + RESCALE_TH;
+    mn[qt] = need ? mx : m[qt];
+    any_need |= need;
+  }
+  if (__any(any_need)) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float alpha = fast_exp2(m[qt] - mn[qt]);
+      lp[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) OT[dt][qt] *= alpha;
+      m[qt] = mn[qt];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    bf16x8 pf[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float p[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = fast_exp2(ST[2 * c][qt][u] - m[qt]);
+        p[4 + u] = fast_exp2(ST[2 * c + 1][qt][u] - m[qt]);
+      }
+      lp[qt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pf[qt] = as_bf16x8(pack8(p));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x8 a = vt_frag(Vs, 32 * c, dt, l16, lq);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) OT[dt][qt] = mfma16x16x32(a, pf[qt], OT[dt][qt]);
+    }
+  }
+}
+
+// grid: B*Hkv*nqb*ceil(G/4) workgroups of 512 threads (8 waves: 4 heads x 2 row halves)
+constexpr int PF_THREADS = 512;
+constexpr int PF_QT = 2;  // 16-row query tiles per wave
+__global__ void __launch_bounds__(PF_THREADS)
 sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
                            const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
                            const bf16_t* __restrict__ g, const int32_t* __restrict__ sel,
                            bf16_t* __restrict__ out, int n_q, int Hq, int Hkv, long q0, long qb0,
                            int nqb, long kv_len, long cap, int topk, float eps, float qscale) {
-  __shared__ __align__(16) AttnLds L;
+  __shared__ __align__(16) bf16_t lds[NSTAGE][2][TILE];  // [stage][K|V]
+  __shared__ int s_sel[256];
   const int G = Hq / Hkv, nhq = (G + 3) / 4;
   // XCD-aware order: workgroup x runs on XCD x % 8; give each XCD a contiguous run of work
   const unsigned nwg = gridDim.x;
@@ -93,18 +204,20 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   const int gk = rest % Hkv, b = rest / Hkv;
 
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
-  const int hl = 4 * hq + wave;
+  const int hl = 4 * hq + (wave >> 1);
+  const int qrow0 = 32 * (wave & 1);  // this wave's first query row in the block
   const bool head_ok = hl < G;
   const int h = gk * G + (head_ok ? hl : 0);
   const long i = qb0 + r;
   const long row_base = ((long)b * Hkv + gk) * cap;
   const int32_t* srow = sel + (((long)b * Hkv + gk) * nqb + r) * topk;
+  if (j < topk) s_sel[j] = srow[j];
 
   // ---- Q^T fragments (B operand: k = dim, n = query); normalised, scaled by scale*log2(e)
-  bf16x8 qf[4][4];
+  bf16x8 qf[PF_QT][4];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const long t = i * 64 + 16 * qt + l16 - q0;
+  for (int qt = 0; qt < PF_QT; ++qt) {
+    const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
     const bool ok = head_ok && t < n_q;
     float x[4][8];
     float ss = 0.f;
@@ -118,114 +231,65 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    const float inv = qscale / sqrtf(ss * (1.0f / D) + eps);
+    const float inv = qscale * __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = x[ks][e] * inv * (qw ? qw[32 * ks + 8 * lq + e] : 1.0f);
-      qf[qt][ks] = as_bf16x8(pack8(y));
+      uint4 u = pack8(y);
+      // opaque to the optimiser: keep the packed fragment instead of recomputing it per block
+      asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+      qf[qt][ks] = as_bf16x8(u);
     }
   }
-
+  __syncthreads();
   int nsel = 0;
-  while (nsel < topk && srow[nsel] >= 0) ++nsel;
+  while (nsel < topk && s_sel[nsel] >= 0) ++nsel;
 
-  float m[4], lp[4];
-  f32x4 OT[8][4];
+  float m[PF_QT], lp[PF_QT];
+  f32x4 OT[8][PF_QT];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) { m[qt] = -INFINITY; lp[qt] = 0.f; }
+  for (int qt = 0; qt < PF_QT; ++qt) { m[qt] = -INFINITY; lp[qt] = 0.f; }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) OT[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < PF_QT; ++qt) OT[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  BlockRegs br;
-  if (nsel > 0) load_block(br, kc, vc, row_base, srow[0], kv_len);
+  dma_block(kc, vc, row_base, s_sel[0], kv_len, lds[0][0], lds[0][1]);
+  if (nsel > 1) {
+    dma_block(kc, vc, row_base, s_sel[1], kv_len, lds[1][0], lds[1][1]);
+    wait_vmcnt<DMA_PER_WAVE>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+
+  int st = 0;
   for (int e = 0; e < nsel; ++e) {
-    const long blk = srow[e];
+    // block e+2 goes into the stage that held block e-1 (released by the last barrier)
+    if (e + 2 < nsel) {
+      const int s2 = st == 0 ? 2 : st - 1;
+      dma_block(kc, vc, row_base, s_sel[e + 2], kv_len, lds[s2][0], lds[s2][1]);
+    }
+    // the selection is ascending and always holds the query's own block i, so the causal
+    // diagonal block is the last one
+    attend_block<PF_QT>(lds[st][0], lds[st][1], qf, OT, m, lp, l16, lq, qrow0, e + 1 == nsel);
+    // block e+1 must have landed (only block e+2's copies may still be in flight)
+    if (e + 2 < nsel) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();
     __syncthreads();
-    store_block(br, L);
-    __syncthreads();
-    if (e + 1 < nsel) load_block(br, kc, vc, row_base, srow[e + 1], kv_len);
-    if (!head_ok) continue;
-
-    // S^T[kt][qt] = K[kt] Q^T[qt]
-    f32x4 ST[4][4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) ST[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&L.k[(16 * kt + l16) * KS + 32 * ks + 8 * lq]));
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ST[kt][qt]);
-      }
-    }
-    if (blk == i) {  // diagonal block: key after query is masked
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (16 * kt + 4 * lq + c > 16 * qt + l16) ST[kt][qt][c] = -INFINITY;
-    }
-    // online softmax with lazy rescaling
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      float mx = ST[0][qt][0];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, ST[kt][qt][c]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool need = mx > m[qt] + RESCALE_TH;
-      if (__any(need)) {
-        const float mn = need ? mx : m[qt];
-        const float alpha = exp2f(m[qt] - mn);
-        lp[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) OT[dt][qt] *= alpha;
-        m[qt] = mn;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 pf[4];
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        float p[8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          p[u] = exp2f(ST[2 * c][qt][u] - m[qt]);
-          p[4 + u] = exp2f(ST[2 * c + 1][qt][u] - m[qt]);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) lp[qt] += p[u];
-        pf[qt] = as_bf16x8(pack8(p));
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16_t* vr = &L.vt[(16 * dt + l16) * VS + 32 * c + 4 * lq];
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + 16));
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) OT[dt][qt] = mfma16x16x32(a, pf[qt], OT[dt][qt]);
-      }
-    }
+    st = st == NSTAGE - 1 ? 0 : st + 1;
   }
   if (!head_ok) return;
 
-  // ---- normalise, gate, store (lane: query 16qt + l16, dims 16dt + 4lq .. +3)
+  // ---- normalise, gate, store (lane: query qrow0 + 16qt + l16, dims 16dt + 4lq .. +3)
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < PF_QT; ++qt) {
     float l = lp[qt];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const float il = 1.0f / l;
-    const long t = i * 64 + 16 * qt + l16 - q0;
+    const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
     if (t >= n_q) continue;
     const long base = ((long)(b * (long)n_q + t) * Hq + h) * D;
 #pragma unroll
@@ -520,7 +584,7 @@ hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const fl
     return hipGetLastError();
   }
   const long nwg = (long)d.batch * d.n_kv_heads * gm.nqb * ((G + 3) / 4);
-  hipLaunchKernelGGL(sparse_prefill_bf16_kernel, dim3((unsigned)nwg), dim3(256), 0, st, (const bf16_t*)q,
+  hipLaunchKernelGGL(sparse_prefill_bf16_kernel, dim3((unsigned)nwg), dim3(PF_THREADS), 0, st, (const bf16_t*)q,
                      qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
                      (bf16_t*)out, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0,
                      (int)gm.nqb, (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, qscale);
