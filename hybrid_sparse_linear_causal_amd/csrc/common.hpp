@@ -94,4 +94,51 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+
+// ---- LDS tiles of 256-byte rows (64 or 128 bf16): 16-byte chunk c of row r is stored at chunk
+// position c ^ (r & 15), so 16 rows read at one column land in 16 different bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + 8 * (chunk ^ (row & 15)); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16 lanes, lane i
+// supplies the address of 4 consecutive bf16; lane j receives element j%4 of the chunks of
+// lanes j/4 + 4e, e = 0..3. With lane i pointing at row k0 + i/4, columns c0 + 4*(i%4), lane j
+// receives column c0 + j of rows k0 .. k0+3: four consecutive-k values of one MFMA column.
+__device__ __forceinline__ uint2 ds_read_tr(const bf16_t* p) {
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+// MFMA operand "column j = c0 + l16, k = rows k0 + 0..7" of a row-major swizzled tile, k0 and
+// c0 multiples of 4: two transposing reads (rows k0..k0+3, then k0+d1..k0+d1+3).
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* T, int k0, int d1, int c0, int l16) {
+  const int row = k0 + (l16 >> 2), col = c0 + 4 * (l16 & 3);
+  const uint2 a = ds_read_tr(T + swz(row, col >> 3) + (col & 7));
+  const uint2 b = ds_read_tr(T + swz(row + d1, col >> 3) + (col & 7));
+  return as_bf16x8(a, b);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane l's
+// chunk lands at LDS byte address lds_addr + 16 * l (lds_addr wave-uniform). Issued from inline
+// assembly so that the compiler does not serialise it with unrelated LDS reads; it has no
+// register outputs, and completion is awaited with wait_vmcnt before the barrier that
+// publishes the data.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr_u32(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)p);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// logistic function from hardware exp2 and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float fast_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
 }  // namespace sala

@@ -13,14 +13,22 @@ typedef uint16_t bf16_t;
 
 // RoPE frequencies in revolutions per position, f_i = base^(-2i/d) / (2 pi), i < d/2,
 // computed on the host in double precision and passed by value to the kernels.
+// c64/s64: cos and sin of the rotation by 64 positions (64 * theta_i), used to advance a
+// table of angles from one 64-token chunk to the next.
 struct RopeFreqs {
   double f[64];
+  float c64[64], s64[64];
 };
 
 inline RopeFreqs make_rope_freqs(int d, float base) {
   RopeFreqs r;
-  for (int i = 0; i < 64; ++i)
-    r.f[i] = (i < d / 2) ? pow((double)base, -2.0 * i / d) / 6.283185307179586476925286766559 : 0.0;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < 64; ++i) {
+    const double theta = (i < d / 2) ? pow((double)base, -2.0 * i / d) : 0.0;
+    r.f[i] = theta / two_pi;
+    r.c64[i] = (float)cos(fmod(64.0 * theta, two_pi));
+    r.s64[i] = (float)sin(fmod(64.0 * theta, two_pi));
+  }
   return r;
 }
 

@@ -26,38 +26,32 @@ namespace sala {
 
 namespace {
 
-constexpr int D = 128;        // head dim of the bf16 MFMA path
-constexpr int CH = 64;        // chunk length (tokens)
-constexpr int NT = 256;       // threads per workgroup (4 waves)
-constexpr int QS = D + 8;     // LDS row stride (bf16) of token-major tiles: 272 B
-constexpr int TS = CH + 8;    // LDS row stride (bf16) of feature-major tiles: 144 B
-constexpr int SS = D + 8;     // LDS row stride (bf16) of the transposed state
-constexpr int OS = D + 4;     // LDS row stride (fp32) of the output staging tile
+constexpr int D = 128;   // head dim of the bf16 MFMA path
+constexpr int CH = 64;   // chunk length (tokens)
+constexpr int NT = 256;  // threads per workgroup (4 waves)
 
+// 80 KB: two workgroups fit in one CU's 160 KB. All tiles are row-major with 256-byte rows in
+// the swizzled layout of swz(); column operands along the token axis come from transposing
+// reads, so nothing is ever transposed in registers.
 struct LinearLds {
-  bf16_t q[CH * QS];    // q~  [token][dk]
-  bf16_t k[CH * QS];    // k~  [token][dk]
-  bf16_t kt[D * TS];    // k~^T [dk][token]
-  bf16_t vt[D * TS];    // v^T  [dv][token]
-  bf16_t st[D * SS];    // S^T  [dv][dk] as bf16 (state entering the chunk)
-  float o[CH * OS];     // output staging [token][dv]
-};
-
-// Raw chunk data held in registers by thread j: tokens 2*(j/8) + {0,1}, 16-byte segments
-// s = j%8 and s+8 (dims 8s..8s+7 and 64+8s..64+8s+7, which RoPE pairs with each other).
-struct ChunkRegs {
-  uint4 q[2][2], k[2][2], v[2][2], g[2][2];
+  bf16_t q[CH * D];   // q~  [token][dk]
+  bf16_t k[CH * D];   // k~  [token][dk]
+  bf16_t v[CH * D];   // v   [token][dv] (DMA copy of the input rows)
+  bf16_t st[D * D];   // S^T [dv][dk] as bf16: the state entering the chunk
 };
 
 __device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Raw q and k of thread j's two tokens 2*(j/8) + u, 16-byte segments s = j%8 and s+8 (dims
+// 8s..8s+7 and 64+8s..64+8s+7, which RoPE pairs with each other).
+struct QKRegs {
+  uint4 q[2][2], k[2][2];
+};
+
 template <bool STATE_ONLY>
-__device__ __forceinline__ void load_chunk(ChunkRegs& r, const bf16_t* q, const bf16_t* k,
-                                           const bf16_t* v, const bf16_t* g, long row0, int t0,
-                                           int n_valid, int H) {
-  // row0 = element offset of (b, token 0 of the chunk, h, 0); token stride = H * D
-  const int j = threadIdx.x;
-  const int s = j & 7;
+__device__ __forceinline__ void load_qk(QKRegs& r, const bf16_t* q, const bf16_t* k, long row0,
+                                        int t0, int n_valid, int H) {
+  const int j = threadIdx.x, s = j & 7;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int t = 2 * (j >> 3) + u;
@@ -68,63 +62,55 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& r, const bf16_t* q, const 
       const int off = 8 * (s + 8 * hs);
       const uint4 z = make_uint4(0, 0, 0, 0);
       r.k[u][hs] = ok ? ld16(k + base + off) : z;
-      r.v[u][hs] = ok ? ld16(v + base + off) : z;
-      if (!STATE_ONLY) {
-        r.q[u][hs] = ok ? ld16(q + base + off) : z;
-        r.g[u][hs] = ok ? ld16(g + base + off) : z;
-      }
+      if (!STATE_ONLY) r.q[u][hs] = ok ? ld16(q + base + off) : z;
     }
   }
 }
 
+// V tile of one chunk by DMA: wave w copies rows 16w .. 16w+15 (four 1 KB pieces). Rows past
+// the end of the sequence are clamped to its last row: their k~ rows are zero, so they add
+// exactly nothing, and a finite copy keeps 0 * v finite.
+__device__ __forceinline__ void dma_v(const bf16_t* v, long row0, int t0, int n_valid, int H,
+                                      bf16_t* Vs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int I = 4 * wave + m;
+    const int row = 4 * I + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);
+    const int t = min(t0 + row, n_valid - 1) - t0;
+    dma16(v + row0 + (long)t * H * D + 8 * ch, lds_addr_u32(Vs + I * 512));
+  }
+}
+
 // QK-norm + RoPE of one token's 16 values held by this thread (two 8-dim halves that RoPE
-// pairs), given the 8 angles' sin/cos. Row sum of squares is reduced over the 8 lanes of the
-// token. Writes the rotated bf16 values into x (as packed uint4).
+// pairs), given the cos/sin of its 8 angles. The row's sum of squares is reduced over the 8
+// lanes of the token. Returns the rotated values packed to bf16 in x.
 __device__ __forceinline__ void norm_rope(uint4 (&x)[2], const float* w, int s, float eps,
-                                          const float* sn, const float* cs) {
+                                          const float* cs, const float* sn) {
   float a[8], b[8];
   unpack8(x[0], a);
   unpack8(x[1], b);
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ss += a[e] * a[e] + b[e] * b[e];
+  for (int e = 0; e < 8; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
   ss = group_sum<8>(ss);
-  const float inv = 1.0f / sqrtf(ss * (1.0f / D) + eps);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
   float ra[8], rb[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float xa = a[e] * inv, xb = b[e] * inv;
+    float xa = a[e], xb = b[e];
     if (w) { xa *= w[8 * s + e]; xb *= w[64 + 8 * s + e]; }
-    ra[e] = xa * cs[e] - xb * sn[e];
-    rb[e] = xa * sn[e] + xb * cs[e];
+    const float c = cs[e] * inv, sg = sn[e] * inv;
+    ra[e] = xa * c - xb * sg;
+    rb[e] = xa * sg + xb * c;
   }
   x[0] = pack8(ra);
   x[1] = pack8(rb);
 }
 
-// write 16 bf16 values of one token (dims 8s..8s+7, 64+8s..) as 2-byte entries of a
-// feature-major tile T[dim][token] (pairs of tokens packed into one 32-bit store)
-__device__ __forceinline__ void store_T_pair(bf16_t* T, int t_even, int s, const uint4 (&x0)[2],
-                                             const uint4 (&x1)[2]) {
-  // x0: token t_even, x1: token t_even + 1
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    const uint32_t a[4] = {x0[hs].x, x0[hs].y, x0[hs].z, x0[hs].w};
-    const uint32_t b[4] = {x1[hs].x, x1[hs].y, x1[hs].z, x1[hs].w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int dim = 8 * (s + 8 * hs) + 2 * w;
-      // low halves: dim, high halves: dim + 1
-      const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
-      const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(T + dim * TS + t_even) = lo;
-      *reinterpret_cast<uint32_t*>(T + (dim + 1) * TS + t_even) = hi;
-    }
-  }
-}
-
 template <bool STATE_ONLY>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, 2)
 linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ g,
                     const float* __restrict__ qw, const float* __restrict__ kw,
@@ -163,69 +149,63 @@ linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           S[it][jt][e] = src ? src[dk * D + dv] : 0.f;
         }
   }
+
+  // ---- RoPE table: cos/sin of this thread's 8 frequencies at its 2 token offsets, exact at
+  // the segment start (fp64 range reduction) and advanced by a fixed rotation of 64 positions
+  // per chunk.
+  float rc[2][8], rs[2][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double f = freqs.f[8 * s8 + e];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      sincos_rev(rope_rev((double)(pos0 + t_begin + 2 * tp + u), f), &rs[u][e], &rc[u][e]);
+  }
+
+  QKRegs cur;
+  load_qk<STATE_ONLY>(cur, q, k, head_off + (long)t_begin * tok_stride, t_begin, N, H);
+  dma_v(v, head_off + (long)t_begin * tok_stride, t_begin, N, H, L.v);
   if (!STATE_ONLY) {
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
-        const int dk0 = 32 * wave + 16 * it + 4 * lq, dv = 16 * jt + l16;
         uint2 p;
         p.x = pack_bf16x2(S[it][jt][0], S[it][jt][1]);
         p.y = pack_bf16x2(S[it][jt][2], S[it][jt][3]);
-        *reinterpret_cast<uint2*>(&L.st[dv * SS + dk0]) = p;
+        const int dk0 = 32 * wave + 16 * it + 4 * lq, dv = 16 * jt + l16;
+        *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
       }
   }
 
-  // frequencies (revolutions per position) of this thread's 8 RoPE pairs
-  double fr[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) fr[e] = freqs.f[8 * s8 + e];
-
-  ChunkRegs cur;
-  load_chunk<STATE_ONLY>(cur, q, k, v, g, head_off + (long)t_begin * tok_stride, t_begin, N, H);
-
   for (int c0 = t_begin; c0 < t_end; c0 += CH) {
-    // ---------------- prep: QK-norm + RoPE, stage tiles in LDS
-    {
+    // ---------------- prep: QK-norm + RoPE into the q~ / k~ tiles
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = 2 * tp + u;
-        const double p = (double)(pos0 + c0 + t);
-        float sn[8], cs[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sincos_rev(rope_rev(p, fr[e]), &sn[e], &cs[e]);
-        norm_rope(cur.k[u], kw, s8, eps, sn, cs);
-        if (!STATE_ONLY) {
-          norm_rope(cur.q[u], qw, s8, eps, sn, cs);
-          *reinterpret_cast<uint4*>(&L.q[t * QS + 8 * s8]) = cur.q[u][0];
-          *reinterpret_cast<uint4*>(&L.q[t * QS + 64 + 8 * s8]) = cur.q[u][1];
-          *reinterpret_cast<uint4*>(&L.k[t * QS + 8 * s8]) = cur.k[u][0];
-          *reinterpret_cast<uint4*>(&L.k[t * QS + 64 + 8 * s8]) = cur.k[u][1];
-        }
+    for (int u = 0; u < 2; ++u) {
+      const int t = 2 * tp + u;
+      norm_rope(cur.k[u], kw, s8, eps, rc[u], rs[u]);
+      *reinterpret_cast<uint4*>(&L.k[swz(t, s8)]) = cur.k[u][0];
+      *reinterpret_cast<uint4*>(&L.k[swz(t, s8 + 8)]) = cur.k[u][1];
+      if (!STATE_ONLY) {
+        norm_rope(cur.q[u], qw, s8, eps, rc[u], rs[u]);
+        *reinterpret_cast<uint4*>(&L.q[swz(t, s8)]) = cur.q[u][0];
+        *reinterpret_cast<uint4*>(&L.q[swz(t, s8 + 8)]) = cur.q[u][1];
       }
-      store_T_pair(L.kt, 2 * tp, s8, cur.k[0], cur.k[1]);
-      store_T_pair(L.vt, 2 * tp, s8, cur.v[0], cur.v[1]);
     }
-    uint4 gk[2][2];
-    if (!STATE_ONLY) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) { gk[u][0] = cur.g[u][0]; gk[u][1] = cur.g[u][1]; }
-    }
+    wait_vmcnt<0>();  // this chunk's V tile has landed
     __syncthreads();
-    // prefetch the next chunk while this one is computed
-    if (c0 + CH < t_end)
-      load_chunk<STATE_ONLY>(cur, q, k, v, g, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H);
-
+    const bool more = c0 + CH < t_end;
+    // this wave's 16 query tokens c0 + 16w + l16: gate values for the output (lane's 4-dim runs)
+    const int tq = c0 + 16 * wave + l16;
+    f32x4 OT[8];
     if (!STATE_ONLY) {
-      // ---------------- intra-chunk: A^T = K~ Q~^T for this wave's 16 queries (16w..16w+15)
-      f32x4 OT[8];
+      // ---------------- intra-chunk: O^T = V^T (K~ Q~^T (.) causal) for queries 16w..16w+15
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) OT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       bf16x8 qfrag[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        qfrag[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&L.q[(16 * wave + l16) * QS + 32 * ks + 8 * lq]));
-      // key tiles kt <= wave; pairs (2c, 2c+1) feed one PV k-step of 32 keys
+        qfrag[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&L.q[swz(16 * wave + l16, 4 * ks + lq)]));
       for (int c = 0; 2 * c <= wave; ++c) {
         f32x4 at[2];
 #pragma unroll
@@ -235,7 +215,7 @@ linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           if (kt <= wave) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-              const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.k[(16 * kt + l16) * QS + 32 * ks + 8 * lq]));
+              const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.k[swz(16 * kt + l16, 4 * ks + lq)]));
               at[hh] = mfma16x16x32(kf, qfrag[ks], at[hh]);
             }
             if (kt == wave) {
@@ -251,27 +231,19 @@ linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         pb.z = pack_bf16x2(at[1][0], at[1][1]);
         pb.w = pack_bf16x2(at[1][2], at[1][3]);
         const bf16x8 pfrag = as_bf16x8(pb);
+        // A = V^T with the keys in P^T's slot order (kb + 4lq + e, kb + 16 + 4lq + e)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const bf16_t* vrow = &L.vt[(16 * dt + l16) * TS + 32 * c + 4 * lq];
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint2*>(vrow),
-                                      *reinterpret_cast<const uint2*>(vrow + 16));
-          OT[dt] = mfma16x16x32(vf, pfrag, OT[dt]);
-        }
+        for (int dt = 0; dt < 8; ++dt)
+          OT[dt] = mfma16x16x32(tr_frag(L.v, 32 * c + 4 * lq, 16, 16 * dt, l16), pfrag, OT[dt]);
       }
       // ---------------- inter-chunk: O^T += S^T Q~^T
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 sf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.st[(16 * dt + l16) * SS + 32 * ks + 8 * lq]));
+          const bf16x8 sf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.st[swz(16 * dt + l16, 4 * ks + lq)]));
           OT[dt] = mfma16x16x32(sf, qfrag[ks], OT[dt]);
         }
-      // stage O (fp32) for the coalesced gated store
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<float4*>(&L.o[(16 * wave + l16) * OS + 16 * dt + 4 * lq]) =
-            make_float4(OT[dt][0], OT[dt][1], OT[dt][2], OT[dt][3]);
     }
 
     // ---------------- state update: S += K~^T V (wave: dk rows 32w..32w+31, all dv)
@@ -279,16 +251,19 @@ linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 af[2];
 #pragma unroll
-      for (int it = 0; it < 2; ++it)
-        af[it] = as_bf16x8(*reinterpret_cast<const uint4*>(&L.kt[(32 * wave + 16 * it + l16) * TS + 32 * ks + 8 * lq]));
+      for (int it = 0; it < 2; ++it) af[it] = tr_frag(L.k, 32 * ks + 8 * lq, 4, 32 * wave + 16 * it, l16);
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt) {
-        const bf16x8 bfr = as_bf16x8(*reinterpret_cast<const uint4*>(&L.vt[(16 * jt + l16) * TS + 32 * ks + 8 * lq]));
+        const bf16x8 bfr = tr_frag(L.v, 32 * ks + 8 * lq, 4, 16 * jt, l16);
 #pragma unroll
         for (int it = 0; it < 2; ++it) S[it][jt] = mfma16x16x32(af[it], bfr, S[it][jt]);
       }
     }
-    __syncthreads();
+    __syncthreads();  // every read of the q~, k~, v and S^T tiles of this chunk is done
+    if (more) {  // next chunk's inputs load while this chunk's results are written
+      dma_v(v, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H, L.v);
+      load_qk<STATE_ONLY>(cur, q, k, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H);
+    }
 
     if (!STATE_ONLY) {
       // new S^T (bf16) for the next chunk
@@ -296,37 +271,43 @@ linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       for (int it = 0; it < 2; ++it)
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
-          const int dk0 = 32 * wave + 16 * it + 4 * lq, dv = 16 * jt + l16;
           uint2 p;
           p.x = pack_bf16x2(S[it][jt][0], S[it][jt][1]);
           p.y = pack_bf16x2(S[it][jt][2], S[it][jt][3]);
-          *reinterpret_cast<uint2*>(&L.st[dv * SS + dk0]) = p;
+          const int dk0 = 32 * wave + 16 * it + 4 * lq, dv = 16 * jt + l16;
+          *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
         }
-      // gated output: out = O * sigmoid(g)
+      // gated output straight from the accumulators: out = O * sigmoid(g)
+      if (tq < t_end) {
+        bf16_t* dst = out + head_off + (long)tq * tok_stride + 4 * lq;
+        const bf16_t* gsrc = g + head_off + (long)tq * tok_stride + 4 * lq;
+        uint2 gv[8];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = 2 * tp + u;
-        if (c0 + t < t_end) {
-          bf16_t* dst = out + head_off + (long)(c0 + t) * tok_stride;
+        for (int dt = 0; dt < 8; ++dt) gv[dt] = *reinterpret_cast<const uint2*>(gsrc + 16 * dt);
 #pragma unroll
-          for (int hs = 0; hs < 2; ++hs) {
-            const int d0 = 8 * (s8 + 8 * hs);
-            float gv[8], ov[8];
-            unpack8(gk[u][hs], gv);
-            const float4 o0 = *reinterpret_cast<const float4*>(&L.o[t * OS + d0]);
-            const float4 o1 = *reinterpret_cast<const float4*>(&L.o[t * OS + d0 + 4]);
-            ov[0] = o0.x; ov[1] = o0.y; ov[2] = o0.z; ov[3] = o0.w;
-            ov[4] = o1.x; ov[5] = o1.y; ov[6] = o1.z; ov[7] = o1.w;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ov[e] *= sigmoidf_(gv[e]);
-            *reinterpret_cast<uint4*>(dst + d0) = pack8(ov);
-          }
+        for (int dt = 0; dt < 8; ++dt) {
+          const float g0 = __uint_as_float(gv[dt].x << 16), g1 = __uint_as_float(gv[dt].x & 0xffff0000u);
+          const float g2 = __uint_as_float(gv[dt].y << 16), g3 = __uint_as_float(gv[dt].y & 0xffff0000u);
+          uint2 o;
+          o.x = pack_bf16x2(OT[dt][0] * fast_sigmoid(g0), OT[dt][1] * fast_sigmoid(g1));
+          o.y = pack_bf16x2(OT[dt][2] * fast_sigmoid(g2), OT[dt][3] * fast_sigmoid(g3));
+          *reinterpret_cast<uint2*>(dst + 16 * dt) = o;
         }
       }
     }
+    // advance the RoPE table by 64 positions
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float c = rc[u][e], sn = rs[u][e];
+        const float ac = freqs.c64[8 * s8 + e], as = freqs.s64[8 * s8 + e];
+        rc[u][e] = c * ac - sn * as;
+        rs[u][e] = sn * ac + c * as;
+      }
   }
 
-  // ---- segment result: state-only -> segment sum into its slot; last segment -> final state
+  // ---- segment result: state-only -> segment sum into slot seg+1; last segment -> final state
   float* dst = nullptr;
   if (STATE_ONLY) dst = ws + ((long)bh * nseg + seg + 1) * D * D;
   else if (seg == nseg - 1 && state_out) dst = state_out + (long)bh * D * D;
@@ -339,6 +320,244 @@ linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int e = 0; e < 4; ++e) {
           const int dk = 32 * wave + 16 * it + 4 * lq + e, dv = 16 * jt + l16;
           dst[dk * D + dv] = S[it][jt][e];
+        }
+  }
+}
+
+// ---- output pass: one workgroup per CU owning the whole 160 KB of LDS. The raw q, k, v and
+// gate tiles of a chunk are copied global -> LDS by DMA one chunk ahead (double buffered), q
+// and k are normalised and rotated in place, and the gated outputs are stored straight from
+// the MFMA accumulators.
+struct OutLds {
+  bf16_t t[2][4][CH * D];  // [buffer][q, k, v, g][token][dim], swizzled 256-byte rows
+  bf16_t st[D * D];        // S^T [dv][dk] bf16: the state entering the chunk
+};
+static_assert(sizeof(OutLds) == 163840, "output-pass LDS plan");
+
+// DMA the four raw tiles of a chunk: 64 pieces of 1 KB, 8 per wave (wave w: pieces 2w, 2w+1
+// of each tile, rows 8w .. 8w+7). Rows past the sequence end are clamped to its last row
+// (finite values; k rows past the end are zeroed by the prep, so they contribute nothing).
+constexpr int OUT_NT = 512;  // 8 waves: 0-3 produce outputs, 4-7 update the state
+__device__ __forceinline__ void dma_chunk(const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                                          const bf16_t* g, long row0, int t0, int n_valid, int H,
+                                          bf16_t (*T)[CH * D]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int I = 2 * wave + m;
+    const int row = 4 * I + (lane >> 4);
+    const int ch = (lane & 15) ^ (row & 15);
+    const long off = row0 + (long)(min(t0 + row, n_valid - 1) - t0) * H * D + 8 * ch;
+    dma16(q + off, lds_addr_u32(T[0] + I * 512));
+    dma16(k + off, lds_addr_u32(T[1] + I * 512));
+    dma16(v + off, lds_addr_u32(T[2] + I * 512));
+    dma16(g + off, lds_addr_u32(T[3] + I * 512));
+  }
+}
+
+__global__ void __launch_bounds__(OUT_NT)
+linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                  const bf16_t* __restrict__ v, const bf16_t* __restrict__ g,
+                  const float* __restrict__ qw, const float* __restrict__ kw,
+                  const float* __restrict__ state_in, const float* __restrict__ ws,
+                  float* __restrict__ state_out, bf16_t* __restrict__ out, int N, int H, long pos0,
+                  int seg_len, int nseg, float eps, RopeFreqs freqs) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  OutLds& L = *reinterpret_cast<OutLds*>(lds_raw);
+  const int seg = blockIdx.x % nseg;
+  const int bh = blockIdx.x / nseg;
+  const int b = bh / H, h = bh % H;
+  const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const bool out_wave = wave < 4;
+  const int w4 = wave & 3;      // query tile (output waves) or dk row block (state waves)
+  const int s8 = j & 7, tok = j >> 3;  // prep: one token, segments s8 and s8+8
+  const int t_begin = seg * seg_len;
+  const int t_end = min(N, t_begin + seg_len);
+  const long head_off = ((long)b * N * H + h) * D;
+  const long tok_stride = (long)H * D;
+
+  dma_chunk(q, k, v, g, head_off + (long)t_begin * tok_stride, t_begin, N, H, L.t[0]);
+
+  // acc: state waves keep S[dk][dv] (C layout, dk rows 32*w4 .. +31) in acc[8*it + jt];
+  // output waves use acc[0..7] for their O^T tiles. One array, so the roles share registers.
+  f32x4 acc[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (!out_wave) {
+    const float* src = (nseg == 1) ? (state_in ? state_in + (long)bh * D * D : nullptr)
+                                   : ws + ((long)bh * nseg + seg) * D * D;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dk = 32 * w4 + 16 * it + 4 * lq + e, dv = 16 * jt + l16;
+          acc[8 * it + jt][e] = src ? src[dk * D + dv] : 0.f;
+        }
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt) {
+        uint2 p;
+        p.x = pack_bf16x2(acc[8 * it + jt][0], acc[8 * it + jt][1]);
+        p.y = pack_bf16x2(acc[8 * it + jt][2], acc[8 * it + jt][3]);
+        const int dk0 = 32 * w4 + 16 * it + 4 * lq, dv = 16 * jt + l16;
+        *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
+      }
+  }
+  // RoPE table for this thread's token x 8 frequencies, advanced 64 positions per chunk
+  float rc[8], rs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    sincos_rev(rope_rev((double)(pos0 + t_begin + tok), freqs.f[8 * s8 + e]), &rs[e], &rc[e]);
+
+  wait_vmcnt<0>();
+  __syncthreads();
+  int buf = 0;
+  for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+    bf16_t* Qt = L.t[buf][0];
+    bf16_t* Kt = L.t[buf][1];
+    const bf16_t* Vt = L.t[buf][2];
+    const bf16_t* Gt = L.t[buf][3];
+    // ---------------- prep in place: QK-norm + RoPE (rows past the end: k~ = 0)
+    {
+      uint4 xq[2], xk[2];
+      xq[0] = *reinterpret_cast<const uint4*>(&Qt[swz(tok, s8)]);
+      xq[1] = *reinterpret_cast<const uint4*>(&Qt[swz(tok, s8 + 8)]);
+      xk[0] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8)]);
+      xk[1] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8 + 8)]);
+      norm_rope(xq, qw, s8, eps, rc, rs);
+      norm_rope(xk, kw, s8, eps, rc, rs);
+      if (c0 + tok >= t_end) { xk[0] = make_uint4(0, 0, 0, 0); xk[1] = xk[0]; }
+      *reinterpret_cast<uint4*>(&Qt[swz(tok, s8)]) = xq[0];
+      *reinterpret_cast<uint4*>(&Qt[swz(tok, s8 + 8)]) = xq[1];
+      *reinterpret_cast<uint4*>(&Kt[swz(tok, s8)]) = xk[0];
+      *reinterpret_cast<uint4*>(&Kt[swz(tok, s8 + 8)]) = xk[1];
+    }
+    __syncthreads();
+    // the next chunk's tiles stream in while this one is computed
+    if (c0 + CH < t_end)
+      dma_chunk(q, k, v, g, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H, L.t[buf ^ 1]);
+
+    const int tl = 16 * w4 + l16, tq = c0 + tl;
+    uint2 gv[8];
+    if (out_wave) {
+      // ---------------- intra-chunk: O^T = V^T (K~ Q~^T (.) causal) for queries 16w..16w+15
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 qfrag[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qfrag[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&Qt[swz(tl, 4 * ks + lq)]));
+      for (int c = 0; 2 * c <= w4; ++c) {
+        f32x4 at[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int kt = 2 * c + hh;
+          at[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (kt <= w4) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[swz(16 * kt + l16, 4 * ks + lq)]));
+              at[hh] = mfma16x16x32(kf, qfrag[ks], at[hh]);
+            }
+            if (kt == w4) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (4 * lq + e > l16) at[hh][e] = 0.f;  // key after query: masked
+            }
+          }
+        }
+        uint4 pb;
+        pb.x = pack_bf16x2(at[0][0], at[0][1]);
+        pb.y = pack_bf16x2(at[0][2], at[0][3]);
+        pb.z = pack_bf16x2(at[1][0], at[1][1]);
+        pb.w = pack_bf16x2(at[1][2], at[1][3]);
+        const bf16x8 pfrag = as_bf16x8(pb);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          acc[dt] = mfma16x16x32(tr_frag(Vt, 32 * c + 4 * lq, 16, 16 * dt, l16), pfrag, acc[dt]);
+      }
+      // ---------------- inter-chunk: O^T += S^T Q~^T
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 sf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.st[swz(16 * dt + l16, 4 * ks + lq)]));
+          acc[dt] = mfma16x16x32(sf, qfrag[ks], acc[dt]);
+        }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int col = 16 * dt + 4 * lq;
+        gv[dt] = *reinterpret_cast<const uint2*>(&Gt[swz(tl, col >> 3) + (col & 7)]);
+      }
+    } else {
+      // ---------------- state update: S += K~^T V (dk rows 32*w4 .. +31, all dv)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 af[2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) af[it] = tr_frag(Kt, 32 * ks + 8 * lq, 4, 32 * w4 + 16 * it, l16);
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+          const bf16x8 bfr = tr_frag(Vt, 32 * ks + 8 * lq, 4, 16 * jt, l16);
+#pragma unroll
+          for (int it = 0; it < 2; ++it) acc[8 * it + jt] = mfma16x16x32(af[it], bfr, acc[8 * it + jt]);
+        }
+      }
+    }
+    __syncthreads();  // every read of this chunk's S^T, q~, k~, v and g tiles is done
+    uint2 ov[8];
+    if (out_wave) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const float g0 = __uint_as_float(gv[dt].x << 16), g1 = __uint_as_float(gv[dt].x & 0xffff0000u);
+        const float g2 = __uint_as_float(gv[dt].y << 16), g3 = __uint_as_float(gv[dt].y & 0xffff0000u);
+        ov[dt].x = pack_bf16x2(acc[dt][0] * fast_sigmoid(g0), acc[dt][1] * fast_sigmoid(g1));
+        ov[dt].y = pack_bf16x2(acc[dt][2] * fast_sigmoid(g2), acc[dt][3] * fast_sigmoid(g3));
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 8; ++jt) {
+          uint2 p;
+          p.x = pack_bf16x2(acc[8 * it + jt][0], acc[8 * it + jt][1]);
+          p.y = pack_bf16x2(acc[8 * it + jt][2], acc[8 * it + jt][3]);
+          const int dk0 = 32 * w4 + 16 * it + 4 * lq, dv = 16 * jt + l16;
+          *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = rc[e], sn = rs[e];
+      const float ac = freqs.c64[8 * s8 + e], as = freqs.s64[8 * s8 + e];
+      rc[e] = c * ac - sn * as;
+      rs[e] = sn * ac + c * as;
+    }
+    // the next chunk's tiles must have landed before the barrier; the output stores are issued
+    // after this wait so that they never hold it up
+    wait_vmcnt<0>();
+    if (out_wave && tq < t_end) {
+      bf16_t* dst = out + head_off + (long)tq * tok_stride + 4 * lq;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(dst + 16 * dt) = ov[dt];
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+  if (!out_wave && seg == nseg - 1 && state_out) {
+    float* dst = state_out + (long)bh * D * D;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dk = 32 * w4 + 16 * it + 4 * lq + e, dv = 16 * jt + l16;
+          dst[dk * D + dv] = acc[8 * it + jt][e];
         }
   }
 }
@@ -559,7 +778,10 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
     hipLaunchKernelGGL(linear_scan_kernel, dim3(B * H, D * D / 256), dim3(256), 0, st, state_in,
                        wsf, nseg, D * D);
   }
-  hipLaunchKernelGGL(linear_chunk_kernel<false>, dim3(B * H * nseg), dim3(NT), 0, st, qb, kb, vb,
+  static const hipError_t attr_ok = hipFuncSetAttribute(
+      (const void*)linear_out_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutLds));
+  if (attr_ok != hipSuccess) return attr_ok;
+  hipLaunchKernelGGL(linear_out_kernel, dim3(B * H * nseg), dim3(OUT_NT), sizeof(OutLds), st, qb, kb, vb,
                      gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, N, H, (long)d.pos0, seg,
                      nseg, d.norm_eps, fr);
   return hipGetLastError();

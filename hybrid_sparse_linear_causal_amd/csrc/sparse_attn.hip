@@ -33,39 +33,12 @@ constexpr int VS = 64 + 8;   // V^T tile row stride (bf16): 144 B
 constexpr float RESCALE_TH = 8.0f;  // log2 units
 constexpr int DEC_SPLIT = 16;       // decode workgroups per (b, g)
 
-// LDS tile of one 64-key block: 64 rows x 256 B, 16-byte chunk c of row r stored at chunk
-// position c ^ (r & 15) so that 16 rows read at the same column hit 16 different bank groups.
-constexpr int TILE = 64 * 128;  // bf16 elements per tile
+constexpr int TILE = 64 * 128;  // bf16 elements per 64-row tile
 constexpr int NSTAGE = 3;       // LDS ring depth (blocks in flight)
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + 8 * (chunk ^ (row & 15)); }
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16 lanes, lane i
-// supplies the address of 4 consecutive bf16; lane j receives element j%4 of the chunks of
-// lanes j/4 + 4e, e = 0..3. With lane i pointing at row k0 + i/4, columns c0 + 4*(i%4), lane j
-// receives column c0 + j of rows k0 .. k0+3: four consecutive-k values of one MFMA column.
-__device__ __forceinline__ uint2 ds_read_tr(const bf16_t* p) {
-  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-  return __builtin_bit_cast(uint2, r);
-}
 
 __device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
   const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane l's
-// chunk lands at LDS byte address lds_addr + 16 * l. Issued from inline assembly so that the
-// compiler does not serialise it with unrelated LDS reads; it has no register outputs, and
-// completion is awaited explicitly with s_waitcnt vmcnt before the barrier that publishes it.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_addr)
-               : "memory", "m0");
-}
-template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Issue the DMA of one 64-key block (K and V tiles, 16 KB each = 16 pieces of 1 KB) into a
@@ -102,7 +75,6 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16_t* Vs, int kb, int dt, int 
   return as_bf16x8(a, b);
 }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // One wave's work on one staged 64-key block for its QT x 16 query rows (rows qrow0 + 16*qt
 // + l16 of the query block): S^T = K Q^T, online softmax (lazy rescale), O^T += V^T P^T.
