@@ -145,6 +145,7 @@ score_row_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
   }
 }
 
+template <int NTS>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -157,24 +158,29 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   __syncthreads();
   if (threadIdx.x == 0) {
     int acc = 0;
-    for (int w = 0; w < NT / 64; ++w) { const int t = tmp[w]; tmp[w] = acc; acc += t; }
-    tmp[NT / 64] = acc;
+    for (int w = 0; w < NTS / 64; ++w) { const int t = tmp[w]; tmp[w] = acc; acc += t; }
+    tmp[NTS / 64] = acc;
   }
   __syncthreads();
   const int res = x - v + tmp[wave];
-  *total = tmp[NT / 64];
+  *total = tmp[NTS / 64];
   __syncthreads();
   return res;
 }
 
 // grid (B*Hkv*nqb); row (bg, r) with i = qb0 + r. Exact top-r over candidate keys
-// (score desc, index asc) by MSB-first radix select on 32-bit monotone keys, then an ordered
-// walk over blocks 0..i that emits forced and chosen blocks ascending; -1 pads to topk.
-__global__ void __launch_bounds__(NT)
+// (score desc, index asc): MSB-first radix select over the 32-bit monotone keys (histograms
+// updated once per distinct digit per wave), then an ordered walk over blocks 0..i that emits
+// forced and chosen blocks ascending; -1 pads to topk.
+// CAP candidate keys are staged in LDS; rows with more candidates read the scores in global
+// memory (correct, slower).
+template <int NTS, int CAP>
+__global__ void __launch_bounds__(NTS)
 select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, long qb0, int RL,
               int topk, int n_local) {
+  __shared__ uint32_t keys[CAP];
   __shared__ int hist[256];
-  __shared__ int scan_tmp[NT / 64 + 1];
+  __shared__ int scan_tmp[NTS / 64 + 1];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const long row = blockIdx.x;
@@ -182,12 +188,18 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
   const long i = qb0 + r;
   const float* srow = sc + row * RL;
   int32_t* out = sel + row * topk;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const long nc = i - n_local > 0 ? i - n_local : 0;             // candidates j = 1..nc
   const long f_lo = i - n_local + 1 > 0 ? i - n_local + 1 : 0;   // forced local range [f_lo, i]
   const int n_forced = (int)(i - f_lo + 1) + (f_lo > 0 ? 1 : 0);
   const int rsel = topk - n_forced;
   const bool take_all = nc <= rsel;
+  const bool in_lds = nc <= CAP;
+
+  if (!take_all && in_lds)
+    for (long jj = tid; jj < nc; jj += NTS) keys[jj] = score_key(srow[jj + 1]);
+  __syncthreads();
+  auto key_of = [&](long jj) -> uint32_t { return in_lds ? keys[jj - 1] : score_key(srow[jj]); };
 
   uint32_t T = 0;
   int need = 0;
@@ -196,21 +208,53 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
     int remaining = rsel;
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      hist[tid] = 0;
+      for (int x = tid; x < 256; x += NTS) hist[x] = 0;
       __syncthreads();
-      for (long jj = 1 + tid; jj <= nc; jj += NT) {
-        const uint32_t key = score_key(srow[jj]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      for (long base = 0; base < nc; base += NTS) {
+        const long jj = 1 + base + tid;
+        uint32_t key = 0;
+        bool match = false;
+        if (jj <= nc) {
+          key = key_of(jj);
+          match = (key & pmask) == prefix;
+        }
+        const uint32_t dgt = (key >> shift) & 255u;
+        // one atomic per distinct digit present in the wave
+        uint64_t active = __ballot(match);
+        while (active) {
+          const int leader = __ffsll((unsigned long long)active) - 1;
+          const uint32_t dl = __shfl(dgt, leader, 64);
+          const uint64_t same = __ballot(match && dgt == dl);
+          if (lane == leader) atomicAdd(&hist[dl], __popcll(same));
+          active &= ~same;
+        }
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, dgt = 255;
-        for (; dgt > 0; --dgt) {
-          if (cum + hist[dgt] >= remaining) break;
-          cum += hist[dgt];
+      if (tid < 64) {
+        // digit with cum(digits > d) < remaining <= cum(digits >= d); lane l owns digits
+        // 255-4l .. 252-4l (descending)
+        int v[4], sum = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { v[e] = hist[255 - 4 * lane - e]; sum += v[e]; }
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
         }
-        s_prefix = prefix | ((uint32_t)dgt << shift);
-        s_need = remaining - cum;
+        const uint64_t hit = __ballot(incl >= remaining);
+        const int L = __ffsll((unsigned long long)hit) - 1;  // first lane reaching the count
+        if (hit == 0 && lane == 0) { s_prefix = prefix; s_need = remaining; }  // unreachable
+        if (lane == L) {
+          int cum = incl - sum;
+          int e = 0;
+          for (; e < 3; ++e) {
+            if (cum + v[e] >= remaining) break;
+            cum += v[e];
+          }
+          s_prefix = prefix | ((uint32_t)(255 - 4 * lane - e) << shift);
+          s_need = remaining - cum;
+        }
       }
       __syncthreads();
       prefix = s_prefix;
@@ -223,19 +267,17 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
 
   // ordered pass over blocks 0..i: each thread owns a contiguous index range
   const long nall = i + 1;
-  const long per = (nall + NT - 1) / NT;
+  const long per = (nall + NTS - 1) / NTS;
   const long a = tid * per, e_end = min(nall, a + per);
-  // (1) equal-key counts in index order
   int eq = 0;
   if (!take_all)
-    for (long jj = max(a, 1L); jj < e_end && jj <= nc; ++jj) eq += (score_key(srow[jj]) == T);
+    for (long jj = max(a, 1L); jj < e_end && jj <= nc; ++jj) eq += (key_of(jj) == T);
   int eq_total;
-  int eq_before = block_excl_scan(eq, scan_tmp, &eq_total);
-  // (2) count selected blocks in the range
+  const int eq_before = block_excl_scan<NTS>(eq, scan_tmp, &eq_total);
   auto picked = [&](long jj, int& eqb) -> bool {
     if (jj == 0 || jj >= f_lo) return true;  // forced
     if (take_all) return true;              // 1 <= jj <= nc
-    const uint32_t key = score_key(srow[jj]);
+    const uint32_t key = key_of(jj);
     if (key > T) return true;
     if (key == T) return (eqb++) < need;
     return false;
@@ -246,7 +288,7 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
     for (long jj = a; jj < e_end; ++jj) cnt += picked(jj, eqb);
   }
   int total;
-  int pos = block_excl_scan(cnt, scan_tmp, &total);
+  int pos = block_excl_scan<NTS>(cnt, scan_tmp, &total);
   {
     int eqb = eq_before;
     for (long jj = a; jj < e_end; ++jj)
@@ -255,7 +297,7 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
         ++pos;
       }
   }
-  for (int k = total + tid; k < topk; k += NT) out[k] = -1;
+  for (int k = total + tid; k < topk; k += NTS) out[k] = -1;
 }
 
 }  // namespace
@@ -312,8 +354,13 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
                            (long)g.qb0, (int)RL, (long)g.nblk_cap, d.n_local);
     }
   }
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)(BG * g.nqb)), dim3(NT), 0, st, sc, sel,
-                     (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
+  // few long rows (decode): 1024 threads per row; many rows (prefill): 256
+  if (g.nqb == 1)
+    hipLaunchKernelGGL((select_kernel<1024, 16384>), dim3((unsigned)(BG * g.nqb)), dim3(1024), 0, st, sc, sel,
+                       (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
+  else
+    hipLaunchKernelGGL((select_kernel<256, 4096>), dim3((unsigned)(BG * g.nqb)), dim3(256), 0, st, sc, sel,
+                       (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
   return hipGetLastError();
 }
 

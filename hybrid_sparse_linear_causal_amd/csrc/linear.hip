@@ -421,6 +421,10 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     bf16_t* Kt = L.t[buf][1];
     const bf16_t* Vt = L.t[buf][2];
     const bf16_t* Gt = L.t[buf][3];
+    // the next chunk's tiles stream into the other buffer (free since the last barrier) for
+    // the whole of this chunk
+    if (c0 + CH < t_end)
+      dma_chunk(q, k, v, g, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H, L.t[buf ^ 1]);
     // ---------------- prep in place: QK-norm + RoPE (rows past the end: k~ = 0)
     {
       uint4 xq[2], xk[2];
@@ -437,9 +441,6 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       *reinterpret_cast<uint4*>(&Kt[swz(tok, s8 + 8)]) = xk[1];
     }
     __syncthreads();
-    // the next chunk's tiles stream in while this one is computed
-    if (c0 + CH < t_end)
-      dma_chunk(q, k, v, g, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H, L.t[buf ^ 1]);
 
     const int tl = 16 * w4 + l16, tq = c0 + tl;
     uint2 gv[8];

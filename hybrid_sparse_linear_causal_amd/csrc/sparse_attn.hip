@@ -434,26 +434,35 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
   }
 }
 
-// grid (B*Hkv); combine DEC_SPLIT partials, normalise, gate, store out[b, h, :]
-__global__ void __launch_bounds__(256)
+// grid (B*Hkv*G): one workgroup of D threads per (b, head); combine the DEC_SPLIT partials
+// of the head's KV group, normalise, gate, store out[b, h, :]
+__global__ void __launch_bounds__(D)
 sparse_decode_combine_kernel(const float* __restrict__ part, const bf16_t* __restrict__ g,
                              bf16_t* __restrict__ out, int Hq, int Hkv) {
-  const int bg = blockIdx.x, b = bg / Hkv, gk = bg % Hkv, G = Hq / Hkv;
-  const float* src = part + (long)bg * DEC_SPLIT * 16 * (D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int hh = idx / D, dd = idx % D;
-    float M = -INFINITY;
-    for (int s = 0; s < DEC_SPLIT; ++s) M = fmaxf(M, src[(s * 16 + hh) * (D + 2)]);
-    float o = 0.f, l = 0.f;
-    for (int s = 0; s < DEC_SPLIT; ++s) {
-      const float* ps = src + (s * 16 + hh) * (D + 2);
-      const float sc = (ps[0] == -INFINITY) ? 0.f : exp2f(ps[0] - M);
-      o += ps[2 + dd] * sc;
-      l += ps[1] * sc;
-    }
-    const long off = ((long)b * Hq + gk * G + hh) * D + dd;
-    out[off] = f2bf(o / l * sigmoidf_(bf2f(g[off])));
+  const int G = Hq / Hkv;
+  const int bg = blockIdx.x / G, hh = blockIdx.x % G;
+  const int b = bg / Hkv, gk = bg % Hkv, dd = threadIdx.x;
+  const float* src = part + ((long)bg * DEC_SPLIT * 16 + hh) * (D + 2);
+  float ms[DEC_SPLIT], ls[DEC_SPLIT], os[DEC_SPLIT];
+#pragma unroll
+  for (int s = 0; s < DEC_SPLIT; ++s) {
+    const float* ps = src + (long)s * 16 * (D + 2);
+    ms[s] = ps[0];
+    ls[s] = ps[1];
+    os[s] = ps[2 + dd];
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < DEC_SPLIT; ++s) M = fmaxf(M, ms[s]);
+  float o = 0.f, l = 0.f;
+#pragma unroll
+  for (int s = 0; s < DEC_SPLIT; ++s) {
+    const float w = (ms[s] == -INFINITY) ? 0.f : fast_exp2(ms[s] - M);
+    o += os[s] * w;
+    l += ls[s] * w;
+  }
+  const long off = ((long)b * Hq + gk * G + hh) * D + dd;
+  out[off] = f2bf(o / l * fast_sigmoid(bf2f(g[off])));
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -551,7 +560,7 @@ hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const fl
                        st, (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, sel,
                        part, d.n_heads, d.n_kv_heads, (long)d.kv_len, (long)d.kv_capacity, d.topk,
                        d.norm_eps, qscale);
-    hipLaunchKernelGGL(sparse_decode_combine_kernel, dim3(d.batch * d.n_kv_heads), dim3(256), 0, st,
+    hipLaunchKernelGGL(sparse_decode_combine_kernel, dim3(d.batch * d.n_heads), dim3(D), 0, st,
                        part, (const bf16_t*)g, (bf16_t*)out, d.n_heads, d.n_kv_heads);
     return hipGetLastError();
   }
