@@ -105,6 +105,31 @@ def cpu_baseline_sample(W, seconds_budget=20.0):
     }
 
 
+def kernel_source_sha(files):
+    """sha256 over the source files a kernel is built from (for matching stored counters)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel, launches_per_profile=1):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary
+    (profiles/pmc_traffic.json), scaled by the copy-kernel calibration it records, or None if
+    the summary is missing or the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(kernel)
+    if not rec or rec.get("source_sha256") != kernel_source_sha(rec["sources"]):
+        return None
+    return (rec["fetch_kb"] * rec["fetch_scale"] + rec["write_kb"] * rec["write_scale"]) * 1024.0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,7 +292,8 @@ def main():
                    "decode_batch": B, "decode_context": L},
         "roofline": {"kernel": "sparse_prefill_bf16_kernel", "bound": "mfma", "achieved": att_tflops,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": att_tflops / BF16_PEAK_TFLOPS,
-                     "traffic": None, "flops_per_launch": flops_attn, "avg_launch_ms": t_att},
+                     "traffic": stored_traffic("sparse_prefill_bf16_kernel"),
+                     "flops_per_launch": flops_attn, "avg_launch_ms": t_att},
         "breakdown": {
             "prefill_ms": t_prefill,
             "linear_layer_ms": t_lin,
