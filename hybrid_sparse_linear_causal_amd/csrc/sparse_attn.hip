@@ -34,7 +34,7 @@ constexpr float RESCALE_TH = 8.0f;  // log2 units
 constexpr int DEC_SPLIT = 16;       // decode workgroups per (b, g)
 
 constexpr int TILE = 64 * 128;  // bf16 elements per 64-row tile
-constexpr int NSTAGE = 3;       // LDS ring depth (blocks in flight)
+constexpr int NSTAGE = 4;       // LDS ring depth (blocks resident or in flight)
 
 __device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
   const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
@@ -76,14 +76,13 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16_t* Vs, int kb, int dt, int 
 }
 
 
-// One wave's work on one staged 64-key block for its QT x 16 query rows (rows qrow0 + 16*qt
-// + l16 of the query block): S^T = K Q^T, online softmax (lazy rescale), O^T += V^T P^T.
-// diag masks keys after the query (the query's own block).
+// ---- pieces of one wave's work on a staged 64-key block for its QT x 16 query rows (rows
+// qrow0 + 16*qt + l16 of the query block)
+
+// S^T[kt][qt] = K[kt] Q^T[qt] (scores in log2 units: scale*log2(e) is folded into q)
 template <int QT>
-__device__ __forceinline__ void attend_block(const bf16_t* Ks, const bf16_t* Vs, const bf16x8 (&qf)[QT][4],
-                                             f32x4 (&OT)[8][QT], float (&m)[QT], float (&lp)[QT],
-                                             int l16, int lq, int qrow0, bool diag) {
-  f32x4 ST[4][QT];
+__device__ __forceinline__ void scores(const bf16_t* Ks, const bf16x8 (&qf)[QT][4], f32x4 (&ST)[4][QT],
+                                       int l16, int lq) {
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
@@ -95,17 +94,26 @@ __device__ __forceinline__ void attend_block(const bf16_t* Ks, const bf16_t* Vs,
       for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ST[kt][qt]);
     }
   }
-  if (diag) {
+}
+
+// causal mask of the query's own block: key after query -> -inf
+template <int QT>
+__device__ __forceinline__ void mask_diag(f32x4 (&ST)[4][QT], int l16, int lq, int qrow0) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (16 * kt + 4 * lq + c > qrow0 + 16 * qt + l16) ST[kt][qt][c] = -INFINITY;
-  }
-  // the running maximum moves only when a row maximum exceeds it by more than RESCALE_TH
-  // (log2 units), so exp2 arguments stay <= RESCALE_TH and the output is rarely rescaled
+      for (int c = 0; c < 4; ++c)
+        if (16 * kt + 4 * lq + c > qrow0 + 16 * qt + l16) ST[kt][qt][c] = -INFINITY;
+}
+
+// Lazy online-softmax rescale: the running maximum moves only when a row maximum exceeds it
+// by more than RESCALE_TH (log2 units), so exp2 arguments stay <= RESCALE_TH and the running
+// output is rarely rescaled.
+template <int QT>
+__device__ __forceinline__ void rescale(const f32x4 (&ST)[4][QT], f32x4 (&OT)[8][QT], float (&m)[QT],
+                                        float (&lp)[QT]) {
   bool any_need = false;
   float mn[QT];
 #pragma unroll
@@ -130,6 +138,12 @@ __device__ __forceinline__ void attend_block(const bf16_t* Ks, const bf16_t* Vs,
       m[qt] = mn[qt];
     }
   }
+}
+
+// P^T = exp2(S^T - m) per 32-key half, O^T += V^T P^T (P^T straight from the accumulators)
+template <int QT>
+__device__ __forceinline__ void exp_pv(const bf16_t* Vs, const f32x4 (&ST)[4][QT], f32x4 (&OT)[8][QT],
+                                       const float (&m)[QT], float (&lp)[QT], int l16, int lq) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     bf16x8 pf[QT];
@@ -228,30 +242,45 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
 #pragma unroll
     for (int qt = 0; qt < PF_QT; ++qt) OT[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  dma_block(kc, vc, row_base, s_sel[0], kv_len, lds[0][0], lds[0][1]);
-  if (nsel > 1) {
-    dma_block(kc, vc, row_base, s_sel[1], kv_len, lds[1][0], lds[1][1]);
-    wait_vmcnt<DMA_PER_WAVE>();
-  } else {
-    wait_vmcnt<0>();
-  }
+  // Software pipeline over the selected blocks (ring of NSTAGE = 4 stages, block e in stage
+  // e % 4): iteration e computes the scores of block e+1 on MFMA while the exponentials of
+  // block e run on VALU, then O^T += V^T P^T for block e. Blocks e+2 and e+3 are in flight.
+  // The selection is ascending and always ends with the query's own block i, so the causal
+  // diagonal block is the last one and is finished after the loop.
+#pragma unroll
+  for (int x = 0; x < 3; ++x)
+    if (x < nsel) dma_block(kc, vc, row_base, s_sel[x], kv_len, lds[x][0], lds[x][1]);
+  if (nsel > 2) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();  // blocks 0 and 1 landed
   __syncthreads();
 
-  int st = 0;
-  for (int e = 0; e < nsel; ++e) {
-    // block e+2 goes into the stage that held block e-1 (released by the last barrier)
-    if (e + 2 < nsel) {
-      const int s2 = st == 0 ? 2 : st - 1;
-      dma_block(kc, vc, row_base, s_sel[e + 2], kv_len, lds[s2][0], lds[s2][1]);
-    }
-    // the selection is ascending and always holds the query's own block i, so the causal
-    // diagonal block is the last one
-    attend_block<PF_QT>(lds[st][0], lds[st][1], qf, OT, m, lp, l16, lq, qrow0, e + 1 == nsel);
-    // block e+1 must have landed (only block e+2's copies may still be in flight)
-    if (e + 2 < nsel) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();
+  f32x4 SA[4][PF_QT], SB[4][PF_QT];
+  scores<PF_QT>(lds[0][0], qf, SA, l16, lq);
+  auto step = [&](int e, f32x4 (&Sc)[4][PF_QT], f32x4 (&Sn)[4][PF_QT]) {
+    rescale<PF_QT>(Sc, OT, m, lp);
+    const bool more = e + 3 < nsel;
+    if (more) dma_block(kc, vc, row_base, s_sel[e + 3], kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
+    scores<PF_QT>(lds[(e + 1) & 3][0], qf, Sn, l16, lq);
+    exp_pv<PF_QT>(lds[e & 3][1], Sc, OT, m, lp, l16, lq);
+    // block e+2 must have landed (only block e+3's copies may still be in flight)
+    if (more) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();
     __syncthreads();
-    st = st == NSTAGE - 1 ? 0 : st + 1;
+  };
+  int e = 0;
+  for (; e + 2 <= nsel - 1; e += 2) {
+    step(e, SA, SB);
+    step(e + 1, SB, SA);
   }
+  if (e < nsel - 1) {
+    step(e, SA, SB);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < PF_QT; ++qt) SA[kt][qt] = SB[kt][qt];
+  }
+  // diagonal block (index nsel-1)
+  mask_diag<PF_QT>(SA, l16, lq, qrow0);
+  rescale<PF_QT>(SA, OT, m, lp);
+  exp_pv<PF_QT>(lds[(nsel - 1) & 3][1], SA, OT, m, lp, l16, lq);
   if (!head_ok) return;
 
   // ---- normalise, gate, store (lane: query qrow0 + 16qt + l16, dims 16dt + 4lq .. +3)
@@ -271,8 +300,8 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
       const float g0 = __uint_as_float(gv.x << 16), g1 = __uint_as_float(gv.x & 0xffff0000u);
       const float g2 = __uint_as_float(gv.y << 16), g3 = __uint_as_float(gv.y & 0xffff0000u);
       uint2 o;
-      o.x = pack_bf16x2(OT[dt][qt][0] * il * sigmoidf_(g0), OT[dt][qt][1] * il * sigmoidf_(g1));
-      o.y = pack_bf16x2(OT[dt][qt][2] * il * sigmoidf_(g2), OT[dt][qt][3] * il * sigmoidf_(g3));
+      o.x = pack_bf16x2(OT[dt][qt][0] * il * fast_sigmoid(g0), OT[dt][qt][1] * il * fast_sigmoid(g1));
+      o.y = pack_bf16x2(OT[dt][qt][2] * il * fast_sigmoid(g2), OT[dt][qt][3] * il * fast_sigmoid(g3));
       *reinterpret_cast<uint2*>(out + off) = o;
     }
   }
