@@ -22,10 +22,13 @@ typedef uint16_t bf16_t;  // bf16 bits as stored in memory
 
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// round-to-nearest-even conversion (hardware v_cvt_pk_bf16_f32 on gfx950)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// round-to-nearest-even conversion of a pair: one v_cvt_pk_bf16_f32 on gfx950 (converting the
+// two halves separately costs two conversions plus a shift and an OR)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 __device__ __forceinline__ bf16_t f2bf(float x) {
   __bf16 a = (__bf16)x;

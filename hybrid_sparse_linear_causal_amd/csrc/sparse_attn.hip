@@ -30,7 +30,6 @@ namespace {
 constexpr int D = 128;
 constexpr int KS = D + 8;    // K tile row stride (bf16): 272 B
 constexpr int VS = 64 + 8;   // V^T tile row stride (bf16): 144 B
-constexpr float RESCALE_TH = 8.0f;  // log2 units
 constexpr int DEC_SPLIT = 16;       // decode workgroups per (b, g)
 
 constexpr int TILE = 64 * 128;  // bf16 elements per 64-row tile
@@ -41,10 +40,17 @@ __device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
+// V tiles use their own swizzle: chunk c of row r sits at chunk position c ^ 2(r & 7). The
+// transposing reads of 32 lanes touch 8 consecutive rows x 2 adjacent chunks; this puts those
+// 16 chunks at 16 different positions, so they never share a bank (the K swizzle would put two
+// rows on the same banks).
+__device__ __forceinline__ int swzv(int row, int chunk) { return row * 128 + 8 * (chunk ^ (2 * (row & 7))); }
+
 // Issue the DMA of one 64-key block (K and V tiles, 16 KB each = 16 pieces of 1 KB) into a
 // stage. With 8 waves each wave moves pieces 2w and 2w+1 (rows 8w .. 8w+7) of both tiles:
-// DMA_PER_WAVE instructions. Rows at or beyond kv_len are clamped to the last valid row: they
-// are causally masked (K) or weighted 0 (V).
+// DMA_PER_WAVE instructions. Lane l of a piece fills chunk position l % 16 of row 4I + l / 16,
+// so it loads the source chunk that the tile's swizzle puts there. Rows at or beyond kv_len
+// are clamped to the last valid row: they are causally masked (K) or weighted 0 (V).
 constexpr int DMA_PER_WAVE = 4;
 __device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, long row_base,
                                           long blk, long kv_len, bf16_t* Ks, bf16_t* Vs) {
@@ -53,12 +59,13 @@ __device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, lo
   for (int m = 0; m < 2; ++m) {
     const int I = 2 * wave + m;                 // 1 KB piece: rows 4I .. 4I+3
     const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);    // source chunk stored at swizzled position
+    const int chk = (lane & 15) ^ (row & 15);   // K source chunk stored at this position
+    const int chv = (lane & 15) ^ (2 * (row & 7));
     long p = blk * 64 + row;
     if (p >= kv_len) p = kv_len - 1;
-    const long off = (row_base + p) * D + 8 * ch;
-    dma16(kc + off, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Ks + I * 512)));
-    dma16(vc + off, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Vs + I * 512)));
+    const long off = (row_base + p) * D;
+    dma16(kc + off + 8 * chk, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Ks + I * 512)));
+    dma16(vc + off + 8 * chv, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Vs + I * 512)));
   }
 }
 
@@ -70,8 +77,8 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16_t* Vs, int kb, int dt, int 
   const int row0 = kb + 4 * lq + (l16 >> 2);
   const int col = 16 * dt + 4 * (l16 & 3);          // element column; chunk = col / 8
   const int ch = col >> 3, sub = col & 7;
-  const uint2 a = ds_read_tr(Vs + swz(row0, ch) + sub);
-  const uint2 b = ds_read_tr(Vs + swz(row0 + 16, ch) + sub);
+  const uint2 a = ds_read_tr(Vs + swzv(row0, ch) + sub);
+  const uint2 b = ds_read_tr(Vs + swzv(row0 + 16, ch) + sub);
   return as_bf16x8(a, b);
 }
 
@@ -79,19 +86,19 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16_t* Vs, int kb, int dt, int 
 // ---- pieces of one wave's work on a staged 64-key block for its QT x 16 query rows (rows
 // qrow0 + 16*qt + l16 of the query block)
 
-// S^T[kt][qt] = K[kt] Q^T[qt] (scores in log2 units: scale*log2(e) is folded into q)
+// S^T[kt][qt] = K[kt] Q^T[qt] - m[qt] (scores in log2 units: scale*log2(e) is folded into q;
+// the running reference m enters as the accumulator's initial value, minit = -m)
 template <int QT>
-__device__ __forceinline__ void scores(const bf16_t* Ks, const bf16x8 (&qf)[QT][4], f32x4 (&ST)[4][QT],
-                                       int l16, int lq) {
+__device__ __forceinline__ void scores(const bf16_t* Ks, const bf16x8 (&qf)[QT][4], const f32x4 (&minit)[QT],
+                                       f32x4 (&ST)[4][QT], int l16) {
+  const int lq = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + swz(16 * kt + l16, 4 * ks + lq)));
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ST[kt][qt]);
+      for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ks == 0 ? minit[qt] : ST[kt][qt]);
     }
   }
 }
@@ -108,55 +115,75 @@ __device__ __forceinline__ void mask_diag(f32x4 (&ST)[4][QT], int l16, int lq, i
         if (16 * kt + 4 * lq + c > qrow0 + 16 * qt + l16) ST[kt][qt][c] = -INFINITY;
 }
 
-// Lazy online-softmax rescale: the running maximum moves only when a row maximum exceeds it
-// by more than RESCALE_TH (log2 units), so exp2 arguments stay <= RESCALE_TH and the running
-// output is rarely rescaled.
+// Online softmax with a lazily raised reference. The score accumulators already hold s - m,
+// so the probabilities are plain exp2 of them. A 32-key half whose per-lane partial sum exceeds
+// P_LIMIT (some probability above 2^20), and the first half the row ever sees, raise m to the
+// half's row maximum first: the running output and sum are rescaled, and the not yet consumed
+// scores (this block and the next one, already issued with the old reference) are shifted.
+// The reference is always a score of the row, so the row's largest probability is >= 1.
+constexpr float P_LIMIT = 1048576.0f;  // 2^20
+
 template <int QT>
-__device__ __forceinline__ void rescale(const f32x4 (&ST)[4][QT], f32x4 (&OT)[8][QT], float (&m)[QT],
-                                        float (&lp)[QT]) {
-  bool any_need = false;
-  float mn[QT];
+__device__ __forceinline__ void exp_half(const f32x4 (&ST)[4][QT], int c, float (&p)[QT][8], float (&part)[QT]) {
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    float mx = fmaxf(fmaxf(ST[0][qt][0], ST[0][qt][1]), fmaxf(ST[0][qt][2], ST[0][qt][3]));
 #pragma unroll
-    for (int kt = 1; kt < 4; ++kt)
-      mx = fmaxf(mx, fmaxf(fmaxf(ST[kt][qt][0], ST[kt][qt][1]), fmaxf(ST[kt][qt][2], ST[kt][qt][3])));
+    for (int u = 0; u < 4; ++u) {
+      p[qt][u] = fast_exp2(ST[2 * c][qt][u]);
+      p[qt][4 + u] = fast_exp2(ST[2 * c + 1][qt][u]);
+    }
+    part[qt] = ((p[qt][0] + p[qt][1]) + (p[qt][2] + p[qt][3])) + ((p[qt][4] + p[qt][5]) + (p[qt][6] + p[qt][7]));
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ void raise_ref(f32x4 (&ST)[4][QT], f32x4 (&SN)[4][QT], f32x4 (&OT)[8][QT], float (&m)[QT],
+                                       f32x4 (&minit)[QT], float (&lp)[QT], int c, bool first) {
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(ST[2 * c][qt][u], ST[2 * c + 1][qt][u]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool need = mx > m[qt] + RESCALE_TH;
-    mn[qt] = need ? mx : m[qt];
-    any_need |= need;
-  }
-  if (__any(any_need)) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const float alpha = fast_exp2(m[qt] - mn[qt]);
+    const float delta = first ? mx : fmaxf(mx, 0.0f);
+    if (!first) {
+      const float alpha = fast_exp2(-delta);
       lp[qt] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) OT[dt][qt] *= alpha;
-      m[qt] = mn[qt];
+    }
+    m[qt] += delta;
+    minit[qt] = f32x4{-m[qt], -m[qt], -m[qt], -m[qt]};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      ST[kt][qt] -= delta;
+      SN[kt][qt] -= delta;
     }
   }
 }
 
-// P^T = exp2(S^T - m) per 32-key half, O^T += V^T P^T (P^T straight from the accumulators)
+// P^T = exp2(S^T) per 32-key half, O^T += V^T P^T (P^T straight from the accumulators)
 template <int QT>
-__device__ __forceinline__ void exp_pv(const bf16_t* Vs, const f32x4 (&ST)[4][QT], f32x4 (&OT)[8][QT],
-                                       const float (&m)[QT], float (&lp)[QT], int l16, int lq) {
+__device__ __forceinline__ void exp_pv(const bf16_t* Vs, f32x4 (&ST)[4][QT], f32x4 (&SN)[4][QT], f32x4 (&OT)[8][QT],
+                                       float (&m)[QT], f32x4 (&minit)[QT], float (&lp)[QT], int l16, int lq,
+                                       bool first) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
+    float p[QT][8], part[QT];
+    exp_half<QT>(ST, c, p, part);
+    bool big = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) big |= part[qt] > P_LIMIT;
+    if (__builtin_expect(__any(big) || (first && c == 0), 0)) {
+      raise_ref<QT>(ST, SN, OT, m, minit, lp, c, first && c == 0);
+      exp_half<QT>(ST, c, p, part);
+    }
     bf16x8 pf[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      float p[8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        p[u] = fast_exp2(ST[2 * c][qt][u] - m[qt]);
-        p[4 + u] = fast_exp2(ST[2 * c + 1][qt][u] - m[qt]);
-      }
-      lp[qt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      pf[qt] = as_bf16x8(pack8(p));
+      lp[qt] += part[qt];
+      pf[qt] = as_bf16x8(pack8(p[qt]));
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -234,9 +261,14 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   while (nsel < topk && s_sel[nsel] >= 0) ++nsel;
 
   float m[PF_QT], lp[PF_QT];
+  f32x4 minit[PF_QT];
   f32x4 OT[8][PF_QT];
 #pragma unroll
-  for (int qt = 0; qt < PF_QT; ++qt) { m[qt] = -INFINITY; lp[qt] = 0.f; }
+  for (int qt = 0; qt < PF_QT; ++qt) {
+    m[qt] = 0.f;  // replaced by the row maximum of the first half-block
+    lp[qt] = 0.f;
+    minit[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -254,13 +286,12 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   __syncthreads();
 
   f32x4 SA[4][PF_QT], SB[4][PF_QT];
-  scores<PF_QT>(lds[0][0], qf, SA, l16, lq);
+  scores<PF_QT>(lds[0][0], qf, minit, SA, l16);
   auto step = [&](int e, f32x4 (&Sc)[4][PF_QT], f32x4 (&Sn)[4][PF_QT]) {
-    rescale<PF_QT>(Sc, OT, m, lp);
     const bool more = e + 3 < nsel;
     if (more) dma_block(kc, vc, row_base, s_sel[e + 3], kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
-    scores<PF_QT>(lds[(e + 1) & 3][0], qf, Sn, l16, lq);
-    exp_pv<PF_QT>(lds[e & 3][1], Sc, OT, m, lp, l16, lq);
+    scores<PF_QT>(lds[(e + 1) & 3][0], qf, minit, Sn, l16);
+    exp_pv<PF_QT>(lds[e & 3][1], Sc, Sn, OT, m, minit, lp, l16, lq, e == 0);
     // block e+2 must have landed (only block e+3's copies may still be in flight)
     if (more) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();
     __syncthreads();
@@ -277,10 +308,9 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
 #pragma unroll
       for (int qt = 0; qt < PF_QT; ++qt) SA[kt][qt] = SB[kt][qt];
   }
-  // diagonal block (index nsel-1)
+  // diagonal block (index nsel-1); SB only receives the (unused) shift of a raised reference
   mask_diag<PF_QT>(SA, l16, lq, qrow0);
-  rescale<PF_QT>(SA, OT, m, lp);
-  exp_pv<PF_QT>(lds[(nsel - 1) & 3][1], SA, OT, m, lp, l16, lq);
+  exp_pv<PF_QT>(lds[(nsel - 1) & 3][1], SA, SB, OT, m, minit, lp, l16, lq, nsel == 1);
   if (!head_ok) return;
 
   // ---- normalise, gate, store (lane: query qrow0 + 16qt + l16, dims 16dt + 4lq .. +3)
