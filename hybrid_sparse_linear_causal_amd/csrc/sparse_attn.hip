@@ -92,13 +92,17 @@ template <int QT>
 __device__ __forceinline__ void scores(const bf16_t* Ks, const bf16x8 (&qf)[QT][4], const f32x4 (&minit)[QT],
                                        f32x4 (&ST)[4][QT], int l16) {
   const int lq = (threadIdx.x & 63) >> 4;
+  // two key tiles per k-step: 2*QT independent accumulators between reuses of one
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int kp = 0; kp < 4; kp += 2) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + swz(16 * kt + l16, 4 * ks + lq)));
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ks == 0 ? minit[qt] : ST[kt][qt]);
+      for (int kt = kp; kt < kp + 2; ++kt) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + swz(16 * kt + l16, 4 * ks + lq)));
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ks == 0 ? minit[qt] : ST[kt][qt]);
+      }
     }
   }
 }
