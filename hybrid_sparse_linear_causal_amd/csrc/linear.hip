@@ -109,6 +109,29 @@ __device__ __forceinline__ void norm_rope(uint4 (&x)[2], const float* w, int s, 
   x[1] = pack8(rb);
 }
 
+// norm_rope with the 16 norm weights of the thread's dims already in registers
+__device__ __forceinline__ void norm_rope_w(uint4 (&x)[2], const float* w, float eps, const float* cs,
+                                            const float* sn) {
+  float a[8], b[8];
+  unpack8(x[0], a);
+  unpack8(x[1], b);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
+  ss = group_sum<8>(ss);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  float ra[8], rb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float xa = a[e] * w[e], xb = b[e] * w[8 + e];
+    const float c = cs[e] * inv, sg = sn[e] * inv;
+    ra[e] = xa * c - xb * sg;
+    rb[e] = xa * sg + xb * c;
+  }
+  x[0] = pack8(ra);
+  x[1] = pack8(rb);
+}
+
 template <bool STATE_ONLY>
 __global__ void __launch_bounds__(NT, 2)
 linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -355,6 +378,7 @@ __device__ __forceinline__ void dma_chunk(const bf16_t* q, const bf16_t* k, cons
   }
 }
 
+template <bool HAS_W>
 __global__ void __launch_bounds__(OUT_NT)
 linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                   const bf16_t* __restrict__ v, const bf16_t* __restrict__ g,
@@ -407,11 +431,16 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
       }
   }
-  // RoPE table for this thread's token x 8 frequencies, advanced 64 positions per chunk
-  float rc[8], rs[8];
+  // norm weights of this thread's 16 dims (segments s8 and s8+8), loaded once: a load inside
+  // the chunk loop would wait for the in-flight copies of the next chunk
+  float wq[16], wk[16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    sincos_rev(rope_rev((double)(pos0 + t_begin + tok), freqs.f[8 * s8 + e]), &rs[e], &rc[e]);
+  for (int e = 0; e < 8; ++e) {
+    wq[e] = HAS_W && qw ? qw[8 * s8 + e] : 1.0f;
+    wq[8 + e] = HAS_W && qw ? qw[64 + 8 * s8 + e] : 1.0f;
+    wk[e] = HAS_W && kw ? kw[8 * s8 + e] : 1.0f;
+    wk[8 + e] = HAS_W && kw ? kw[64 + 8 * s8 + e] : 1.0f;
+  }
 
   wait_vmcnt<0>();
   __syncthreads();
@@ -432,8 +461,13 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       xq[1] = *reinterpret_cast<const uint4*>(&Qt[swz(tok, s8 + 8)]);
       xk[0] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8)]);
       xk[1] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8 + 8)]);
-      norm_rope(xq, qw, s8, eps, rc, rs);
-      norm_rope(xk, kw, s8, eps, rc, rs);
+      // RoPE angles of this token, computed afresh (fp64 reduction of the position)
+      float rc[8], rs[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sincos_rev(rope_rev((double)(pos0 + c0 + tok), freqs.f[8 * s8 + e]), &rs[e], &rc[e]);
+      norm_rope_w(xq, wq, eps, rc, rs);
+      norm_rope_w(xk, wk, eps, rc, rs);
       if (c0 + tok >= t_end) { xk[0] = make_uint4(0, 0, 0, 0); xk[1] = xk[0]; }
       *reinterpret_cast<uint4*>(&Qt[swz(tok, s8)]) = xq[0];
       *reinterpret_cast<uint4*>(&Qt[swz(tok, s8 + 8)]) = xq[1];
@@ -442,7 +476,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
     __syncthreads();
 
-    const int tl = 16 * w4 + l16, tq = c0 + tl;
+    const int tl = 16 * w4 + l16;
     uint2 gv[8];
     if (out_wave) {
       // ---------------- intra-chunk: O^T = V^T (K~ Q~^T (.) causal) for queries 16w..16w+15
@@ -510,14 +544,18 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       }
     }
     __syncthreads();  // every read of this chunk's S^T, q~, k~, v and g tiles is done
-    uint2 ov[8];
     if (out_wave) {
+      // gated outputs staged in this wave's 16 rows of the (consumed) q~ tile, so that the
+      // stores below write whole 256-byte rows
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const float g0 = __uint_as_float(gv[dt].x << 16), g1 = __uint_as_float(gv[dt].x & 0xffff0000u);
         const float g2 = __uint_as_float(gv[dt].y << 16), g3 = __uint_as_float(gv[dt].y & 0xffff0000u);
-        ov[dt].x = pack_bf16x2(acc[dt][0] * fast_sigmoid(g0), acc[dt][1] * fast_sigmoid(g1));
-        ov[dt].y = pack_bf16x2(acc[dt][2] * fast_sigmoid(g2), acc[dt][3] * fast_sigmoid(g3));
+        uint2 o;
+        o.x = pack_bf16x2(acc[dt][0] * fast_sigmoid(g0), acc[dt][1] * fast_sigmoid(g1));
+        o.y = pack_bf16x2(acc[dt][2] * fast_sigmoid(g2), acc[dt][3] * fast_sigmoid(g3));
+        const int col = 16 * dt + 4 * lq;
+        *reinterpret_cast<uint2*>(&Qt[swz(tl, col >> 3) + (col & 7)]) = o;
       }
     } else {
 #pragma unroll
@@ -531,20 +569,18 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
         }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float c = rc[e], sn = rs[e];
-      const float ac = freqs.c64[8 * s8 + e], as = freqs.s64[8 * s8 + e];
-      rc[e] = c * ac - sn * as;
-      rs[e] = sn * ac + c * as;
-    }
     // the next chunk's tiles must have landed before the barrier; the output stores are issued
     // after this wait so that they never hold it up
     wait_vmcnt<0>();
-    if (out_wave && tq < t_end) {
-      bf16_t* dst = out + head_off + (long)tq * tok_stride + 4 * lq;
+    if (out_wave) {
+      // a wave's LDS accesses complete in order, so its staged rows are read back as written
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<uint2*>(dst + 16 * dt) = ov[dt];
+      for (int r = 0; r < 4; ++r) {
+        const int rl = 16 * w4 + 4 * r + lq, tr = c0 + rl;  // lane: row rl, 16-byte chunk l16
+        const uint4 o = *reinterpret_cast<const uint4*>(&Qt[swz(rl, l16)]);
+        if (tr < t_end) *reinterpret_cast<uint4*>(out + head_off + (long)tr * tok_stride + 8 * l16) = o;
+      }
     }
     __syncthreads();
     buf ^= 1;
@@ -779,12 +815,22 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
     hipLaunchKernelGGL(linear_scan_kernel, dim3(B * H, D * D / 256), dim3(256), 0, st, state_in,
                        wsf, nseg, D * D);
   }
-  static const hipError_t attr_ok = hipFuncSetAttribute(
-      (const void*)linear_out_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutLds));
+  static const hipError_t attr_ok = [] {
+    const hipError_t e0 = hipFuncSetAttribute((const void*)linear_out_kernel<false>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutLds));
+    const hipError_t e1 = hipFuncSetAttribute((const void*)linear_out_kernel<true>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutLds));
+    return e0 != hipSuccess ? e0 : e1;
+  }();
   if (attr_ok != hipSuccess) return attr_ok;
-  hipLaunchKernelGGL(linear_out_kernel, dim3(B * H * nseg), dim3(OUT_NT), sizeof(OutLds), st, qb, kb, vb,
-                     gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, N, H, (long)d.pos0, seg,
-                     nseg, d.norm_eps, fr);
+  if (qw || kw)
+    hipLaunchKernelGGL(linear_out_kernel<true>, dim3(B * H * nseg), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
+                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, N, H, (long)d.pos0, seg,
+                       nseg, d.norm_eps, fr);
+  else
+    hipLaunchKernelGGL(linear_out_kernel<false>, dim3(B * H * nseg), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
+                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, N, H, (long)d.pos0, seg,
+                       nseg, d.norm_eps, fr);
   return hipGetLastError();
 }
 
