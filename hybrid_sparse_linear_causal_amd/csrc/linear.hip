@@ -442,6 +442,12 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     wk[8 + e] = HAS_W && kw ? kw[64 + 8 * s8 + e] : 1.0f;
   }
 
+  // this thread's 8 RoPE frequencies, also loaded once (indexing the argument block per lane
+  // compiles to memory loads)
+  double fr8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) fr8[e] = freqs.f[8 * s8 + e];
+
   wait_vmcnt<0>();
   __syncthreads();
   int buf = 0;
@@ -465,7 +471,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       float rc[8], rs[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        sincos_rev(rope_rev((double)(pos0 + c0 + tok), freqs.f[8 * s8 + e]), &rs[e], &rc[e]);
+        sincos_rev(rope_rev((double)(pos0 + c0 + tok), fr8[e]), &rs[e], &rc[e]);
       norm_rope_w(xq, wq, eps, rc, rs);
       norm_rope_w(xk, wk, eps, rc, rs);
       if (c0 + tok >= t_end) { xk[0] = make_uint4(0, 0, 0, 0); xk[1] = xk[0]; }
