@@ -11,12 +11,12 @@
 // MFMA 16x16x32 (bf16 operands, fp32 accumulation); the state is kept in fp32 registers and
 // handed to MFMA as bf16 once per chunk. To fill 256 CUs at batch 1 the sequence is cut into
 // segments processed in parallel:
-//   1. linear_chunk_kernel<true>  : per (b, h, segment s < last) the segment's sum of k^T v,
-//                                   written to workspace slot s + 1
-//   2. linear_scan_kernel         : per (b, h): slot 0 = state_in (or 0), slot s = slot s-1 +
-//                                   slot s, i.e. the state entering segment s
-//   3. linear_chunk_kernel<false> : per (b, h, segment) the chunk loop from its start state,
-//                                   writing gated outputs (and, last segment, the final state)
+//   1. linear_segsum_kernel : per (b, h, segment s < last) the segment's sum of k^T v,
+//                             written to workspace slot s + 1
+//   2. linear_scan_kernel   : per (b, h): slot 0 = state_in (or 0), slot s = slot s-1 +
+//                             slot s, i.e. the state entering segment s
+//   3. linear_out_kernel    : per (b, h, segment) the chunk loop from its start state, writing
+//                             gated outputs (and, last segment, the final state)
 // With a single segment the workspace is unused and state_in is read directly. Reading the
 // entering state from the workspace otherwise lets state_out alias state_in safely.
 #include "common.hpp"
@@ -28,60 +28,6 @@ namespace {
 
 constexpr int D = 128;   // head dim of the bf16 MFMA path
 constexpr int CH = 64;   // chunk length (tokens)
-constexpr int NT = 256;  // threads per workgroup (4 waves)
-
-// 80 KB: two workgroups fit in one CU's 160 KB. All tiles are row-major with 256-byte rows in
-// the swizzled layout of swz(); column operands along the token axis come from transposing
-// reads, so nothing is ever transposed in registers.
-struct LinearLds {
-  bf16_t q[CH * D];   // q~  [token][dk]
-  bf16_t k[CH * D];   // k~  [token][dk]
-  bf16_t v[CH * D];   // v   [token][dv] (DMA copy of the input rows)
-  bf16_t st[D * D];   // S^T [dv][dk] as bf16: the state entering the chunk
-};
-
-__device__ __forceinline__ uint4 ld16(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// Raw q and k of thread j's two tokens 2*(j/8) + u, 16-byte segments s = j%8 and s+8 (dims
-// 8s..8s+7 and 64+8s..64+8s+7, which RoPE pairs with each other).
-struct QKRegs {
-  uint4 q[2][2], k[2][2];
-};
-
-template <bool STATE_ONLY>
-__device__ __forceinline__ void load_qk(QKRegs& r, const bf16_t* q, const bf16_t* k, long row0,
-                                        int t0, int n_valid, int H) {
-  const int j = threadIdx.x, s = j & 7;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int t = 2 * (j >> 3) + u;
-    const bool ok = (t0 + t) < n_valid;
-    const long base = row0 + (long)t * H * D;
-#pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-      const int off = 8 * (s + 8 * hs);
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      r.k[u][hs] = ok ? ld16(k + base + off) : z;
-      if (!STATE_ONLY) r.q[u][hs] = ok ? ld16(q + base + off) : z;
-    }
-  }
-}
-
-// V tile of one chunk by DMA: wave w copies rows 16w .. 16w+15 (four 1 KB pieces). Rows past
-// the end of the sequence are clamped to its last row: their k~ rows are zero, so they add
-// exactly nothing, and a finite copy keeps 0 * v finite.
-__device__ __forceinline__ void dma_v(const bf16_t* v, long row0, int t0, int n_valid, int H,
-                                      bf16_t* Vs) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int I = 4 * wave + m;
-    const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
-    const int t = min(t0 + row, n_valid - 1) - t0;
-    dma16(v + row0 + (long)t * H * D + 8 * ch, lds_addr_u32(Vs + I * 512));
-  }
-}
 
 // QK-norm + RoPE of one token's 16 values held by this thread (two 8-dim halves that RoPE
 // pairs), given the cos/sin of its 8 angles. The row's sum of squares is reduced over the 8
@@ -132,219 +78,128 @@ __device__ __forceinline__ void norm_rope_w(uint4 (&x)[2], const float* w, float
   x[1] = pack8(rb);
 }
 
-template <bool STATE_ONLY>
-__global__ void __launch_bounds__(NT, 2)
-linear_chunk_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                    const bf16_t* __restrict__ v, const bf16_t* __restrict__ g,
-                    const float* __restrict__ qw, const float* __restrict__ kw,
-                    const float* __restrict__ state_in, float* __restrict__ ws,
-                    float* __restrict__ state_out, bf16_t* __restrict__ out, int N, int H,
-                    long pos0, int seg_len, int nseg, float eps, RopeFreqs freqs) {
-  __shared__ __align__(16) LinearLds L;
-  const int nseg_w = STATE_ONLY ? nseg - 1 : nseg;
-  const int seg = blockIdx.x % nseg_w;
-  const int bh = blockIdx.x / nseg_w;
+// ---- segment sums: per (b, h, segment s < last) the sum over the segment of k~^T v, into
+// workspace slot s + 1. The k and v tiles of the chunks stream through a ring of SS_NS stages
+// by DMA (the next chunk lands while one is processed), k is normalised and rotated in place,
+// and wave w accumulates rows 16w .. 16w+15 of the 128 x 128 sum. With two stages (64 KB) two
+// workgroups share a CU, which measured faster than deeper rings with one workgroup per CU.
+constexpr int SS_NT = 512;
+constexpr int SS_NS = 2;
+struct SegLds {
+  bf16_t k[SS_NS][CH * D];  // [stage][token][dk]
+  bf16_t v[SS_NS][CH * D];  // [stage][token][dv]
+};
+static_assert(sizeof(SegLds) == SS_NS * 32768, "segment-sum LDS plan");
+
+// Both tiles are read only by transposing reads (4 rows x 2 chunks per 16 lanes, rows r and
+// r + 8 in the same 32 lanes); chunk c of row r sits at position c ^ f(r) with
+// f(r) = 2(r & 3) + 8((r >> 3) & 1), which gives those reads distinct banks.
+__device__ __forceinline__ int swzt(int row, int chunk) {
+  return row * 128 + 8 * (chunk ^ (2 * (row & 3) + 8 * ((row >> 3) & 1)));
+}
+__device__ __forceinline__ bf16x8 tr_frag_t(const bf16_t* T, int k0, int d1, int c0, int l16) {
+  const int row = k0 + (l16 >> 2), col = c0 + 4 * (l16 & 3);
+  const uint2 a = ds_read_tr(T + swzt(row, col >> 3) + (col & 7));
+  const uint2 b = ds_read_tr(T + swzt(row + d1, col >> 3) + (col & 7));
+  return as_bf16x8(a, b);
+}
+// DMA of one chunk's k and v tiles (32 pieces of 1 KB; wave w moves pieces 2w and 2w+1 of
+// each): SS_DMA instructions per wave. The segment is whole, so every row exists.
+constexpr int SS_DMA = 4;
+__device__ __forceinline__ void dma_kv(const bf16_t* k, const bf16_t* v, long row0, long tok_stride,
+                                       bf16_t* Ks, bf16_t* Vs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int I = 2 * wave + m;
+    const int row = 4 * I + (lane >> 4);
+    const int ch = (lane & 15) ^ (2 * (row & 3) + 8 * ((row >> 3) & 1));
+    const long off = row0 + (long)row * tok_stride + 8 * ch;
+    dma16(k + off, lds_addr_u32(Ks + I * 512));
+    dma16(v + off, lds_addr_u32(Vs + I * 512));
+  }
+}
+
+template <bool HAS_W>
+__global__ void __launch_bounds__(SS_NT)
+linear_segsum_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                     const float* __restrict__ kw, float* __restrict__ ws, int N, int H, long pos0,
+                     int seg_len, int nseg, float eps, RopeFreqs freqs) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  SegLds& L = *reinterpret_cast<SegLds*>(lds_raw);
+  const int nsw = nseg - 1;
+  const int seg = blockIdx.x % nsw;
+  const int bh = blockIdx.x / nsw;
   const int b = bh / H, h = bh % H;
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
-  const int s8 = j & 7, tp = j >> 3;
-
+  const int s8 = j & 7, tok = j >> 3;  // prep: one token, segments s8 and s8+8
   const int t_begin = seg * seg_len;
-  const int t_end = min(N, t_begin + seg_len);
-  const long head_off = ((long)b * N * H + h) * D;  // element offset of (b, t=0, h, 0)
+  const int nch = seg_len / CH;
   const long tok_stride = (long)H * D;
+  const long row0 = ((long)b * N * H + h) * D + (long)t_begin * tok_stride;
 
-  // ---- state entering the segment: S[dk][dv] in MFMA C layout; wave owns dk rows 32w..32w+31
-  f32x4 S[2][8];
-  {
-    const float* src = nullptr;
-    if (!STATE_ONLY) {
-      if (nseg == 1) src = state_in ? state_in + (long)bh * D * D : nullptr;
-      else src = ws + ((long)bh * nseg + seg) * D * D;
-    }
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int dk = 32 * wave + 16 * it + 4 * lq + e, dv = 16 * jt + l16;
-          S[it][jt][e] = src ? src[dk * D + dv] : 0.f;
-        }
-  }
+  for (int x = 0; x < SS_NS - 1; ++x)
+    if (x < nch) dma_kv(k, v, row0 + (long)x * CH * tok_stride, tok_stride, L.k[x], L.v[x]);
 
-  // ---- RoPE table: cos/sin of this thread's 8 frequencies at its 2 token offsets, exact at
-  // the segment start (fp64 range reduction) and advanced by a fixed rotation of 64 positions
-  // per chunk.
-  float rc[2][8], rs[2][8];
+  // Norm weights of this thread's 16 dims and its RoPE table, set up once (a memory load in
+  // the loop would wait for the chunks in flight): cos/sin of its token's 8 angles, exact at
+  // the segment start (fp64 reduction) and advanced by the rotation of 64 positions per chunk.
+  float wk[16], rc[8], rs[8], ac[8], as[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const double f = freqs.f[8 * s8 + e];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      sincos_rev(rope_rev((double)(pos0 + t_begin + 2 * tp + u), f), &rs[u][e], &rc[u][e]);
+    wk[e] = HAS_W ? kw[8 * s8 + e] : 1.0f;
+    wk[8 + e] = HAS_W ? kw[64 + 8 * s8 + e] : 1.0f;
+    sincos_rev(rope_rev((double)(pos0 + t_begin + tok), freqs.f[8 * s8 + e]), &rs[e], &rc[e]);
+    ac[e] = freqs.c64[8 * s8 + e];
+    as[e] = freqs.s64[8 * s8 + e];
   }
+  f32x4 S[8];
+#pragma unroll
+  for (int jt = 0; jt < 8; ++jt) S[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  QKRegs cur;
-  load_qk<STATE_ONLY>(cur, q, k, head_off + (long)t_begin * tok_stride, t_begin, N, H);
-  dma_v(v, head_off + (long)t_begin * tok_stride, t_begin, N, H, L.v);
-  if (!STATE_ONLY) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        uint2 p;
-        p.x = pack_bf16x2(S[it][jt][0], S[it][jt][1]);
-        p.y = pack_bf16x2(S[it][jt][2], S[it][jt][3]);
-        const int dk0 = 32 * wave + 16 * it + 4 * lq, dv = 16 * jt + l16;
-        *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
-      }
-  }
-
-  for (int c0 = t_begin; c0 < t_end; c0 += CH) {
-    // ---------------- prep: QK-norm + RoPE into the q~ / k~ tiles
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = 2 * tp + u;
-      norm_rope(cur.k[u], kw, s8, eps, rc[u], rs[u]);
-      *reinterpret_cast<uint4*>(&L.k[swz(t, s8)]) = cur.k[u][0];
-      *reinterpret_cast<uint4*>(&L.k[swz(t, s8 + 8)]) = cur.k[u][1];
-      if (!STATE_ONLY) {
-        norm_rope(cur.q[u], qw, s8, eps, rc[u], rs[u]);
-        *reinterpret_cast<uint4*>(&L.q[swz(t, s8)]) = cur.q[u][0];
-        *reinterpret_cast<uint4*>(&L.q[swz(t, s8 + 8)]) = cur.q[u][1];
-      }
-    }
-    wait_vmcnt<0>();  // this chunk's V tile has landed
-    __syncthreads();
-    const bool more = c0 + CH < t_end;
-    // this wave's 16 query tokens c0 + 16w + l16: gate values for the output (lane's 4-dim runs)
-    const int tq = c0 + 16 * wave + l16;
-    f32x4 OT[8];
-    if (!STATE_ONLY) {
-      // ---------------- intra-chunk: O^T = V^T (K~ Q~^T (.) causal) for queries 16w..16w+15
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) OT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 qfrag[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qfrag[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&L.q[swz(16 * wave + l16, 4 * ks + lq)]));
-      for (int c = 0; 2 * c <= wave; ++c) {
-        f32x4 at[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int kt = 2 * c + hh;
-          at[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (kt <= wave) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.k[swz(16 * kt + l16, 4 * ks + lq)]));
-              at[hh] = mfma16x16x32(kf, qfrag[ks], at[hh]);
-            }
-            if (kt == wave) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (4 * lq + e > l16) at[hh][e] = 0.f;  // key after query: masked
-            }
-          }
-        }
-        uint4 pb;
-        pb.x = pack_bf16x2(at[0][0], at[0][1]);
-        pb.y = pack_bf16x2(at[0][2], at[0][3]);
-        pb.z = pack_bf16x2(at[1][0], at[1][1]);
-        pb.w = pack_bf16x2(at[1][2], at[1][3]);
-        const bf16x8 pfrag = as_bf16x8(pb);
-        // A = V^T with the keys in P^T's slot order (kb + 4lq + e, kb + 16 + 4lq + e)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          OT[dt] = mfma16x16x32(tr_frag(L.v, 32 * c + 4 * lq, 16, 16 * dt, l16), pfrag, OT[dt]);
-      }
-      // ---------------- inter-chunk: O^T += S^T Q~^T
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 sf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.st[swz(16 * dt + l16, 4 * ks + lq)]));
-          OT[dt] = mfma16x16x32(sf, qfrag[ks], OT[dt]);
-        }
-    }
-
-    // ---------------- state update: S += K~^T V (wave: dk rows 32w..32w+31, all dv)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[2];
-#pragma unroll
-      for (int it = 0; it < 2; ++it) af[it] = tr_frag(L.k, 32 * ks + 8 * lq, 4, 32 * wave + 16 * it, l16);
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        const bf16x8 bfr = tr_frag(L.v, 32 * ks + 8 * lq, 4, 16 * jt, l16);
-#pragma unroll
-        for (int it = 0; it < 2; ++it) S[it][jt] = mfma16x16x32(af[it], bfr, S[it][jt]);
-      }
-    }
-    __syncthreads();  // every read of the q~, k~, v and S^T tiles of this chunk is done
-    if (more) {  // next chunk's inputs load while this chunk's results are written
-      dma_v(v, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H, L.v);
-      load_qk<STATE_ONLY>(cur, q, k, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H);
-    }
-
-    if (!STATE_ONLY) {
-      // new S^T (bf16) for the next chunk
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int jt = 0; jt < 8; ++jt) {
-          uint2 p;
-          p.x = pack_bf16x2(S[it][jt][0], S[it][jt][1]);
-          p.y = pack_bf16x2(S[it][jt][2], S[it][jt][3]);
-          const int dk0 = 32 * wave + 16 * it + 4 * lq, dv = 16 * jt + l16;
-          *reinterpret_cast<uint2*>(&L.st[swz(dv, dk0 >> 3) + (dk0 & 7)]) = p;
-        }
-      // gated output straight from the accumulators: out = O * sigmoid(g)
-      if (tq < t_end) {
-        bf16_t* dst = out + head_off + (long)tq * tok_stride + 4 * lq;
-        const bf16_t* gsrc = g + head_off + (long)tq * tok_stride + 4 * lq;
-        uint2 gv[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) gv[dt] = *reinterpret_cast<const uint2*>(gsrc + 16 * dt);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const float g0 = __uint_as_float(gv[dt].x << 16), g1 = __uint_as_float(gv[dt].x & 0xffff0000u);
-          const float g2 = __uint_as_float(gv[dt].y << 16), g3 = __uint_as_float(gv[dt].y & 0xffff0000u);
-          uint2 o;
-          o.x = pack_bf16x2(OT[dt][0] * fast_sigmoid(g0), OT[dt][1] * fast_sigmoid(g1));
-          o.y = pack_bf16x2(OT[dt][2] * fast_sigmoid(g2), OT[dt][3] * fast_sigmoid(g3));
-          *reinterpret_cast<uint2*>(dst + 16 * dt) = o;
-        }
-      }
-    }
-    // advance the RoPE table by 64 positions
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
+  for (int c = 0; c < nch; ++c) {
+    const int st = c % SS_NS;
+    // chunk c has landed once at most the chunks issued after it are in flight
+    const int ahead = min(SS_NS - 2, nch - 1 - c);
+    if (ahead >= 2) wait_vmcnt<2 * SS_DMA>();
+    else if (ahead == 1) wait_vmcnt<SS_DMA>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // chunk c visible to all; every wave is done with chunk c-1's stage
+    if (c + SS_NS - 1 < nch)
+      dma_kv(k, v, row0 + (long)(c + SS_NS - 1) * CH * tok_stride, tok_stride,
+             L.k[(c + SS_NS - 1) % SS_NS], L.v[(c + SS_NS - 1) % SS_NS]);
+    bf16_t* Kt = L.k[st];
+    {
+      uint4 x[2];
+      x[0] = *reinterpret_cast<const uint4*>(&Kt[swzt(tok, s8)]);
+      x[1] = *reinterpret_cast<const uint4*>(&Kt[swzt(tok, s8 + 8)]);
+      norm_rope_w(x, wk, eps, rc, rs);
+      *reinterpret_cast<uint4*>(&Kt[swzt(tok, s8)]) = x[0];
+      *reinterpret_cast<uint4*>(&Kt[swzt(tok, s8 + 8)]) = x[1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float c = rc[u][e], sn = rs[u][e];
-        const float ac = freqs.c64[8 * s8 + e], as = freqs.s64[8 * s8 + e];
-        rc[u][e] = c * ac - sn * as;
-        rs[u][e] = sn * ac + c * as;
+        const float c0 = rc[e], s0 = rs[e];
+        rc[e] = c0 * ac[e] - s0 * as[e];
+        rs[e] = s0 * ac[e] + c0 * as[e];
       }
-  }
-
-  // ---- segment result: state-only -> segment sum into slot seg+1; last segment -> final state
-  float* dst = nullptr;
-  if (STATE_ONLY) dst = ws + ((long)bh * nseg + seg + 1) * D * D;
-  else if (seg == nseg - 1 && state_out) dst = state_out + (long)bh * D * D;
-  if (dst) {
+    }
+    __syncthreads();
+    const bf16_t* Vt = L.v[st];
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 af = tr_frag_t(Kt, 32 * ks + 8 * lq, 4, 16 * wave, l16);
 #pragma unroll
       for (int jt = 0; jt < 8; ++jt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int dk = 32 * wave + 16 * it + 4 * lq + e, dv = 16 * jt + l16;
-          dst[dk * D + dv] = S[it][jt][e];
-        }
+        S[jt] = mfma16x16x32(af, tr_frag_t(Vt, 32 * ks + 8 * lq, 4, 16 * jt, l16), S[jt]);
+    }
   }
+  float* dst = ws + ((long)bh * nseg + seg + 1) * D * D;
+#pragma unroll
+  for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * lq + e) * D + 16 * jt + l16] = S[jt][e];
 }
 
 // ---- output pass: one workgroup per CU owning the whole 160 KB of LDS. The raw q, k, v and
@@ -442,11 +297,15 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     wk[8 + e] = HAS_W && kw ? kw[64 + 8 * s8 + e] : 1.0f;
   }
 
-  // this thread's 8 RoPE frequencies, also loaded once (indexing the argument block per lane
-  // compiles to memory loads)
-  double fr8[8];
+  // RoPE phases of this thread's token (in revolutions, reduced to [-1/2, 1/2]): exact at the
+  // segment start (fp64 reduction) and advanced by frac(64 f) per chunk in fp32, set up once
+  // (indexing the argument block per lane compiles to memory loads)
+  float ph[8], dph[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) fr8[e] = freqs.f[8 * s8 + e];
+  for (int e = 0; e < 8; ++e) {
+    ph[e] = rope_rev((double)(pos0 + t_begin + tok), freqs.f[8 * s8 + e]);
+    dph[e] = rope_rev(64.0, freqs.f[8 * s8 + e]);
+  }
 
   wait_vmcnt<0>();
   __syncthreads();
@@ -467,11 +326,13 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       xq[1] = *reinterpret_cast<const uint4*>(&Qt[swz(tok, s8 + 8)]);
       xk[0] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8)]);
       xk[1] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8 + 8)]);
-      // RoPE angles of this token, computed afresh (fp64 reduction of the position)
       float rc[8], rs[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sincos_rev(rope_rev((double)(pos0 + c0 + tok), fr8[e]), &rs[e], &rc[e]);
+      for (int e = 0; e < 8; ++e) {
+        sincos_rev(ph[e], &rs[e], &rc[e]);
+        const float x = ph[e] + dph[e];
+        ph[e] = x - rintf(x);
+      }
       norm_rope_w(xq, wq, eps, rc, rs);
       norm_rope_w(xk, wk, eps, rc, rs);
       if (c0 + tok >= t_end) { xk[0] = make_uint4(0, 0, 0, 0); xk[1] = xk[0]; }
@@ -815,9 +676,20 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
   float* wsf = static_cast<float*>(ws);
   const bf16_t *qb = (const bf16_t*)q, *kb = (const bf16_t*)k, *vb = (const bf16_t*)v, *gb = (const bf16_t*)g;
   if (nseg > 1) {
-    hipLaunchKernelGGL(linear_chunk_kernel<true>, dim3(B * H * (nseg - 1)), dim3(NT), 0, st, qb, kb,
-                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, N, H, (long)d.pos0,
-                       seg, nseg, d.norm_eps, fr);
+    static const hipError_t ss_ok = [] {
+      const hipError_t e0 = hipFuncSetAttribute((const void*)linear_segsum_kernel<false>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SegLds));
+      const hipError_t e1 = hipFuncSetAttribute((const void*)linear_segsum_kernel<true>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SegLds));
+      return e0 != hipSuccess ? e0 : e1;
+    }();
+    if (ss_ok != hipSuccess) return ss_ok;
+    if (kw)
+      hipLaunchKernelGGL(linear_segsum_kernel<true>, dim3(B * H * (nseg - 1)), dim3(SS_NT), sizeof(SegLds), st,
+                         kb, vb, kw, wsf, N, H, (long)d.pos0, seg, nseg, d.norm_eps, fr);
+    else
+      hipLaunchKernelGGL(linear_segsum_kernel<false>, dim3(B * H * (nseg - 1)), dim3(SS_NT), sizeof(SegLds), st,
+                         kb, vb, kw, wsf, N, H, (long)d.pos0, seg, nseg, d.norm_eps, fr);
     hipLaunchKernelGGL(linear_scan_kernel, dim3(B * H, D * D / 256), dim3(256), 0, st, state_in,
                        wsf, nseg, D * D);
   }
