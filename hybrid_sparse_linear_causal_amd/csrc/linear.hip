@@ -22,6 +22,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <algorithm>
+
 namespace sala {
 
 namespace {
@@ -466,6 +468,14 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 }
 
+// dst = src, or 0 where src is null (n floats): the state of an empty sequence. A kernel, not
+// a runtime copy or fill, so that the call stays capturable in a graph as plain kernel nodes.
+__global__ void __launch_bounds__(256)
+copy_or_zero_kernel(const float* __restrict__ src, float* __restrict__ dst, long n) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+    dst[i] = src ? src[i] : 0.0f;
+}
+
 // Slot s >= 1 holds segment s-1's own sum on entry; on exit slot s holds the state entering
 // segment s: state_in + sum of the sums of segments 0..s-1. One thread per state element.
 __global__ void __launch_bounds__(256)
@@ -650,9 +660,10 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
   if (N == 0) {
     // no tokens: state passes through
     if (state_out && state_out != state_in) {
-      if (state_in)
-        return hipMemcpyAsync(state_out, state_in, sizeof(float) * B * H * hd * hd, hipMemcpyDeviceToDevice, st);
-      return hipMemsetAsync(state_out, 0, sizeof(float) * B * H * hd * hd, st);
+      const long n = (long)B * H * hd * hd;
+      const unsigned nb = (unsigned)std::min<long>((n + 255) / 256, 4096);
+      hipLaunchKernelGGL(copy_or_zero_kernel, dim3(nb), dim3(256), 0, st, state_in, state_out, n);
+      return hipGetLastError();
     }
     return hipSuccess;
   }

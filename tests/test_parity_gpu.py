@@ -66,6 +66,11 @@ def test_linear_prefill_empty_passes_state(S):
     out, st = S.linear_prefill(z, z, z, z, state_in=s_in)
     torch.cuda.synchronize()
     assert out.numel() == 0 and torch.equal(st, s_in)
+    # no state_in: the state of an empty sequence is zero
+    st2 = torch.full((1, 2, 128, 128), 7.0, dtype=torch.float32, device="cuda")
+    S.linear_prefill(z, z, z, z, state_out=st2)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(st2)) == 0
 
 
 def test_linear_state_alias_and_split_prefill(S):
