@@ -9,10 +9,13 @@
 // queries of block i (decode: the single token); score[j] = q~ . k_pool[j] in fp32; keep the
 // topk - |forced| best candidates j in [1, i - n_local], ties to the lowest index.
 //
-// Kernels: (1) qtilde_kernel — one pass over q; (2) score_tile_kernel (prefill, 64x64 fp32
-// tiles of q~ k_pool^T) or score_row_kernel (one query block: streams the pooled keys);
-// (3) select_kernel — per row an exact radix select on monotone uint32 keys of the scores,
-// then ordered compaction so the output is ascending and deterministic.
+// Kernels: (1) qtilde_kernel — one pass over q; (2) prefill: score_tile_kernel (64x64 fp32
+// tiles of q~ k_pool^T), then select_kernel — per row an exact radix select on monotone uint32
+// keys of the scores and ordered compaction, so the output is ascending and deterministic;
+// (3) decode (one query block): decode_slice_kernel scores slices of 512 candidates and keeps
+// each slice's best (radix threshold, ties to the lower index), decode_merge_kernel selects
+// among the slice winners and emits them ascending through a bitmap; very long ranges fall
+// back to score_row_kernel + select_kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -145,6 +148,22 @@ score_row_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
   }
 }
 
+// Histogram update of one wave: when every matching lane has the same digit (the common case
+// for the leading digit of similar scores) one atomic adds the count; otherwise each lane adds
+// its own (LDS atomics serialise only lanes that hit the same bin).
+__device__ __forceinline__ void hist_add(int* hist, uint32_t dgt, bool match, int lane) {
+  const uint64_t act = __ballot(match);
+  if (act == 0) return;
+  const int leader = __ffsll((unsigned long long)act) - 1;
+  const uint32_t dl = __shfl(dgt, leader, 64);
+  const uint64_t same = __ballot(match && dgt == dl);
+  if (same == act) {
+    if (lane == leader) atomicAdd(&hist[dl], __popcll(same));
+  } else if (match) {
+    atomicAdd(&hist[dgt], 1);
+  }
+}
+
 template <int NTS>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -170,7 +189,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 
 // grid (B*Hkv*nqb); row (bg, r) with i = qb0 + r. Exact top-r over candidate keys
 // (score desc, index asc): MSB-first radix select over the 32-bit monotone keys (histograms
-// updated once per distinct digit per wave), then an ordered walk over blocks 0..i that emits
+// updated by hist_add), then an ordered walk over blocks 0..i that emits
 // forced and chosen blocks ascending; -1 pads to topk.
 // CAP candidate keys are staged in LDS; rows with more candidates read the scores in global
 // memory (correct, slower).
@@ -219,15 +238,7 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
           match = (key & pmask) == prefix;
         }
         const uint32_t dgt = (key >> shift) & 255u;
-        // one atomic per distinct digit present in the wave
-        uint64_t active = __ballot(match);
-        while (active) {
-          const int leader = __ffsll((unsigned long long)active) - 1;
-          const uint32_t dl = __shfl(dgt, leader, 64);
-          const uint64_t same = __ballot(match && dgt == dl);
-          if (lane == leader) atomicAdd(&hist[dl], __popcll(same));
-          active &= ~same;
-        }
+        hist_add(hist, dgt, match, lane);
       }
       __syncthreads();
       if (tid < 64) {
@@ -300,6 +311,238 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
   for (int k = total + tid; k < topk; k += NTS) out[k] = -1;
 }
 
+// ---- decode selection (one query block per row, long candidate ranges): two levels.
+// Candidates are ordered by score, equal scores by lower index (a strict total order), so the
+// best R of the whole range are among the best R of each slice. Level-1 winners are passed on
+// as composites key(score) << 32 | (2^32 - 1 - j); composite 0 marks an empty entry (no score
+// maps to key 0).
+constexpr int DSL = 512;      // candidates per slice (level 1)
+constexpr int DNSL_MAX = 32;  // slices per row handled by the merge
+constexpr int DMERGE = 2048;  // slice winners the merge holds (nsl * R)
+constexpr int DBITS = DSL * DNSL_MAX / 32 + 1;  // bitmap words over candidate indices 0 .. nc
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, long j) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+// Exact threshold of the R largest of n keys in LDS (1 <= R < n): T = the R-th largest key and
+// need = how many keys equal to T belong to the R largest. Four 8-bit radix passes; histogram
+// updates by hist_add.
+template <int NTH>
+__device__ __forceinline__ void radix_threshold(const uint32_t* keys, int n, int R, int* hist,
+                                                uint32_t* s_prefix, int* s_need, uint32_t& T,
+                                                int& need) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = R;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int x = tid; x < 256; x += NTH) hist[x] = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += NTH) {
+      const int x = base + tid;
+      uint32_t key = 0;
+      bool match = false;
+      if (x < n) {
+        key = keys[x];
+        match = (key & pmask) == prefix;
+      }
+      const uint32_t dgt = (key >> shift) & 255u;
+      hist_add(hist, dgt, match, lane);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      int v[4], sum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[e] = hist[255 - 4 * lane - e]; sum += v[e]; }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const uint64_t hit = __ballot(incl >= remaining);
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      if (lane == L) {
+        int cum = incl - sum;
+        int e = 0;
+        for (; e < 3; ++e) {
+          if (cum + v[e] >= remaining) break;
+          cum += v[e];
+        }
+        *s_prefix = prefix | ((uint32_t)(255 - 4 * lane - e) << shift);
+        *s_need = remaining - cum;
+      }
+    }
+    __syncthreads();
+    prefix = *s_prefix;
+    remaining = *s_need;
+    pmask |= 255u << shift;
+  }
+  T = prefix;
+  need = remaining;
+}
+
+// Level 1: grid (B*Hkv, nsl), NT threads. Slice s holds candidates j = j0 .. j0+n-1 with
+// j0 = 1 + s*DSL, n = min(DSL, nc - j0 + 1): scores q~ . k_pool[j] (8 lanes per pooled row),
+// then the slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered).
+template <int DD>
+__global__ void __launch_bounds__(NT)
+decode_slice_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
+                    uint64_t* __restrict__ cand, long nblk_cap, long nc, int R) {
+  constexpr int LPB = 8, FPL = DD / LPB, RPI = NT / LPB;  // rows per iteration
+  __shared__ uint32_t keys[DSL];
+  __shared__ int hist[256];
+  __shared__ int scan_tmp[NT / 64 + 1];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int bg = blockIdx.x, sl = blockIdx.y, nsl = gridDim.y;
+  const int tid = threadIdx.x, sub = tid / LPB, part = tid % LPB;
+  const long j0 = 1 + (long)sl * DSL;
+  const int n = (int)min((long)DSL, nc - j0 + 1);
+  float qv[FPL];
+#pragma unroll
+  for (int e = 0; e < FPL; ++e) qv[e] = qt[(long)bg * DD + part * FPL + e];
+  const float* kb = kpool + ((long)bg * nblk_cap + j0) * DD + part * FPL;
+#pragma unroll 4
+  for (int it = 0; it < DSL / RPI; ++it) {
+    const int x = it * RPI + sub;
+    float sdot = 0.f;
+    if (x < n) {
+      const float* row = kb + (long)x * DD;
+#pragma unroll
+      for (int e = 0; e < FPL; e += 4) {
+        const float4 u = *reinterpret_cast<const float4*>(row + e);
+        sdot += u.x * qv[e] + u.y * qv[e + 1] + u.z * qv[e + 2] + u.w * qv[e + 3];
+      }
+    }
+    sdot = group_sum<LPB>(sdot);
+    if (part == 0) keys[x] = score_key(sdot);
+  }
+  __syncthreads();
+  uint64_t* dst = cand + ((long)bg * nsl + sl) * R;
+  if (n <= R) {
+    for (int t = tid; t < R; t += NT) dst[t] = t < n ? composite(keys[t], j0 + t) : 0ull;
+    return;
+  }
+  uint32_t T;
+  int need;
+  radix_threshold<NT>(keys, n, R, hist, &s_prefix, &s_need, T, need);
+  // keys above T, then the first `need` keys equal to T in index order: thread t owns
+  // positions PER*t .. PER*t + PER-1
+  constexpr int PER = DSL / NT;
+  int eq = 0, gt = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int x = PER * tid + u;
+    if (x < n) { eq += keys[x] == T; gt += keys[x] > T; }
+  }
+  int eq_total;
+  int eqb = block_excl_scan<NT>(eq, scan_tmp, &eq_total);
+  int cnt = gt + max(0, min(eq, need - eqb));
+  int total;
+  int pos = block_excl_scan<NT>(cnt, scan_tmp, &total);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int x = PER * tid + u;
+    if (x >= n) continue;
+    const uint32_t key = keys[x];
+    const bool pick = key > T || (key == T && (eqb++) < need);
+    if (pick && pos < R) dst[pos++] = composite(key, j0 + x);
+  }
+}
+
+// Second-stage keys for surplus ties at threshold T: keys above T become 0xFFFFFFFF (always
+// kept), keys equal to T become ~index (larger for lower indices), the rest 0.
+__device__ __forceinline__ void idx2key(uint32_t* keys, const uint32_t* idx, int t, uint32_t T) {
+  const uint32_t k = keys[t];
+  keys[t] = k > T ? 0xFFFFFFFFu : (k == T ? ~idx[t] : 0u);
+}
+
+// Level 2: grid (B*Hkv), NT threads. The best R of the nsl*R slice winners (empties excluded),
+// then the output row: forced block 0 (if outside the local range), the chosen candidates
+// ascending (a bitmap over candidate indices compacted in order), the forced local blocks
+// f_lo .. i, and -1 padding.
+template <int CAPB>
+__global__ void __launch_bounds__(NT)
+decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel, int nsl, int R,
+                    long i, int n_local, int topk, long nc) {
+  __shared__ uint32_t keys[CAPB];
+  __shared__ uint32_t idx[CAPB];
+  __shared__ uint32_t bits[DBITS];
+  __shared__ int hist[256];
+  __shared__ int scan_tmp[NT / 64 + 1];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int bg = blockIdx.x, tid = threadIdx.x;
+  const int n = nsl * R;
+  int valid = 0;
+  for (int t = tid; t < n; t += NT) {
+    const uint64_t c = cand[(long)bg * n + t];
+    keys[t] = (uint32_t)(c >> 32);
+    idx[t] = 0xFFFFFFFFu - (uint32_t)c;
+    valid += c != 0ull;
+  }
+  const int nw = (int)(nc / 32) + 1;  // bitmap words over indices 0 .. nc
+  for (int w = tid; w < nw; w += NT) bits[w] = 0u;
+  int n_valid;
+  block_excl_scan<NT>(valid, scan_tmp, &n_valid);  // also orders the fills above
+  uint32_t T = 0, T2 = 0;
+  int need = 0;
+  const bool all = n_valid <= R;
+  bool all_ties = true;
+  if (!all) {
+    radix_threshold<NT>(keys, n, R, hist, &s_prefix, &s_need, T, need);
+    int ties = 0;
+    for (int t = tid; t < n; t += NT) ties += keys[t] == T;
+    int ties_total;
+    block_excl_scan<NT>(ties, scan_tmp, &ties_total);
+    all_ties = ties_total == need;  // the usual case: no surplus equal scores
+    if (!all_ties) {
+      // surplus ties: keep the `need` lowest indices. After idx2key the R largest keys are the
+      // R - need keys above T (all ones) and the ties with the `need` largest ~index; indices
+      // are distinct, so the R-th largest T2 separates them exactly.
+      __syncthreads();
+      for (int t = tid; t < n; t += NT) idx2key(keys, idx, t, T);
+      __syncthreads();
+      int need2;
+      radix_threshold<NT>(keys, n, R, hist, &s_prefix, &s_need, T2, need2);
+    }
+  }
+  for (int t = tid; t < n; t += NT) {
+    bool pick;
+    if (all) pick = keys[t] != 0u;
+    else if (all_ties) pick = keys[t] >= T;
+    else pick = keys[t] >= T2;
+    if (pick && idx[t] <= (uint32_t)nc) atomicOr(&bits[idx[t] >> 5], 1u << (idx[t] & 31));
+  }
+  __syncthreads();
+  const long f_lo = i - n_local + 1 > 0 ? i - n_local + 1 : 0;
+  const int head = f_lo > 0 ? 1 : 0;
+  int32_t* out = sel + (long)bg * topk;
+  // thread t owns bitmap words wpt*t .. wpt*t + wpt-1
+  const int wpt = (nw + NT - 1) / NT;
+  int c = 0;
+  for (int w = wpt * tid; w < min(nw, wpt * tid + wpt); ++w) c += __popc(bits[w]);
+  int cnt;
+  int pos = head + block_excl_scan<NT>(c, scan_tmp, &cnt);
+  for (int w = wpt * tid; w < min(nw, wpt * tid + wpt); ++w) {
+    uint32_t m = bits[w];
+    while (m) {
+      const int b = __ffs(m) - 1;
+      m &= m - 1;
+      if (pos < topk) out[pos] = 32 * w + b;
+      ++pos;
+    }
+  }
+  if (tid == 0 && head) out[0] = 0;
+  const int nloc = (int)(i - f_lo + 1);
+  for (int t = tid; t < nloc; t += NT)
+    if (head + cnt + t < topk) out[head + cnt + t] = (int32_t)(f_lo + t);
+  for (int t = head + cnt + nloc + tid; t < topk; t += NT) out[t] = -1;
+}
+
 }  // namespace
 
 static long select_row_len(const sala_sparse_desc& d) {
@@ -307,11 +550,29 @@ static long select_row_len(const sala_sparse_desc& d) {
   return g.qb0 + g.nqb;  // blocks 0 .. i_max
 }
 
+// decode (one query block) uses the two-level selection while the candidates fit DNSL_MAX
+// slices; it needs nsl * R composites per row instead of the score row
+static bool decode_two_level(const sala_sparse_desc& d, long* nc_out, int* nsl_out, int* r_out) {
+  const SparseGeom g = sparse_geom(d);
+  if (g.nqb != 1) return false;
+  const long i = g.qb0;
+  const long nc = i - d.n_local > 0 ? i - d.n_local : 0;
+  const long f_lo = i - d.n_local + 1 > 0 ? i - d.n_local + 1 : 0;
+  const int n_forced = (int)(i - f_lo + 1) + (f_lo > 0 ? 1 : 0);
+  const int R = d.topk - n_forced;
+  const long nsl = (nc + DSL - 1) / DSL;
+  if (nc < 1 || R < 1 || nsl > DNSL_MAX || nsl * R > DMERGE) return false;
+  *nc_out = nc; *nsl_out = (int)nsl; *r_out = R;
+  return true;
+}
+
 size_t block_select_workspace(const sala_sparse_desc& d) {
   const SparseGeom g = sparse_geom(d);
   const size_t bg = (size_t)d.batch * d.n_kv_heads;
   const size_t qt = bg * g.nqb * d.head_dim * sizeof(float);
-  const size_t sc = bg * g.nqb * select_row_len(d) * sizeof(float);
+  size_t sc = bg * g.nqb * select_row_len(d) * sizeof(float);
+  long nc; int nsl, R;
+  if (decode_two_level(d, &nc, &nsl, &R)) sc = bg * (size_t)nsl * R * sizeof(uint64_t);
   return ((qt + 255) & ~(size_t)255) + sc;
 }
 
@@ -334,6 +595,19 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
   }
 #undef SALA_QT
   const long i_max = g.qb0 + g.nqb - 1;
+  long nc; int nsl, R;
+  if (decode_two_level(d, &nc, &nsl, &R)) {
+    uint64_t* cand = reinterpret_cast<uint64_t*>(sc);
+    if (d.head_dim == 128)
+      hipLaunchKernelGGL(decode_slice_kernel<128>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand,
+                         (long)g.nblk_cap, nc, R);
+    else
+      hipLaunchKernelGGL(decode_slice_kernel<64>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand,
+                         (long)g.nblk_cap, nc, R);
+    hipLaunchKernelGGL(decode_merge_kernel<DMERGE>, dim3(BG), dim3(NT), 0, st, cand, sel, nsl, R, i_max,
+                       d.n_local, d.topk, nc);
+    return hipGetLastError();
+  }
   if (i_max - d.n_local >= 1) {
     if (g.nqb == 1) {
       const long ncand_end = i_max - d.n_local + 1;  // score blocks 0 .. i - n_local

@@ -292,6 +292,45 @@ def test_sparse_decode(S, B, Hq, Hkv, L, topk):
         assert_rel(host(out)[:, 0], o2, 1e-2, "decode out (gpu selection)")
 
 
+def test_decode_select_exact_ties_across_slices(S):
+    """Decode selection over ~1,200 candidate blocks (several 512-block slices): two needle
+    blocks score highest, 1,001 blocks hold identical keys (exactly equal scores in the oracle
+    and on the GPU), the rest score clearly lower. The selection must be the needles plus the
+    lowest-index tied blocks, exactly as the oracle's ordering (ties to the lower index)."""
+    import torch
+
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, d, topk, n_local = 1, 4, 1, 128, 16, 2
+    L = 64 * 1200 + 5
+    i = (L - 1) // 64
+    kc_h = (rng.standard_normal((B, Hkv, L, d)) * 0.05).astype(np.float32)
+    q = (rng.standard_normal((B, 1, Hq, d)) * 0.1).astype(np.float32)
+    q[..., 0] += 2.0
+    tied = (rng.standard_normal((64, d)) * 0.05).astype(np.float32)
+    tied[:, 0] += 0.5
+    for j in [7] + list(range(100, 1100)):
+        kc_h[0, 0, j * 64:(j + 1) * 64] = tied
+    for j in (450, 900):
+        kc_h[0, 0, j * 64:(j + 1) * 64, 0] += 2.0
+    from hybrid_sparse_linear_causal_amd.inputs import bf16_round
+
+    kc_h, q = bf16_round(kc_h), bf16_round(q)
+    cap = ((L + 63) // 64) * 64
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    kc[:, :, :L] = dev(kc_h, "bf16")
+    kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    S.kv_pool(kc, kp, L, 0, i)
+    sel = S.block_select(dev(q, "bf16"), kp, L, cap, n_kv_heads=Hkv, topk=topk, n_local=n_local)
+    got = sel.cpu().numpy()[0, 0, 0]
+    qt = O.qk_norm(q[0, 0]).sum(axis=0)
+    kb = kc_h[0, 0, : i * 64].astype(np.float64).reshape(i, 64, d).mean(axis=1)
+    sc = np.full(i - n_local + 1, -np.inf)
+    sc[1:] = kb[1: i - n_local + 1] @ qt
+    ref = O.select_row(sc, i, topk, n_local)
+    assert list(got) == list(ref), (got, ref)
+    assert {450, 900, 7, 100} <= set(got.tolist())
+
+
 # ---------------------------------------------------------------- determinism
 
 
