@@ -574,17 +574,29 @@ linear_scan_f32_kernel(const float* __restrict__ qt, const float* __restrict__ k
 
 // grid (B*H, d/32): each workgroup owns 32 state columns of one (b, h). Thread j: column
 // 32*blockIdx.y + j%32, rows j/32 + 8m. q~, k~ (norm + RoPE at pos) computed by wave 0.
+// grid (B*H, DD/64), 256 threads: one token's step for 64 state columns of one head. Thread
+// (row group r0 = j/16, column quad c4 = j%16) owns columns 64y + 4c4 .. +3 of rows r0 + 16m;
+// its state rows are loaded as float4 before the q/k preparation, so their latency overlaps it.
 template <typename T, int DD>
 __global__ void __launch_bounds__(256)
 linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                      const T* __restrict__ g, const float* __restrict__ qw,
                      const float* __restrict__ kw, float* __restrict__ state, T* __restrict__ out,
                      long pos, float eps, RopeFreqs freqs) {
+  constexpr int NR = DD / 16;  // rows per thread
   __shared__ float sq[DD], sk[DD];
-  __shared__ float red[8][32];
+  __shared__ float4 red[16][16];
   const int bh = blockIdx.x;
-  const int j = threadIdx.x;
+  const int j = threadIdx.x, r0 = j >> 4, c4 = j & 15;
   const long vec = (long)bh * DD;
+  const int col = 64 * blockIdx.y + 4 * c4;
+  float* Sp = state + (long)bh * DD * DD + col;
+  float4 sv[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) sv[m] = *reinterpret_cast<const float4*>(Sp + (long)(r0 + 16 * m) * DD);
+  float vc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[vec + col + e]);
   if (j < 64) {
     constexpr int HALF = DD / 2;
     const bool on = j < HALF;
@@ -609,26 +621,29 @@ linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
     }
   }
   __syncthreads();
-  const int col = 32 * blockIdx.y + (j & 31);
-  const int r0 = j >> 5;
-  const float vc = to_f32(v[vec + col]);
-  float* Sp = state + (long)bh * DD * DD + col;
-  float o = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int m = 0; m < DD / 8; ++m) {
-    const int r = r0 + 8 * m;
-    const float s = Sp[(long)r * DD] + sk[r] * vc;
-    Sp[(long)r * DD] = s;
-    o += sq[r] * s;
+  for (int m = 0; m < NR; ++m) {
+    const int r = r0 + 16 * m;
+    const float kr = sk[r], qr = sq[r];
+    float4 s4 = sv[m];
+    s4.x += kr * vc[0]; s4.y += kr * vc[1]; s4.z += kr * vc[2]; s4.w += kr * vc[3];
+    *reinterpret_cast<float4*>(Sp + (long)r * DD) = s4;
+    o.x += qr * s4.x; o.y += qr * s4.y; o.z += qr * s4.z; o.w += qr * s4.w;
   }
-  red[r0][j & 31] = o;
+  red[r0][c4] = o;
   __syncthreads();
-  if (j < 32) {
+  if (j < 64) {
+    const int cc = j >> 2, e = j & 3;  // column 64y + 4cc + e
     float acc = 0.f;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc += red[m][j];
-    const float gv = to_f32(g[vec + col]);
-    out[vec + col] = from_f32<T>(acc / (1.0f + expf(-gv)));
+    for (int m = 0; m < 16; ++m) {
+      const float4 t = red[m][cc];
+      acc += e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w;
+    }
+    const long oc = vec + 64 * blockIdx.y + j;
+    const float gv = to_f32(g[oc]);
+    out[oc] = from_f32<T>(acc / (1.0f + expf(-gv)));
   }
 }
 
@@ -728,7 +743,7 @@ hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const 
                                 float* state, void* out, hipStream_t st) {
   const int BH = d.batch * d.n_heads, hd = d.head_dim;
   const RopeFreqs fr = make_rope_freqs(hd, d.rope_base);
-  const dim3 grid(BH, hd / 32);
+  const dim3 grid(BH, hd / 64);
   const long pos = (long)d.pos0;
   if (d.dtype == SALA_BF16) {
     if (hd == 128)

@@ -357,9 +357,14 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
   const long p = kv_len - 1;
   const long row_base = (long)bg * cap;
+  // the selection row (ascending, -1 padded; topk <= 256): lane x holds entries x + 64u
   const int32_t* srow = sel + (long)bg * topk;
+  int sv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) sv[u] = lane + 64 * u < topk ? srow[lane + 64 * u] : -1;
   int nsel = 0;
-  while (nsel < topk && srow[nsel] >= 0) ++nsel;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) nsel += __popcll(__ballot(sv[u] >= 0));
 
   // Q^T fragments: column l16 = head gk*G + l16 (zero beyond the group)
   bf16x8 qf[4];
@@ -392,83 +397,86 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) OT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int stride = 4 * DEC_SPLIT;
-  const int iters = (nsel + stride - 1) / stride;
-  bf16_t* vt = vts[wave];
-  for (int it = 0; it < iters; ++it) {
-    const int e = it * stride + split * 4 + wave;
-    const bool act = e < nsel;
-    const long blk = act ? srow[e] : 0;
-    // stage V^T of this wave's block: lane handles keys 4*(lane/16)+u+16m..., dims 8*(lane%16)
-    if (act) {
+  bf16_t* vt = vts[wave];  // this wave's own V^T tile: no workgroup barrier needed
+  for (int e = split * 4 + wave; e < nsel; e += stride) {
+    const int su = e >> 6;
+    const long blk = __shfl(su == 0 ? sv[0] : su == 1 ? sv[1] : su == 2 ? sv[2] : sv[3], e & 63, 64);
+    // both tiles of the block in flight at once: K in MFMA A layout (key 16kt + l16, dims
+    // 32ks + 8lq ..), V as 4 consecutive keys x 8 dims per lane for the transpose
+    uint4 kk[4][4], vv[4][4];
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        uint4 vv[4];
+    for (int kt = 0; kt < 4; ++kt) {
+      const long pk = blk * 64 + 16 * kt + l16;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const long pk = blk * 64 + 16 * mm + 4 * lq + u;
-          vv[u] = pk < kv_len ? *reinterpret_cast<const uint4*>(vc + (row_base + pk) * D + 8 * l16)
-                              : make_uint4(0, 0, 0, 0);
-        }
+      for (int ks = 0; ks < 4; ++ks)
+        kk[kt][ks] = pk < kv_len ? *reinterpret_cast<const uint4*>(kc + (row_base + pk) * D + 32 * ks + 8 * lq)
+                                 : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-        for (int ee = 0; ee < 8; ++ee) {
-          uint2 w;
-          w.x = bf_half(vv[0], ee) | (bf_half(vv[1], ee) << 16);
-          w.y = bf_half(vv[2], ee) | (bf_half(vv[3], ee) << 16);
-          *reinterpret_cast<uint2*>(&vt[(8 * l16 + ee) * VS + 16 * mm + 4 * lq]) = w;
-        }
+    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long pk = blk * 64 + 16 * mm + 4 * lq + u;
+        vv[mm][u] = pk < kv_len ? *reinterpret_cast<const uint4*>(vc + (row_base + pk) * D + 8 * l16)
+                                : make_uint4(0, 0, 0, 0);
+      }
+    f32x4 ST[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      ST[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ST[kt] = mfma16x16x32(as_bf16x8(kk[kt][ks]), qf[ks], ST[kt]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (blk * 64 + 16 * kt + 4 * lq + c > p) ST[kt][c] = -INFINITY;
+    }
+    // V^T into the wave's tile (lane: keys 16mm + 4lq + u, dims 8 l16 + ee)
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+      for (int ee = 0; ee < 8; ++ee) {
+        uint2 w;
+        w.x = bf_half(vv[mm][0], ee) | (bf_half(vv[mm][1], ee) << 16);
+        w.y = bf_half(vv[mm][2], ee) | (bf_half(vv[mm][3], ee) << 16);
+        *reinterpret_cast<uint2*>(&vt[(8 * l16 + ee) * VS + 16 * mm + 4 * lq]) = w;
+      }
+    // a wave's LDS accesses complete in order: its reads below see these writes
+    __builtin_amdgcn_wave_barrier();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, ST[kt][c]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    lp *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) OT[dt] *= alpha;
+    m = mn;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float pr[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pr[u] = exp2f(ST[2 * c][u] - m);
+        pr[4 + u] = exp2f(ST[2 * c + 1][u] - m);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) lp += pr[u];
+      const bf16x8 pf = as_bf16x8(pack8(pr));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16_t* vr = &vt[(16 * dt + l16) * VS + 32 * c + 4 * lq];
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + 16));
+        OT[dt] = mfma16x16x32(a, pf, OT[dt]);
       }
     }
-    __syncthreads();
-    if (act) {
-      f32x4 ST[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        ST[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const long pk = blk * 64 + 16 * kt + l16;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          uint4 u = make_uint4(0, 0, 0, 0);
-          if (pk < kv_len) u = *reinterpret_cast<const uint4*>(kc + (row_base + pk) * D + 32 * ks + 8 * lq);
-          ST[kt] = mfma16x16x32(as_bf16x8(u), qf[ks], ST[kt]);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (blk * 64 + 16 * kt + 4 * lq + c > p) ST[kt][c] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, ST[kt][c]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
-      const float alpha = exp2f(m - mn);
-      lp *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) OT[dt] *= alpha;
-      m = mn;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float pr[8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pr[u] = exp2f(ST[2 * c][u] - m);
-          pr[4 + u] = exp2f(ST[2 * c + 1][u] - m);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) lp += pr[u];
-        const bf16x8 pf = as_bf16x8(pack8(pr));
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const bf16_t* vr = &vt[(16 * dt + l16) * VS + 32 * c + 4 * lq];
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + 16));
-          OT[dt] = mfma16x16x32(a, pf, OT[dt]);
-        }
-      }
-    }
-    __syncthreads();
+    // the tile is rewritten by this wave's next block: its reads must be done first
+    __builtin_amdgcn_wave_barrier();
   }
+  __syncthreads();  // every wave is done with its V^T tile (reused below)
   // combine the 4 waves: O staged in the (now free) V^T area as fp32 [wave][head][D]
   lp += __shfl_xor(lp, 16, 64);
   lp += __shfl_xor(lp, 32, 64);
