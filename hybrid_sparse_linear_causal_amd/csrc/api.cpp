@@ -36,15 +36,16 @@ sala_status check_linear(const sala_linear_desc* d) {
   return SALA_OK;
 }
 
-sala_status check_sparse(const sala_sparse_desc* d) {
+// with_sel: the call uses topk / n_local (selection, sparse attention); dense attention does not
+sala_status check_sparse(const sala_sparse_desc* d, bool with_sel = true) {
   if (!d) return SALA_ERR_NULL;
   if (d->batch < 1 || d->n_q < 1 || d->n_heads < 1 || d->n_kv_heads < 1) return SALA_ERR_INVALID;
   if (d->n_heads % d->n_kv_heads != 0) return SALA_ERR_INVALID;
   if (d->head_dim != 64 && d->head_dim != 128) return SALA_ERR_UNSUPPORTED;
   if (d->dtype != SALA_F32 && d->dtype != SALA_BF16) return SALA_ERR_INVALID;
   if (d->block != 64) return SALA_ERR_UNSUPPORTED;
-  if (d->n_local != 1 && d->n_local != 2) return SALA_ERR_UNSUPPORTED;
-  if (d->topk < 1 + d->n_local || d->topk > 256) return SALA_ERR_INVALID;
+  if (with_sel && d->n_local != 1 && d->n_local != 2) return SALA_ERR_UNSUPPORTED;
+  if (with_sel && (d->topk < 1 + d->n_local || d->topk > 256)) return SALA_ERR_INVALID;
   if (!(d->norm_eps >= 0.f) || !isfinite(d->norm_eps)) return SALA_ERR_INVALID;
   if (!(d->scale >= 0.f) || !isfinite(d->scale)) return SALA_ERR_INVALID;
   if (d->kv_len < d->n_q || d->kv_capacity < d->kv_len || d->kv_capacity % 64 != 0)
@@ -96,6 +97,11 @@ size_t sala_workspace_bytes(int op, const void* desc) {
     case SALA_OP_SPARSE_ATTN: {
       const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
       if (check_sparse(d) != SALA_OK) return SIZE_MAX;
+      return sala::sparse_attn_workspace(*d);
+    }
+    case SALA_OP_DENSE_ATTN: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse(d, false) != SALA_OK) return SIZE_MAX;
       return sala::sparse_attn_workspace(*d);
     }
     default: return SIZE_MAX;
@@ -183,6 +189,27 @@ sala_status sala_sparse_attn(const sala_sparse_desc* desc, const void* q, const 
   if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
   return hip_status(sala::launch_sparse_attn(d, q, q_norm_w, k_cache, v_cache, gate, sel, out,
                                              workspace, (hipStream_t)stream));
+}
+
+sala_status sala_dense_attn(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                            const void* k_cache, const void* v_cache, const void* gate, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  sala_status s = check_sparse(desc, false);
+  if (s != SALA_OK) return s;
+  const sala_sparse_desc& d = *desc;
+  if (d.dtype == SALA_BF16 && d.head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (d.dtype == SALA_BF16 && d.n_q == 1 && d.n_heads / d.n_kv_heads > 16) return SALA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !gate || !out) return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, out, workspace})) return SALA_ERR_INVALID;
+  const size_t need = sala::sparse_attn_workspace(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_dense_attn(d, q, q_norm_w, k_cache, v_cache, gate, out, workspace,
+                                            (hipStream_t)stream));
+}
+
+int sala_sparse_layer_uses_dense(const sala_sparse_desc* desc) {
+  if (check_sparse(desc) != SALA_OK) return -1;
+  return desc->kv_len <= (int64_t)desc->topk * 64 ? 1 : 0;
 }
 
 }  // extern "C"

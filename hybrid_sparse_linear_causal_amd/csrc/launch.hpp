@@ -74,5 +74,9 @@ size_t sparse_attn_workspace(const sala_sparse_desc& d);
 hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
                               const void* k_cache, const void* v_cache, const void* g,
                               const int32_t* sel, void* out, void* ws, hipStream_t st);
+// dense causal attention over every cached block up to the query's own (no selection)
+hipError_t launch_dense_attn(const sala_sparse_desc& d, const void* q, const float* qw,
+                             const void* k_cache, const void* v_cache, const void* g, void* out,
+                             void* ws, hipStream_t st);
 
 }  // namespace sala

@@ -201,6 +201,7 @@ __device__ __forceinline__ void exp_pv(const bf16_t* Vs, f32x4 (&ST)[4][QT], f32
 // grid: B*Hkv*nqb*ceil(G/4) workgroups of 512 threads (8 waves: 4 heads x 2 row halves)
 constexpr int PF_THREADS = 512;
 constexpr int PF_QT = 2;  // 16-row query tiles per wave
+template <bool DENSE>
 __global__ void __launch_bounds__(PF_THREADS)
 sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
                            const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
@@ -227,8 +228,10 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   const int h = gk * G + (head_ok ? hl : 0);
   const long i = qb0 + r;
   const long row_base = ((long)b * Hkv + gk) * cap;
-  const int32_t* srow = sel + (((long)b * Hkv + gk) * nqb + r) * topk;
-  if (j < topk) s_sel[j] = srow[j];
+  if (!DENSE) {
+    const int32_t* srow = sel + (((long)b * Hkv + gk) * nqb + r) * topk;
+    if (j < topk) s_sel[j] = srow[j];
+  }
 
   // ---- Q^T fragments (B operand: k = dim, n = query); normalised, scaled by scale*log2(e)
   bf16x8 qf[PF_QT][4];
@@ -261,8 +264,12 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     }
   }
   __syncthreads();
+  // the blocks attended: the selection (ascending, ends with block i), or every block 0 .. i
   int nsel = 0;
-  while (nsel < topk && s_sel[nsel] >= 0) ++nsel;
+  if (DENSE) nsel = (int)(i + 1);
+  else
+    while (nsel < topk && s_sel[nsel] >= 0) ++nsel;
+  auto blk = [&](int x) -> long { return DENSE ? (long)x : (long)s_sel[x]; };
 
   float m[PF_QT], lp[PF_QT];
   f32x4 minit[PF_QT];
@@ -285,7 +292,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   // diagonal block is the last one and is finished after the loop.
 #pragma unroll
   for (int x = 0; x < 3; ++x)
-    if (x < nsel) dma_block(kc, vc, row_base, s_sel[x], kv_len, lds[x][0], lds[x][1]);
+    if (x < nsel) dma_block(kc, vc, row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
   if (nsel > 2) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();  // blocks 0 and 1 landed
   __syncthreads();
 
@@ -293,7 +300,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   scores<PF_QT>(lds[0][0], qf, minit, SA, l16);
   auto step = [&](int e, f32x4 (&Sc)[4][PF_QT], f32x4 (&Sn)[4][PF_QT]) {
     const bool more = e + 3 < nsel;
-    if (more) dma_block(kc, vc, row_base, s_sel[e + 3], kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
+    if (more) dma_block(kc, vc, row_base, blk(e + 3), kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
     scores<PF_QT>(lds[(e + 1) & 3][0], qf, minit, Sn, l16);
     exp_pv<PF_QT>(lds[e & 3][1], Sc, Sn, OT, m, minit, lp, l16, lq, e == 0);
     // block e+2 must have landed (only block e+3's copies may still be in flight)
@@ -345,6 +352,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
 
 // grid (B*Hkv, DEC_SPLIT); wave-global index wi = split*4 + wave takes sel entries
 // wi, wi + 4*DEC_SPLIT, ... Partial per workgroup: m[16], l[16], O[16][D] (fp32).
+template <bool DENSE>
 __global__ void __launch_bounds__(256)
 sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
                           const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
@@ -358,13 +366,16 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
   const long p = kv_len - 1;
   const long row_base = (long)bg * cap;
   // the selection row (ascending, -1 padded; topk <= 256): lane x holds entries x + 64u
-  const int32_t* srow = sel + (long)bg * topk;
-  int sv[4];
+  int sv[4] = {-1, -1, -1, -1};
+  int nsel = (int)(p / 64 + 1);  // dense: every block 0 .. i
+  if (!DENSE) {
+    const int32_t* srow = sel + (long)bg * topk;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) sv[u] = lane + 64 * u < topk ? srow[lane + 64 * u] : -1;
-  int nsel = 0;
+    for (int u = 0; u < 4; ++u) sv[u] = lane + 64 * u < topk ? srow[lane + 64 * u] : -1;
+    nsel = 0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) nsel += __popcll(__ballot(sv[u] >= 0));
+    for (int u = 0; u < 4; ++u) nsel += __popcll(__ballot(sv[u] >= 0));
+  }
 
   // Q^T fragments: column l16 = head gk*G + l16 (zero beyond the group)
   bf16x8 qf[4];
@@ -400,7 +411,7 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
   bf16_t* vt = vts[wave];  // this wave's own V^T tile: no workgroup barrier needed
   for (int e = split * 4 + wave; e < nsel; e += stride) {
     const int su = e >> 6;
-    const long blk = __shfl(su == 0 ? sv[0] : su == 1 ? sv[1] : su == 2 ? sv[2] : sv[3], e & 63, 64);
+    const long blk = DENSE ? (long)e : (long)__shfl(su == 0 ? sv[0] : su == 1 ? sv[1] : su == 2 ? sv[2] : sv[3], e & 63, 64);
     // both tiles of the block in flight at once: K in MFMA A layout (key 16kt + l16, dims
     // 32ks + 8lq ..), V as 4 consecutive keys x 8 dims per lane for the transpose
     uint4 kk[4][4], vv[4][4];
@@ -539,7 +550,7 @@ sparse_decode_combine_kernel(const float* __restrict__ part, const bf16_t* __res
 // ------------------------------------------------------------------ fp32 path
 
 // grid (B*Hq, nqb); 64 threads, thread = query row of the block; keys staged in LDS.
-template <int DD>
+template <int DD, bool DENSE>
 __global__ void __launch_bounds__(64)
 sparse_attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ qw,
                        const float* __restrict__ kc, const float* __restrict__ vc,
@@ -564,10 +575,11 @@ sparse_attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ qw
 #pragma unroll
   for (int d = 0; d < DD; ++d) qv[d] *= inv * (qw ? qw[d] : 1.0f);
   float m = -INFINITY, l = 0.f;
-  const int32_t* srow = sel + (((long)b * Hkv + gk) * nqb + r) * topk;
+  const int32_t* srow = DENSE ? nullptr : sel + (((long)b * Hkv + gk) * nqb + r) * topk;
   const long row_base = ((long)b * Hkv + gk) * cap;
-  for (int e = 0; e < topk; ++e) {
-    const long blk = srow[e];
+  const long nblk = DENSE ? i + 1 : topk;
+  for (long e = 0; e < nblk; ++e) {
+    const long blk = DENSE ? e : (long)srow[e];
     if (blk < 0) break;
     __syncthreads();
     for (int idx = lane; idx < 64 * DD; idx += 64) {
@@ -605,7 +617,8 @@ size_t sparse_attn_workspace(const sala_sparse_desc& d) {
   return 0;
 }
 
-hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
+template <bool DENSE>
+static hipError_t launch_attn(const sala_sparse_desc& d, const void* q, const float* qw,
                               const void* k_cache, const void* v_cache, const void* g,
                               const int32_t* sel, void* out, void* ws, hipStream_t st) {
   const SparseGeom gm = sparse_geom(d);
@@ -613,12 +626,12 @@ hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const fl
   if (d.dtype == SALA_F32) {
     const dim3 grid(d.batch * d.n_heads, (unsigned)gm.nqb);
     if (d.head_dim == 128)
-      hipLaunchKernelGGL(sparse_attn_f32_kernel<128>, grid, dim3(64), 0, st, (const float*)q, qw,
+      hipLaunchKernelGGL((sparse_attn_f32_kernel<128, DENSE>), grid, dim3(64), 0, st, (const float*)q, qw,
                          (const float*)k_cache, (const float*)v_cache, (const float*)g, sel, (float*)out,
                          d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0, (int)gm.nqb,
                          (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, gm.scale);
     else
-      hipLaunchKernelGGL(sparse_attn_f32_kernel<64>, grid, dim3(64), 0, st, (const float*)q, qw,
+      hipLaunchKernelGGL((sparse_attn_f32_kernel<64, DENSE>), grid, dim3(64), 0, st, (const float*)q, qw,
                          (const float*)k_cache, (const float*)v_cache, (const float*)g, sel, (float*)out,
                          d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0, (int)gm.nqb,
                          (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, gm.scale);
@@ -627,7 +640,7 @@ hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const fl
   const float qscale = gm.scale * 1.4426950408889634f;  // exp -> exp2
   if (d.n_q == 1) {
     float* part = static_cast<float*>(ws);
-    hipLaunchKernelGGL(sparse_decode_bf16_kernel, dim3(d.batch * d.n_kv_heads, DEC_SPLIT), dim3(256), 0,
+    hipLaunchKernelGGL(sparse_decode_bf16_kernel<DENSE>, dim3(d.batch * d.n_kv_heads, DEC_SPLIT), dim3(256), 0,
                        st, (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, sel,
                        part, d.n_heads, d.n_kv_heads, (long)d.kv_len, (long)d.kv_capacity, d.topk,
                        d.norm_eps, qscale);
@@ -636,11 +649,23 @@ hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const fl
     return hipGetLastError();
   }
   const long nwg = (long)d.batch * d.n_kv_heads * gm.nqb * ((G + 3) / 4);
-  hipLaunchKernelGGL(sparse_prefill_bf16_kernel, dim3((unsigned)nwg), dim3(PF_THREADS), 0, st, (const bf16_t*)q,
-                     qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
-                     (bf16_t*)out, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0,
+  hipLaunchKernelGGL(sparse_prefill_bf16_kernel<DENSE>, dim3((unsigned)nwg), dim3(PF_THREADS), 0, st,
+                     (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g,
+                     sel, (bf16_t*)out, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0,
                      (int)gm.nqb, (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, qscale);
   return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
+                              const void* k_cache, const void* v_cache, const void* g,
+                              const int32_t* sel, void* out, void* ws, hipStream_t st) {
+  return launch_attn<false>(d, q, qw, k_cache, v_cache, g, sel, out, ws, st);
+}
+
+hipError_t launch_dense_attn(const sala_sparse_desc& d, const void* q, const float* qw,
+                             const void* k_cache, const void* v_cache, const void* g, void* out,
+                             void* ws, hipStream_t st) {
+  return launch_attn<true>(d, q, qw, k_cache, v_cache, g, nullptr, out, ws, st);
 }
 
 }  // namespace sala

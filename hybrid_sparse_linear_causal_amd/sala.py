@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsala.so")
 
 SALA_F32, SALA_BF16 = 0, 1
-OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN = 1, 2, 3
+OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN, OP_DENSE_ATTN = 1, 2, 3, 4
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid", 3: "unsupported", 4: "workspace", 5: "hip"}
 
 
@@ -61,12 +61,15 @@ def lib():
         L.sala_kv_pool.argtypes = [ctypes.POINTER(SparseDesc), _VP, _VP, ctypes.c_int64, ctypes.c_int64, _VP]
         L.sala_block_select.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 5 + [ctypes.c_size_t, _VP]
         L.sala_sparse_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 8 + [ctypes.c_size_t, _VP]
+        L.sala_dense_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7 + [ctypes.c_size_t, _VP]
+        L.sala_sparse_layer_uses_dense.argtypes = [ctypes.POINTER(SparseDesc)]
         L.sala_workspace_bytes.argtypes = [ctypes.c_int, _VP]
         L.sala_workspace_bytes.restype = ctypes.c_size_t
         L.sala_status_str.argtypes = [ctypes.c_int]
         L.sala_status_str.restype = ctypes.c_char_p
         for name in ("sala_linear_prefill", "sala_linear_decode_step", "sala_kv_append", "sala_kv_pool",
-                     "sala_block_select", "sala_sparse_attn", "sala_abi_version", "sala_last_hip_error"):
+                     "sala_block_select", "sala_sparse_attn", "sala_dense_attn",
+                     "sala_sparse_layer_uses_dense", "sala_abi_version", "sala_last_hip_error"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -240,3 +243,32 @@ def sparse_attn(q, k_cache, v_cache, g, sel, kv_len, *, topk=None, n_local=2, ep
           _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(out), _ptr(ws), ws_bytes, _stream(stream),
           what="sparse_attn")
     return out
+
+
+def dense_attn(q, k_cache, v_cache, g, kv_len, *, eps=1e-6, scale=0.0, q_norm_w=None, out=None,
+               workspace=None, stream=None):
+    """Dense mode of the sparse layer: causal attention over every cached block up to each
+    query's own. q, g [B, n_q, Hq, d]; caches [B, Hkv, cap, d]. Returns out."""
+    for n, t in (("q", q), ("g", g), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, n, q.dtype)
+    B, nq, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    desc = sparse_desc(batch=B, n_q=nq, n_heads=Hq, n_kv_heads=Hkv, head_dim=d, dtype=q.dtype,
+                       kv_len=kv_len, kv_capacity=cap, topk=3, n_local=2, eps=eps, scale=scale)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, ws_bytes = _workspace(OP_DENSE_ATTN, desc, q.device, workspace)
+    _call(lib().sala_dense_attn, ctypes.byref(desc), _ptr(q), _ptr(q_norm_w), _ptr(k_cache),
+          _ptr(v_cache), _ptr(g), _ptr(out), _ptr(ws), ws_bytes, _stream(stream), what="dense_attn")
+    return out
+
+
+def sparse_layer_uses_dense(*, batch, n_q, n_heads, n_kv_heads, head_dim, dtype, kv_len, kv_capacity,
+                            topk=64, n_local=2):
+    """The library's dense/sparse switch for a sparse-layer call (1 dense, 0 sparse)."""
+    desc = sparse_desc(batch=batch, n_q=n_q, n_heads=n_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
+                       dtype=dtype, kv_len=kv_len, kv_capacity=kv_capacity, topk=topk, n_local=n_local)
+    r = lib().sala_sparse_layer_uses_dense(ctypes.byref(desc))
+    if r < 0:
+        raise SalaError(2, "sparse_layer_uses_dense: invalid descriptor")
+    return bool(r)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SALA_ABI_VERSION 1
+#define SALA_ABI_VERSION 2
 
 typedef enum {
   SALA_OK = 0,
@@ -49,7 +49,12 @@ typedef enum {
 
 typedef enum { SALA_F32 = 0, SALA_BF16 = 1 } sala_dtype;
 
-typedef enum { SALA_OP_LINEAR_PREFILL = 1, SALA_OP_BLOCK_SELECT = 2, SALA_OP_SPARSE_ATTN = 3 } sala_op;
+typedef enum {
+  SALA_OP_LINEAR_PREFILL = 1,
+  SALA_OP_BLOCK_SELECT = 2,
+  SALA_OP_SPARSE_ATTN = 3,
+  SALA_OP_DENSE_ATTN = 4
+} sala_op;
 
 /* Linear-attention layer shape.
  *   batch      B >= 1
@@ -179,6 +184,23 @@ sala_status sala_sparse_attn(const sala_sparse_desc* desc, const void* q, const 
                              const void* k_cache, const void* v_cache, const void* gate,
                              const int32_t* sel, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Dense mode of the sparse layer ("MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模" §2.1: the
+ * sparse attention module switches between a dense and a sparse mode with the same weights).
+ * As sala_sparse_attn with every block 0 .. i attended (plain causal softmax attention over
+ * the cache, QK-norm on q, no positional encoding, output gate); no selection is read.
+ * desc->topk and desc->n_local are ignored. Same layouts, ownership and errors as
+ * sala_sparse_attn. Workspace: sala_workspace_bytes(SALA_OP_DENSE_ATTN, desc). */
+sala_status sala_dense_attn(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                            const void* k_cache, const void* v_cache, const void* gate, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* The switch between the two modes (same section; the pages give no length, so the rule is the
+ * one under which both modes give the same result): 1 when every query of the call would
+ * select all of its causal blocks (kv_len <= topk * 64, so sala_dense_attn equals block
+ * selection + sala_sparse_attn and the selection can be skipped), 0 when the sparse path must
+ * run, -1 for an invalid descriptor. Host-side, no device work. */
+int sala_sparse_layer_uses_dense(const sala_sparse_desc* desc);
 
 /* Workspace bytes an operation needs for this descriptor (0 if none; SIZE_MAX if the
  * descriptor is invalid). `desc` points to a sala_linear_desc for SALA_OP_LINEAR_PREFILL and

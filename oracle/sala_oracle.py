@@ -57,6 +57,7 @@ __all__ = [
     "select_row",
     "select_blocks",
     "sparse_attention",
+    "dense_attention",
     "sparse_prefill",
     "sparse_decode",
 ]
@@ -292,6 +293,30 @@ def sparse_attention(q_hat, k_hat, v, sel, block, scale, q_positions=None):
                     p = np.exp(s)
                     p = p / p.sum(axis=1, keepdims=True)
                     o[b, rows, h] = p @ V
+    return o
+
+
+def dense_attention(q_hat, k_hat, v, scale, q_positions=None):
+    """Dense mode of the sparse layer ([SALA-zh] §2.1: the sparse module can run in a dense
+    mode with the same weights): causal softmax attention of every query over all keys at
+    positions s <= its own position t, by definition (no blocks).
+
+    q_hat [B, Nq, H, d] at positions q_positions (default 0..Nq-1); k_hat, v [B, L, Hkv, d].
+    Returns o [B, Nq, H, d].
+    """
+    q_hat, k_hat, v = _f64(q_hat), _f64(k_hat), _f64(v)
+    B, Nq, H, d = q_hat.shape
+    L, Hkv = k_hat.shape[1], k_hat.shape[2]
+    group = H // Hkv
+    qpos = np.arange(Nq) if q_positions is None else np.asarray(q_positions)
+    allowed = np.arange(L)[None, :] <= qpos[:, None]  # [Nq, L]
+    o = np.empty((B, Nq, H, d))
+    for b in range(B):
+        for h in range(H):
+            s = (q_hat[b, :, h] @ k_hat[b, :, h // group].T) * scale
+            s = np.where(allowed, s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            o[b, :, h] = (p / p.sum(axis=1, keepdims=True)) @ v[b, :, h // group]
     return o
 
 

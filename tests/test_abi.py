@@ -32,7 +32,7 @@ def test_abi_version_and_status_strings():
     from hybrid_sparse_linear_causal_amd import sala as S
 
     L = S.lib()
-    assert L.sala_abi_version() == 1
+    assert L.sala_abi_version() == 2
     for code in range(6):
         assert L.sala_status_str(code)
     assert L.sala_last_hip_error() == 0
@@ -136,3 +136,26 @@ def test_sparse_null_workspace_and_pool_range():
     assert L.sala_sparse_attn(ctypes.byref(dd), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
                               None) == 3
     assert S.workspace_bytes(S.OP_SPARSE_ATTN, _sp(n_q=1, kv_len=1000, kv_capacity=1024)) > 0
+
+
+def test_dense_attn_arguments_and_mode_switch():
+    """Argument errors of sala_dense_attn (no device work), and the dense/sparse switch rule
+    (host-side): dense exactly while kv_len <= topk * 64."""
+    import torch
+
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = S.sparse_desc(batch=1, n_q=64, n_heads=8, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
+                      kv_len=640, kv_capacity=640, topk=10, n_local=2)
+    assert L.sala_dense_attn(None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert L.sala_dense_attn(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    bad = S.sparse_desc(batch=1, n_q=64, n_heads=8, n_kv_heads=3, head_dim=128, dtype=torch.bfloat16,
+                        kv_len=640, kv_capacity=640, topk=10, n_local=2)
+    assert L.sala_dense_attn(ctypes.byref(bad), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+    assert L.sala_sparse_layer_uses_dense(ctypes.byref(d)) == 1          # 640 <= 10 * 64
+    d.kv_len = d.kv_capacity = 641 + 63  # 704 > 640
+    d.n_q = 704 - 640
+    assert L.sala_sparse_layer_uses_dense(ctypes.byref(d)) == 0
+    assert L.sala_sparse_layer_uses_dense(ctypes.byref(bad)) == -1
+    assert L.sala_workspace_bytes(S.OP_DENSE_ATTN, ctypes.byref(d)) == 0  # prefill: none

@@ -236,6 +236,33 @@ def test_sparse_full_coverage_equals_dense_causal_sdpa(N, H, Hkv, d, block):
         assert sorted(j for j in r["sel"][0, 0, i] if j >= 0) == list(range(i + 1))
 
 
+@pytest.mark.parametrize("N,H,Hkv,d,q0", [(50, 2, 1, 8, 0), (70, 4, 2, 16, 0), (40, 4, 2, 8, 33), (65, 2, 2, 8, 64)])
+def test_dense_attention_equals_torch_sdpa(N, H, Hkv, d, q0):
+    """The dense-mode definition against torch's scaled_dot_product_attention: causal for a
+    prompt (q0 = 0), an explicit position mask for queries at positions q0 .. N-1 of a longer
+    cache; and equal to block attention with every causal block selected."""
+    import torch
+
+    q, k, v = rnd(1, N - q0, H, d), rnd(1, N, Hkv, d), rnd(1, N, Hkv, d)
+    qh, kh = O.qk_norm(q), O.qk_norm(k)
+    pos = np.arange(q0, N)
+    o = O.dense_attention(qh, kh, v, 1.0 / np.sqrt(d), q_positions=pos)
+    grp = H // Hkv
+    Q = torch.from_numpy(qh[0].transpose(1, 0, 2).copy())
+    K = torch.from_numpy(repeat_kv(kh, grp)[0].transpose(1, 0, 2).copy())
+    V = torch.from_numpy(repeat_kv(v, grp)[0].transpose(1, 0, 2).copy())
+    mask = torch.from_numpy(np.arange(N)[None, :] <= pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask).numpy()
+    np.testing.assert_allclose(o, ref.transpose(1, 0, 2)[None], rtol=1e-11, atol=1e-12)
+    block = 8
+    nqb = -(-N // block)
+    sel = np.full((1, Hkv, nqb, nqb), -1)
+    for i in range(nqb):
+        sel[0, :, i, : i + 1] = np.arange(i + 1)
+    ob = O.sparse_attention(qh, kh, v, sel, block, 1.0 / np.sqrt(d), q_positions=pos)
+    np.testing.assert_allclose(o, ob, rtol=1e-11, atol=1e-12)
+
+
 def test_pooled_score_equals_mean_of_pair_products():
     beta, d, H, Hkv = 8, 16, 4, 2
     q = rnd(1, 4 * beta, H, d)

@@ -331,6 +331,73 @@ def test_decode_select_exact_ties_across_slices(S):
     assert {450, 900, 7, 100} <= set(got.tolist())
 
 
+# ---------------------------------------------------------------- dense mode of the sparse layer
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,dtype", [
+    (1, 512, 2, 2, "f32"),
+    (1, 64 * 9 + 33, 8, 2, "bf16"),   # ragged last block
+    (2, 64 * 20, 16, 1, "bf16"),
+])
+def test_dense_attn_prefill(S, B, N, Hq, Hkv, dtype):
+    import torch
+
+    d = 64 if dtype == "f32" else 128
+    print(f"dense prefill B={B} N={N} Hq={Hq} Hkv={Hkv} {dtype}", flush=True)
+    q, k, v, g = sparse_case(41 + N, B, N, Hq, Hkv, d, dtype)
+    cap = ((N + 63) // 64) * 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kc = torch.zeros((B, Hkv, cap, d), dtype=tdt, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    S.kv_append(dev(k, dtype), dev(v, dtype), kc, vc, kp, N)
+    out = S.dense_attn(dev(q, dtype), kc, vc, dev(g, dtype), N)
+    ref = O.dense_attention(O.qk_norm(q), O.qk_norm(k), v, 1.0 / np.sqrt(d)) * O.sigmoid(g)
+    assert_rel(host(out), ref, TOL[dtype], "dense out")
+
+
+def test_dense_attn_decode(S):
+    """One decode token over a cache of already-normalised keys, every block attended."""
+    import torch
+
+    B, Hq, Hkv, d, L = 2, 32, 2, 128, 64 * 30 + 7
+    cap = ((L + 63) // 64) * 64
+    kc_h = host_normal(51, 5, (B, Hkv, L - 1, d), "bf16")
+    vc_h = host_normal(51, 6, (B, Hkv, L - 1, d), "bf16")
+    q = host_normal(51, 0, (B, 1, Hq, d), "bf16")
+    kn = host_normal(51, 1, (B, 1, Hkv, d), "bf16")
+    vn = host_normal(51, 2, (B, 1, Hkv, d), "bf16")
+    g = host_normal(51, 3, (B, 1, Hq, d), "bf16")
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[:, :, :L - 1] = dev(kc_h, "bf16")
+    vc[:, :, :L - 1] = dev(vc_h, "bf16")
+    kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    S.kv_append(dev(kn, "bf16"), dev(vn, "bf16"), kc, vc, kp, L, n_heads=Hq)
+    out = S.dense_attn(dev(q, "bf16"), kc, vc, dev(g, "bf16"), L)
+    K = np.concatenate([kc_h, O.qk_norm(kn).transpose(0, 2, 1, 3)], axis=2).transpose(0, 2, 1, 3)
+    V = np.concatenate([vc_h, vn.transpose(0, 2, 1, 3)], axis=2).transpose(0, 2, 1, 3)
+    ref = O.dense_attention(O.qk_norm(q), K, V, 1.0 / np.sqrt(d), q_positions=[L - 1]) * O.sigmoid(g)
+    assert_rel(host(out), ref, 1e-2, "dense decode out")
+
+
+@pytest.mark.parametrize("N,topk", [(64 * 8, 8), (64 * 7 + 5, 8)])
+def test_dense_equals_sparse_when_selection_covers_all(S, N, topk):
+    """Where the library's switch picks dense mode (kv_len <= topk * 64), block selection keeps
+    every causal block and the two modes give bit-identical outputs."""
+    import torch
+
+    B, Hq, Hkv, d = 1, 8, 2, 128
+    assert S.sparse_layer_uses_dense(batch=B, n_q=N, n_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                                     dtype=torch.bfloat16, kv_len=N, kv_capacity=((N + 63) // 64) * 64,
+                                     topk=topk)
+    q, k, v, g = sparse_case(61, B, N, Hq, Hkv, d, "bf16")
+    r = gpu_sparse_prefill(S, q, k, v, g, "bf16", topk, 2)
+    dense = S.dense_attn(dev(q, "bf16"), r["kc"], r["vc"], dev(g, "bf16"), N)
+    torch.cuda.synchronize()
+    assert torch.equal(dense, r["out"])
+
+
 # ---------------------------------------------------------------- determinism
 
 
