@@ -628,8 +628,9 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
                            (long)g.qb0, (int)RL, (long)g.nblk_cap, d.n_local);
     }
   }
-  // few long rows (decode): 1024 threads per row; many rows (prefill): 256
-  if (g.nqb == 1)
+  // long rows (decode past the two-level range, prefill beyond 4,096 candidate blocks): 1024
+  // threads and 16,384 keys in LDS per row; shorter rows: 256 threads, 4,096 keys
+  if (g.nqb == 1 || RL > 4096)
     hipLaunchKernelGGL((select_kernel<1024, 16384>), dim3((unsigned)(BG * g.nqb)), dim3(1024), 0, st, sc, sel,
                        (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
   else
