@@ -136,11 +136,16 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="stack_256k", choices=["stack_256k", "segmented_1m"],
+                    help="stack_256k: the headline line; segmented_1m: 1M-token prefill in segments + decode")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               f"multi-GPU path; the sharding design is described in DESIGN.md.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "segmented_1m":
+        segmented_1m(args)
+        return
 
     import torch
 
@@ -242,6 +247,17 @@ def main():
             e["end"] = ev(); e["end"].record()
         return e
 
+    def decode_step():
+        for Dr in dl:
+            q, k, v, g = Dr["qkvg"]
+            S.linear_decode_step(q, k, v, g, Dr["state"], L - 1, rope_base=W.rope_base, eps=W.norm_eps,
+                                 out=Dr["out"])
+        S.kv_append(dkn, dvn, dkc, dvc, dkp, L, eps=W.norm_eps, n_heads=H)
+        S.block_select(dq, dkp, L, L, n_kv_heads=Hkv, topk=Dw.topk, n_local=Dw.n_local, eps=W.norm_eps,
+                       sel=dsel, workspace=ws_dsel)
+        S.sparse_attn(dq, dkc, dvc, dg, dsel, L, n_local=Dw.n_local, eps=W.norm_eps, out=dsout,
+                      workspace=ws_datt)
+
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -309,8 +325,211 @@ def main():
             "decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
         },
     }
+    result["breakdown"].update(extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_sample(W)
+    print(json.dumps(result))
+
+
+def _time_events(torch, fn, reps):
+    """Average ms of fn() over reps calls, HIP events on the current stream."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d):
+    """Per-configuration layer times (32K linear, 128K sparse), the decode step as one graph
+    replay, and the decode step with the 256 MB last-level cache flushed before each step."""
+    from hybrid_sparse_linear_causal_amd.inputs import WORKLOADS, device_normal
+
+    res = {}
+    # linear prefill, 32,768 tokens x 32 heads
+    Wl = WORKLOADS["linear_32k"]
+    t = [device_normal(Wl.seed, tid, (1, Wl.seq_len, H, d)) for tid in range(4)]
+    out = torch.empty_like(t[0])
+    st = torch.empty((1, H, d, d), dtype=torch.float32, device="cuda")
+    ld = S.linear_desc(t[0], 0, W.rope_base, W.norm_eps)
+    ws = torch.empty(max(1, S.workspace_bytes(S.OP_LINEAR_PREFILL, ld)), dtype=torch.uint8, device="cuda")
+    ms = _time_events(torch, lambda: S.linear_prefill(*t, state_out=st, out=out, workspace=ws), 10)
+    res["linear_32k"] = {"ms": ms, "tokens_per_s": Wl.seq_len / (ms * 1e-3),
+                         "hbm_frac": Wl.seq_len * H * d * 2 * 5 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del t, out
+    # sparse prefill, 131,072 tokens (append + select + attention)
+    Ws = WORKLOADS["sparse_128k"]
+    N = Ws.seq_len
+    q, g = device_normal(Ws.seed, 0, (1, N, H, d)), device_normal(Ws.seed, 3, (1, N, H, d))
+    k, v = device_normal(Ws.seed, 1, (1, N, Hkv, d)), device_normal(Ws.seed, 2, (1, N, Hkv, d))
+    kc = torch.zeros((1, Hkv, N, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((1, Hkv, N // 64, d), dtype=torch.float32, device="cuda")
+    sel = torch.empty((1, Hkv, N // 64, Ws.topk), dtype=torch.int32, device="cuda")
+    sd = S.sparse_desc(batch=1, n_q=N, n_heads=H, n_kv_heads=Hkv, head_dim=d, dtype=torch.bfloat16,
+                       kv_len=N, kv_capacity=N, topk=Ws.topk, n_local=Ws.n_local)
+    wsel = torch.empty(S.workspace_bytes(S.OP_BLOCK_SELECT, sd), dtype=torch.uint8, device="cuda")
+    so = torch.empty_like(q)
+
+    def sparse_layer():
+        S.kv_append(k, v, kc, vc, kp, N, n_heads=H)
+        S.block_select(q, kp, N, N, n_kv_heads=Hkv, topk=Ws.topk, n_local=Ws.n_local, sel=sel, workspace=wsel)
+        S.sparse_attn(q, kc, vc, g, sel, N, n_local=Ws.n_local, out=so)
+
+    ms = _time_events(torch, sparse_layer, 5)
+    ms_att = _time_events(torch, lambda: S.sparse_attn(q, kc, vc, g, sel, N, n_local=Ws.n_local, out=so), 5)
+    fl = sparse_prefill_flops(N, H, d, Ws.topk)
+    res["sparse_128k"] = {"ms": ms, "tokens_per_s": N / (ms * 1e-3), "attention_ms": ms_att,
+                          "attention_mfma_frac": fl / (ms_att * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del q, g, k, v, kc, vc, so
+    # decode step: individual launches (above) vs one graph replay; linear states restored after
+    saved = [Dr["state"].clone() for Dr in dl]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        decode_step()
+    us_graph = _time_events(torch, graph.replay, 20) * 1e3
+    # last-level-cache-cold decode: 512 MB written between steps, outside the timed region
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for r in range(10):
+        flush.fill_(r)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        decode_step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    for Dr, s0 in zip(dl, saved):
+        Dr["state"].copy_(s0)
+    cold.sort()
+    res["decode_graph_step_us"] = us_graph
+    res["decode_graph_us_per_token"] = us_graph / B
+    res["decode_cold_step_us_median"] = cold[len(cold) // 2]
+    return res
+
+
+def segmented_1m(args):
+    """One 1,048,576-token sequence through the L,L,L,S stack, prefilled in segments of 131,072
+    tokens (linear state carried through state_in/pos0, KV and pooled caches grown through
+    kv_len), then decode steps at position 1,048,576. Inputs of each segment are drawn on the
+    GPU before its calls (not timed); only the library calls are timed, with HIP events."""
+    import torch
+
+    from hybrid_sparse_linear_causal_amd import sala as S
+    from hybrid_sparse_linear_causal_amd.inputs import device_normal
+
+    torch.cuda.set_device(0)
+    N, SEG, H, Hkv, d, topk, n_local = 1 << 20, 1 << 17, 32, 2, 128, 64, 2
+    bf = torch.bfloat16
+    cap = N + 64 * 64  # room for the decode tokens
+    states = [torch.zeros((1, H, d, d), dtype=torch.float32, device="cuda") for _ in range(3)]
+    kc = torch.zeros((1, Hkv, cap, d), dtype=bf, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((1, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    lout = torch.empty((1, SEG, H, d), dtype=bf, device="cuda")
+    sout = torch.empty_like(lout)
+    ld = S.linear_desc(lout, 0, 10000.0, 1e-6)
+    ws_lin = torch.empty(max(1, S.workspace_bytes(S.OP_LINEAR_PREFILL, ld)), dtype=torch.uint8, device="cuda")
+    sd_last = S.sparse_desc(batch=1, n_q=SEG, n_heads=H, n_kv_heads=Hkv, head_dim=d, dtype=bf, kv_len=N,
+                            kv_capacity=cap, topk=topk, n_local=n_local)
+    ws_sel = torch.empty(S.workspace_bytes(S.OP_BLOCK_SELECT, sd_last), dtype=torch.uint8, device="cuda")
+    sel = torch.empty((1, Hkv, SEG // 64, topk), dtype=torch.int32, device="cuda")
+
+    def prefill(record):
+        for st in states:
+            st.zero_()
+        kp.zero_()
+        ms = {"linear": 0.0, "sparse": 0.0}
+        for s in range(N // SEG):
+            s0, s1 = s * SEG, (s + 1) * SEG
+            lin_in = [[device_normal(1000 * li + s, tid, (1, SEG, H, d)) for tid in range(4)] for li in range(3)]
+            sq, sg = device_normal(3000 + s, 0, (1, SEG, H, d)), device_normal(3000 + s, 3, (1, SEG, H, d))
+            sk, sv = device_normal(3000 + s, 1, (1, SEG, Hkv, d)), device_normal(3000 + s, 2, (1, SEG, Hkv, d))
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            for li in range(3):
+                S.linear_prefill(*lin_in[li], pos0=s0, state_in=states[li], state_out=states[li], out=lout,
+                                 workspace=ws_lin)
+            e[1].record()
+            S.kv_append(sk, sv, kc, vc, kp, s1, n_heads=H)
+            S.block_select(sq, kp, s1, cap, n_kv_heads=Hkv, topk=topk, n_local=n_local, sel=sel, workspace=ws_sel)
+            S.sparse_attn(sq, kc, vc, sg, sel, s1, n_local=n_local, out=sout)
+            e[2].record()
+            torch.cuda.synchronize()
+            ms["linear"] += e[0].elapsed_time(e[1])
+            ms["sparse"] += e[1].elapsed_time(e[2])
+            del lin_in, sq, sg, sk, sv
+        return ms
+
+    prefill(False)
+    ms = prefill(True)
+    # decode at position N, N+1, ... (batch 1): 3 linear layers + the sparse layer
+    dl = [[device_normal(5000 + li, tid, (1, H, d)) for tid in range(4)] for li in range(3)]
+    dq, dg = device_normal(5100, 0, (1, 1, H, d)), device_normal(5100, 3, (1, 1, H, d))
+    dk, dv = device_normal(5100, 1, (1, 1, Hkv, d)), device_normal(5100, 2, (1, 1, Hkv, d))
+    ddesc = S.sparse_desc(batch=1, n_q=1, n_heads=H, n_kv_heads=Hkv, head_dim=d, dtype=bf, kv_len=N + 1,
+                          kv_capacity=cap, topk=topk, n_local=n_local)
+    ws_ds = torch.empty(S.workspace_bytes(S.OP_BLOCK_SELECT, ddesc), dtype=torch.uint8, device="cuda")
+    ws_da = torch.empty(S.workspace_bytes(S.OP_SPARSE_ATTN, ddesc), dtype=torch.uint8, device="cuda")
+    dsel = torch.empty((1, Hkv, 1, topk), dtype=torch.int32, device="cuda")
+    douts = [torch.empty((1, H, d), dtype=bf, device="cuda") for _ in range(3)]
+    dso = torch.empty_like(dq)
+
+    def dstep(p):
+        for li in range(3):
+            S.linear_decode_step(*dl[li], states[li], p, out=douts[li])
+        S.kv_append(dk, dv, kc, vc, kp, p + 1, n_heads=H)
+        S.block_select(dq, kp, p + 1, cap, n_kv_heads=Hkv, topk=topk, n_local=n_local, sel=dsel, workspace=ws_ds)
+        S.sparse_attn(dq, kc, vc, dg, dsel, p + 1, n_local=n_local, out=dso, workspace=ws_da)
+
+    dstep(N)
+    torch.cuda.synchronize()
+    steps = 32
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(steps):
+        dstep(N + 1 + t)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) * 1e3 / steps
+    t_prefill = ms["linear"] + ms["sparse"]
+    resident = {
+        "linear_state_per_layer": H * d * d * 4,
+        "sparse_kv_cache_per_layer": 2 * Hkv * cap * d * 2,
+        "sparse_pooled_keys_per_layer": Hkv * (cap // 64) * d * 4,
+        "segment_activations_per_layer": SEG * H * d * 2 * 5,
+        "select_workspace": ws_sel.numel(),
+        "linear_workspace": ws_lin.numel(),
+    }
+    result = {
+        "metric": "prefill tokens/s at 1M (segmented, L,L,L,S, batch 1); decode us/step at 1M (batch 1)",
+        "value": N / (t_prefill * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 1,
+        "ms_per_step": t_prefill,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 on the GPU, drawn per segment; no trained weights)",
+        "config": {"workload": "segmented_1m: 1,048,576 tokens in 8 segments of 131,072 through L,L,L,S, "
+                               "then decode at 1M", "seq_len": N, "segment": SEG, "batch": 1, "heads": H,
+                   "kv_heads_sparse": Hkv, "head_dim": d, "topk": topk, "n_local": n_local},
+        "breakdown": {"linear_ms_total_3_layers": ms["linear"], "sparse_ms_total": ms["sparse"],
+                      "decode_step_us": dec_us, "resident_bytes": resident},
+    }
     print(json.dumps(result))
 
 

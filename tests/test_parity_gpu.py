@@ -415,3 +415,78 @@ def test_deterministic_reruns(S):
     r2 = gpu_sparse_prefill(S, q, k, v, g, "bf16", 8, 2)
     torch.cuda.synchronize()
     assert torch.equal(r1["sel"], r2["sel"]) and torch.equal(r1["out"], r2["out"])
+
+
+# ---------------------------------------------------------------- graph capture
+
+
+def test_decode_step_graph_replay_matches_eager(S):
+    """A decode step (3 linear layers + sparse layer: append, select, attention) captured once
+    as a HIP graph and replayed three times, with eager work and synchronisation between the
+    replays; every replay must reproduce the eager step exactly (same inputs, reset state)."""
+    import torch
+
+    from hybrid_sparse_linear_causal_amd.inputs import device_normal
+
+    B, H, Hkv, d, L, topk, n_local = 2, 32, 2, 128, 64 * 300 + 9, 32, 2
+    bf = torch.bfloat16
+    lin = []
+    for li in range(3):
+        t = [device_normal(200 + li, tid, (B, H, d)) for tid in range(4)]
+        s0 = device_normal(200 + li, 4, (B, H, d, d), dtype="f32")
+        lin.append(dict(qkvg=t, s0=s0, state=s0.clone(), out=torch.empty_like(t[0])))
+    q, g = device_normal(210, 0, (B, 1, H, d)), device_normal(210, 3, (B, 1, H, d))
+    kn, vn = device_normal(210, 1, (B, 1, Hkv, d)), device_normal(210, 2, (B, 1, Hkv, d))
+    cap = ((L + 63) // 64) * 64
+    kc = torch.zeros((B, Hkv, cap, d), dtype=bf, device="cuda")
+    vc = torch.zeros_like(kc)
+    kc[:, :, :L - 1] = device_normal(211, 5, (B, Hkv, L - 1, d))
+    vc[:, :, :L - 1] = device_normal(211, 6, (B, Hkv, L - 1, d))
+    kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    S.kv_pool(kc, kp, L - 1, 0, (L - 1) // 64)
+    desc = S.sparse_desc(batch=B, n_q=1, n_heads=H, n_kv_heads=Hkv, head_dim=d, dtype=bf, kv_len=L,
+                         kv_capacity=cap, topk=topk, n_local=n_local)
+    sel = torch.empty((B, Hkv, 1, topk), dtype=torch.int32, device="cuda")
+    ws_sel = torch.empty(S.workspace_bytes(S.OP_BLOCK_SELECT, desc), dtype=torch.uint8, device="cuda")
+    ws_att = torch.empty(S.workspace_bytes(S.OP_SPARSE_ATTN, desc), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+
+    def step():
+        for Lr in lin:
+            S.linear_decode_step(*Lr["qkvg"], Lr["state"], L - 1, out=Lr["out"])
+        S.kv_append(kn, vn, kc, vc, kp, L, n_heads=H)
+        S.block_select(q, kp, L, cap, n_kv_heads=Hkv, topk=topk, n_local=n_local, sel=sel, workspace=ws_sel)
+        S.sparse_attn(q, kc, vc, g, sel, L, n_local=n_local, out=out, workspace=ws_att)
+
+    def reset():
+        for Lr in lin:
+            Lr["state"].copy_(Lr["s0"])
+
+    def snapshot():
+        return [x.clone() for x in [out, sel] + [Lr["out"] for Lr in lin] + [Lr["state"] for Lr in lin]]
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = snapshot()
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        reset()
+        out.zero_()
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {rep}"
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()  # eager work between replays
