@@ -73,6 +73,15 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Sum over aligned groups of 8 lanes with DPP (VALU-speed lane exchange, no LDS round trip):
+// swap neighbours, swap pairs, then mirror within the 8-lane half-row.
+__device__ __forceinline__ float group_sum8_dpp(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
 // logistic function for the output gate
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 

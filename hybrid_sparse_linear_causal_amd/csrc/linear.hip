@@ -42,7 +42,7 @@ __device__ __forceinline__ void norm_rope(uint4 (&x)[2], const float* w, int s, 
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
-  ss = group_sum<8>(ss);
+  ss = group_sum8_dpp(ss);
   const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
   float ra[8], rb[8];
 #pragma unroll
@@ -66,7 +66,7 @@ __device__ __forceinline__ void norm_rope_w(uint4 (&x)[2], const float* w, float
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss = fmaf(a[e], a[e], fmaf(b[e], b[e], ss));
-  ss = group_sum<8>(ss);
+  ss = group_sum8_dpp(ss);
   const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
   float ra[8], rb[8];
 #pragma unroll
@@ -346,7 +346,6 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     __syncthreads();
 
     const int tl = 16 * w4 + l16;
-    uint2 gv[8];
     if (out_wave) {
       // ---------------- intra-chunk: O^T = V^T (K~ Q~^T (.) causal) for queries 16w..16w+15
 #pragma unroll
@@ -392,11 +391,6 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           const bf16x8 sf = as_bf16x8(*reinterpret_cast<const uint4*>(&L.st[swz(16 * dt + l16, 4 * ks + lq)]));
           acc[dt] = mfma16x16x32(sf, qfrag[ks], acc[dt]);
         }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int col = 16 * dt + 4 * lq;
-        gv[dt] = *reinterpret_cast<const uint2*>(&Gt[swz(tl, col >> 3) + (col & 7)]);
-      }
     } else {
       // ---------------- state update: S += K~^T V (dk rows 32*w4 .. +31, all dv)
 #pragma unroll
@@ -411,19 +405,30 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           for (int it = 0; it < 2; ++it) acc[8 * it + jt] = mfma16x16x32(af[it], bfr, acc[8 * it + jt]);
         }
       }
+      // the gate tile becomes sigmoid(g) in place (bf16; elementwise, so the swizzle does not
+      // matter) while the output waves are still busy
+      bf16_t* Gw = L.t[buf][3];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint4* p = reinterpret_cast<uint4*>(Gw) + (j - 256) + 256 * m;
+        float x[8];
+        unpack8(*p, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = fast_sigmoid(x[e]);
+        *p = pack8(x);
+      }
     }
-    __syncthreads();  // every read of this chunk's S^T, q~, k~, v and g tiles is done
+    __syncthreads();  // every read of this chunk's S^T, q~, k~, v tiles is done; g holds sigmoid(g)
     if (out_wave) {
       // gated outputs staged in this wave's 16 rows of the (consumed) q~ tile, so that the
       // stores below write whole 256-byte rows
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const float g0 = __uint_as_float(gv[dt].x << 16), g1 = __uint_as_float(gv[dt].x & 0xffff0000u);
-        const float g2 = __uint_as_float(gv[dt].y << 16), g3 = __uint_as_float(gv[dt].y & 0xffff0000u);
-        uint2 o;
-        o.x = pack_bf16x2(acc[dt][0] * fast_sigmoid(g0), acc[dt][1] * fast_sigmoid(g1));
-        o.y = pack_bf16x2(acc[dt][2] * fast_sigmoid(g2), acc[dt][3] * fast_sigmoid(g3));
         const int col = 16 * dt + 4 * lq;
+        const uint2 sg = *reinterpret_cast<const uint2*>(&Gt[swz(tl, col >> 3) + (col & 7)]);
+        uint2 o;
+        o.x = pack_bf16x2(acc[dt][0] * bf2f(sg.x & 0xffffu), acc[dt][1] * bf2f(sg.x >> 16));
+        o.y = pack_bf16x2(acc[dt][2] * bf2f(sg.y & 0xffffu), acc[dt][3] * bf2f(sg.y >> 16));
         *reinterpret_cast<uint2*>(&Qt[swz(tl, col >> 3) + (col & 7)]) = o;
       }
     } else {
