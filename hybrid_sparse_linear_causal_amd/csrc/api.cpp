@@ -104,6 +104,11 @@ size_t sala_workspace_bytes(int op, const void* desc) {
       if (check_sparse(d, false) != SALA_OK) return SIZE_MAX;
       return sala::sparse_attn_workspace(*d);
     }
+    case SALA_OP_LINEAR_BACKWARD: {
+      const sala_linear_desc* d = static_cast<const sala_linear_desc*>(desc);
+      if (check_linear(d) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128) return SIZE_MAX;
+      return sala::linear_backward_workspace(*d);
+    }
     default: return SIZE_MAX;
   }
 }
@@ -123,6 +128,27 @@ sala_status sala_linear_prefill(const sala_linear_desc* desc, const void* q, con
   if (d.seq_len > 0 && need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
   return hip_status(sala::launch_linear_prefill(d, q, k, v, gate, q_norm_w, k_norm_w, state_in,
                                                 state_out, out, workspace, (hipStream_t)stream));
+}
+
+sala_status sala_linear_backward(const sala_linear_desc* desc, const void* q, const void* k,
+                                 const void* v, const void* gate, const float* q_norm_w,
+                                 const float* k_norm_w, const float* state_in, const void* dout,
+                                 const float* dstate_out, float* dq, float* dk, float* dv,
+                                 float* dg, float* dq_norm_w, float* dk_norm_w, float* dstate_in,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  sala_status s = check_linear(desc);
+  if (s != SALA_OK) return s;
+  const sala_linear_desc& d = *desc;
+  if (d.dtype != SALA_BF16 || d.head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (d.seq_len > 0 && (!q || !k || !v || !gate || !dout || !dq || !dk || !dv || !dg)) return SALA_ERR_NULL;
+  if (!all_aligned({q, k, v, gate, q_norm_w, k_norm_w, state_in, dout, dstate_out, dq, dk, dv, dg, dq_norm_w,
+                    dk_norm_w, dstate_in, workspace}))
+    return SALA_ERR_INVALID;
+  const size_t need = sala::linear_backward_workspace(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_linear_backward(d, q, k, v, gate, q_norm_w, k_norm_w, state_in, dout,
+                                                 dstate_out, dq, dk, dv, dg, dq_norm_w, dk_norm_w, dstate_in,
+                                                 workspace, (hipStream_t)stream));
 }
 
 sala_status sala_linear_decode_step(const sala_linear_desc* desc, const void* q, const void* k,

@@ -51,6 +51,11 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
 hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const void* k,
                                 const void* v, const void* g, const float* qw, const float* kw,
                                 float* state, void* out, hipStream_t st);
+size_t linear_backward_workspace(const sala_linear_desc& d);
+hipError_t launch_linear_backward(const sala_linear_desc& d, const void* q, const void* k, const void* v,
+                                  const void* g, const float* qw, const float* kw, const float* state_in,
+                                  const void* dout, const float* dstate_out, float* dq, float* dk, float* dv,
+                                  float* dg, float* dqw, float* dkw, float* dstate_in, void* ws, hipStream_t st);
 
 // ---- sparse layer
 struct SparseGeom {

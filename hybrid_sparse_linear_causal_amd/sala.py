@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsala.so")
 
 SALA_F32, SALA_BF16 = 0, 1
-OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN, OP_DENSE_ATTN = 1, 2, 3, 4
+OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN, OP_DENSE_ATTN, OP_LINEAR_BACKWARD = 1, 2, 3, 4, 5
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid", 3: "unsupported", 4: "workspace", 5: "hip"}
 
 
@@ -57,6 +57,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.sala_linear_prefill.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 10 + [ctypes.c_size_t, _VP]
         L.sala_linear_decode_step.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 9
+        L.sala_linear_backward.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 17 + [ctypes.c_size_t, _VP]
         L.sala_kv_append.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7
         L.sala_kv_pool.argtypes = [ctypes.POINTER(SparseDesc), _VP, _VP, ctypes.c_int64, ctypes.c_int64, _VP]
         L.sala_block_select.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 5 + [ctypes.c_size_t, _VP]
@@ -67,7 +68,8 @@ def lib():
         L.sala_workspace_bytes.restype = ctypes.c_size_t
         L.sala_status_str.argtypes = [ctypes.c_int]
         L.sala_status_str.restype = ctypes.c_char_p
-        for name in ("sala_linear_prefill", "sala_linear_decode_step", "sala_kv_append", "sala_kv_pool",
+        for name in ("sala_linear_prefill", "sala_linear_decode_step", "sala_linear_backward",
+                     "sala_kv_append", "sala_kv_pool",
                      "sala_block_select", "sala_sparse_attn", "sala_dense_attn",
                      "sala_sparse_layer_uses_dense", "sala_abi_version", "sala_last_hip_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -157,6 +159,35 @@ def linear_prefill(q, k, v, g, *, pos0=0, rope_base=10000.0, eps=1e-6, state_in=
           _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(ws),
           ws_bytes, _stream(stream), what="linear_prefill")
     return out, state_out
+
+
+def linear_backward(q, k, v, g, dout, *, pos0=0, rope_base=10000.0, eps=1e-6, state_in=None,
+                    dstate_out=None, q_norm_w=None, k_norm_w=None, need_norm_w_grads=False,
+                    need_dstate_in=True, workspace=None, stream=None):
+    """Gradients of the linear layer (bf16 inputs [B, N, H, d], d = 128). Returns a dict with
+    dq, dk, dv, dg [B, N, H, d] f32, dstate_in [B, H, d, d] f32 (or None) and, when
+    need_norm_w_grads, dq_norm_w, dk_norm_w [d] f32."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("dout", dout)):
+        _check(t, n, torch.bfloat16)
+    B, N, H, d = q.shape
+    for n, t in (("k", k), ("v", v), ("g", g), ("dout", dout)):
+        if tuple(t.shape) != (B, N, H, d):
+            raise SalaError(2, f"{n} shape {tuple(t.shape)} != {(B, N, H, d)}")
+    for n, t in (("state_in", state_in), ("dstate_out", dstate_out), ("q_norm_w", q_norm_w),
+                 ("k_norm_w", k_norm_w)):
+        _check(t, n, torch.float32)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    grads = {n: torch.empty((B, N, H, d), **f32) for n in ("dq", "dk", "dv", "dg")}
+    grads["dstate_in"] = torch.empty((B, H, d, d), **f32) if need_dstate_in else None
+    grads["dq_norm_w"] = torch.empty(d, **f32) if need_norm_w_grads else None
+    grads["dk_norm_w"] = torch.empty(d, **f32) if need_norm_w_grads else None
+    desc = linear_desc(q, pos0, rope_base, eps)
+    ws, ws_bytes = _workspace(OP_LINEAR_BACKWARD, desc, q.device, workspace)
+    _call(lib().sala_linear_backward, ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+          _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state_in), _ptr(dout), _ptr(dstate_out),
+          *(_ptr(grads[n]) for n in ("dq", "dk", "dv", "dg", "dq_norm_w", "dk_norm_w", "dstate_in")),
+          _ptr(ws), ws_bytes, _stream(stream), what="linear_backward")
+    return grads
 
 
 def linear_decode_step(q, k, v, g, state, pos, *, rope_base=10000.0, eps=1e-6, q_norm_w=None,

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SALA_ABI_VERSION 2
+#define SALA_ABI_VERSION 3
 
 typedef enum {
   SALA_OK = 0,
@@ -53,7 +53,8 @@ typedef enum {
   SALA_OP_LINEAR_PREFILL = 1,
   SALA_OP_BLOCK_SELECT = 2,
   SALA_OP_SPARSE_ATTN = 3,
-  SALA_OP_DENSE_ATTN = 4
+  SALA_OP_DENSE_ATTN = 4,
+  SALA_OP_LINEAR_BACKWARD = 5
 } sala_op;
 
 /* Linear-attention layer shape.
@@ -134,6 +135,28 @@ sala_status sala_linear_prefill(const sala_linear_desc* desc, const void* q, con
 sala_status sala_linear_decode_step(const sala_linear_desc* desc, const void* q, const void* k,
                                     const void* v, const void* gate, const float* q_norm_w,
                                     const float* k_norm_w, float* state, void* out, void* stream);
+
+/* Linear layer backward (pages: as sala_linear_prefill; "面壁智能发布MiniCPM-SALA：稀疏-线性混合
+ * 架构，9B模型端侧跑通百万上下文，速度飙升3.5倍" section "高效训练范式：以25%的成本完成转换" — the
+ * linear layers are trained first, all parameters later). Given dout = dL/d out and, optionally,
+ * dstate_out = dL/d state_out, returns the gradients of L through sala_linear_prefill with the
+ * same desc and inputs:
+ *   dq, dk, dv, dg: [B, N, H, d] float (required);
+ *   dq_norm_w, dk_norm_w: [d] float, or NULL to skip (computed as if the weight were all ones
+ *   when the matching input weight is NULL);
+ *   dstate_in: [B, H, d, d] float, or NULL to skip.
+ * Inputs q, k, v, gate, dout: [B, N, H, d] bf16 (desc->dtype must be SALA_BF16, head_dim 128);
+ * q_norm_w, k_norm_w, state_in, dstate_out as in sala_linear_prefill (NULL = ones / zeros).
+ * The gradients are chunked causal linear attentions over the normalised, rotated q and k (two
+ * of them in reverse token order) on MFMA with bf16 operands and fp32 accumulation; the norm,
+ * RoPE and gate transposes run in fp32. Deterministic (no atomics). Nothing may alias.
+ * Workspace: sala_workspace_bytes(SALA_OP_LINEAR_BACKWARD, desc) bytes. */
+sala_status sala_linear_backward(const sala_linear_desc* desc, const void* q, const void* k,
+                                 const void* v, const void* gate, const float* q_norm_w,
+                                 const float* k_norm_w, const float* state_in, const void* dout,
+                                 const float* dstate_out, float* dq, float* dk, float* dv,
+                                 float* dg, float* dq_norm_w, float* dk_norm_w, float* dstate_in,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sparse layer KV append (pages: "面壁智能发布MiniCPM-SALA…" section "SALA混合架构…" — the sparse
  * layers keep the full KV cache without positional encoding; the block-selection mechanism

@@ -32,7 +32,7 @@ def test_abi_version_and_status_strings():
     from hybrid_sparse_linear_causal_amd import sala as S
 
     L = S.lib()
-    assert L.sala_abi_version() == 2
+    assert L.sala_abi_version() == 3
     for code in range(6):
         assert L.sala_status_str(code)
     assert L.sala_last_hip_error() == 0
@@ -159,3 +159,26 @@ def test_dense_attn_arguments_and_mode_switch():
     assert L.sala_sparse_layer_uses_dense(ctypes.byref(d)) == 0
     assert L.sala_sparse_layer_uses_dense(ctypes.byref(bad)) == -1
     assert L.sala_workspace_bytes(S.OP_DENSE_ATTN, ctypes.byref(d)) == 0  # prefill: none
+
+
+def test_linear_backward_arguments():
+    """Argument errors of sala_linear_backward (no device work): bf16 and d = 128 only, the four
+    input-gradient buffers are required, the workspace must be large enough."""
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = _lin(seq_len=256)
+    need = S.workspace_bytes(S.OP_LINEAR_BACKWARD, d)
+    assert need > 0
+    # q k v gate | q_norm_w k_norm_w state_in | dout dstate_out | dq dk dv dg | dqw dkw dstate_in
+    args = [FAKE] * 4 + [None, None, None] + [FAKE, None] + [FAKE] * 4 + [None, None, None]
+    assert L.sala_linear_backward(ctypes.byref(d), *args, FAKE, need - 1, None) == 4
+    assert L.sala_linear_backward(ctypes.byref(d), *args, None, need, None) == 4
+    bad = list(args)
+    bad[9] = None  # dq
+    assert L.sala_linear_backward(ctypes.byref(d), *bad, FAKE, need, None) == 1
+    f32 = _lin(seq_len=256, dtype=S.SALA_F32)
+    assert L.sala_linear_backward(ctypes.byref(f32), *args, FAKE, need, None) == 3
+    assert L.sala_workspace_bytes(S.OP_LINEAR_BACKWARD, ctypes.byref(f32)) == ctypes.c_size_t(-1).value
+    d64 = _lin(seq_len=256, head_dim=64, n_heads=2, n_kv_heads=2)
+    assert L.sala_linear_backward(ctypes.byref(d64), *args, FAKE, need, None) == 3
