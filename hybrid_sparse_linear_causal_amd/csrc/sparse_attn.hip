@@ -8,20 +8,24 @@
 //   out[t, h] = softmax_s(scale * q^ . k_s) . v_s * sigmoid(gate[t, h]),
 //   s ranging over tokens s <= p of the blocks in sel[g, i].
 //
-// bf16 prefill (d = 128): one workgroup per (b, g, query block, 4 query heads); each wave owns
-// one head's 64 query rows. For every selected block the 64x128 K tile and the transposed V
-// tile are staged once in LDS for the 4 waves. Per wave and block:
-//   S^T = K Q^T   (16 MFMA 16x16x32 tiles x 4 k-steps; queries are the MFMA columns)
-//   online softmax on S^T in fp32 (exp2 with scale*log2(e) folded into q; rescaling of the
-//                 running output only when a row maximum grows by more than 2^8)
-//   O^T += V^T P^T (P^T comes straight from the S^T accumulators: the 16x16x32 k-index is
-//                 permuted consistently for both operands, so no cross-lane moves)
+// bf16 prefill (d = 128): one workgroup per (b, g, query block, 4 query heads); 8 waves, each
+// owning 32 query rows of one head. Every selected block's 64x128 K and V tiles are copied into
+// a 4-stage LDS ring by global->LDS DMA and shared by the 8 waves. Per wave and block:
+//   S^T = K Q^T - m  (MFMA 16x16x32; queries are the MFMA columns; the running reference m
+//                 enters as the accumulator's initial value)
+//   P^T = exp2(S^T)  (scale*log2(e) folded into q; the reference is raised lazily, only when a
+//                 probability could exceed 2^20)
+//   O^T += V^T P^T   (P^T comes straight from the S^T accumulators: the 16x16x32 k-index is
+//                 permuted consistently for both operands, so no cross-lane moves; V^T
+//                 fragments come from transposing LDS reads)
+// The scores of block e+1 are issued before the probabilities of block e (software pipeline).
 // bf16 decode (n_q = 1): split over the selected blocks (one block per wave), the query
 // heads of the GQA group are the 16 MFMA columns; partial (max, sum, output) are combined by
 // a second kernel that also applies the gate.
 // f32 (any shape, correctness-scale inputs): one thread per query row, keys from LDS.
 #include "common.hpp"
 #include "launch.hpp"
+#include "sparse_tiles.hpp"
 
 namespace sala {
 
@@ -32,170 +36,9 @@ constexpr int KS = D + 8;    // K tile row stride (bf16): 272 B
 constexpr int VS = 64 + 8;   // V^T tile row stride (bf16): 144 B
 constexpr int DEC_SPLIT = 16;       // decode workgroups per (b, g)
 
-constexpr int TILE = 64 * 128;  // bf16 elements per 64-row tile
-constexpr int NSTAGE = 4;       // LDS ring depth (blocks resident or in flight)
-
 __device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
   const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// V tiles use their own swizzle: chunk c of row r sits at chunk position c ^ 2(r & 7). The
-// transposing reads of 32 lanes touch 8 consecutive rows x 2 adjacent chunks; this puts those
-// 16 chunks at 16 different positions, so they never share a bank (the K swizzle would put two
-// rows on the same banks).
-__device__ __forceinline__ int swzv(int row, int chunk) { return row * 128 + 8 * (chunk ^ (2 * (row & 7))); }
-
-// Issue the DMA of one 64-key block (K and V tiles, 16 KB each = 16 pieces of 1 KB) into a
-// stage. With 8 waves each wave moves pieces 2w and 2w+1 (rows 8w .. 8w+7) of both tiles:
-// DMA_PER_WAVE instructions. Lane l of a piece fills chunk position l % 16 of row 4I + l / 16,
-// so it loads the source chunk that the tile's swizzle puts there. Rows at or beyond kv_len
-// are clamped to the last valid row: they are causally masked (K) or weighted 0 (V).
-constexpr int DMA_PER_WAVE = 4;
-__device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, long row_base,
-                                          long blk, long kv_len, bf16_t* Ks, bf16_t* Vs) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int I = 2 * wave + m;                 // 1 KB piece: rows 4I .. 4I+3
-    const int row = 4 * I + (lane >> 4);
-    const int chk = (lane & 15) ^ (row & 15);   // K source chunk stored at this position
-    const int chv = (lane & 15) ^ (2 * (row & 7));
-    long p = blk * 64 + row;
-    if (p >= kv_len) p = kv_len - 1;
-    const long off = (row_base + p) * D;
-    dma16(kc + off + 8 * chk, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Ks + I * 512)));
-    dma16(vc + off + 8 * chv, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Vs + I * 512)));
-  }
-}
-
-// A operand V^T (rows dv = 16*dt + l16, k = keys in the permuted order of the P^T fragments:
-// slots 0..3 = keys kb + 4*lq + e, slots 4..7 = keys kb + 16 + 4*lq + e) via two
-// transposing reads. Source lane (i = l16) points at key row kb(+16) + 4*lq + i/4, columns
-// 16*dt + 4*(i%4).
-__device__ __forceinline__ bf16x8 vt_frag(const bf16_t* Vs, int kb, int dt, int l16, int lq) {
-  const int row0 = kb + 4 * lq + (l16 >> 2);
-  const int col = 16 * dt + 4 * (l16 & 3);          // element column; chunk = col / 8
-  const int ch = col >> 3, sub = col & 7;
-  const uint2 a = ds_read_tr(Vs + swzv(row0, ch) + sub);
-  const uint2 b = ds_read_tr(Vs + swzv(row0 + 16, ch) + sub);
-  return as_bf16x8(a, b);
-}
-
-
-// ---- pieces of one wave's work on a staged 64-key block for its QT x 16 query rows (rows
-// qrow0 + 16*qt + l16 of the query block)
-
-// S^T[kt][qt] = K[kt] Q^T[qt] - m[qt] (scores in log2 units: scale*log2(e) is folded into q;
-// the running reference m enters as the accumulator's initial value, minit = -m)
-template <int QT>
-__device__ __forceinline__ void scores(const bf16_t* Ks, const bf16x8 (&qf)[QT][4], const f32x4 (&minit)[QT],
-                                       f32x4 (&ST)[4][QT], int l16) {
-  const int lq = (threadIdx.x & 63) >> 4;
-  // two key tiles per k-step: 2*QT independent accumulators between reuses of one
-#pragma unroll
-  for (int kp = 0; kp < 4; kp += 2) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int kt = kp; kt < kp + 2; ++kt) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + swz(16 * kt + l16, 4 * ks + lq)));
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ks == 0 ? minit[qt] : ST[kt][qt]);
-      }
-    }
-  }
-}
-
-// causal mask of the query's own block: key after query -> -inf
-template <int QT>
-__device__ __forceinline__ void mask_diag(f32x4 (&ST)[4][QT], int l16, int lq, int qrow0) {
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (16 * kt + 4 * lq + c > qrow0 + 16 * qt + l16) ST[kt][qt][c] = -INFINITY;
-}
-
-// Online softmax with a lazily raised reference. The score accumulators already hold s - m,
-// so the probabilities are plain exp2 of them. A 32-key half whose per-lane partial sum exceeds
-// P_LIMIT (some probability above 2^20), and the first half the row ever sees, raise m to the
-// half's row maximum first: the running output and sum are rescaled, and the not yet consumed
-// scores (this block and the next one, already issued with the old reference) are shifted.
-// The reference is always a score of the row, so the row's largest probability is >= 1.
-constexpr float P_LIMIT = 1048576.0f;  // 2^20
-
-template <int QT>
-__device__ __forceinline__ void exp_half(const f32x4 (&ST)[4][QT], int c, float (&p)[QT][8], float (&part)[QT]) {
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      p[qt][u] = fast_exp2(ST[2 * c][qt][u]);
-      p[qt][4 + u] = fast_exp2(ST[2 * c + 1][qt][u]);
-    }
-    part[qt] = ((p[qt][0] + p[qt][1]) + (p[qt][2] + p[qt][3])) + ((p[qt][4] + p[qt][5]) + (p[qt][6] + p[qt][7]));
-  }
-}
-
-template <int QT>
-__device__ __forceinline__ void raise_ref(f32x4 (&ST)[4][QT], f32x4 (&SN)[4][QT], f32x4 (&OT)[8][QT], float (&m)[QT],
-                                       f32x4 (&minit)[QT], float (&lp)[QT], int c, bool first) {
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(ST[2 * c][qt][u], ST[2 * c + 1][qt][u]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float delta = first ? mx : fmaxf(mx, 0.0f);
-    if (!first) {
-      const float alpha = fast_exp2(-delta);
-      lp[qt] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) OT[dt][qt] *= alpha;
-    }
-    m[qt] += delta;
-    minit[qt] = f32x4{-m[qt], -m[qt], -m[qt], -m[qt]};
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      ST[kt][qt] -= delta;
-      SN[kt][qt] -= delta;
-    }
-  }
-}
-
-// P^T = exp2(S^T) per 32-key half, O^T += V^T P^T (P^T straight from the accumulators)
-template <int QT>
-__device__ __forceinline__ void exp_pv(const bf16_t* Vs, f32x4 (&ST)[4][QT], f32x4 (&SN)[4][QT], f32x4 (&OT)[8][QT],
-                                       float (&m)[QT], f32x4 (&minit)[QT], float (&lp)[QT], int l16, int lq,
-                                       bool first) {
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    float p[QT][8], part[QT];
-    exp_half<QT>(ST, c, p, part);
-    bool big = false;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) big |= part[qt] > P_LIMIT;
-    if (__builtin_expect(__any(big) || (first && c == 0), 0)) {
-      raise_ref<QT>(ST, SN, OT, m, minit, lp, c, first && c == 0);
-      exp_half<QT>(ST, c, p, part);
-    }
-    bf16x8 pf[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      lp[qt] += part[qt];
-      pf[qt] = as_bf16x8(pack8(p[qt]));
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const bf16x8 a = vt_frag(Vs, 32 * c, dt, l16, lq);
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) OT[dt][qt] = mfma16x16x32(a, pf[qt], OT[dt][qt]);
-    }
-  }
 }
 
 // grid: B*Hkv*nqb*ceil(G/4) workgroups of 512 threads (8 waves: 4 heads x 2 row halves)
