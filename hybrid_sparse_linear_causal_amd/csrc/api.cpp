@@ -104,6 +104,17 @@ size_t sala_workspace_bytes(int op, const void* desc) {
       if (check_sparse(d, false) != SALA_OK) return SIZE_MAX;
       return sala::sparse_attn_workspace(*d);
     }
+    case SALA_OP_SPARSE_ATTN_BACKWARD: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse(d) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128 || d->n_q < 2)
+        return SIZE_MAX;
+      return sala::sparse_attn_backward_workspace(*d);
+    }
+    case SALA_OP_KV_NORM_BACKWARD: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse(d, false) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128) return SIZE_MAX;
+      return sala::kv_norm_backward_workspace(*d);
+    }
     case SALA_OP_LINEAR_BACKWARD: {
       const sala_linear_desc* d = static_cast<const sala_linear_desc*>(desc);
       if (check_linear(d) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128) return SIZE_MAX;
@@ -231,6 +242,42 @@ sala_status sala_dense_attn(const sala_sparse_desc* desc, const void* q, const f
   if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
   return hip_status(sala::launch_dense_attn(d, q, q_norm_w, k_cache, v_cache, gate, out, workspace,
                                             (hipStream_t)stream));
+}
+
+sala_status sala_sparse_attn_backward(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                                      const void* k_cache, const void* v_cache, const void* gate,
+                                      const int32_t* sel, const void* dout, float* dq, float* dk_cache,
+                                      float* dv_cache, float* dg, float* dq_norm_w, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  sala_status s = check_sparse(desc);
+  if (s != SALA_OK) return s;
+  const sala_sparse_desc& d = *desc;
+  if (d.dtype != SALA_BF16 || d.head_dim != 128 || d.n_q < 2) return SALA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !gate || !sel || !dout || !dq || !dk_cache || !dv_cache || !dg)
+    return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, sel, dout, dq, dk_cache, dv_cache, dg, dq_norm_w,
+                    workspace}))
+    return SALA_ERR_INVALID;
+  const size_t need = sala::sparse_attn_backward_workspace(d);
+  if (!workspace || workspace_bytes < need) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_sparse_attn_backward(d, q, q_norm_w, k_cache, v_cache, gate, sel, dout, dq,
+                                                      dk_cache, dv_cache, dg, dq_norm_w, workspace,
+                                                      (hipStream_t)stream));
+}
+
+sala_status sala_kv_norm_backward(const sala_sparse_desc* desc, const void* k_new, const float* k_norm_w,
+                                  const float* dk_cache, float* dk_new, float* dk_norm_w, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  sala_status s = check_sparse(desc, false);
+  if (s != SALA_OK) return s;
+  const sala_sparse_desc& d = *desc;
+  if (d.dtype != SALA_BF16 || d.head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (!k_new || !dk_cache || !dk_new) return SALA_ERR_NULL;
+  if (!all_aligned({k_new, k_norm_w, dk_cache, dk_new, dk_norm_w, workspace})) return SALA_ERR_INVALID;
+  const size_t need = sala::kv_norm_backward_workspace(d);
+  if (!workspace || workspace_bytes < need) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_kv_norm_backward(d, k_new, k_norm_w, dk_cache, dk_new, dk_norm_w, workspace,
+                                                  (hipStream_t)stream));
 }
 
 int sala_sparse_layer_uses_dense(const sala_sparse_desc* desc) {

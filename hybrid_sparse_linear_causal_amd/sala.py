@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libsala.so")
 
 SALA_F32, SALA_BF16 = 0, 1
 OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN, OP_DENSE_ATTN, OP_LINEAR_BACKWARD = 1, 2, 3, 4, 5
+OP_SPARSE_ATTN_BACKWARD, OP_KV_NORM_BACKWARD = 6, 7
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid", 3: "unsupported", 4: "workspace", 5: "hip"}
 
 
@@ -58,6 +59,8 @@ def lib():
         L.sala_linear_prefill.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 10 + [ctypes.c_size_t, _VP]
         L.sala_linear_decode_step.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 9
         L.sala_linear_backward.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 17 + [ctypes.c_size_t, _VP]
+        L.sala_sparse_attn_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 13 + [ctypes.c_size_t, _VP]
+        L.sala_kv_norm_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 6 + [ctypes.c_size_t, _VP]
         L.sala_kv_append.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7
         L.sala_kv_pool.argtypes = [ctypes.POINTER(SparseDesc), _VP, _VP, ctypes.c_int64, ctypes.c_int64, _VP]
         L.sala_block_select.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 5 + [ctypes.c_size_t, _VP]
@@ -69,6 +72,7 @@ def lib():
         L.sala_status_str.argtypes = [ctypes.c_int]
         L.sala_status_str.restype = ctypes.c_char_p
         for name in ("sala_linear_prefill", "sala_linear_decode_step", "sala_linear_backward",
+                     "sala_sparse_attn_backward", "sala_kv_norm_backward",
                      "sala_kv_append", "sala_kv_pool",
                      "sala_block_select", "sala_sparse_attn", "sala_dense_attn",
                      "sala_sparse_layer_uses_dense", "sala_abi_version", "sala_last_hip_error"):
@@ -274,6 +278,49 @@ def sparse_attn(q, k_cache, v_cache, g, sel, kv_len, *, topk=None, n_local=2, ep
           _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(out), _ptr(ws), ws_bytes, _stream(stream),
           what="sparse_attn")
     return out
+
+
+def sparse_attn_backward(q, k_cache, v_cache, g, sel, kv_len, dout, *, topk=None, n_local=2, eps=1e-6,
+                         scale=0.0, q_norm_w=None, need_norm_w_grad=False, workspace=None, stream=None):
+    """Gradients of sparse_attn (bf16, prefill, fixed selection). Returns a dict with dq, dg
+    [B, n_q, Hq, d], dk_cache, dv_cache [B, Hkv, cap, d] (all f32) and dq_norm_w [d] f32 when
+    need_norm_w_grad (else None)."""
+    for n, t in (("q", q), ("g", g), ("k_cache", k_cache), ("v_cache", v_cache), ("dout", dout)):
+        _check(t, n, torch.bfloat16)
+    _check(sel, "sel", torch.int32)
+    B, nq, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    desc = sparse_desc(batch=B, n_q=nq, n_heads=Hq, n_kv_heads=Hkv, head_dim=d, dtype=q.dtype,
+                       kv_len=kv_len, kv_capacity=cap, topk=topk or sel.shape[-1], n_local=n_local,
+                       eps=eps, scale=scale)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    r = dict(dq=torch.empty((B, nq, Hq, d), **f32), dg=torch.empty((B, nq, Hq, d), **f32),
+             dk_cache=torch.empty((B, Hkv, cap, d), **f32), dv_cache=torch.empty((B, Hkv, cap, d), **f32),
+             dq_norm_w=torch.empty(d, **f32) if need_norm_w_grad else None)
+    ws, ws_bytes = _workspace(OP_SPARSE_ATTN_BACKWARD, desc, q.device, workspace)
+    _call(lib().sala_sparse_attn_backward, ctypes.byref(desc), _ptr(q), _ptr(q_norm_w), _ptr(k_cache),
+          _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(dout), _ptr(r["dq"]), _ptr(r["dk_cache"]),
+          _ptr(r["dv_cache"]), _ptr(r["dg"]), _ptr(r["dq_norm_w"]), _ptr(ws), ws_bytes, _stream(stream),
+          what="sparse_attn_backward")
+    return r
+
+
+def kv_norm_backward(k_new, dk_cache, kv_len, *, n_heads, eps=1e-6, k_norm_w=None, need_norm_w_grad=False,
+                     workspace=None, stream=None):
+    """Backward of the key normalisation of kv_append for the appended tokens. k_new bf16
+    [B, n_q, Hkv, d]; dk_cache f32 [B, Hkv, cap, d]. Returns (dk_new f32, dk_norm_w f32 or None)."""
+    _check(k_new, "k_new", torch.bfloat16)
+    _check(dk_cache, "dk_cache", torch.float32)
+    B, nq, Hkv, d = k_new.shape
+    cap = dk_cache.shape[2]
+    desc = sparse_desc(batch=B, n_q=nq, n_heads=n_heads, n_kv_heads=Hkv, head_dim=d, dtype=k_new.dtype,
+                       kv_len=kv_len, kv_capacity=cap, topk=3, n_local=2, eps=eps)
+    dk = torch.empty((B, nq, Hkv, d), dtype=torch.float32, device=k_new.device)
+    dw = torch.empty(d, dtype=torch.float32, device=k_new.device) if need_norm_w_grad else None
+    ws, ws_bytes = _workspace(OP_KV_NORM_BACKWARD, desc, k_new.device, workspace)
+    _call(lib().sala_kv_norm_backward, ctypes.byref(desc), _ptr(k_new), _ptr(k_norm_w), _ptr(dk_cache), _ptr(dk),
+          _ptr(dw), _ptr(ws), ws_bytes, _stream(stream), what="kv_norm_backward")
+    return dk, dw
 
 
 def dense_attn(q, k_cache, v_cache, g, kv_len, *, eps=1e-6, scale=0.0, q_norm_w=None, out=None,

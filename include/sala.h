@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SALA_ABI_VERSION 3
+#define SALA_ABI_VERSION 4
 
 typedef enum {
   SALA_OK = 0,
@@ -54,7 +54,9 @@ typedef enum {
   SALA_OP_BLOCK_SELECT = 2,
   SALA_OP_SPARSE_ATTN = 3,
   SALA_OP_DENSE_ATTN = 4,
-  SALA_OP_LINEAR_BACKWARD = 5
+  SALA_OP_LINEAR_BACKWARD = 5,
+  SALA_OP_SPARSE_ATTN_BACKWARD = 6,
+  SALA_OP_KV_NORM_BACKWARD = 7
 } sala_op;
 
 /* Linear-attention layer shape.
@@ -217,6 +219,36 @@ sala_status sala_sparse_attn(const sala_sparse_desc* desc, const void* q, const 
 sala_status sala_dense_attn(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
                             const void* k_cache, const void* v_cache, const void* gate, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sparse layer attention backward (pages: as sala_sparse_attn; "面壁智能发布MiniCPM-SALA…" section
+ * "高效训练范式：以25%的成本完成转换" — sparse attention is on in the later training stages, which
+ * train every parameter). Given dout = dL/d out of a bf16 prefill sala_sparse_attn call (n_q > 1)
+ * with the same desc and inputs, returns, with the selection held fixed (a discrete choice):
+ *   dq, dg: [B, n_q, Hq, d] float (required);
+ *   dk_cache, dv_cache: [B, Hkv, kv_capacity, d] float (required): the gradients with respect to
+ *     the cache contents (the normalised keys k^ and the values); every row is written, 0 for
+ *     rows no query attends;
+ *   dq_norm_w: [d] float or NULL to skip (computed as if all ones when q_norm_w is NULL).
+ * The softmax statistics are recomputed (the forward keeps none). Products run on MFMA with bf16
+ * operands (q^ scale log2 e, dO = dout sigmoid(gate), P and dS) and fp32 accumulation. The
+ * key/value gradients are accumulated key-block by key-block over the query blocks that chose
+ * each block, in a fixed order: the result is deterministic. Nothing may alias.
+ * Workspace: sala_workspace_bytes(SALA_OP_SPARSE_ATTN_BACKWARD, desc) bytes. */
+sala_status sala_sparse_attn_backward(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
+                                      const void* k_cache, const void* v_cache, const void* gate,
+                                      const int32_t* sel, const void* dout, float* dq, float* dk_cache,
+                                      float* dv_cache, float* dg, float* dq_norm_w, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Backward of the key normalisation sala_kv_append applies to the n_q appended tokens (k^ =
+ * RMSNorm(k_new) * k_norm_w, written at cache positions [kv_len - n_q, kv_len)). dk_cache is the
+ * cache gradient from sala_sparse_attn_backward; returns dk_new [B, n_q, Hkv, d] float and, unless
+ * NULL, dk_norm_w [d] float. The value gradient of the appended tokens is the dv_cache rows of
+ * those positions (the append copies v unchanged). k_new: bf16 [B, n_q, Hkv, d].
+ * Workspace: sala_workspace_bytes(SALA_OP_KV_NORM_BACKWARD, desc) bytes. */
+sala_status sala_kv_norm_backward(const sala_sparse_desc* desc, const void* k_new, const float* k_norm_w,
+                                  const float* dk_cache, float* dk_new, float* dk_norm_w, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* The switch between the two modes (same section; the pages give no length, so the rule is the
  * one under which both modes give the same result): 1 when every query of the call would

@@ -105,17 +105,19 @@ def linear_layer_grads(q, k, v, g, dout, *, dstate_out=None, pos0=0, rope_base=1
                 dq_norm_w=grad(tqw), dk_norm_w=grad(tkw))
 
 
-def sparse_attention_layer(q, k_hat, v, g, sel, *, block=64, scale=None, eps=1e-6, q_norm_w=None):
+def sparse_attention_layer(q, k_hat, v, g, sel, *, block=64, scale=None, eps=1e-6, q_norm_w=None,
+                           q_positions=None):
     """The sparse layer's attention step for a fixed selection (sala_oracle.sparse_attention on
-    q_hat = qk_norm(q), then the sigmoid gate). q, g [B, N, H, d] at positions 0..N-1; k_hat,
-    v [B, L, Hkv, d]; sel [B, Hkv, N // block (ceil), topk] of block indices (-1 ignored)."""
+    q_hat = qk_norm(q), then the sigmoid gate). q, g [B, N, H, d] at positions q_positions
+    (default 0..N-1); k_hat, v [B, L, Hkv, d]; sel [B, Hkv, nqb, topk] of block indices (-1
+    ignored), indexed by the query's block position // block."""
     B, N, H, d = q.shape
     L, Hkv = k_hat.shape[1], k_hat.shape[2]
     group = H // Hkv
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     q_hat = _qk_norm(q, q_norm_w, eps)
-    qpos = np.arange(N)
+    qpos = np.arange(N) if q_positions is None else np.asarray(q_positions)
     o = torch.zeros((B, N, H, d), dtype=torch.float64)
     blocks_of_q = qpos // block
     for b in range(B):
@@ -135,12 +137,13 @@ def sparse_attention_layer(q, k_hat, v, g, sel, *, block=64, scale=None, eps=1e-
 
 
 def sparse_attention_grads(q, k_hat, v, g, sel, dout, *, block=64, scale=None, eps=1e-6,
-                           q_norm_w=None):
+                           q_norm_w=None, q_positions=None):
     """Gradients of <out, dout> for the sparse layer's attention step with a fixed selection.
     Returns dict(dq, dk_hat, dv, dg, dq_norm_w) as float64 numpy arrays (dq_norm_w None when
     no weight was given)."""
     tq, tk, tv, tg, tw = _t(q, True), _t(k_hat, True), _t(v, True), _t(g, True), _t(q_norm_w, True)
-    out = sparse_attention_layer(tq, tk, tv, tg, sel, block=block, scale=scale, eps=eps, q_norm_w=tw)
+    out = sparse_attention_layer(tq, tk, tv, tg, sel, block=block, scale=scale, eps=eps, q_norm_w=tw,
+                                 q_positions=q_positions)
     (out * _t(dout)).sum().backward()
     return dict(dq=tq.grad.numpy().copy(), dk_hat=tk.grad.numpy().copy(), dv=tv.grad.numpy().copy(),
                 dg=tg.grad.numpy().copy(), dq_norm_w=None if tw is None else tw.grad.numpy().copy())

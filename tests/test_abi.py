@@ -32,7 +32,7 @@ def test_abi_version_and_status_strings():
     from hybrid_sparse_linear_causal_amd import sala as S
 
     L = S.lib()
-    assert L.sala_abi_version() == 3
+    assert L.sala_abi_version() == 4
     for code in range(6):
         assert L.sala_status_str(code)
     assert L.sala_last_hip_error() == 0
@@ -182,3 +182,34 @@ def test_linear_backward_arguments():
     assert L.sala_workspace_bytes(S.OP_LINEAR_BACKWARD, ctypes.byref(f32)) == ctypes.c_size_t(-1).value
     d64 = _lin(seq_len=256, head_dim=64, n_heads=2, n_kv_heads=2)
     assert L.sala_linear_backward(ctypes.byref(d64), *args, FAKE, need, None) == 3
+
+
+def test_sparse_backward_arguments():
+    """Argument errors of sala_sparse_attn_backward and sala_kv_norm_backward (no device work)."""
+    import torch
+
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = S.sparse_desc(batch=1, n_q=128, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
+                      kv_len=128, kv_capacity=128, topk=3, n_local=2)
+    need = S.workspace_bytes(S.OP_SPARSE_ATTN_BACKWARD, d)
+    assert need > 0
+    # q qw k v gate sel dout | dq dk dv dg dqw
+    args = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    assert L.sala_sparse_attn_backward(ctypes.byref(d), *args, FAKE, need - 1, None) == 4
+    assert L.sala_sparse_attn_backward(ctypes.byref(d), *args, None, need, None) == 4
+    bad = list(args)
+    bad[5] = None  # sel
+    assert L.sala_sparse_attn_backward(ctypes.byref(d), *bad, FAKE, need, None) == 1
+    dec = S.sparse_desc(batch=1, n_q=1, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
+                        kv_len=128, kv_capacity=128, topk=3, n_local=2)
+    assert L.sala_sparse_attn_backward(ctypes.byref(dec), *args, FAKE, need, None) == 3  # decode: not built
+    f32 = S.sparse_desc(batch=1, n_q=128, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.float32,
+                        kv_len=128, kv_capacity=128, topk=3, n_local=2)
+    assert L.sala_sparse_attn_backward(ctypes.byref(f32), *args, FAKE, need, None) == 3
+    assert L.sala_workspace_bytes(S.OP_SPARSE_ATTN_BACKWARD, ctypes.byref(f32)) == ctypes.c_size_t(-1).value
+    kneed = S.workspace_bytes(S.OP_KV_NORM_BACKWARD, d)
+    assert kneed > 0
+    assert L.sala_kv_norm_backward(ctypes.byref(d), FAKE, None, FAKE, None, None, FAKE, kneed, None) == 1
+    assert L.sala_kv_norm_backward(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, FAKE, kneed - 1, None) == 4

@@ -72,3 +72,85 @@ def test_linear_backward_empty_sequence(S):
     torch.cuda.synchronize()
     assert torch.equal(got["dstate_in"], ds_out)
     assert int(torch.count_nonzero(got["dq_norm_w"])) == 0 and got["dq"].numel() == 0
+
+
+# ---------------------------------------------------------------- sparse layer
+
+
+def _sparse_setup(S, seed, B, kv_len, n_q, Hq, Hkv, topk, with_w):
+    """Caches filled by kv_append (the prefix, then the n_q queried tokens), the selection of the
+    queried tokens by block_select; returns host copies for the oracle."""
+    import torch
+
+    d, cap = 128, ((kv_len + 63) // 64) * 64
+    q, g, dout = (host_normal(seed, t, (B, n_q, Hq, d), "bf16") for t in range(3))
+    k, v = (host_normal(seed, t, (B, kv_len, Hkv, d), "bf16") for t in (3, 4))
+    qw = (1.0 + 0.25 * host_normal(seed, 5, (d,), "f32")) if with_w else None
+    kw = (1.0 + 0.25 * host_normal(seed, 6, (d,), "f32")) if with_w else None
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    p0 = kv_len - n_q
+    wk = None if kw is None else dev(kw, "f32")
+    if p0 > 0:
+        S.kv_append(dev(k[:, :p0], "bf16"), dev(v[:, :p0], "bf16"), kc, vc, kp, p0, n_heads=Hq, k_norm_w=wk)
+    S.kv_append(dev(k[:, p0:], "bf16"), dev(v[:, p0:], "bf16"), kc, vc, kp, kv_len, n_heads=Hq, k_norm_w=wk)
+    qd = dev(q, "bf16")
+    wq = None if qw is None else dev(qw, "f32")
+    sel = S.block_select(qd, kp, kv_len, cap, n_kv_heads=Hkv, topk=topk, n_local=2, q_norm_w=wq)
+    # oracle inputs: the cache contents token-major, the selection indexed by absolute query block
+    k_hat = host(kc)[:, :, :kv_len].transpose(0, 2, 1, 3)
+    v_h = host(vc)[:, :, :kv_len].transpose(0, 2, 1, 3)
+    sel_h = sel.cpu().numpy()
+    nqb_all = (kv_len + 63) // 64
+    sel_full = np.full((B, Hkv, nqb_all, topk), -1, dtype=np.int64)
+    sel_full[:, :, p0 // 64:] = sel_h
+    return dict(q=q, g=g, dout=dout, k=k, qw=qw, kw=kw, kc=kc, vc=vc, sel=sel, qd=qd, wq=wq, wk=wk,
+                k_hat=k_hat, v=v_h, sel_full=sel_full, p0=p0, cap=cap)
+
+
+@pytest.mark.parametrize("B,kv_len,n_q,Hq,Hkv,topk,with_w", [
+    (1, 640, 640, 4, 2, 4, True),       # 10 query blocks
+    (1, 2150, 2150, 2, 1, 6, False),    # 34 query blocks: block 0 chosen by 34 > one slice; ragged tail; 2 heads
+    (1, 640, 256, 4, 2, 4, True),       # queries continue a cached prefix of 384 tokens
+    (2, 384, 384, 32, 2, 3, False),     # a 16-head GQA group (4 head quads), batch 2
+])
+def test_sparse_attn_backward(S, B, kv_len, n_q, Hq, Hkv, topk, with_w):
+    print(f"sparse_attn_backward B={B} kv_len={kv_len} n_q={n_q} Hq={Hq} Hkv={Hkv} topk={topk} w={with_w}",
+          flush=True)
+    c = _sparse_setup(S, 500 + kv_len + n_q, B, kv_len, n_q, Hq, Hkv, topk, with_w)
+    got = S.sparse_attn_backward(c["qd"], c["kc"], c["vc"], dev(c["g"], "bf16"), c["sel"], kv_len,
+                                 dev(c["dout"], "bf16"), topk=topk, q_norm_w=c["wq"], need_norm_w_grad=True)
+    qw = c["qw"] if with_w else np.ones(128)
+    ref = G.sparse_attention_grads(c["q"], c["k_hat"], c["v"], c["g"], c["sel_full"], c["dout"], q_norm_w=qw,
+                                   q_positions=np.arange(c["p0"], kv_len))
+    errs = {}
+    errs["dq"] = assert_rel(host(got["dq"]), ref["dq"], TOL, "dq")
+    errs["dg"] = assert_rel(host(got["dg"]), ref["dg"], TOL, "dg")
+    errs["dq_norm_w"] = assert_rel(host(got["dq_norm_w"]), ref["dq_norm_w"], TOL, "dq_norm_w")
+    dk = host(got["dk_cache"])
+    dv = host(got["dv_cache"])
+    errs["dk_cache"] = assert_rel(dk[:, :, :kv_len].transpose(0, 2, 1, 3), ref["dk_hat"], TOL, "dk_cache")
+    errs["dv_cache"] = assert_rel(dv[:, :, :kv_len].transpose(0, 2, 1, 3), ref["dv"], TOL, "dv_cache")
+    assert np.all(dk[:, :, kv_len:] == 0) and np.all(dv[:, :, kv_len:] == 0)  # capacity past kv_len
+    print("  relative errors:", {n: f"{e:.2e}" for n, e in errs.items()}, flush=True)
+
+    # the key normalisation of the appended tokens, given this cache gradient
+    dk_new, dkw = S.kv_norm_backward(dev(c["k"][:, c["p0"]:], "bf16"), got["dk_cache"], kv_len, n_heads=Hq,
+                                     k_norm_w=c["wk"], need_norm_w_grad=True)
+    kref = G.key_norm_grads(c["k"][:, c["p0"]:], dk[:, :, c["p0"]:kv_len].transpose(0, 2, 1, 3),
+                            c["kw"] if with_w else np.ones(128))
+    assert_rel(host(dk_new), kref["dk"], 1e-4, "dk_new")
+    assert_rel(host(dkw), kref["dk_norm_w"], 1e-4, "dk_norm_w")
+
+
+def test_sparse_attn_backward_repeatable(S):
+    """The key/value gradients are summed in a fixed order: two calls give identical bits."""
+    import torch
+
+    c = _sparse_setup(S, 77, 1, 2150, 2150, 2, 1, 6, False)
+    a = S.sparse_attn_backward(c["qd"], c["kc"], c["vc"], dev(c["g"], "bf16"), c["sel"], 2150, dev(c["dout"], "bf16"))
+    b = S.sparse_attn_backward(c["qd"], c["kc"], c["vc"], dev(c["g"], "bf16"), c["sel"], 2150, dev(c["dout"], "bf16"))
+    torch.cuda.synchronize()
+    for n in ("dq", "dg", "dk_cache", "dv_cache"):
+        assert torch.equal(a[n], b[n]), n

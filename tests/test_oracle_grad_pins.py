@@ -179,3 +179,24 @@ def test_key_norm_grads_match_finite_differences():
         u = rnd(*x.shape)
         num = fd(f, x, u)
         assert abs(num - float(np.sum(gr[gname] * u))) <= 1e-6 * max(1.0, abs(num))
+
+
+def test_sparse_grads_with_query_positions_match_finite_differences():
+    """Queries at later positions (a prompt continued after earlier tokens are cached): the
+    q_positions path of the torch re-expression against the numpy oracle by finite differences."""
+    c = _sparse_case()
+    qpos = np.arange(8, 20)  # the last 12 tokens (blocks 2..4 of 4 tokens) query the cache
+    q, g, dout = c["q"][:, 8:], c["g"][:, 8:], c["dout"][:, 8:]
+    sel = c["sel"]
+    scale = 1.0 / np.sqrt(q.shape[-1])
+    gr = G.sparse_attention_grads(q, c["k_hat"], c["v"], g, sel, dout, block=c["block"], q_positions=qpos)
+
+    def loss(qq=q, kk=c["k_hat"], vv=c["v"]):
+        o = O.sparse_attention(O.qk_norm(qq), kk, vv, sel, c["block"], scale, q_positions=qpos)
+        return float(np.sum(o * O.sigmoid(g) * dout))
+
+    for x, gname, f in ((q, "dq", lambda xx: loss(qq=xx)), (c["k_hat"], "dk_hat", lambda xx: loss(kk=xx)),
+                        (c["v"], "dv", lambda xx: loss(vv=xx))):
+        u = rnd(*x.shape)
+        num = fd(f, x, u)
+        assert abs(num - float(np.sum(gr[gname] * u))) <= 1e-6 * max(1.0, abs(num))
