@@ -15,10 +15,12 @@
 //   dS_in = dS_N + sum_t q~_t^T dO_t                             (that pass's final state)
 // and dg needs o, the forward recurrence without the gate. One chunked MFMA kernel family,
 //   Y_u = sum_{w<=u} (A_u . B_w) C_w + A_u S0  over token order u (the sequence or its reverse),
-// computes all four; elementwise kernels before (norm, RoPE, gate) and after (their
-// transposes, the norm-weight sums) complete the chain. Workspace: q~, k~, dO in bf16 (the
-// forward also feeds q~ and k~ to MFMA in bf16), o in fp32, segment states, two transposed
-// states and the norm-weight partial sums.
+// computes all four. The o pass writes dg = dout o sigmoid'(g) directly; the dq~ pass's states
+// are the transposes of the o pass's, and the dk~ pass's of the dv pass's, so two of the four
+// segment-sum passes are shared. Elementwise kernels before (norm, RoPE, gate) and after
+// (their transposes, the norm-weight sums) complete the chain. Workspace: q~, k~, dO in bf16
+// (the forward also feeds q~ and k~ to MFMA in bf16), segment states and the norm-weight
+// partial sums.
 #include <algorithm>
 
 #include "common.hpp"
@@ -102,16 +104,6 @@ lbwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, con
 __global__ void __launch_bounds__(256)
 lbwd_copy_kernel(const float* __restrict__ src, float* __restrict__ dst, long n) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) dst[i] = src ? src[i] : 0.0f;
-}
-
-// dst[bh] = src[bh]^T (d x d fp32), the state handed to a pass that needs the transpose
-__global__ void __launch_bounds__(256)
-lbwd_transpose_kernel(const float* __restrict__ src, float* __restrict__ dst) {
-  const long bh = blockIdx.x;
-  for (int e = threadIdx.x; e < D * D; e += 256) {
-    const int i = e / D, jj = e % D;
-    dst[bh * D * D + (long)jj * D + i] = src[bh * D * D + e];
-  }
 }
 
 // ---- plain chunked causal linear attention: Y_u = sum_{w<=u} (A_u . B_w) C_w + A_u S0, token
@@ -204,11 +196,15 @@ lplain_scan_kernel(const float* __restrict__ S0, float* __restrict__ ws, int nsl
 
 // per (b, h, segment): the chunk loop from the segment's entering state. Waves 0-3 produce the
 // outputs of query tiles 0-3, waves 4-7 carry S (dk rows 32(w-4) .. +31) and publish S^T.
-template <bool REV>
+// TRANS: the entering states (S0 and the segment slots) are stored transposed, i.e. this pass's
+// state is the transpose of another pass's (the slots are then that pass's). GATE: instead of
+// Y, the output is dg = dout * Y * sigmoid'(g) (Y is the layer's pre-gate output).
+template <bool REV, bool TRANS, bool GATE>
 __global__ void __launch_bounds__(PL_NT)
 lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ C,
                     const float* __restrict__ S0, const float* __restrict__ ws, float* __restrict__ S_final,
-                    float* __restrict__ Y, int N, int H, int seg_len, int nseg) {
+                    float* __restrict__ Y, const bf16_t* __restrict__ gate, const bf16_t* __restrict__ dout, int N,
+                    int H, int seg_len, int nseg) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   PlainLds& L = *reinterpret_cast<PlainLds*>(lds_raw);
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
@@ -233,7 +229,9 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
       for (int jt = 0; jt < 8; ++jt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[8 * it + jt][e] = s0 ? s0[(32 * w4 + 16 * it + 4 * lq + e) * D + 16 * jt + l16] : 0.f;
+          acc[8 * it + jt][e] = !s0 ? 0.f
+                                : TRANS ? s0[(16 * jt + l16) * D + 32 * w4 + 16 * it + 4 * lq + e]
+                                        : s0[(32 * w4 + 16 * it + 4 * lq + e) * D + 16 * jt + l16];
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
@@ -252,6 +250,17 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
     const bf16_t* At = L.t[buf][0];
     bf16_t* Bt = L.t[buf][1];
     const bf16_t* Ct = L.t[buf][2];
+    // gate and output gradient of this lane's query (used after the chunk's final wait)
+    uint2 gv[8], dov[8];
+    if (GATE && out_wave) {
+      const long u = u0 + 16 * w4 + l16;
+      const long off = head_off + tok_of(REV, u < u_end ? u : u_end - 1, N) * tok_stride + 4 * lq;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        gv[dt] = *reinterpret_cast<const uint2*>(gate + off + 16 * dt);
+        dov[dt] = *reinterpret_cast<const uint2*>(dout + off + 16 * dt);
+      }
+    }
     if (u0 + CH < u_end) dma_tiles(src, head_off, tok_stride, u0 + CH, N, REV, L.t[buf ^ 1]);
     const int nvalid = u_end - u0 < CH ? (int)(u_end - u0) : CH;
     if (nvalid < CH) {
@@ -340,7 +349,21 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
       if (u < u_end) {
         float* yp = Y + head_off + tok_of(REV, u, N) * tok_stride + 4 * lq;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(yp + 16 * dt) = acc[dt];
+        for (int dt = 0; dt < 8; ++dt) {
+          f32x4 y = acc[dt];
+          if (GATE) {
+            const float gg[4] = {bf2f(gv[dt].x & 0xffffu), bf2f(gv[dt].x >> 16), bf2f(gv[dt].y & 0xffffu),
+                                 bf2f(gv[dt].y >> 16)};
+            const float dd[4] = {bf2f(dov[dt].x & 0xffffu), bf2f(dov[dt].x >> 16), bf2f(dov[dt].y & 0xffffu),
+                                 bf2f(dov[dt].y >> 16)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = fast_sigmoid(gg[e]);
+              y[e] = dd[e] * y[e] * sg * (1.0f - sg);
+            }
+          }
+          *reinterpret_cast<f32x4*>(yp + 16 * dt) = y;
+        }
       }
     }
     __syncthreads();
@@ -399,13 +422,12 @@ __device__ __forceinline__ void norm_rope_bwd(float* __restrict__ dx, const bf16
   }
 }
 
-// dq, dk (in place, from dq~ and dk~), dg = dout o sigmoid'(g); per-block partial sums of the
-// norm-weight gradients into wpart[block][2][D] (q then k)
+// dq, dk (in place, from dq~ and dk~); per-block partial sums of the norm-weight gradients into
+// wpart[block][2][D] (q then k)
 __global__ void __launch_bounds__(EW_NT)
-lbwd_post_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ g,
-                 const bf16_t* __restrict__ dout, const float* __restrict__ qw, const float* __restrict__ kw,
-                 const float* __restrict__ o, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dg,
-                 float* __restrict__ wpart, long nrows, int N, int H, long pos0, float eps, RopeFreqs fr) {
+lbwd_post_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ qw,
+                 const float* __restrict__ kw, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ wpart,
+                 long nrows, int N, int H, long pos0, float eps, RopeFreqs fr) {
   __shared__ float red[EW_ROWS][2][D];
   const int s8 = threadIdx.x & 7, rl = threadIdx.x >> 3;
   float wq_sum[16], wk_sum[16];
@@ -420,24 +442,6 @@ lbwd_post_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, con
     rope_cs(pos, s8, fr, c, s);
     norm_rope_bwd(dq + base, q + base, qw, s8, eps, c, s, ok, wq_sum);
     norm_rope_bwd(dk + base, k + base, kw, s8, eps, c, s, ok, wk_sum);
-    float gv[16], dv16[16];
-    load16(g + base, s8, gv);
-    load16(dout + base, s8, dv16);
-#pragma unroll
-    for (int hlf = 0; hlf < 2; ++hlf) {
-      const float* op = o + base + 64 * hlf + 8 * s8;
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(op), o1 = *reinterpret_cast<const f32x4*>(op + 4);
-      f32x4 r[2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float sg = fast_sigmoid(gv[8 * hlf + e]);
-        r[e / 4][e % 4] = dv16[8 * hlf + e] * (e < 4 ? o0[e] : o1[e - 4]) * sg * (1.0f - sg);
-      }
-      if (ok) {
-        *reinterpret_cast<f32x4*>(dg + base + 64 * hlf + 8 * s8) = r[0];
-        *reinterpret_cast<f32x4*>(dg + base + 64 * hlf + 8 * s8 + 4) = r[1];
-      }
-    }
   }
   // block partial sums of the weight gradients over its rows
 #pragma unroll
@@ -454,21 +458,29 @@ lbwd_post_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, con
   wpart[((long)blockIdx.x * 2 + which) * D + dim] = a;
 }
 
-// dw_q, dw_k = sums of the per-block partials (one thread per output)
+// dw_q, dw_k = sums of the per-block partials: one block per output (q dims, then k dims), a
+// fixed-order tree reduction
 __global__ void __launch_bounds__(256)
 lbwd_wsum_kernel(const float* __restrict__ wpart, int nblocks, float* __restrict__ dqw, float* __restrict__ dkw) {
-  const int which = threadIdx.x >> 7, dim = threadIdx.x & 127;
+  __shared__ float red[256];
+  const int which = blockIdx.x / D, dim = blockIdx.x % D;
   float a = 0.f;
-  for (int bk = 0; bk < nblocks; ++bk) a += wpart[((long)bk * 2 + which) * D + dim];
+  for (int bk = threadIdx.x; bk < nblocks; bk += 256) a += wpart[((long)bk * 2 + which) * D + dim];
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
   float* dst = which ? dkw : dqw;
-  if (dst) dst[dim] = a;
+  if (threadIdx.x == 0 && dst) dst[dim] = red[0];
 }
 
 constexpr int EW_BLOCKS_MAX = 2048;
 
 struct BwdPlan {
   int seg, nseg, ew_blocks;
-  size_t off_qh, off_kh, off_do, off_o, off_slots, off_tin, off_tout, off_wpart, total;
+  size_t off_qh, off_kh, off_do, off_slots, off_wpart, total;
 };
 
 BwdPlan bwd_plan(const sala_linear_desc& d) {
@@ -484,33 +496,33 @@ BwdPlan bwd_plan(const sala_linear_desc& d) {
   p.off_qh = take(act * 2);
   p.off_kh = take(act * 2);
   p.off_do = take(act * 2);
-  p.off_o = take(act * 4);
   p.off_slots = take(p.nseg > 1 ? bh * p.nseg * D * D * 4 : 0);
-  p.off_tin = take(bh * D * D * 4);
-  p.off_tout = take(bh * D * D * 4);
   p.off_wpart = take((size_t)p.ew_blocks * 2 * D * 4);
   p.total = off;
   return p;
 }
 
-template <bool REV>
+// one plain pass; with SEGSUM false the segment slots of an earlier pass (whose state this
+// pass's is the transpose of) are reused as they are
+template <bool REV, bool TRANS, bool GATE>
 hipError_t run_plain(const bf16_t* A, const bf16_t* Bm, const bf16_t* C, const float* S0, float* S_final, float* Y,
-                     float* slots, int B, int N, int H, int seg, int nseg, hipStream_t st) {
+                     const bf16_t* gate, const bf16_t* dout, float* slots, bool segsum, int B, int N, int H, int seg,
+                     int nseg, hipStream_t st) {
   static const hipError_t attr_ok = [] {
-    const hipError_t e0 = hipFuncSetAttribute((const void*)lplain_chunk_kernel<REV>,
+    const hipError_t e0 = hipFuncSetAttribute((const void*)lplain_chunk_kernel<REV, TRANS, GATE>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PlainLds));
     const hipError_t e1 = hipFuncSetAttribute((const void*)lplain_segsum_kernel<REV>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PlainSegLds));
     return e0 != hipSuccess ? e0 : e1;
   }();
   if (attr_ok != hipSuccess) return attr_ok;
-  if (nseg > 1) {
+  if (segsum && nseg > 1) {
     hipLaunchKernelGGL(lplain_segsum_kernel<REV>, dim3(B * H * (nseg - 1)), dim3(PL_NT), sizeof(PlainSegLds), st,
                        Bm, C, slots, N, H, seg, nseg);
     hipLaunchKernelGGL(lplain_scan_kernel, dim3(B * H, D * D / 256), dim3(256), 0, st, S0, slots, nseg);
   }
-  hipLaunchKernelGGL(lplain_chunk_kernel<REV>, dim3(B * H * nseg), dim3(PL_NT), sizeof(PlainLds), st, A, Bm, C, S0,
-                     slots, S_final, Y, N, H, seg, nseg);
+  hipLaunchKernelGGL((lplain_chunk_kernel<REV, TRANS, GATE>), dim3(B * H * nseg), dim3(PL_NT), sizeof(PlainLds), st, A,
+                     Bm, C, S0, slots, S_final, Y, gate, dout, N, H, seg, nseg);
   return hipGetLastError();
 }
 
@@ -532,7 +544,7 @@ hipError_t launch_linear_backward(const sala_linear_desc& d, const void* q, cons
     if (dstate_in)
       hipLaunchKernelGGL(lbwd_copy_kernel, dim3((unsigned)std::min<long>((n + 255) / 256, 4096)), dim3(256), 0,
                          st, dstate_out, dstate_in, n);
-    if (dqw || dkw) hipLaunchKernelGGL(lbwd_wsum_kernel, dim3(1), dim3(256), 0, st, nullptr, 0, dqw, dkw);
+    if (dqw || dkw) hipLaunchKernelGGL(lbwd_wsum_kernel, dim3(2 * D), dim3(256), 0, st, nullptr, 0, dqw, dkw);
     return hipGetLastError();
   }
   const BwdPlan p = bwd_plan(d);
@@ -540,10 +552,7 @@ hipError_t launch_linear_backward(const sala_linear_desc& d, const void* q, cons
   bf16_t* qh = reinterpret_cast<bf16_t*>(w + p.off_qh);
   bf16_t* kh = reinterpret_cast<bf16_t*>(w + p.off_kh);
   bf16_t* dO = reinterpret_cast<bf16_t*>(w + p.off_do);
-  float* o = reinterpret_cast<float*>(w + p.off_o);
   float* slots = reinterpret_cast<float*>(w + p.off_slots);
-  float* t_in = reinterpret_cast<float*>(w + p.off_tin);
-  float* t_out = reinterpret_cast<float*>(w + p.off_tout);
   float* wpart = reinterpret_cast<float*>(w + p.off_wpart);
   const long nrows = (long)B * N * H;
   const RopeFreqs fr = make_rope_freqs(D, d.rope_base);
@@ -552,22 +561,24 @@ hipError_t launch_linear_backward(const sala_linear_desc& d, const void* q, cons
 
   hipLaunchKernelGGL(lbwd_prep_kernel, dim3(p.ew_blocks), dim3(EW_NT), 0, st, qb, kb, gb, db, qw, kw, qh, kh, dO, nrows,
                      N, H, (long)d.pos0, d.norm_eps, fr);
-  if (state_in) hipLaunchKernelGGL(lbwd_transpose_kernel, dim3(B * H), dim3(256), 0, st, state_in, t_in);
-  if (dstate_out) hipLaunchKernelGGL(lbwd_transpose_kernel, dim3(B * H), dim3(256), 0, st, dstate_out, t_out);
   hipError_t e;
-  // o (for dg), dq~, dk~, dv and dS_in
-  if ((e = run_plain<false>(qh, kh, vb, state_in, nullptr, o, slots, B, N, H, p.seg, p.nseg, st)) != hipSuccess) return e;
-  if ((e = run_plain<false>(dO, vb, kh, state_in ? t_in : nullptr, nullptr, dq, slots, B, N, H, p.seg, p.nseg, st)) !=
-      hipSuccess)
+  // dg (from o), dq~ (state = the o pass's, transposed), dv and dS_in, dk~ (state = the dv
+  // pass's, transposed)
+  if ((e = run_plain<false, false, true>(qh, kh, vb, state_in, nullptr, dg, gb, db, slots, true, B, N, H, p.seg,
+                                         p.nseg, st)) != hipSuccess)
     return e;
-  if ((e = run_plain<true>(vb, dO, qh, dstate_out ? t_out : nullptr, nullptr, dk, slots, B, N, H, p.seg, p.nseg, st)) !=
-      hipSuccess)
+  if ((e = run_plain<false, true, false>(dO, vb, kh, state_in, nullptr, dq, nullptr, nullptr, slots, false, B, N, H,
+                                         p.seg, p.nseg, st)) != hipSuccess)
     return e;
-  if ((e = run_plain<true>(kh, qh, dO, dstate_out, dstate_in, dv, slots, B, N, H, p.seg, p.nseg, st)) != hipSuccess)
+  if ((e = run_plain<true, false, false>(kh, qh, dO, dstate_out, dstate_in, dv, nullptr, nullptr, slots, true, B, N,
+                                         H, p.seg, p.nseg, st)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(lbwd_post_kernel, dim3(p.ew_blocks), dim3(EW_NT), 0, st, qb, kb, gb, db, qw, kw, o, dq, dk, dg,
-                     wpart, nrows, N, H, (long)d.pos0, d.norm_eps, fr);
-  if (dqw || dkw) hipLaunchKernelGGL(lbwd_wsum_kernel, dim3(1), dim3(256), 0, st, wpart, p.ew_blocks, dqw, dkw);
+  if ((e = run_plain<true, true, false>(vb, dO, qh, dstate_out, nullptr, dk, nullptr, nullptr, slots, false, B, N, H,
+                                        p.seg, p.nseg, st)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(lbwd_post_kernel, dim3(p.ew_blocks), dim3(EW_NT), 0, st, qb, kb, qw, kw, dq, dk, wpart, nrows, N,
+                     H, (long)d.pos0, d.norm_eps, fr);
+  if (dqw || dkw) hipLaunchKernelGGL(lbwd_wsum_kernel, dim3(2 * D), dim3(256), 0, st, wpart, p.ew_blocks, dqw, dkw);
   return hipGetLastError();
 }
 
