@@ -48,6 +48,24 @@ __device__ __forceinline__ bf16x8 ktr_frag(const bf16_t* T, int kb, int dt, int 
   return as_bf16x8(a, b);
 }
 
+// Layout of tiles read both by rows and transposed: 16-byte chunk c of row r sits at chunk
+// c ^ swt_of(r), swt_of(r) = 2(r & 7) + ((r >> 3) & 1). Over 16 aligned rows swt_of is a
+// permutation of 0..15 (a row read of 16 rows x 16 bytes touches 16 distinct chunk columns), and
+// over 8 aligned rows its upper three bits are distinct (a transposing read of 8 rows x 32 bytes
+// touches 8 distinct 32-byte column pairs): both kinds of read are free of bank conflicts.
+__device__ __forceinline__ int swt_of(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int swt(int row, int chunk) { return row * D + 8 * (chunk ^ swt_of(row)); }
+
+// as ktr_frag, for a tile in the swt layout
+__device__ __forceinline__ bf16x8 ktr_frag_t(const bf16_t* T, int kb, int dt, int l16, int lq) {
+  const int row0 = kb + 4 * lq + (l16 >> 2);
+  const int col = 16 * dt + 4 * (l16 & 3);
+  const int ch = col >> 3, sub = col & 7;
+  const uint2 a = ds_read_tr(T + swt(row0, ch) + sub);
+  const uint2 b = ds_read_tr(T + swt(row0 + 16, ch) + sub);
+  return as_bf16x8(a, b);
+}
+
 struct ItemGeom {
   int hq, r, gk, b, hl, h;
   bool head_ok;
@@ -441,27 +459,29 @@ sbwd_slices_kernel(const uint32_t* __restrict__ bm, int* __restrict__ soff, int 
   if (threadIdx.x == 0) soff[bg * (nkb + 1) + nkb] = carry;
 }
 
-// ---- 4. dK, dV per slice. LDS: K and V of the key block, and a double buffer of the
-// (q~, dO, stats) tiles of one (query block, head) step.
+// ---- 4. dK, dV per slice: workgroups of four waves, two per CU, so that one workgroup's
+// gathers and barriers overlap the other's products. Wave w owns key tile w (16 keys) for all
+// 64 queries of a step: its K and V fragments stay in registers and it accumulates dK^T, dV^T
+// of its keys over every step. LDS holds a double buffer of the (q~, dO, stats) tiles of one
+// (query block, head) step.
+constexpr int SB_KV_NT = 256;
 struct DkvLds {
-  bf16_t kt[TILE];
-  bf16_t vt[TILE];
-  bf16_t qd[2][2][TILE];     // [buffer][q~, dO]
-  float st[2][64 * 4];       // [buffer][row][lse2, D, -, -]
+  bf16_t qd[2][2][TILE];  // [buffer][q~, dO]
+  float st[2][64 * 4];    // [buffer][row][lse2, D, -, -]
   int list[SB_SL];
   int n;
 };
 
-// copies of one step: q~ and dO tiles (16 pieces of 1 KB each, wave w moves 2w, 2w+1 of both)
-// and, by wave 0, the 1 KB stats rows
+// copies of one step: q~ and dO tiles in the swt layout (16 pieces of 1 KB each, wave w moves
+// 4w .. 4w+3 of both) and, by wave 0, the 1 KB stats rows
 __device__ __forceinline__ void dma_step(const bf16_t* qtb, const bf16_t* dob, const float* stb, long pad0,
                                          DkvLds& L, int bufi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int I = 2 * wave + m;
+  for (int m = 0; m < 4; ++m) {
+    const int I = 4 * wave + m;
     const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
+    const int ch = (lane & 15) ^ swt_of(row);
     const long off = (pad0 + row) * D + 8 * ch;
     dma16(qtb + off, lds_addr_u32(L.qd[bufi][0] + I * 512));
     dma16(dob + off, lds_addr_u32(L.qd[bufi][1] + I * 512));
@@ -469,7 +489,7 @@ __device__ __forceinline__ void dma_step(const bf16_t* qtb, const bf16_t* dob, c
   if (wave == 0) dma16(stb + pad0 * 4 + 4 * lane, lds_addr_u32(L.st[bufi]));
 }
 
-__global__ void __launch_bounds__(SB_NT)
+__global__ void __launch_bounds__(SB_KV_NT, 2)
 sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, const bf16_t* __restrict__ qtb,
                 const bf16_t* __restrict__ dob, const float* __restrict__ stb, const uint32_t* __restrict__ bm,
                 const int* __restrict__ soff, float* __restrict__ part, int Hq, int Hkv, long qb0, int nqb,
@@ -502,18 +522,6 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
     }
     L.n = n;
   }
-  // K, V of the key block: plain swz layout for both (wave w: pieces 2w, 2w+1 of each)
-  const long row_base = (long)bg * cap;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int I = 2 * wave + m;
-    const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
-    long p = (long)kb * 64 + row;
-    if (p >= kv_len) p = kv_len - 1;
-    dma16(kc + (row_base + p) * D + 8 * ch, lds_addr_u32(L.kt + I * 512));
-    dma16(vc + (row_base + p) * D + 8 * ch, lds_addr_u32(L.vt + I * 512));
-  }
   __syncthreads();  // the list
   const int nl = L.n, nsteps = nl * G;
   auto pad_of = [&](int st) -> long {
@@ -522,84 +530,97 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
   };
   if (nsteps > 0) dma_step(qtb, dob, stb, pad_of(0), L, 0);
 
-  const int kt = wave & 3, qh = wave >> 2;  // key tile, query half
+  const int kt = wave;  // key tile
+  // this wave's K and V fragments (B operand: key 16kt + l16, dims 32ks + 8lq .. +7); rows past
+  // kv_len repeat the last row (only the diagonal block reaches them, where they are masked)
+  bf16x8 kf[4], vf[4];
+  {
+    long p = (long)kb * 64 + 16 * kt + l16;
+    if (p >= kv_len) p = kv_len - 1;
+    const long off = ((long)bg * cap + p) * D + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kc + off + 32 * ks));
+      vf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(vc + off + 32 * ks));
+    }
+  }
+
   f32x4 dKT[8], dVT[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) dKT[dt] = dVT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int st = 0; st < nsteps; ++st) {
     const int bi = st & 1;
-    wait_vmcnt<0>();  // this step's copies (and, first time, K and V) have landed
+    wait_vmcnt<0>();  // this step's copies have landed
     __syncthreads();  // visible to all; every wave is done with the other buffer
     if (st + 1 < nsteps) dma_step(qtb, dob, stb, pad_of(st + 1), L, bi ^ 1);
     const bf16_t* Qs = L.qd[bi][0];
     const bf16_t* Ds = L.qd[bi][1];
     const float* S4 = L.st[bi];
     const bool diag = qb0 + L.list[st / G] == kb;
-    f32x4 S[2], P[2];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int qr = 32 * qh + 16 * qt;  // C layout: query qr + 4lq + e, key 16kt + l16
-      f32x4 mi;
+    for (int qh = 0; qh < 2; ++qh) {  // query half: rows 32qh .. 32qh + 31
+      // every LDS operand of the scores and dP products is read ahead of them
+      float2 ld[8];  // (lse2, D) of query row 32qh + 16qt + 4lq + e
+      bf16x8 qa[2][4], da[2][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mi[e] = -S4[(qr + 4 * lq + e) * 4];
-      S[qt] = mi;
-      P[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Qs + swz(qr + l16, 4 * ks + lq)));
-        const bf16x8 kb8 = as_bf16x8(*reinterpret_cast<const uint4*>(L.kt + swz(16 * kt + l16, 4 * ks + lq)));
-        S[qt] = mfma16x16x32(a, kb8, S[qt]);
-        const bf16x8 d8 = as_bf16x8(*reinterpret_cast<const uint4*>(Ds + swz(qr + l16, 4 * ks + lq)));
-        const bf16x8 v8 = as_bf16x8(*reinterpret_cast<const uint4*>(L.vt + swz(16 * kt + l16, 4 * ks + lq)));
-        P[qt] = mfma16x16x32(d8, v8, P[qt]);  // dP
+        for (int e = 0; e < 4; ++e)
+          ld[4 * qt + e] = *reinterpret_cast<const float2*>(S4 + (32 * qh + 16 * qt + 4 * lq + e) * 4);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          qa[qt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(Qs + swt(32 * qh + 16 * qt + l16, 4 * ks + lq)));
+          da[qt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(Ds + swt(32 * qh + 16 * qt + l16, 4 * ks + lq)));
+        }
+      // C layout: query 32qh + 16qt + 4lq + e, key 16kt + l16; S starts at -lse2
+      f32x4 S[2], P[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        S[qt] = f32x4{-ld[4 * qt].x, -ld[4 * qt + 1].x, -ld[4 * qt + 2].x, -ld[4 * qt + 3].x};
+        P[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    float pv[8], dsv[8];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int qrow = 32 * qh + 16 * qt + 4 * lq + e, key = 16 * kt + l16;
-        float s2 = S[qt][e];
-        if (diag && key > qrow) s2 = -INFINITY;  // key after query
-        const float p = fast_exp2(s2);
-        pv[4 * qt + e] = p;
-        dsv[4 * qt + e] = p * (P[qt][e] - S4[qrow * 4 + 1]);
-      }
-    const bf16x8 pf = as_bf16x8(pack8(pv)), sf = as_bf16x8(pack8(dsv));
+        for (int qt = 0; qt < 2; ++qt) {
+          S[qt] = mfma16x16x32(qa[qt][ks], kf[ks], S[qt]);
+          P[qt] = mfma16x16x32(da[qt][ks], vf[ks], P[qt]);  // dP
+        }
+      bf16x8 tv[8];  // dO^T fragments of this half, read while the products run
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      dVT[dt] = mfma16x16x32(ktr_frag(Ds, 32 * qh, dt, l16, lq), pf, dVT[dt]);
-      dKT[dt] = mfma16x16x32(ktr_frag(Qs, 32 * qh, dt, l16, lq), sf, dKT[dt]);
+      for (int dt = 0; dt < 8; ++dt) tv[dt] = ktr_frag_t(Ds, 32 * qh, dt, l16, lq);
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int qrow = 32 * qh + 16 * qt + 4 * lq + e, key = 16 * kt + l16;
+          float s2 = S[qt][e];
+          if (diag && key > qrow) s2 = -INFINITY;  // key after query
+          const float p = fast_exp2(s2);
+          pv[4 * qt + e] = p;
+          dsv[4 * qt + e] = p * (P[qt][e] - ld[4 * qt + e].y);
+        }
+      const bf16x8 pf = as_bf16x8(pack8(pv)), sf = as_bf16x8(pack8(dsv));
+      bf16x8 tk[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) tk[dt] = ktr_frag_t(Qs, 32 * qh, dt, l16, lq);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) dVT[dt] = mfma16x16x32(tv[dt], pf, dVT[dt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) dKT[dt] = mfma16x16x32(tk[dt], sf, dKT[dt]);
     }
   }
-  // the two query halves of each key tile meet in LDS (the step buffers are free after the
-  // barrier); dK carries 1 / log2(e) since q~ holds scale * log2(e) * q^
-  __syncthreads();
-  float* xch = reinterpret_cast<float*>(L.qd);  // [kt][dt][lane][2][4] floats = 64 KB
-  if (qh == 1) {
+  // dK carries 1 / log2(e) since q~ holds scale * log2(e) * q^. C layout: dk / dv dim
+  // 16dt + 4lq + e, key 16kt + l16
+  float* dst = part + ((long)bg * maxsl + s) * 2 * 64 * D + (long)(16 * kt + l16) * D + 4 * lq;
+  const float ln2 = 0.69314718055994531f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      *reinterpret_cast<f32x4*>(xch + (((kt * 8 + dt) * 64 + lane) * 2 + 0) * 4) = dKT[dt];
-      *reinterpret_cast<f32x4*>(xch + (((kt * 8 + dt) * 64 + lane) * 2 + 1) * 4) = dVT[dt];
-    }
-  }
-  __syncthreads();
-  if (qh == 0) {
-    float* dst = part + ((long)bg * maxsl + s) * 2 * 64 * D;
-    const float ln2 = 0.69314718055994531f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const f32x4 ok = *reinterpret_cast<const f32x4*>(xch + (((kt * 8 + dt) * 64 + lane) * 2 + 0) * 4);
-      const f32x4 ov = *reinterpret_cast<const f32x4*>(xch + (((kt * 8 + dt) * 64 + lane) * 2 + 1) * 4);
-      // C layout: dv / dk = 16dt + 4lq + e, key = 16kt + l16
-      const int key = 16 * kt + l16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[(long)key * D + 16 * dt + 4 * lq + e] = (dKT[dt][e] + ok[e]) * ln2;
-        dst[64L * D + (long)key * D + 16 * dt + 4 * lq + e] = dVT[dt][e] + ov[e];
-      }
-    }
+  for (int dt = 0; dt < 8; ++dt) {
+    *reinterpret_cast<f32x4*>(dst + 16 * dt) = dKT[dt] * ln2;
+    *reinterpret_cast<f32x4*>(dst + 64L * D + 16 * dt) = dVT[dt];
   }
 }
 
@@ -776,7 +797,7 @@ hipError_t launch_sparse_attn_backward(const sala_sparse_desc& d, const void* q,
                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                                         (int)sizeof(DkvLds));
   if (attr_ok != hipSuccess) return attr_ok;
-  hipLaunchKernelGGL(sbwd_dkv_kernel, dim3((unsigned)(BG * p.maxsl)), dim3(SB_NT), sizeof(DkvLds), st, kb, vb, qtb,
+  hipLaunchKernelGGL(sbwd_dkv_kernel, dim3((unsigned)(BG * p.maxsl)), dim3(SB_KV_NT), sizeof(DkvLds), st, kb, vb, qtb,
                      dob, stb, bm, soff, part, d.n_heads, d.n_kv_heads, (long)gm.qb0, (int)p.nqb, (long)d.kv_len,
                      (long)d.kv_capacity, (int)p.nkb, (int)p.words, (int)p.maxsl);
   hipLaunchKernelGGL(sbwd_reduce_kernel, dim3((unsigned)(BG * (d.kv_capacity / 64))), dim3(256), 0, st, part, soff,
