@@ -385,7 +385,30 @@ def extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d):
     fl = sparse_prefill_flops(N, H, d, Ws.topk)
     res["sparse_128k"] = {"ms": ms, "tokens_per_s": N / (ms * 1e-3), "attention_ms": ms_att,
                           "attention_mfma_frac": fl / (ms_att * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-    del q, g, k, v, kc, vc, so
+    # backward of the sparse layer's attention for the same selection and a synthetic upstream
+    # gradient. Algorithmic flops: five products per attended (query, head, key) — S, dP, dV,
+    # dK, dQ — 2.5x the forward's; the kernels execute nine (S is recomputed twice).
+    dout = device_normal(Ws.seed, 10, (1, N, H, d))
+    wsb = torch.empty(S.workspace_bytes(S.OP_SPARSE_ATTN_BACKWARD, sd), dtype=torch.uint8, device="cuda")
+    ms_b = _time_events(torch, lambda: S.sparse_attn_backward(q, kc, vc, g, sel, N, dout, topk=Ws.topk,
+                                                               n_local=Ws.n_local, workspace=wsb), 3)
+    res["sparse_backward_128k"] = {"ms": ms_b, "tokens_per_s": N / (ms_b * 1e-3),
+                                   "mfma_frac": 2.5 * fl / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del q, g, k, v, kc, vc, so, dout, wsb
+    # backward of the linear layer (32 heads, d 128) at 32,768 and 262,144 tokens; HBM bytes
+    # per (token, head): q, k, v, g, dout read in bf16 and dq, dk, dv, dg written in fp32
+    for name, key in (("linear_backward_32k", "linear_32k"), ("linear_backward_256k", "stack_256k")):
+        Wb = WORKLOADS[key]
+        Nb = Wb.seq_len
+        tb = [device_normal(Wb.seed, tid, (1, Nb, H, d)) for tid in (0, 1, 2, 3, 10)]
+        lb = S.linear_desc(tb[0], 0, W.rope_base, W.norm_eps)
+        wsl = torch.empty(S.workspace_bytes(S.OP_LINEAR_BACKWARD, lb), dtype=torch.uint8, device="cuda")
+        ms_l = _time_events(torch, lambda: S.linear_backward(*tb, rope_base=W.rope_base, eps=W.norm_eps,
+                                                             need_norm_w_grads=True, workspace=wsl), 3)
+        byts = Nb * H * d * (5 * 2 + 4 * 4)
+        res[name] = {"ms": ms_l, "tokens_per_s": Nb / (ms_l * 1e-3),
+                     "hbm_frac": byts / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del tb, wsl
     # decode step: individual launches (above) vs one graph replay; linear states restored after
     saved = [Dr["state"].clone() for Dr in dl]
     graph = torch.cuda.CUDAGraph()
