@@ -23,7 +23,9 @@ Sources (the pages this follows; cited by title and section):
   block-selection mechanism lets each query process only a small set of key/value pairs in
   the InfLLM-V2 sparse layers; HyPE: RoPE kept in the linear layers, no positional encoding
   in the sparse layers so the KV cache carries no position information).
-* [SALA-blog] "MiniCPM-SALA：混合注意力机制突破LLM长文本处理瓶颈", §2.2 混合位置编码（HyPE）.
+* [SALA-blog] "MiniCPM-SALA：混合注意力机制突破LLM长文本处理瓶颈", §2.2 混合位置编码（HyPE）, and
+  §5.1 部署建议 (batch size chosen against context length: the packed variable-length batches
+  of the *_varlen functions).
 
 Where the pages are silent the reading taken is stated at the function (the pages give no
 formula at all): no decay, no normaliser and no scale in the linear layer; an inclusive causal
@@ -60,6 +62,8 @@ __all__ = [
     "dense_attention",
     "sparse_prefill",
     "sparse_decode",
+    "linear_prefill_varlen",
+    "sparse_prefill_varlen",
 ]
 
 
@@ -392,3 +396,69 @@ def sparse_decode(q, k_new, v_new, g, k_cache_hat, v_cache, kv_len, *, block=64,
                 w = np.exp(s)
                 out[b, h] = (w / w.sum()) @ Vs
     return dict(out=out * sigmoid(g), sel=sel)
+
+
+# ---------------------------------------------------------------- packed variable-length batches
+
+
+def _cu(seqlens):
+    cu = np.zeros(len(seqlens) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(seqlens)
+    return cu
+
+
+def linear_prefill_varlen(q, k, v, g, seqlens, pos0=None, *, rope_base=10000.0, eps=1e-6, state_in=None,
+                          q_norm_w=None, k_norm_w=None):
+    """A packed batch of independent sequences through the linear layer ([SALA-blog] §5.1: the
+    batch is sized to the context, so one batch holds prompts of different lengths).
+
+    q, k, v, g [T, H, d] hold the sequences back to back (sequence s owns rows
+    cu[s] .. cu[s+1] - 1, cu = prefix sums of seqlens); pos0[s] is the position of its first
+    token; state_in [nseq, H, d, d] or None. Each sequence is ``linear_prefill`` on its own
+    rows with its own state: no state or position crosses sequences.
+    Returns (out [T, H, d], states [nseq, H, d, d]).
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    T, H, d = q.shape
+    Hkv = k.shape[1]
+    cu = _cu(seqlens)
+    assert cu[-1] == T
+    pos0 = [0] * len(seqlens) if pos0 is None else list(pos0)
+    out = np.empty((T, H, d))
+    states = np.empty((len(seqlens), Hkv, d, d))
+    for s in range(len(seqlens)):
+        a, b = cu[s], cu[s + 1]
+        o, S = linear_prefill(q[None, a:b], k[None, a:b], v[None, a:b], g[None, a:b], pos0=pos0[s],
+                              rope_base=rope_base, eps=eps,
+                              state_in=None if state_in is None else _f64(state_in)[s:s + 1],
+                              q_norm_w=q_norm_w, k_norm_w=k_norm_w)
+        out[a:b] = o[0]
+        states[s] = S[0]
+    return out, states
+
+
+def sparse_prefill_varlen(q, k, v, g, seqlens, *, block=64, topk=64, n_local=2, eps=1e-6, scale=None,
+                          q_norm_w=None, k_norm_w=None):
+    """A packed batch of prompts through the sparse layer, each prompt from position 0 with
+    its own KV cache, pooled keys and selection. q, g [T, Hq, d]; k, v [T, Hkv, d], sequences
+    back to back as in ``linear_prefill_varlen``. Each sequence is ``sparse_prefill`` on its own
+    rows. Returns dict(out [T, Hq, d], sel: list of [Hkv, nqb_s, topk] per sequence).
+    (The queries of a prompt continued after a cached prefix give the outputs of the whole
+    prompt's last tokens, as when one prompt is prefilled in consecutive calls.)
+    """
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(g)
+    T, Hq, d = q.shape
+    cu = _cu(seqlens)
+    assert cu[-1] == T
+    out = np.empty((T, Hq, d))
+    sels = []
+    for s in range(len(seqlens)):
+        a, b = cu[s], cu[s + 1]
+        if b == a:
+            sels.append(np.zeros((k.shape[1], 0, topk), dtype=np.int64))
+            continue
+        r = sparse_prefill(q[None, a:b], k[None, a:b], v[None, a:b], g[None, a:b], block=block, topk=topk,
+                           n_local=n_local, eps=eps, scale=scale, q_norm_w=q_norm_w, k_norm_w=k_norm_w)
+        out[a:b] = r["out"][0]
+        sels.append(r["sel"][0])
+    return dict(out=out, sel=sels)
