@@ -56,6 +56,43 @@ sala_status check_sparse(const sala_sparse_desc* d, bool with_sel = true) {
   return SALA_OK;
 }
 
+// a packed batch: nseq = desc batch sequences, cu_seqlens[0] = 0, nondecreasing, ending at the
+// packed token count; positions >= 0 (and multiples of 64 with the cache row within capacity
+// for the sparse layer)
+sala_status check_varlen(int nseq, int64_t total, const int32_t* cu, const int64_t* pos0, int64_t cap) {
+  if (!cu || !pos0) return SALA_ERR_NULL;
+  if (nseq < 1) return SALA_ERR_INVALID;
+  if (nseq > SALA_VARLEN_MAX_SEQS) return SALA_ERR_UNSUPPORTED;
+  if (cu[0] != 0 || cu[nseq] != total) return SALA_ERR_INVALID;
+  for (int s = 0; s < nseq; ++s) {
+    if (cu[s + 1] < cu[s] || pos0[s] < 0) return SALA_ERR_INVALID;
+    if (cap >= 0 && (pos0[s] % 64 != 0 || pos0[s] + (cu[s + 1] - cu[s]) > cap)) return SALA_ERR_INVALID;
+  }
+  return SALA_OK;
+}
+
+// the sparse shape fields of a packed batch: as check_sparse, with n_q = packed token count and
+// kv_len unused (each sequence's cache holds pos0 + its token count)
+sala_status check_sparse_varlen(const sala_sparse_desc* d, const int32_t* cu, const int64_t* pos0) {
+  if (!d) return SALA_ERR_NULL;
+  sala_sparse_desc x = *d;
+  x.batch = 1;
+  x.n_q = 1;
+  x.kv_len = 1;
+  const sala_status s = check_sparse(&x);
+  if (s != SALA_OK) return s;
+  if (d->n_q < 0) return SALA_ERR_INVALID;
+  if (d->dtype != SALA_BF16 || d->head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  return check_varlen(d->batch, d->n_q, cu, pos0, d->kv_capacity);
+}
+
+sala_status check_linear_varlen(const sala_linear_desc* d, const int32_t* cu, const int64_t* pos0) {
+  const sala_status s = check_linear(d);
+  if (s != SALA_OK) return s;
+  if (d->dtype != SALA_BF16 || d->head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  return check_varlen(d->batch, d->seq_len, cu, pos0, -1);
+}
+
 bool all_aligned(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if (p && !aligned16(p)) return false;
@@ -183,6 +220,83 @@ sala_status sala_kv_append(const sala_sparse_desc* desc, const void* k_new, cons
   if (!all_aligned({k_new, v_new, k_norm_w, k_cache, v_cache, k_pool})) return SALA_ERR_INVALID;
   return hip_status(sala::launch_kv_append(*desc, k_new, v_new, k_norm_w, k_cache, v_cache, k_pool,
                                            (hipStream_t)stream));
+}
+
+sala_status sala_linear_prefill_varlen(const sala_linear_desc* desc, const int32_t* cu_seqlens,
+                                       const int64_t* pos0, const void* q, const void* k, const void* v,
+                                       const void* gate, const float* q_norm_w, const float* k_norm_w,
+                                       const float* state_in, float* state_out, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const sala_status s = check_linear_varlen(desc, cu_seqlens, pos0);
+  if (s != SALA_OK) return s;
+  const sala_linear_desc& d = *desc;
+  if (d.seq_len > 0 && (!q || !k || !v || !gate || !out)) return SALA_ERR_NULL;
+  if (!all_aligned({q, k, v, gate, out, q_norm_w, k_norm_w, state_in, state_out, workspace})) return SALA_ERR_INVALID;
+  const size_t need = sala::linear_prefill_varlen_workspace(d, cu_seqlens);
+  if (d.seq_len > 0 && need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_linear_prefill_varlen(d, cu_seqlens, pos0, q, k, v, gate, q_norm_w, k_norm_w,
+                                                       state_in, state_out, out, workspace, (hipStream_t)stream));
+}
+
+sala_status sala_kv_append_varlen(const sala_sparse_desc* desc, const int32_t* cu_seqlens, const int64_t* pos0,
+                                  const void* k_new, const void* v_new, const float* k_norm_w, void* k_cache,
+                                  void* v_cache, float* k_pool, void* stream) {
+  const sala_status s = check_sparse_varlen(desc, cu_seqlens, pos0);
+  if (s != SALA_OK) return s;
+  if (!k_cache || !v_cache || !k_pool || (desc->n_q > 0 && (!k_new || !v_new))) return SALA_ERR_NULL;
+  if (!all_aligned({k_new, v_new, k_norm_w, k_cache, v_cache, k_pool})) return SALA_ERR_INVALID;
+  return hip_status(sala::launch_kv_append_varlen(*desc, cu_seqlens, pos0, k_new, v_new, k_norm_w, k_cache, v_cache,
+                                                  k_pool, (hipStream_t)stream));
+}
+
+sala_status sala_block_select_varlen(const sala_sparse_desc* desc, const int32_t* cu_seqlens, const int64_t* pos0,
+                                     const void* q, const float* q_norm_w, const float* k_pool, int32_t* sel,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  const sala_status s = check_sparse_varlen(desc, cu_seqlens, pos0);
+  if (s != SALA_OK) return s;
+  if (!k_pool || (desc->n_q > 0 && (!q || !sel))) return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_pool, sel, workspace})) return SALA_ERR_INVALID;
+  const size_t need = sala::block_select_varlen_workspace(*desc, cu_seqlens, pos0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
+  return hip_status(sala::launch_block_select_varlen(*desc, cu_seqlens, pos0, q, q_norm_w, k_pool, sel, workspace,
+                                                     (hipStream_t)stream));
+}
+
+sala_status sala_sparse_attn_varlen(const sala_sparse_desc* desc, const int32_t* cu_seqlens, const int64_t* pos0,
+                                    const void* q, const float* q_norm_w, const void* k_cache, const void* v_cache,
+                                    const void* gate, const int32_t* sel, void* out, void* stream) {
+  const sala_status s = check_sparse_varlen(desc, cu_seqlens, pos0);
+  if (s != SALA_OK) return s;
+  if (!k_cache || !v_cache || (desc->n_q > 0 && (!q || !gate || !sel || !out))) return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, sel, out})) return SALA_ERR_INVALID;
+  return hip_status(sala::launch_sparse_attn_varlen(*desc, cu_seqlens, pos0, q, q_norm_w, k_cache, v_cache, gate, sel,
+                                                    out, (hipStream_t)stream));
+}
+
+int64_t sala_varlen_query_blocks(int32_t nseq, const int32_t* cu_seqlens) {
+  if (!cu_seqlens || nseq < 1 || nseq > SALA_VARLEN_MAX_SEQS) return -1;
+  return sala::varlen_query_blocks(nseq, cu_seqlens);
+}
+
+size_t sala_varlen_workspace_bytes(int op, const void* desc, const int32_t* cu_seqlens, const int64_t* pos0) {
+  switch (op) {
+    case SALA_OP_LINEAR_PREFILL: {
+      const sala_linear_desc* d = static_cast<const sala_linear_desc*>(desc);
+      if (check_linear_varlen(d, cu_seqlens, pos0) != SALA_OK) return SIZE_MAX;
+      return sala::linear_prefill_varlen_workspace(*d, cu_seqlens);
+    }
+    case SALA_OP_BLOCK_SELECT: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse_varlen(d, cu_seqlens, pos0) != SALA_OK) return SIZE_MAX;
+      return sala::block_select_varlen_workspace(*d, cu_seqlens, pos0);
+    }
+    case SALA_OP_SPARSE_ATTN: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse_varlen(d, cu_seqlens, pos0) != SALA_OK) return SIZE_MAX;
+      return 0;
+    }
+    default: return SIZE_MAX;
+  }
 }
 
 sala_status sala_kv_pool(const sala_sparse_desc* desc, const void* k_cache, float* k_pool,

@@ -48,6 +48,11 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
                                  const void* v, const void* g, const float* qw, const float* kw,
                                  const float* state_in, float* state_out, void* out, void* ws,
                                  hipStream_t st);
+size_t linear_prefill_varlen_workspace(const sala_linear_desc& d, const int32_t* cu_seqlens);
+hipError_t launch_linear_prefill_varlen(const sala_linear_desc& d, const int32_t* cu_seqlens, const int64_t* pos0,
+                                        const void* q, const void* k, const void* v, const void* g,
+                                        const float* qw, const float* kw, const float* state_in,
+                                        float* state_out, void* out, void* ws, hipStream_t st);
 hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const void* k,
                                 const void* v, const void* g, const float* qw, const float* kw,
                                 float* state, void* out, hipStream_t st);
@@ -76,6 +81,18 @@ size_t block_select_workspace(const sala_sparse_desc& d);
 hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
                                const float* k_pool, int32_t* sel, void* ws, hipStream_t st);
 size_t sparse_attn_workspace(const sala_sparse_desc& d);
+// packed variable-length batches (desc.batch = sequences, cu_seqlens / pos0 on the host)
+int64_t varlen_query_blocks(int nseq, const int32_t* cu_seqlens);
+size_t block_select_varlen_workspace(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0);
+hipError_t launch_kv_append_varlen(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0,
+                                   const void* k_new, const void* v_new, const float* kw, void* k_cache,
+                                   void* v_cache, float* k_pool, hipStream_t st);
+hipError_t launch_block_select_varlen(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0,
+                                      const void* q, const float* qw, const float* k_pool, int32_t* sel, void* ws,
+                                      hipStream_t st);
+hipError_t launch_sparse_attn_varlen(const sala_sparse_desc& d, const int32_t* cu_seqlens, const int64_t* pos0,
+                                     const void* q, const float* qw, const void* k_cache, const void* v_cache,
+                                     const void* g, const int32_t* sel, void* out, hipStream_t st);
 hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
                               const void* k_cache, const void* v_cache, const void* g,
                               const int32_t* sel, void* out, void* ws, hipStream_t st);

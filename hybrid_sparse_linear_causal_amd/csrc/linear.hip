@@ -21,12 +21,73 @@
 // entering state from the workspace otherwise lets state_out alias state_in safely.
 #include "common.hpp"
 #include "launch.hpp"
+#include "varlen.hpp"
 
 #include <algorithm>
 
 namespace sala {
 
 namespace {
+
+// ---- work geometry: which (sequence s, head h, segment) a workgroup handles, where the
+// sequence's tokens start in the token dimension, and where its segment slots are. `slot` is
+// the index (in d x d blocks) of the (s, h) run of nseg workspace slots.
+struct LinItem {
+  int s, h, seg, nseg, n;
+  long tok0, pos0, slot;
+};
+// B sequences of N tokens each, all starting at position pos0 (tensors [B, N, H, d])
+struct LinUniform {
+  int N;
+  long pos0;
+  int nseg;
+  // segsum: items exclude each (s, h)'s last segment
+  __device__ __forceinline__ LinItem item(int x, int H, bool segsum) const {
+    const int per = segsum ? nseg - 1 : nseg;
+    LinItem it;
+    it.seg = x % per;
+    const int sh = x / per;
+    it.s = sh / H;
+    it.h = sh % H;
+    it.nseg = nseg;
+    it.n = N;
+    it.tok0 = (long)it.s * N;
+    it.pos0 = pos0;
+    it.slot = (long)sh * nseg;
+    return it;
+  }
+  // scan: (s, h) = x; returns the slot run and its length
+  __device__ __forceinline__ long scan_item(int x, int H, int* nslots) const {
+    *nslots = nseg;
+    return (long)x * nseg;
+  }
+};
+// packed sequences (tensors [T, H, d]): aux0 = prefix of the per-sequence segment counts;
+// item0 = H * aux0 (output pass) or H * (aux0[s] - s) (segment sums)
+struct LinVarlen {
+  VarlenTable t;
+  __device__ __forceinline__ LinItem item(int x, int H, bool segsum) const {
+    const int s = vl_seq(t, x);
+    const int nseg = t.aux0[s + 1] - t.aux0[s];
+    const int per = segsum ? nseg - 1 : nseg;
+    const int r = x - t.item0[s];
+    LinItem it;
+    it.s = s;
+    it.h = r / per;
+    it.seg = r % per;
+    it.nseg = nseg;
+    it.n = t.n[s];
+    it.tok0 = t.tok0[s];
+    it.pos0 = t.pos0[s];
+    it.slot = (long)H * t.aux0[s] + (long)it.h * nseg;
+    return it;
+  }
+  __device__ __forceinline__ long scan_item(int x, int H, int* nslots) const {
+    const int s = x / H, h = x % H;
+    *nslots = t.aux0[s + 1] - t.aux0[s];
+    return (long)H * t.aux0[s] + (long)h * *nslots;
+  }
+};
 
 constexpr int D = 128;   // head dim of the bf16 MFMA path
 constexpr int CH = 64;   // chunk length (tokens)
@@ -122,24 +183,23 @@ __device__ __forceinline__ void dma_kv(const bf16_t* k, const bf16_t* v, long ro
   }
 }
 
-template <bool HAS_W>
+template <bool HAS_W, class Geo>
 __global__ void __launch_bounds__(SS_NT)
 linear_segsum_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                     const float* __restrict__ kw, float* __restrict__ ws, int N, int H, long pos0,
-                     int seg_len, int nseg, float eps, RopeFreqs freqs) {
+                     const float* __restrict__ kw, float* __restrict__ ws, int H, int seg_len, float eps,
+                     RopeFreqs freqs, Geo geo) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   SegLds& L = *reinterpret_cast<SegLds*>(lds_raw);
-  const int nsw = nseg - 1;
-  const int seg = blockIdx.x % nsw;
-  const int bh = blockIdx.x / nsw;
-  const int b = bh / H, h = bh % H;
+  const LinItem it = geo.item(blockIdx.x, H, true);
+  const int seg = it.seg, h = it.h;
+  const long pos0 = it.pos0;
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const int s8 = j & 7, tok = j >> 3;  // prep: one token, segments s8 and s8+8
   const int t_begin = seg * seg_len;
   const int nch = seg_len / CH;
   const long tok_stride = (long)H * D;
-  const long row0 = ((long)b * N * H + h) * D + (long)t_begin * tok_stride;
+  const long row0 = (it.tok0 * H + h) * D + (long)t_begin * tok_stride;
 
 #pragma unroll
   for (int x = 0; x < SS_NS - 1; ++x)
@@ -197,7 +257,7 @@ linear_segsum_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
         S[jt] = mfma16x16x32(af, tr_frag_t(Vt, 32 * ks + 8 * lq, 4, 16 * jt, l16), S[jt]);
     }
   }
-  float* dst = ws + ((long)bh * nseg + seg + 1) * D * D;
+  float* dst = ws + (it.slot + seg + 1) * D * D;
 #pragma unroll
   for (int jt = 0; jt < 8; ++jt)
 #pragma unroll
@@ -235,19 +295,20 @@ __device__ __forceinline__ void dma_chunk(const bf16_t* q, const bf16_t* k, cons
   }
 }
 
-template <bool HAS_W>
+template <bool HAS_W, class Geo>
 __global__ void __launch_bounds__(OUT_NT)
 linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                   const bf16_t* __restrict__ v, const bf16_t* __restrict__ g,
                   const float* __restrict__ qw, const float* __restrict__ kw,
                   const float* __restrict__ state_in, const float* __restrict__ ws,
-                  float* __restrict__ state_out, bf16_t* __restrict__ out, int N, int H, long pos0,
-                  int seg_len, int nseg, float eps, RopeFreqs freqs) {
+                  float* __restrict__ state_out, bf16_t* __restrict__ out, int H, int seg_len, float eps,
+                  RopeFreqs freqs, Geo geo) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   OutLds& L = *reinterpret_cast<OutLds*>(lds_raw);
-  const int seg = blockIdx.x % nseg;
-  const int bh = blockIdx.x / nseg;
-  const int b = bh / H, h = bh % H;
+  const LinItem it = geo.item(blockIdx.x, H, false);
+  const int seg = it.seg, nseg = it.nseg, h = it.h, N = it.n;
+  const long pos0 = it.pos0;
+  const long bh = (long)it.s * H + h;  // state index
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const bool out_wave = wave < 4;
@@ -255,7 +316,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int s8 = j & 7, tok = j >> 3;  // prep: one token, segments s8 and s8+8
   const int t_begin = seg * seg_len;
   const int t_end = min(N, t_begin + seg_len);
-  const long head_off = ((long)b * N * H + h) * D;
+  const long head_off = (it.tok0 * H + h) * D;
   const long tok_stride = (long)H * D;
 
   dma_chunk(q, k, v, g, head_off + (long)t_begin * tok_stride, t_begin, N, H, L.t[0]);
@@ -266,8 +327,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
   for (int x = 0; x < 16; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (!out_wave) {
-    const float* src = (nseg == 1) ? (state_in ? state_in + (long)bh * D * D : nullptr)
-                                   : ws + ((long)bh * nseg + seg) * D * D;
+    const float* src = (nseg == 1) ? (state_in ? state_in + bh * D * D : nullptr) : ws + (it.slot + seg) * D * D;
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
@@ -460,7 +520,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     buf ^= 1;
   }
   if (!out_wave && seg == nseg - 1 && state_out) {
-    float* dst = state_out + (long)bh * D * D;
+    float* dst = state_out + bh * D * D;
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
@@ -483,13 +543,16 @@ copy_or_zero_kernel(const float* __restrict__ src, float* __restrict__ dst, long
 
 // Slot s >= 1 holds segment s-1's own sum on entry; on exit slot s holds the state entering
 // segment s: state_in + sum of the sums of segments 0..s-1. One thread per state element.
+template <class Geo>
 __global__ void __launch_bounds__(256)
-linear_scan_kernel(const float* __restrict__ state_in, float* __restrict__ ws, int nslots, int dd) {
+linear_scan_kernel(const float* __restrict__ state_in, float* __restrict__ ws, int H, int dd, Geo geo) {
   const int bh = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;
-  if (e >= dd) return;
+  int nslots;
+  const long slot = geo.scan_item(bh, H, &nslots);
+  if (e >= dd || nslots <= 1) return;
   float acc = state_in ? state_in[(long)bh * dd + e] : 0.f;
-  float* p = ws + (long)bh * nslots * dd + e;
+  float* p = ws + slot * dd + e;
   p[0] = acc;
   for (int s = 1; s < nslots; ++s) {
     acc += p[(long)s * dd];
@@ -652,6 +715,51 @@ linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
   }
 }
 
+// The bf16 prefill over a geometry: segment sums (when some sequence has several segments),
+// their scan, then the output pass. GS is the segment-sum geometry, GO the output/scan one.
+template <class GS, class GO>
+hipError_t run_linear_bf16(const GS& gs, const GO& go, long n_ss, long n_out, long n_bh, bool scan, int H, int seg,
+                           const void* q, const void* k, const void* v, const void* g, const float* qw,
+                           const float* kw, const float* state_in, float* state_out, void* out, void* ws, float eps,
+                           const RopeFreqs& fr, hipStream_t st) {
+  float* wsf = static_cast<float*>(ws);
+  const bf16_t *qb = (const bf16_t*)q, *kb = (const bf16_t*)k, *vb = (const bf16_t*)v, *gb = (const bf16_t*)g;
+  static const hipError_t attr_ok = [] {
+    const hipError_t e[4] = {
+        hipFuncSetAttribute((const void*)linear_segsum_kernel<false, GS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sizeof(SegLds)),
+        hipFuncSetAttribute((const void*)linear_segsum_kernel<true, GS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sizeof(SegLds)),
+        hipFuncSetAttribute((const void*)linear_out_kernel<false, GO>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sizeof(OutLds)),
+        hipFuncSetAttribute((const void*)linear_out_kernel<true, GO>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sizeof(OutLds))};
+    for (hipError_t x : e)
+      if (x != hipSuccess) return x;
+    return hipSuccess;
+  }();
+  if (attr_ok != hipSuccess) return attr_ok;
+  if (scan) {
+    if (n_ss > 0) {
+      if (kw)
+        hipLaunchKernelGGL((linear_segsum_kernel<true, GS>), dim3((unsigned)n_ss), dim3(SS_NT), sizeof(SegLds), st, kb,
+                           vb, kw, wsf, H, seg, eps, fr, gs);
+      else
+        hipLaunchKernelGGL((linear_segsum_kernel<false, GS>), dim3((unsigned)n_ss), dim3(SS_NT), sizeof(SegLds), st, kb,
+                           vb, kw, wsf, H, seg, eps, fr, gs);
+    }
+    hipLaunchKernelGGL((linear_scan_kernel<GO>), dim3((unsigned)n_bh, D * D / 256), dim3(256), 0, st, state_in, wsf, H,
+                       D * D, go);
+  }
+  if (qw || kw)
+    hipLaunchKernelGGL((linear_out_kernel<true, GO>), dim3((unsigned)n_out), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
+                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, H, seg, eps, fr, go);
+  else
+    hipLaunchKernelGGL((linear_out_kernel<false, GO>), dim3((unsigned)n_out), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
+                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, H, seg, eps, fr, go);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -704,43 +812,57 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
   }
   const int seg = linear_segment_len(d);
   const int nseg = (N + seg - 1) / seg;
-  float* wsf = static_cast<float*>(ws);
-  const bf16_t *qb = (const bf16_t*)q, *kb = (const bf16_t*)k, *vb = (const bf16_t*)v, *gb = (const bf16_t*)g;
-  if (nseg > 1) {
-    static const hipError_t ss_ok = [] {
-      const hipError_t e0 = hipFuncSetAttribute((const void*)linear_segsum_kernel<false>,
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SegLds));
-      const hipError_t e1 = hipFuncSetAttribute((const void*)linear_segsum_kernel<true>,
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(SegLds));
-      return e0 != hipSuccess ? e0 : e1;
-    }();
-    if (ss_ok != hipSuccess) return ss_ok;
-    if (kw)
-      hipLaunchKernelGGL(linear_segsum_kernel<true>, dim3(B * H * (nseg - 1)), dim3(SS_NT), sizeof(SegLds), st,
-                         kb, vb, kw, wsf, N, H, (long)d.pos0, seg, nseg, d.norm_eps, fr);
-    else
-      hipLaunchKernelGGL(linear_segsum_kernel<false>, dim3(B * H * (nseg - 1)), dim3(SS_NT), sizeof(SegLds), st,
-                         kb, vb, kw, wsf, N, H, (long)d.pos0, seg, nseg, d.norm_eps, fr);
-    hipLaunchKernelGGL(linear_scan_kernel, dim3(B * H, D * D / 256), dim3(256), 0, st, state_in,
-                       wsf, nseg, D * D);
+  const LinUniform geo{N, (long)d.pos0, nseg};
+  return run_linear_bf16(geo, geo, (long)B * H * (nseg - 1), (long)B * H * nseg, (long)B * H, nseg > 1, H, seg, q, k,
+                         v, g, qw, kw, state_in, state_out, out, ws, d.norm_eps, fr, st);
+}
+
+// segment length of a packed batch: chosen for its total token count, as for one sequence
+static int varlen_segment_len(const sala_linear_desc& d) {
+  sala_linear_desc one = d;
+  one.batch = 1;
+  return linear_segment_len(one);
+}
+
+size_t linear_prefill_varlen_workspace(const sala_linear_desc& d, const int32_t* cu_seqlens) {
+  const int seg = varlen_segment_len(d);
+  size_t slots = 0;
+  for (int s = 0; s < d.batch; ++s) slots += (cu_seqlens[s + 1] - cu_seqlens[s] + seg - 1) / seg;
+  return (size_t)d.n_heads * slots * d.head_dim * d.head_dim * sizeof(float);
+}
+
+hipError_t launch_linear_prefill_varlen(const sala_linear_desc& d, const int32_t* cu_seqlens, const int64_t* pos0,
+                                        const void* q, const void* k, const void* v, const void* g,
+                                        const float* qw, const float* kw, const float* state_in,
+                                        float* state_out, void* out, void* ws, hipStream_t st) {
+  const int H = d.n_heads, nseq = d.batch;
+  const RopeFreqs fr = make_rope_freqs(d.head_dim, d.rope_base);
+  const int seg = varlen_segment_len(d);
+  LinVarlen ss{make_varlen_table(nseq, cu_seqlens, pos0)};
+  bool any_multi = false;
+  for (int s = 0; s < nseq; ++s) {
+    const int n = ss.t.n[s];
+    const int ns = (n + seg - 1) / seg;
+    ss.t.aux0[s + 1] = ss.t.aux0[s] + ns;
+    any_multi = any_multi || ns > 1;
+    // a sequence without tokens: its state passes through
+    if (n == 0 && state_out && state_out != state_in) {
+      const long off = (long)s * H * D * D;
+      hipLaunchKernelGGL(copy_or_zero_kernel, dim3(64), dim3(256), 0, st, state_in ? state_in + off : nullptr,
+                         state_out + off, (long)H * D * D);
+    }
   }
-  static const hipError_t attr_ok = [] {
-    const hipError_t e0 = hipFuncSetAttribute((const void*)linear_out_kernel<false>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutLds));
-    const hipError_t e1 = hipFuncSetAttribute((const void*)linear_out_kernel<true>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(OutLds));
-    return e0 != hipSuccess ? e0 : e1;
-  }();
-  if (attr_ok != hipSuccess) return attr_ok;
-  if (qw || kw)
-    hipLaunchKernelGGL(linear_out_kernel<true>, dim3(B * H * nseg), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
-                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, N, H, (long)d.pos0, seg,
-                       nseg, d.norm_eps, fr);
-  else
-    hipLaunchKernelGGL(linear_out_kernel<false>, dim3(B * H * nseg), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
-                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, N, H, (long)d.pos0, seg,
-                       nseg, d.norm_eps, fr);
-  return hipGetLastError();
+  LinVarlen ou = ss;
+  for (int s = 0; s <= nseq; ++s) {
+    ou.t.item0[s] = H * ss.t.aux0[s];
+    // segment-sum items: every segment but the last of each sequence with tokens
+    int skip = 0;
+    for (int x = 0; x < s; ++x) skip += ss.t.n[x] > 0;
+    ss.t.item0[s] = H * (ss.t.aux0[s] - skip);
+  }
+  if (ou.t.item0[nseq] == 0) return hipGetLastError();
+  return run_linear_bf16(ss, ou, ss.t.item0[nseq], ou.t.item0[nseq], nseq * H, any_multi, H, seg, q, k, v, g, qw,
+                         kw, state_in, state_out, out, ws, d.norm_eps, fr, st);
 }
 
 hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const void* k,

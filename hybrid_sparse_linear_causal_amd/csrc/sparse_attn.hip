@@ -24,6 +24,7 @@
 // a second kernel that also applies the gate.
 // f32 (any shape, correctness-scale inputs): one thread per query row, keys from LDS.
 #include "common.hpp"
+#include "varlen.hpp"
 #include "launch.hpp"
 #include "sparse_tiles.hpp"
 
@@ -41,16 +42,69 @@ __device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// grid: B*Hkv*nqb*ceil(G/4) workgroups of 512 threads (8 waves: 4 heads x 2 row halves)
+// ---- work geometry of the prefill kernel: which (sequence b, KV group gk, query block r of
+// the call, head quad hq) a workgroup handles, where the call's query tokens of sequence b sit
+// (tok0: packed index of its first one; q0: its position; n_q: their count), the cache length
+// and the row of `sel`.
+struct AttnItem {
+  int b, gk, r, hq, n_q;
+  long q0, tok0, kv_len, sel_row;
+};
+// B sequences with the same n_q queries at positions [q0, q0 + n_q) (tensors [B, n_q, Hq, d])
+struct AttnUniform {
+  int n_q, nqb;
+  long q0, kv_len;
+  __device__ __forceinline__ AttnItem item(unsigned w, int Hkv, int nhq) const {
+    AttnItem it;
+    it.hq = w % nhq;
+    unsigned rest = w / nhq;
+    it.r = rest % nqb;
+    rest /= nqb;
+    it.gk = rest % Hkv;
+    it.b = rest / Hkv;
+    it.n_q = n_q;
+    it.q0 = q0;
+    it.tok0 = (long)it.b * n_q;
+    it.kv_len = kv_len;
+    it.sel_row = ((long)it.b * Hkv + it.gk) * nqb + it.r;
+    return it;
+  }
+};
+// packed sequences (tensors [T, Hq, d]); sequence s has n[s] queries at positions pos0[s] ..,
+// pos0[s] a multiple of 64, and a cache of pos0[s] + n[s] tokens. item0 = prefix of
+// nqb_s * Hkv * nhq; aux0 = prefix of nqb_s (its rows of `sel` are Hkv * aux0[s] ..)
+struct AttnVarlen {
+  VarlenTable t;
+  __device__ __forceinline__ AttnItem item(unsigned w, int Hkv, int nhq) const {
+    const int s = vl_seq(t, (int)w);
+    const int nqb = t.aux0[s + 1] - t.aux0[s];
+    const unsigned x = w - t.item0[s];
+    AttnItem it;
+    it.b = s;
+    it.hq = x % nhq;
+    const unsigned rest = x / nhq;
+    it.r = rest % nqb;
+    it.gk = rest / nqb;
+    it.n_q = t.n[s];
+    it.q0 = t.pos0[s];
+    it.tok0 = t.tok0[s];
+    it.kv_len = t.pos0[s] + t.n[s];
+    it.sel_row = (long)Hkv * t.aux0[s] + (long)it.gk * nqb + it.r;
+    return it;
+  }
+};
+
+// grid: one workgroup per item (B*Hkv*nqb*ceil(G/4) for uniform batches) of 512 threads (8
+// waves: 4 heads x 2 row halves)
 constexpr int PF_THREADS = 512;
 constexpr int PF_QT = 2;  // 16-row query tiles per wave
-template <bool DENSE>
+template <bool DENSE, class Geo>
 __global__ void __launch_bounds__(PF_THREADS)
 sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
                            const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
                            const bf16_t* __restrict__ g, const int32_t* __restrict__ sel,
-                           bf16_t* __restrict__ out, int n_q, int Hq, int Hkv, long q0, long qb0,
-                           int nqb, long kv_len, long cap, int topk, float eps, float qscale) {
+                           bf16_t* __restrict__ out, int Hq, int Hkv, long cap, int topk, float eps, float qscale,
+                           Geo geo) {
   __shared__ __align__(16) bf16_t lds[NSTAGE][2][TILE];  // [stage][K|V]
   __shared__ int s_sel[256];
   const int G = Hq / Hkv, nhq = (G + 3) / 4;
@@ -58,11 +112,9 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   const unsigned nwg = gridDim.x;
   unsigned w = blockIdx.x;
   if ((nwg & 7u) == 0) w = (blockIdx.x & 7u) * (nwg >> 3) + (blockIdx.x >> 3);
-  const int hq = w % nhq;
-  unsigned rest = w / nhq;
-  const int r = rest % nqb;
-  rest /= nqb;
-  const int gk = rest % Hkv, b = rest / Hkv;
+  const AttnItem it = geo.item(w, Hkv, nhq);
+  const int hq = it.hq, r = it.r, gk = it.gk, b = it.b, n_q = it.n_q;
+  const long q0 = it.q0, kv_len = it.kv_len, qb0 = q0 / 64;
 
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
   const int hl = 4 * hq + (wave >> 1);
@@ -72,7 +124,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   const long i = qb0 + r;
   const long row_base = ((long)b * Hkv + gk) * cap;
   if (!DENSE) {
-    const int32_t* srow = sel + (((long)b * Hkv + gk) * nqb + r) * topk;
+    const int32_t* srow = sel + it.sel_row * topk;
     if (j < topk) s_sel[j] = srow[j];
   }
 
@@ -87,7 +139,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) u = *reinterpret_cast<const uint4*>(q + ((long)(b * (long)n_q + t) * Hq + h) * D + 32 * ks + 8 * lq);
+      if (ok) u = *reinterpret_cast<const uint4*>(q + ((it.tok0 + t) * Hq + h) * D + 32 * ks + 8 * lq);
       unpack8(u, x[ks]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
@@ -176,7 +228,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     const float il = 1.0f / l;
     const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
     if (t >= n_q) continue;
-    const long base = ((long)(b * (long)n_q + t) * Hq + h) * D;
+    const long base = ((it.tok0 + t) * Hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const long off = base + 16 * dt + 4 * lq;
@@ -492,10 +544,10 @@ static hipError_t launch_attn(const sala_sparse_desc& d, const void* q, const fl
     return hipGetLastError();
   }
   const long nwg = (long)d.batch * d.n_kv_heads * gm.nqb * ((G + 3) / 4);
-  hipLaunchKernelGGL(sparse_prefill_bf16_kernel<DENSE>, dim3((unsigned)nwg), dim3(PF_THREADS), 0, st,
-                     (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g,
-                     sel, (bf16_t*)out, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0,
-                     (int)gm.nqb, (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, qscale);
+  const AttnUniform geo{d.n_q, (int)gm.nqb, (long)gm.q0, (long)d.kv_len};
+  hipLaunchKernelGGL((sparse_prefill_bf16_kernel<DENSE, AttnUniform>), dim3((unsigned)nwg), dim3(PF_THREADS), 0, st,
+                     (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
+                     (bf16_t*)out, d.n_heads, d.n_kv_heads, (long)d.kv_capacity, d.topk, d.norm_eps, qscale, geo);
   return hipGetLastError();
 }
 
@@ -509,6 +561,31 @@ hipError_t launch_dense_attn(const sala_sparse_desc& d, const void* q, const flo
                              const void* k_cache, const void* v_cache, const void* g, void* out,
                              void* ws, hipStream_t st) {
   return launch_attn<true>(d, q, qw, k_cache, v_cache, g, nullptr, out, ws, st);
+}
+
+int64_t varlen_query_blocks(int nseq, const int32_t* cu_seqlens) {
+  int64_t n = 0;
+  for (int s = 0; s < nseq; ++s) n += (cu_seqlens[s + 1] - cu_seqlens[s] + 63) / 64;
+  return n;
+}
+
+hipError_t launch_sparse_attn_varlen(const sala_sparse_desc& d, const int32_t* cu_seqlens, const int64_t* pos0,
+                                     const void* q, const float* qw, const void* k_cache, const void* v_cache,
+                                     const void* g, const int32_t* sel, void* out, hipStream_t st) {
+  const int nhq = (d.n_heads / d.n_kv_heads + 3) / 4;
+  AttnVarlen geo{make_varlen_table(d.batch, cu_seqlens, pos0)};
+  for (int s = 0; s < d.batch; ++s) {
+    const int nqb = (geo.t.n[s] + 63) / 64;
+    geo.t.aux0[s + 1] = geo.t.aux0[s] + nqb;
+    geo.t.item0[s + 1] = geo.t.item0[s] + nqb * d.n_kv_heads * nhq;
+  }
+  const long nwg = geo.t.item0[d.batch];
+  if (nwg == 0) return hipSuccess;
+  const float qscale = sparse_geom(d).scale * 1.4426950408889634f;  // exp -> exp2
+  hipLaunchKernelGGL((sparse_prefill_bf16_kernel<false, AttnVarlen>), dim3((unsigned)nwg), dim3(PF_THREADS), 0, st,
+                     (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
+                     (bf16_t*)out, d.n_heads, d.n_kv_heads, (long)d.kv_capacity, d.topk, d.norm_eps, qscale, geo);
+  return hipGetLastError();
 }
 
 }  // namespace sala

@@ -6,7 +6,8 @@ raises on a non-OK status. It fails loudly (SalaError at import of the library) 
 libsala.so is missing: there is no CPU fallback.
 
 Entry points mirror include/sala.h: linear_prefill, linear_decode_step, kv_append, kv_pool,
-block_select, sparse_attn (+ workspace_bytes, abi_version).
+block_select, sparse_attn, dense_attn, the backward calls, the packed variable-length (varlen)
+calls (+ workspace_bytes, abi_version).
 """
 
 from __future__ import annotations
@@ -67,6 +68,14 @@ def lib():
         L.sala_sparse_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 8 + [ctypes.c_size_t, _VP]
         L.sala_dense_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7 + [ctypes.c_size_t, _VP]
         L.sala_sparse_layer_uses_dense.argtypes = [ctypes.POINTER(SparseDesc)]
+        L.sala_linear_prefill_varlen.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 12 + [ctypes.c_size_t, _VP]
+        L.sala_kv_append_varlen.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 9
+        L.sala_block_select_varlen.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7 + [ctypes.c_size_t, _VP]
+        L.sala_sparse_attn_varlen.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 10
+        L.sala_varlen_query_blocks.argtypes = [ctypes.c_int32, _VP]
+        L.sala_varlen_query_blocks.restype = ctypes.c_int64
+        L.sala_varlen_workspace_bytes.argtypes = [ctypes.c_int, _VP, _VP, _VP]
+        L.sala_varlen_workspace_bytes.restype = ctypes.c_size_t
         L.sala_workspace_bytes.argtypes = [ctypes.c_int, _VP]
         L.sala_workspace_bytes.restype = ctypes.c_size_t
         L.sala_status_str.argtypes = [ctypes.c_int]
@@ -75,7 +84,9 @@ def lib():
                      "sala_sparse_attn_backward", "sala_kv_norm_backward",
                      "sala_kv_append", "sala_kv_pool",
                      "sala_block_select", "sala_sparse_attn", "sala_dense_attn",
-                     "sala_sparse_layer_uses_dense", "sala_abi_version", "sala_last_hip_error"):
+                     "sala_sparse_layer_uses_dense", "sala_abi_version", "sala_last_hip_error",
+                     "sala_linear_prefill_varlen", "sala_kv_append_varlen", "sala_block_select_varlen",
+                     "sala_sparse_attn_varlen"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -350,3 +361,127 @@ def sparse_layer_uses_dense(*, batch, n_q, n_heads, n_kv_heads, head_dim, dtype,
     if r < 0:
         raise SalaError(2, "sparse_layer_uses_dense: invalid descriptor")
     return bool(r)
+
+
+# ---------------------------------------------------------------- packed variable-length batches
+
+
+class Varlen:
+    """Host arrays of a packed batch: seqlens (token counts of this call) and pos0 (position of
+    each sequence's first token of this call). cu_seqlens / pos0 are kept as ctypes arrays, which
+    the library reads during each call."""
+
+    def __init__(self, seqlens, pos0=None):
+        seqlens = [int(n) for n in seqlens]
+        self.nseq = len(seqlens)
+        cu = [0]
+        for n in seqlens:
+            cu.append(cu[-1] + n)
+        self.seqlens, self.cu = seqlens, cu
+        self.pos0 = [0] * self.nseq if pos0 is None else [int(p) for p in pos0]
+        self._cu = (ctypes.c_int32 * (self.nseq + 1))(*cu)
+        self._pos0 = (ctypes.c_int64 * max(1, self.nseq))(*self.pos0)
+
+    @property
+    def total(self):
+        return self.cu[-1]
+
+    def query_blocks(self):
+        n = lib().sala_varlen_query_blocks(self.nseq, self._cu)
+        if n < 0:
+            raise SalaError(2, "varlen_query_blocks")
+        return n
+
+    def args(self):
+        return self._cu, self._pos0
+
+
+def varlen_workspace_bytes(op, desc, vl):
+    n = lib().sala_varlen_workspace_bytes(op, ctypes.byref(desc), *vl.args())
+    if n == ctypes.c_size_t(-1).value:
+        raise SalaError(2, "varlen_workspace_bytes: invalid arguments")
+    return n
+
+
+def _varlen_workspace(op, desc, vl, device, workspace):
+    need = varlen_workspace_bytes(op, desc, vl)
+    if need == 0:
+        return None, 0
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(need, dtype=torch.uint8, device=device), need
+
+
+def linear_prefill_varlen(q, k, v, g, vl, *, rope_base=10000.0, eps=1e-6, state_in=None, state_out=None,
+                          q_norm_w=None, k_norm_w=None, out=None, workspace=None, stream=None):
+    """q, k, v, g: [T, H, d] bf16 packed by vl (Varlen); states [nseq, H, d, d] f32. Returns
+    (out [T, H, d], state_out)."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, torch.bfloat16)
+    T, H, d = q.shape
+    if T != vl.total:
+        raise SalaError(2, f"packed tokens {T} != sum of seqlens {vl.total}")
+    if out is None:
+        out = torch.empty_like(q)
+    if state_out is None:
+        state_out = torch.empty((vl.nseq, H, d, d), dtype=torch.float32, device=q.device)
+    for n, t in (("state_in", state_in), ("state_out", state_out), ("q_norm_w", q_norm_w),
+                 ("k_norm_w", k_norm_w)):
+        _check(t, n, torch.float32)
+    desc = LinearDesc(vl.nseq, T, H, H, d, SALA_BF16, 0, float(rope_base), float(eps))
+    ws, ws_bytes = _varlen_workspace(OP_LINEAR_PREFILL, desc, vl, q.device, workspace)
+    _call(lib().sala_linear_prefill_varlen, ctypes.byref(desc), *vl.args(), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+          _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(ws), ws_bytes,
+          _stream(stream), what="linear_prefill_varlen")
+    return out, state_out
+
+
+def _sparse_varlen_desc(vl, Hq, Hkv, d, cap, topk, n_local, eps, scale=0.0):
+    return sparse_desc(batch=vl.nseq, n_q=vl.total, n_heads=Hq, n_kv_heads=Hkv, head_dim=d, dtype=torch.bfloat16,
+                       kv_len=0, kv_capacity=cap, topk=topk, n_local=n_local, eps=eps, scale=scale)
+
+
+def kv_append_varlen(k_new, v_new, k_cache, v_cache, k_pool, vl, *, n_heads=None, eps=1e-6, k_norm_w=None,
+                     stream=None):
+    """k_new, v_new [T, Hkv, d] bf16 packed by vl; caches [nseq, Hkv, cap, d]; k_pool
+    [nseq, Hkv, cap/64, d] f32. Sequence s's tokens go to positions pos0[s] .."""
+    T, Hkv, d = k_new.shape
+    for n, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, n, torch.bfloat16)
+    _check(k_pool, "k_pool", torch.float32)
+    desc = _sparse_varlen_desc(vl, n_heads or Hkv, Hkv, d, k_cache.shape[2], 3, 2, eps)
+    _call(lib().sala_kv_append_varlen, ctypes.byref(desc), *vl.args(), _ptr(k_new), _ptr(v_new), _ptr(k_norm_w),
+          _ptr(k_cache), _ptr(v_cache), _ptr(k_pool), _stream(stream), what="kv_append_varlen")
+
+
+def block_select_varlen(q, k_pool, vl, kv_capacity, *, n_kv_heads, topk=64, n_local=2, eps=1e-6, q_norm_w=None,
+                        sel=None, workspace=None, stream=None):
+    """q [T, Hq, d] bf16 packed by vl; returns sel [query_blocks * Hkv, topk] int32: the
+    per-sequence [Hkv, nqb_s, topk] blocks one after another."""
+    _check(q, "q", torch.bfloat16)
+    _check(k_pool, "k_pool", torch.float32)
+    T, Hq, d = q.shape
+    desc = _sparse_varlen_desc(vl, Hq, n_kv_heads, d, kv_capacity, topk, n_local, eps)
+    if sel is None:
+        sel = torch.empty((vl.query_blocks() * n_kv_heads, topk), dtype=torch.int32, device=q.device)
+    ws, ws_bytes = _varlen_workspace(OP_BLOCK_SELECT, desc, vl, q.device, workspace)
+    _call(lib().sala_block_select_varlen, ctypes.byref(desc), *vl.args(), _ptr(q), _ptr(q_norm_w), _ptr(k_pool),
+          _ptr(sel), _ptr(ws), ws_bytes, _stream(stream), what="block_select_varlen")
+    return sel
+
+
+def sparse_attn_varlen(q, k_cache, v_cache, g, sel, vl, *, topk=None, n_local=2, eps=1e-6, scale=0.0,
+                       q_norm_w=None, out=None, stream=None):
+    """q, g [T, Hq, d] bf16 packed by vl; caches [nseq, Hkv, cap, d]; sel from
+    block_select_varlen. Returns out [T, Hq, d]."""
+    for n, t in (("q", q), ("g", g), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _check(t, n, torch.bfloat16)
+    _check(sel, "sel", torch.int32)
+    T, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    desc = _sparse_varlen_desc(vl, Hq, Hkv, d, cap, topk or sel.shape[-1], n_local, eps, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _call(lib().sala_sparse_attn_varlen, ctypes.byref(desc), *vl.args(), _ptr(q), _ptr(q_norm_w), _ptr(k_cache),
+          _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(out), _stream(stream), what="sparse_attn_varlen")
+    return out

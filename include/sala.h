@@ -36,7 +36,10 @@
 extern "C" {
 #endif
 
-#define SALA_ABI_VERSION 4
+#define SALA_ABI_VERSION 5
+
+/* sequences per call of the packed variable-length (varlen) entry points */
+#define SALA_VARLEN_MAX_SEQS 64
 
 typedef enum {
   SALA_OK = 0,
@@ -256,6 +259,61 @@ sala_status sala_kv_norm_backward(const sala_sparse_desc* desc, const void* k_ne
  * selection + sala_sparse_attn and the selection can be skipped), 0 when the sparse path must
  * run, -1 for an invalid descriptor. Host-side, no device work. */
 int sala_sparse_layer_uses_dense(const sala_sparse_desc* desc);
+
+/* ---- Packed variable-length batches ("varlen"). The pages advise sizing the batch to the
+ * context length ("MiniCPM-SALA：混合注意力机制突破LLM长文本处理瓶颈" §5.1 部署建议), so a serving
+ * batch mixes prompts of different lengths. These entry points prefill nseq = desc->batch
+ * sequences (1 .. SALA_VARLEN_MAX_SEQS) whose new tokens are stored back to back along the token
+ * dimension, with the same per-sequence results as one call per sequence.
+ *   cu_seqlens  HOST array [nseq + 1] int32: cu_seqlens[0] = 0, nondecreasing, ending at the
+ *               packed token count (desc->seq_len, resp. desc->n_q); sequence s owns packed
+ *               tokens [cu_seqlens[s], cu_seqlens[s + 1]) (an empty sequence is allowed)
+ *   pos0        HOST array [nseq] int64 >= 0: position of sequence s's first token of the call
+ *               (the number of its tokens processed by earlier calls)
+ * Both arrays are read during the call only. bf16 and d = 128 only (else UNSUPPORTED); more than
+ * SALA_VARLEN_MAX_SEQS sequences: UNSUPPORTED. Activations are [T, H, d]; per-sequence state,
+ * cache and pool tensors are indexed by the sequence (batch) index s.
+ * Workspace: sala_varlen_workspace_bytes(op, desc, cu_seqlens, pos0). */
+
+/* Linear layer prefill of a packed batch: sala_linear_prefill on each sequence, its tokens at
+ * positions pos0[s] + t (desc->pos0 is ignored). desc->batch = nseq, desc->seq_len = T.
+ * q, k, v, gate, out: [T, H, d] bf16; state_in / state_out: [nseq, H, d, d] float (NULL: zeros /
+ * not written; may alias). All sequences run in one launch per kernel. */
+sala_status sala_linear_prefill_varlen(const sala_linear_desc* desc, const int32_t* cu_seqlens,
+                                       const int64_t* pos0, const void* q, const void* k, const void* v,
+                                       const void* gate, const float* q_norm_w, const float* k_norm_w,
+                                       const float* state_in, float* state_out, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Sparse layer of a packed batch. desc: batch = nseq, n_q = T, kv_capacity = capacity of each
+ * sequence's cache row; kv_len is ignored: sequence s's cache holds pos0[s] + n_s tokens once its
+ * n_s new tokens are in it. pos0[s] must be a multiple of 64 and pos0[s] + n_s <= kv_capacity.
+ * k_cache, v_cache: [nseq, Hkv, kv_capacity, d]; k_pool: [nseq, Hkv, kv_capacity / 64, d] float.
+ * sel: the per-sequence selections [Hkv, nqb_s, topk] (nqb_s = ceil(n_s / 64); row r is query
+ * block pos0[s] / 64 + r) stored one after another in sequence order,
+ * sala_varlen_query_blocks() * Hkv rows of topk int32 in all.
+ *   sala_kv_append_varlen:    sala_kv_append per sequence (new k, v: [T, Hkv, d]).
+ *   sala_block_select_varlen: sala_block_select per sequence (q: [T, Hq, d]); one workspace is
+ *                             shared by the sequences, which run one after another.
+ *   sala_sparse_attn_varlen:  sala_sparse_attn per sequence (q, gate, out: [T, Hq, d]), all
+ *                             sequences in one launch; no workspace. */
+sala_status sala_kv_append_varlen(const sala_sparse_desc* desc, const int32_t* cu_seqlens, const int64_t* pos0,
+                                  const void* k_new, const void* v_new, const float* k_norm_w, void* k_cache,
+                                  void* v_cache, float* k_pool, void* stream);
+sala_status sala_block_select_varlen(const sala_sparse_desc* desc, const int32_t* cu_seqlens, const int64_t* pos0,
+                                     const void* q, const float* q_norm_w, const float* k_pool, int32_t* sel,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+sala_status sala_sparse_attn_varlen(const sala_sparse_desc* desc, const int32_t* cu_seqlens, const int64_t* pos0,
+                                    const void* q, const float* q_norm_w, const void* k_cache, const void* v_cache,
+                                    const void* gate, const int32_t* sel, void* out, void* stream);
+
+/* Query blocks of a packed batch: the sum over the sequences of ceil(n_s / 64) (-1 for invalid
+ * arguments). Host-side. */
+int64_t sala_varlen_query_blocks(int32_t nseq, const int32_t* cu_seqlens);
+
+/* Workspace bytes of a varlen operation (SALA_OP_LINEAR_PREFILL, SALA_OP_BLOCK_SELECT or
+ * SALA_OP_SPARSE_ATTN, which needs none) for this batch; SIZE_MAX if the arguments are invalid. */
+size_t sala_varlen_workspace_bytes(int op, const void* desc, const int32_t* cu_seqlens, const int64_t* pos0);
 
 /* Workspace bytes an operation needs for this descriptor (0 if none; SIZE_MAX if the
  * descriptor is invalid). `desc` points to a sala_linear_desc for SALA_OP_LINEAR_PREFILL and

@@ -32,7 +32,7 @@ def test_abi_version_and_status_strings():
     from hybrid_sparse_linear_causal_amd import sala as S
 
     L = S.lib()
-    assert L.sala_abi_version() == 4
+    assert L.sala_abi_version() == 5
     for code in range(6):
         assert L.sala_status_str(code)
     assert L.sala_last_hip_error() == 0
@@ -213,3 +213,53 @@ def test_sparse_backward_arguments():
     assert kneed > 0
     assert L.sala_kv_norm_backward(ctypes.byref(d), FAKE, None, FAKE, None, None, FAKE, kneed, None) == 1
     assert L.sala_kv_norm_backward(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, FAKE, kneed - 1, None) == 4
+
+
+def test_varlen_arguments():
+    """Argument errors of the packed variable-length entry points (no device work): the host
+    arrays must describe the packed tokens, sparse positions must start a block and fit the
+    cache, bf16 / d = 128 only, at most SALA_VARLEN_MAX_SEQS sequences."""
+    import torch
+
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    vl = S.Varlen([100, 0, 300], [0, 5, 64])
+    d = S.LinearDesc(3, 400, 4, 4, 128, S.SALA_BF16, 0, 10000.0, 1e-6)
+    need = S.varlen_workspace_bytes(S.OP_LINEAR_PREFILL, d, vl)
+    assert need > 0
+    # q k v gate | qw kw state_in state_out | out
+    args = [FAKE] * 4 + [None, None, None, None] + [FAKE]
+    assert L.sala_linear_prefill_varlen(ctypes.byref(d), *vl.args(), *args, FAKE, need - 1, None) == 4
+    assert L.sala_linear_prefill_varlen(ctypes.byref(d), None, vl.args()[1], *args, FAKE, need, None) == 1
+    bad = S.LinearDesc(3, 399, 4, 4, 128, S.SALA_BF16, 0, 10000.0, 1e-6)  # packed count != cu_seqlens[3]
+    assert L.sala_linear_prefill_varlen(ctypes.byref(bad), *vl.args(), *args, FAKE, need, None) == 2
+    f32 = S.LinearDesc(3, 400, 4, 4, 128, S.SALA_F32, 0, 10000.0, 1e-6)
+    assert L.sala_linear_prefill_varlen(ctypes.byref(f32), *vl.args(), *args, FAKE, need, None) == 3
+    down = S.Varlen([100, 300, 0], [0, 0, 0])
+    down._cu[2], down._cu[3] = 50, 400  # cu_seqlens not nondecreasing
+    assert L.sala_linear_prefill_varlen(ctypes.byref(d), *down.args(), *args, FAKE, need, None) == 2
+    many = S.Varlen([1] * 65)
+    dm = S.LinearDesc(65, 65, 4, 4, 128, S.SALA_BF16, 0, 10000.0, 1e-6)
+    assert L.sala_linear_prefill_varlen(ctypes.byref(dm), *many.args(), *args, FAKE, 1 << 30, None) == 3
+
+    svl = S.Varlen([100, 0, 300], [64, 0, 128])
+    sd = S.sparse_desc(batch=3, n_q=400, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16, kv_len=0,
+                       kv_capacity=512, topk=3, n_local=2)
+    assert S.Varlen([100, 0, 300]).query_blocks() == 2 + 0 + 5
+    sneed = S.varlen_workspace_bytes(S.OP_BLOCK_SELECT, sd, svl)
+    assert sneed > 0 and S.varlen_workspace_bytes(S.OP_SPARSE_ATTN, sd, svl) == 0
+    assert L.sala_block_select_varlen(ctypes.byref(sd), *svl.args(), FAKE, None, FAKE, FAKE, FAKE, sneed - 1,
+                                      None) == 4
+    assert L.sala_block_select_varlen(ctypes.byref(sd), *svl.args(), FAKE, None, FAKE, None, FAKE, sneed,
+                                      None) == 1
+    unaligned = S.Varlen([100, 0, 300], [64, 0, 100])  # a query start inside a block
+    assert L.sala_sparse_attn_varlen(ctypes.byref(sd), *unaligned.args(), FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, None) == 2
+    over = S.Varlen([100, 0, 300], [64, 0, 256])  # 256 + 300 > capacity 512
+    assert L.sala_kv_append_varlen(ctypes.byref(sd), *over.args(), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == 2
+    assert L.sala_sparse_attn_varlen(ctypes.byref(sd), *svl.args(), FAKE, None, FAKE, FAKE, FAKE, None, FAKE,
+                                     None) == 1
+    sf = S.sparse_desc(batch=3, n_q=400, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.float32, kv_len=0,
+                       kv_capacity=512, topk=3, n_local=2)
+    assert L.sala_kv_append_varlen(ctypes.byref(sf), *svl.args(), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == 3

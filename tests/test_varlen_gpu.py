@@ -1,0 +1,121 @@
+"""GPU parity of the packed variable-length (varlen) entry points against the oracle's varlen
+functions, on seeded bf16-representable inputs with mixed lengths: empty sequences, single
+tokens, ragged chunks and blocks, sequences continuing a cached prefix, and the 64-sequence
+limit. Tolerance as for the single-sequence calls: max|gpu - ref| <= 1e-2 * max|ref|."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from hybrid_sparse_linear_causal_amd.inputs import host_normal
+from sala_testutil import assert_rel, check_selection, dev, host
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def S():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from hybrid_sparse_linear_causal_amd import sala
+
+    sala.lib()
+    return sala
+
+
+def _lengths(seed, n, hi):
+    rng = np.random.default_rng(seed)
+    return [int(x) for x in rng.integers(0, hi, n)]
+
+
+@pytest.mark.parametrize("seqlens,pos0,H,with_state", [
+    ([333, 0, 1500, 64, 1, 200], [17, 3, 0, 4096, 9, 64], 2, True),
+    ([4096 + 100, 70], [0, 1000], 4, False),          # one long (several segments), one short
+    (None, None, 2, True),                              # 64 sequences of 0 .. 149 tokens
+])
+def test_linear_prefill_varlen(S, seqlens, pos0, H, with_state):
+    if seqlens is None:
+        seqlens = _lengths(5, 64, 150)
+        pos0 = _lengths(6, 64, 10000)
+    ns, T, d = len(seqlens), sum(seqlens), 128
+    print(f"linear_prefill_varlen nseq={ns} T={T} H={H} state={with_state}", flush=True)
+    q, k, v, g = (host_normal(600 + T, t, (T, H, d), "bf16") for t in range(4))
+    s_in = host_normal(601, 4, (ns, H, d, d), "f32", std=4.0) if with_state else None
+    qw = 1.0 + 0.25 * host_normal(602, 5, (d,), "f32")
+    ref, S_ref = O.linear_prefill_varlen(q, k, v, g, seqlens, pos0, state_in=s_in, q_norm_w=qw)
+    vl = S.Varlen(seqlens, pos0)
+    out, st = S.linear_prefill_varlen(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(g, "bf16"), vl,
+                                      state_in=None if s_in is None else dev(s_in, "f32"), q_norm_w=dev(qw, "f32"))
+    e1 = assert_rel(host(out), ref, TOL, "out")
+    e2 = assert_rel(host(st), S_ref, TOL, "state")
+    print(f"  relative errors: out {e1:.2e}, state {e2:.2e}", flush=True)
+
+
+def _sparse_full(seed, F, Hq, Hkv, d):
+    return (host_normal(seed, 0, (F, Hq, d), "bf16"), host_normal(seed, 1, (F, Hkv, d), "bf16"),
+            host_normal(seed, 2, (F, Hkv, d), "bf16"), host_normal(seed, 3, (F, Hq, d), "bf16"))
+
+
+@pytest.mark.parametrize("new,prefix,Hq,Hkv,topk", [
+    ([200, 0, 640, 64, 1, 333], [0, 64, 128, 0, 192, 640], 4, 2, 4),
+    ([1500, 130], [0, 256], 32, 2, 8),                  # a full GQA group of 16 heads
+])
+def test_sparse_layer_varlen(S, new, prefix, Hq, Hkv, topk):
+    """Prefixes appended first (one varlen call from position 0), then the new tokens appended,
+    selected and attended at pos0 = prefix: against the oracle on each whole sequence."""
+    import torch
+
+    d, ns = 128, len(new)
+    full = [p + n for p, n in zip(prefix, new)]
+    cap = ((max(full) + 63) // 64) * 64
+    print(f"sparse_layer_varlen new={new} prefix={prefix} Hq={Hq} Hkv={Hkv} topk={topk}", flush=True)
+    seqs = [_sparse_full(700 + s, full[s], Hq, Hkv, d) for s in range(ns)]
+    refs = [O.sparse_prefill(*(x[None] for x in seqs[s]), block=64, topk=topk, n_local=2) if full[s] else None
+            for s in range(ns)]
+
+    def packed(part, which):
+        rows = [seqs[s][which][:prefix[s]] if part == "prefix" else seqs[s][which][prefix[s]:] for s in range(ns)]
+        return np.concatenate(rows, axis=0)
+
+    kc = torch.zeros((ns, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((ns, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    if sum(prefix):
+        S.kv_append_varlen(dev(packed("prefix", 1), "bf16"), dev(packed("prefix", 2), "bf16"), kc, vc, kp,
+                           S.Varlen(prefix), n_heads=Hq)
+    vl = S.Varlen(new, prefix)
+    S.kv_append_varlen(dev(packed("new", 1), "bf16"), dev(packed("new", 2), "bf16"), kc, vc, kp, vl, n_heads=Hq)
+    Q = dev(packed("new", 0), "bf16")
+    sel = S.block_select_varlen(Q, kp, vl, cap, n_kv_heads=Hkv, topk=topk, n_local=2)
+    out = S.sparse_attn_varlen(Q, kc, vc, dev(packed("new", 3), "bf16"), sel, vl, n_local=2)
+    assert tuple(sel.shape) == (vl.query_blocks() * Hkv, topk)
+    sel_h, out_h, kc_h = sel.cpu().numpy(), host(out), host(kc)
+    row, tok = 0, 0
+    for s in range(ns):
+        n, p = new[s], prefix[s]
+        if full[s] == 0:
+            continue
+        ref = refs[s]
+        # cache rows of the sequence: the normalised keys of every position written so far
+        assert_rel(kc_h[s][:, :full[s]], ref["k_hat"][0].transpose(1, 0, 2), 2 ** -8, f"seq {s} k cache")
+        if n == 0:
+            continue
+        nqb, b0 = (n + 63) // 64, p // 64
+        sel_s = sel_h[row * Hkv:(row + nqb) * Hkv].reshape(Hkv, nqb, topk)
+        qt, kb = ref["q_tilde"], ref["k_bar"]
+        nm = check_selection(sel_s[None], ref["sel"][:, :, b0:b0 + nqb], lambda b, g, i: {
+            j: float(qt[b, g, i] @ kb[b, g, j]) for j in range(min(max(i, 1), kb.shape[2]))}, topk, 2, b0)
+        # the oracle's attention for the GPU's selection (identical to its own where nm == 0)
+        sel_full = ref["sel"].copy()
+        sel_full[:, :, b0:b0 + nqb] = sel_s
+        q_full, k_full, v_full, g_full = seqs[s]
+        o_ref = O.sparse_attention(O.qk_norm(q_full[None]), ref["k_hat"], v_full[None], sel_full, 64,
+                                   1.0 / np.sqrt(d)) * O.sigmoid(g_full[None])
+        e = assert_rel(out_h[tok:tok + n], o_ref[0, p:], TOL, f"seq {s} out")
+        print(f"  seq {s}: n={n} pos0={p} margin rows {nm} rel err {e:.2e}", flush=True)
+        row += nqb
+        tok += n
