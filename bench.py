@@ -409,6 +409,7 @@ def extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d):
         res[name] = {"ms": ms_l, "tokens_per_s": Nb / (ms_l * 1e-3),
                      "hbm_frac": byts / (ms_l * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del tb, wsl
+    res["varlen_256k"] = varlen_measurement(S, torch, W, H, Hkv, d)
     # decode step: individual launches (above) vs one graph replay; linear states restored after
     saved = [Dr["state"].clone() for Dr in dl]
     graph = torch.cuda.CUDAGraph()
@@ -438,6 +439,75 @@ def extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d):
     res["decode_graph_step_us"] = us_graph
     res["decode_graph_us_per_token"] = us_graph / B
     res["decode_cold_step_us_median"] = cold[len(cold) // 2]
+    return res
+
+
+def varlen_measurement(S, torch, W, H, Hkv, d):
+    """Packed batch of 16 prompts of mixed lengths (262,144 tokens) through L, L, L, S with the
+    varlen entry points (one launch per kernel for the linear layers and the attention), and
+    the same prompts one call per sequence, both timed with HIP events (3 repetitions)."""
+    from hybrid_sparse_linear_causal_amd.inputs import WORKLOADS, device_normal, varlen_lengths
+
+    Wv = WORKLOADS["varlen_256k"]
+    lens = varlen_lengths(Wv.seed, Wv.batch, Wv.seq_len)
+    T, ns = sum(lens), len(lens)
+    vl = S.Varlen(lens)
+    cu = vl.cu
+    cap = ((max(lens) + 63) // 64) * 64
+    q, k, v, g = (device_normal(Wv.seed, t, (T, H, d)) for t in range(4))
+    sk, sv = device_normal(Wv.seed, 11, (T, Hkv, d)), device_normal(Wv.seed, 12, (T, Hkv, d))
+    out = torch.empty_like(q)
+    st = torch.empty((ns, H, d, d), dtype=torch.float32, device="cuda")
+    kc = torch.zeros((ns, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((ns, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    ld = S.LinearDesc(ns, T, H, H, d, S.SALA_BF16, 0, W.rope_base, W.norm_eps)
+    wsl = torch.empty(max(1, S.varlen_workspace_bytes(S.OP_LINEAR_PREFILL, ld, vl)), dtype=torch.uint8,
+                      device="cuda")
+    sd = S._sparse_varlen_desc(vl, H, Hkv, d, cap, Wv.topk, Wv.n_local, W.norm_eps)
+    wss = torch.empty(max(1, S.varlen_workspace_bytes(S.OP_BLOCK_SELECT, sd, vl)), dtype=torch.uint8, device="cuda")
+    sel = torch.empty((vl.query_blocks() * Hkv, Wv.topk), dtype=torch.int32, device="cuda")
+    sout = torch.empty_like(q)
+    parts = {}
+
+    def lin():
+        for _ in range(3):
+            S.linear_prefill_varlen(q, k, v, g, vl, rope_base=W.rope_base, eps=W.norm_eps, state_out=st, out=out,
+                                    workspace=wsl)
+
+    def sparse():
+        S.kv_append_varlen(sk, sv, kc, vc, kp, vl, n_heads=H, eps=W.norm_eps)
+        S.block_select_varlen(q, kp, vl, cap, n_kv_heads=Hkv, topk=Wv.topk, n_local=Wv.n_local, eps=W.norm_eps,
+                              sel=sel, workspace=wss)
+        S.sparse_attn_varlen(q, kc, vc, g, sel, vl, n_local=Wv.n_local, eps=W.norm_eps, out=sout)
+
+    parts["linear_x3_ms"] = _time_events(torch, lin, 3)
+    parts["sparse_ms"] = _time_events(torch, sparse, 3)
+    parts["attention_ms"] = _time_events(torch, lambda: S.sparse_attn_varlen(
+        q, kc, vc, g, sel, vl, n_local=Wv.n_local, eps=W.norm_eps, out=sout), 3)
+
+    def per_sequence():
+        for s in range(ns):
+            a, b = cu[s], cu[s + 1]
+            n = b - a
+            qs, ks, vs, gs = (x[a:b].unsqueeze(0) for x in (q, k, v, g))
+            for _ in range(3):
+                S.linear_prefill(qs, ks, vs, gs, rope_base=W.rope_base, eps=W.norm_eps, state_out=st[s:s + 1],
+                                 out=out[a:b].unsqueeze(0))
+            S.kv_append(sk[a:b].unsqueeze(0), sv[a:b].unsqueeze(0), kc[s:s + 1], vc[s:s + 1], kp[s:s + 1], n,
+                        eps=W.norm_eps, n_heads=H)
+            ss = S.block_select(qs, kp[s:s + 1], n, cap, n_kv_heads=Hkv, topk=Wv.topk, n_local=Wv.n_local,
+                                eps=W.norm_eps)
+            S.sparse_attn(qs, kc[s:s + 1], vc[s:s + 1], gs, ss, n, n_local=Wv.n_local, eps=W.norm_eps,
+                          out=sout[a:b].unsqueeze(0))
+
+    ms = parts["linear_x3_ms"] + parts["sparse_ms"]
+    ms_seq = _time_events(torch, per_sequence, 3)
+    fl = sum(sparse_prefill_flops(n, H, d, Wv.topk) for n in lens)
+    res = {"lengths": lens, "ms": ms, "tokens_per_s": T / (ms * 1e-3), "per_sequence_calls_ms": ms_seq,
+           "linear_layer_hbm_frac": T * H * d * 2 * 5 * 3 / (parts["linear_x3_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "attention_mfma_frac": fl / (parts["attention_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    res.update(parts)
     return res
 
 

@@ -90,4 +90,18 @@ WORKLOADS = {
                            layers=("L", "L", "L", "S")),
     # Decode step at a 1M-token context, batch 8.
     "decode_1m": Workload("decode_1m", "decode", 8, 1048576, 32, 2, 128, "bf16", 105),
+    # Packed batch of 16 prompts of mixed lengths (varlen_lengths) totalling 262,144 tokens,
+    # through the L, L, L, S stack.
+    "varlen_256k": Workload("varlen_256k", "varlen", 16, 262144, 32, 2, 128, "bf16", 108,
+                            layers=("L", "L", "L", "S")),
 }
+
+
+def varlen_lengths(seed, nseq, total, lo=1024, hi=49152):
+    """Seeded prompt lengths of a packed batch: log-uniform draws in [lo, hi], scaled to sum to
+    `total` (floors, the remainder added to the last). No arithmetic of the method."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), 99])))
+    raw = np.exp(rng.uniform(np.log(lo), np.log(hi), size=nseq))
+    n = np.floor(raw / raw.sum() * total).astype(np.int64)
+    n[-1] += total - int(n.sum())
+    return [int(x) for x in n]
