@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-configuration breakdown measurements that follow the timed steps "
+                         "(for a kernel trace of the step alone)")
     ap.add_argument("--workload", default="stack_256k", choices=["stack_256k", "segmented_1m"],
                     help="stack_256k: the headline line; segmented_1m: 1M-token prefill in segments + decode")
     args = ap.parse_args()
@@ -325,7 +328,8 @@ def main():
             "decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
         },
     }
-    result["breakdown"].update(extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d))
+    if not args.no_extras:
+        result["breakdown"].update(extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_sample(W)
     print(json.dumps(result))
