@@ -396,9 +396,16 @@ def extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d):
     wsb = torch.empty(S.workspace_bytes(S.OP_SPARSE_ATTN_BACKWARD, sd), dtype=torch.uint8, device="cuda")
     ms_b = _time_events(torch, lambda: S.sparse_attn_backward(q, kc, vc, g, sel, N, dout, topk=Ws.topk,
                                                                n_local=Ws.n_local, workspace=wsb), 3)
+    # the same with the forward's out and lse saved (no forward rerun inside the backward)
+    lse = torch.empty((1, N, H), dtype=torch.float32, device="cuda")
+    S.sparse_attn(q, kc, vc, g, sel, N, n_local=Ws.n_local, out=so, lse=lse)
+    ms_s = _time_events(torch, lambda: S.sparse_attn_backward(q, kc, vc, g, sel, N, dout, topk=Ws.topk,
+                                                               n_local=Ws.n_local, out=so, lse=lse, workspace=wsb), 3)
     res["sparse_backward_128k"] = {"ms": ms_b, "tokens_per_s": N / (ms_b * 1e-3),
-                                   "mfma_frac": 2.5 * fl / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
-    del q, g, k, v, kc, vc, so, dout, wsb
+                                   "mfma_frac": 2.5 * fl / (ms_b * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                   "ms_saved_forward": ms_s,
+                                   "mfma_frac_saved_forward": 2.5 * fl / (ms_s * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+    del q, g, k, v, kc, vc, so, dout, wsb, lse
     # backward of the linear layer (32 heads, d 128) at 32,768 and 262,144 tokens; HBM bytes
     # per (token, head): q, k, v, g, dout read in bf16 and dq, dk, dv, dg written in fp32
     for name, key in (("linear_backward_32k", "linear_32k"), ("linear_backward_256k", "stack_256k")):

@@ -327,18 +327,19 @@ sala_status sala_block_select(const sala_sparse_desc* desc, const void* q, const
 
 sala_status sala_sparse_attn(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
                              const void* k_cache, const void* v_cache, const void* gate,
-                             const int32_t* sel, void* out, void* workspace,
+                             const int32_t* sel, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream) {
   sala_status s = check_sparse(desc);
   if (s != SALA_OK) return s;
   const sala_sparse_desc& d = *desc;
   if (d.dtype == SALA_BF16 && d.head_dim != 128) return SALA_ERR_UNSUPPORTED;
   if (d.dtype == SALA_BF16 && d.n_q == 1 && d.n_heads / d.n_kv_heads > 16) return SALA_ERR_UNSUPPORTED;
+  if (lse && (d.dtype != SALA_BF16 || d.n_q < 2)) return SALA_ERR_UNSUPPORTED;  // bf16 prefill only
   if (!q || !k_cache || !v_cache || !gate || !sel || !out) return SALA_ERR_NULL;
-  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, sel, out, workspace})) return SALA_ERR_INVALID;
+  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, sel, out, lse, workspace})) return SALA_ERR_INVALID;
   const size_t need = sala::sparse_attn_workspace(d);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
-  return hip_status(sala::launch_sparse_attn(d, q, q_norm_w, k_cache, v_cache, gate, sel, out,
+  return hip_status(sala::launch_sparse_attn(d, q, q_norm_w, k_cache, v_cache, gate, sel, out, lse,
                                              workspace, (hipStream_t)stream));
 }
 
@@ -360,22 +361,23 @@ sala_status sala_dense_attn(const sala_sparse_desc* desc, const void* q, const f
 
 sala_status sala_sparse_attn_backward(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
                                       const void* k_cache, const void* v_cache, const void* gate,
-                                      const int32_t* sel, const void* dout, float* dq, float* dk_cache,
-                                      float* dv_cache, float* dg, float* dq_norm_w, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      const int32_t* sel, const void* dout, const void* out, const float* lse,
+                                      float* dq, float* dk_cache, float* dv_cache, float* dg, float* dq_norm_w,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
   sala_status s = check_sparse(desc);
   if (s != SALA_OK) return s;
   const sala_sparse_desc& d = *desc;
   if (d.dtype != SALA_BF16 || d.head_dim != 128 || d.n_q < 2) return SALA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !gate || !sel || !dout || !dq || !dk_cache || !dv_cache || !dg)
     return SALA_ERR_NULL;
-  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, sel, dout, dq, dk_cache, dv_cache, dg, dq_norm_w,
+  if ((out == nullptr) != (lse == nullptr)) return SALA_ERR_NULL;  // the saved forward state: both or neither
+  if (!all_aligned({q, q_norm_w, k_cache, v_cache, gate, sel, dout, out, lse, dq, dk_cache, dv_cache, dg, dq_norm_w,
                     workspace}))
     return SALA_ERR_INVALID;
   const size_t need = sala::sparse_attn_backward_workspace(d);
   if (!workspace || workspace_bytes < need) return SALA_ERR_WORKSPACE;
-  return hip_status(sala::launch_sparse_attn_backward(d, q, q_norm_w, k_cache, v_cache, gate, sel, dout, dq,
-                                                      dk_cache, dv_cache, dg, dq_norm_w, workspace,
+  return hip_status(sala::launch_sparse_attn_backward(d, q, q_norm_w, k_cache, v_cache, gate, sel, dout, out, lse,
+                                                      dq, dk_cache, dv_cache, dg, dq_norm_w, workspace,
                                                       (hipStream_t)stream));
 }
 

@@ -95,12 +95,12 @@ hipError_t launch_sparse_attn_varlen(const sala_sparse_desc& d, const int32_t* c
                                      const void* g, const int32_t* sel, void* out, hipStream_t st);
 hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
                               const void* k_cache, const void* v_cache, const void* g,
-                              const int32_t* sel, void* out, void* ws, hipStream_t st);
+                              const int32_t* sel, void* out, float* lse, void* ws, hipStream_t st);
 size_t sparse_attn_backward_workspace(const sala_sparse_desc& d);
 hipError_t launch_sparse_attn_backward(const sala_sparse_desc& d, const void* q, const float* qw, const void* k_cache,
                                        const void* v_cache, const void* g, const int32_t* sel, const void* dout,
-                                       float* dq, float* dk_cache, float* dv_cache, float* dg, float* dqw, void* ws,
-                                       hipStream_t st);
+                                       const void* out, const float* lse, float* dq, float* dk_cache, float* dv_cache,
+                                       float* dg, float* dqw, void* ws, hipStream_t st);
 size_t kv_norm_backward_workspace(const sala_sparse_desc& d);
 hipError_t launch_kv_norm_backward(const sala_sparse_desc& d, const void* k_new, const float* kw,
                                    const float* dk_cache, float* dk_new, float* dkw, void* ws, hipStream_t st);

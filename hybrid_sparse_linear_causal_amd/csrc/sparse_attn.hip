@@ -103,8 +103,8 @@ __global__ void __launch_bounds__(PF_THREADS)
 sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
                            const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
                            const bf16_t* __restrict__ g, const int32_t* __restrict__ sel,
-                           bf16_t* __restrict__ out, int Hq, int Hkv, long cap, int topk, float eps, float qscale,
-                           Geo geo) {
+                           bf16_t* __restrict__ out, float* __restrict__ lse, int Hq, int Hkv, long cap, int topk,
+                           float eps, float qscale, Geo geo) {
   __shared__ __align__(16) bf16_t lds[NSTAGE][2][TILE];  // [stage][K|V]
   __shared__ int s_sel[256];
   const int G = Hq / Hkv, nhq = (G + 3) / 4;
@@ -229,6 +229,8 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
     if (t >= n_q) continue;
     const long base = ((it.tok0 + t) * Hq + h) * D;
+    // log2-domain log-sum-exp of the row's scaled scores (m is a score of the row, l >= 1)
+    if (lse && lq == 0) lse[(it.tok0 + t) * Hq + h] = m[qt] + __log2f(l);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const long off = base + 16 * dt + 4 * lq;
@@ -515,7 +517,7 @@ size_t sparse_attn_workspace(const sala_sparse_desc& d) {
 template <bool DENSE>
 static hipError_t launch_attn(const sala_sparse_desc& d, const void* q, const float* qw,
                               const void* k_cache, const void* v_cache, const void* g,
-                              const int32_t* sel, void* out, void* ws, hipStream_t st) {
+                              const int32_t* sel, void* out, float* lse, void* ws, hipStream_t st) {
   const SparseGeom gm = sparse_geom(d);
   const int G = d.n_heads / d.n_kv_heads;
   if (d.dtype == SALA_F32) {
@@ -547,20 +549,21 @@ static hipError_t launch_attn(const sala_sparse_desc& d, const void* q, const fl
   const AttnUniform geo{d.n_q, (int)gm.nqb, (long)gm.q0, (long)d.kv_len};
   hipLaunchKernelGGL((sparse_prefill_bf16_kernel<DENSE, AttnUniform>), dim3((unsigned)nwg), dim3(PF_THREADS), 0, st,
                      (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
-                     (bf16_t*)out, d.n_heads, d.n_kv_heads, (long)d.kv_capacity, d.topk, d.norm_eps, qscale, geo);
+                     (bf16_t*)out, lse, d.n_heads, d.n_kv_heads, (long)d.kv_capacity, d.topk, d.norm_eps, qscale,
+                     geo);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const sala_sparse_desc& d, const void* q, const float* qw,
                               const void* k_cache, const void* v_cache, const void* g,
-                              const int32_t* sel, void* out, void* ws, hipStream_t st) {
-  return launch_attn<false>(d, q, qw, k_cache, v_cache, g, sel, out, ws, st);
+                              const int32_t* sel, void* out, float* lse, void* ws, hipStream_t st) {
+  return launch_attn<false>(d, q, qw, k_cache, v_cache, g, sel, out, lse, ws, st);
 }
 
 hipError_t launch_dense_attn(const sala_sparse_desc& d, const void* q, const float* qw,
                              const void* k_cache, const void* v_cache, const void* g, void* out,
                              void* ws, hipStream_t st) {
-  return launch_attn<true>(d, q, qw, k_cache, v_cache, g, nullptr, out, ws, st);
+  return launch_attn<true>(d, q, qw, k_cache, v_cache, g, nullptr, out, nullptr, ws, st);
 }
 
 int64_t varlen_query_blocks(int nseq, const int32_t* cu_seqlens) {
@@ -584,7 +587,8 @@ hipError_t launch_sparse_attn_varlen(const sala_sparse_desc& d, const int32_t* c
   const float qscale = sparse_geom(d).scale * 1.4426950408889634f;  // exp -> exp2
   hipLaunchKernelGGL((sparse_prefill_bf16_kernel<false, AttnVarlen>), dim3((unsigned)nwg), dim3(PF_THREADS), 0, st,
                      (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
-                     (bf16_t*)out, d.n_heads, d.n_kv_heads, (long)d.kv_capacity, d.topk, d.norm_eps, qscale, geo);
+                     (bf16_t*)out, nullptr, d.n_heads, d.n_kv_heads, (long)d.kv_capacity, d.topk, d.norm_eps, qscale,
+                     geo);
   return hipGetLastError();
 }
 

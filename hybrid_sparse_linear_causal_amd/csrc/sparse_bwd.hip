@@ -237,6 +237,79 @@ sbwd_stats_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw, co
   }
 }
 
+// ---- 1'. the same buffers from the forward's saved output and lse (no forward loop): per padded
+// row, lse2 as saved, D = rowsum(dout * out) (= rowsum(dO * O) with out = O sigmoid(g)),
+// dg = dout * out * (1 - sigmoid(g)), q~ and dO in bf16. Four lanes per (token, head) row (dims
+// 32ks + 8lq + e, the forward's lane order, so q~ is computed exactly as the forward computed it),
+// heads fastest so that the token-major inputs are read contiguously, 64 rows per block; padded
+// rows past n_q get q~ = dO = 0, lse2 = +inf and D = 0.
+__global__ void __launch_bounds__(256)
+sbwd_prep_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw, const bf16_t* __restrict__ g,
+                 const bf16_t* __restrict__ dout, const bf16_t* __restrict__ out, const float* __restrict__ lse,
+                 float* __restrict__ dg, bf16_t* __restrict__ qtb, bf16_t* __restrict__ dob, float* __restrict__ stb,
+                 int n_q, int Hq, long q0, long qb0, int nqb, float eps, float qscale) {
+  const long item = (long)blockIdx.x * 64 + (threadIdx.x >> 2);  // (b, padded token, head), grid covers them exactly
+  const int lq = threadIdx.x & 3;
+  const int h = (int)(item % Hq);
+  const long bp = item / Hq;
+  const long ptok = bp % ((long)nqb * 64);  // padded token of the call's query blocks
+  const long b = bp / ((long)nqb * 64);
+  const long prow = (b * Hq + h) * nqb * 64 + ptok;  // row of the head-major padded buffers
+  const long t = qb0 * 64 + ptok - q0;
+  const bool ok = t < n_q;
+  const long base = ((b * n_q + (ok ? t : 0)) * Hq + h) * D;
+  float x[4][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (ok) u = *reinterpret_cast<const uint4*>(q + base + 32 * ks + 8 * lq);
+    unpack8(u, x[ks]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
+  }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  const float inv = qscale * __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int col = 32 * ks + 8 * lq;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[ks][e] * inv * (qw ? qw[col + e] : 1.0f);
+    *reinterpret_cast<uint4*>(qtb + prow * D + col) = pack8(y);
+    float gg[8], dd[8], oo[8], dO[8];
+    uint4 ug = make_uint4(0, 0, 0, 0), ud = ug, uo = ug;
+    if (ok) {
+      ug = *reinterpret_cast<const uint4*>(g + base + col);
+      ud = *reinterpret_cast<const uint4*>(dout + base + col);
+      uo = *reinterpret_cast<const uint4*>(out + base + col);
+    }
+    unpack8(ug, gg);
+    unpack8(ud, dd);
+    unpack8(uo, oo);
+    f32x4 d0, d1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sg = fast_sigmoid(gg[e]);
+      dO[e] = dd[e] * sg;
+      const float dge = dd[e] * oo[e] * (1.0f - sg);
+      if (e < 4) d0[e] = dge; else d1[e - 4] = dge;
+      dsum = fmaf(dd[e], oo[e], dsum);
+    }
+    *reinterpret_cast<uint4*>(dob + prow * D + col) = pack8(dO);
+    if (ok) {
+      *reinterpret_cast<f32x4*>(dg + base + col) = d0;
+      *reinterpret_cast<f32x4*>(dg + base + col + 4) = d1;
+    }
+  }
+  dsum += __shfl_xor(dsum, 1, 64);
+  dsum += __shfl_xor(dsum, 2, 64);
+  if (lq == 0)
+    *reinterpret_cast<float2*>(stb + prow * 4) = make_float2(ok ? lse[(b * n_q + t) * Hq + h] : INFINITY, ok ? dsum : 0.f);
+}
+
 // ---- 2. dq: per selected block S - lse2 (log2 units), P, dP = dO V^T, dS = P (dP - D),
 // dq^T += K^T dS^T; then dq = RMSNorm^T (scale dq^) and the norm-weight partial sums.
 __global__ void __launch_bounds__(SB_NT)
@@ -764,8 +837,8 @@ size_t kv_norm_backward_workspace(const sala_sparse_desc& d) {
 
 hipError_t launch_sparse_attn_backward(const sala_sparse_desc& d, const void* q, const float* qw, const void* k_cache,
                                        const void* v_cache, const void* g, const int32_t* sel, const void* dout,
-                                       float* dq, float* dk_cache, float* dv_cache, float* dg, float* dqw, void* ws,
-                                       hipStream_t st) {
+                                       const void* out, const float* lse, float* dq, float* dk_cache, float* dv_cache,
+                                       float* dg, float* dqw, void* ws, hipStream_t st) {
   const SparseGeom gm = sparse_geom(d);
   const SbwdPlan p = sbwd_plan(d);
   char* w = static_cast<char*>(ws);
@@ -780,9 +853,16 @@ hipError_t launch_sparse_attn_backward(const sala_sparse_desc& d, const void* q,
   const float qscale = gm.scale * 1.4426950408889634f;
   const bf16_t *qb = (const bf16_t*)q, *kb = (const bf16_t*)k_cache, *vb = (const bf16_t*)v_cache;
 
-  hipLaunchKernelGGL(sbwd_stats_kernel, dim3((unsigned)p.nwg), dim3(SB_NT), 0, st, qb, qw, kb, vb, (const bf16_t*)g,
-                     sel, (const bf16_t*)dout, dg, qtb, dob, stb, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0,
-                     (long)gm.qb0, (int)p.nqb, (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, qscale);
+  if (out && lse) {
+    const long nprow = (long)d.batch * d.n_heads * p.nqb * 64;
+    hipLaunchKernelGGL(sbwd_prep_kernel, dim3((unsigned)(nprow / 64)), dim3(256), 0, st, qb, qw, (const bf16_t*)g,
+                       (const bf16_t*)dout, (const bf16_t*)out, lse, dg, qtb, dob, stb, d.n_q, d.n_heads,
+                       (long)gm.q0, (long)gm.qb0, (int)p.nqb, d.norm_eps, qscale);
+  } else {
+    hipLaunchKernelGGL(sbwd_stats_kernel, dim3((unsigned)p.nwg), dim3(SB_NT), 0, st, qb, qw, kb, vb, (const bf16_t*)g,
+                       sel, (const bf16_t*)dout, dg, qtb, dob, stb, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0,
+                       (long)gm.qb0, (int)p.nqb, (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, qscale);
+  }
   hipLaunchKernelGGL(sbwd_dq_kernel, dim3((unsigned)p.nwg), dim3(SB_NT), 0, st, qb, qw, kb, vb, sel, qtb, dob, stb,
                      dq, wpart, d.n_q, d.n_heads, d.n_kv_heads, (long)gm.q0, (long)gm.qb0, (int)p.nqb, (long)d.kv_len,
                      (long)d.kv_capacity, d.topk, d.norm_eps, gm.scale);

@@ -60,12 +60,12 @@ def lib():
         L.sala_linear_prefill.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 10 + [ctypes.c_size_t, _VP]
         L.sala_linear_decode_step.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 9
         L.sala_linear_backward.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 17 + [ctypes.c_size_t, _VP]
-        L.sala_sparse_attn_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 13 + [ctypes.c_size_t, _VP]
+        L.sala_sparse_attn_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 15 + [ctypes.c_size_t, _VP]
         L.sala_kv_norm_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 6 + [ctypes.c_size_t, _VP]
         L.sala_kv_append.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7
         L.sala_kv_pool.argtypes = [ctypes.POINTER(SparseDesc), _VP, _VP, ctypes.c_int64, ctypes.c_int64, _VP]
         L.sala_block_select.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 5 + [ctypes.c_size_t, _VP]
-        L.sala_sparse_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 8 + [ctypes.c_size_t, _VP]
+        L.sala_sparse_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 9 + [ctypes.c_size_t, _VP]
         L.sala_dense_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7 + [ctypes.c_size_t, _VP]
         L.sala_sparse_layer_uses_dense.argtypes = [ctypes.POINTER(SparseDesc)]
         L.sala_linear_prefill_varlen.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 12 + [ctypes.c_size_t, _VP]
@@ -272,8 +272,9 @@ def block_select(q, k_pool, kv_len, kv_capacity, *, n_kv_heads, topk=64, n_local
 
 
 def sparse_attn(q, k_cache, v_cache, g, sel, kv_len, *, topk=None, n_local=2, eps=1e-6, scale=0.0,
-                q_norm_w=None, out=None, workspace=None, stream=None):
-    """q, g [B, n_q, Hq, d]; caches [B, Hkv, cap, d]; sel from block_select. Returns out."""
+                q_norm_w=None, out=None, lse=None, workspace=None, stream=None):
+    """q, g [B, n_q, Hq, d]; caches [B, Hkv, cap, d]; sel from block_select. Returns out.
+    lse: optional [B, n_q, Hq] f32 tensor that receives each row's log2-sum-exp2 (bf16 prefill)."""
     for n, t in (("q", q), ("g", g), ("k_cache", k_cache), ("v_cache", v_cache)):
         _check(t, n, q.dtype)
     _check(sel, "sel", torch.int32)
@@ -285,19 +286,23 @@ def sparse_attn(q, k_cache, v_cache, g, sel, kv_len, *, topk=None, n_local=2, ep
     if out is None:
         out = torch.empty_like(q)
     ws, ws_bytes = _workspace(OP_SPARSE_ATTN, desc, q.device, workspace)
+    _check(lse, "lse", torch.float32)
     _call(lib().sala_sparse_attn, ctypes.byref(desc), _ptr(q), _ptr(q_norm_w), _ptr(k_cache),
-          _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(out), _ptr(ws), ws_bytes, _stream(stream),
+          _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream),
           what="sparse_attn")
     return out
 
 
 def sparse_attn_backward(q, k_cache, v_cache, g, sel, kv_len, dout, *, topk=None, n_local=2, eps=1e-6,
-                         scale=0.0, q_norm_w=None, need_norm_w_grad=False, workspace=None, stream=None):
+                         scale=0.0, q_norm_w=None, need_norm_w_grad=False, out=None, lse=None, workspace=None,
+                         stream=None):
     """Gradients of sparse_attn (bf16, prefill, fixed selection). Returns a dict with dq, dg
     [B, n_q, Hq, d], dk_cache, dv_cache [B, Hkv, cap, d] (all f32) and dq_norm_w [d] f32 when
-    need_norm_w_grad (else None)."""
-    for n, t in (("q", q), ("g", g), ("k_cache", k_cache), ("v_cache", v_cache), ("dout", dout)):
+    need_norm_w_grad (else None). out, lse: the forward's output and lse (both or neither);
+    given, the forward is not rerun."""
+    for n, t in (("q", q), ("g", g), ("k_cache", k_cache), ("v_cache", v_cache), ("dout", dout), ("out", out)):
         _check(t, n, torch.bfloat16)
+    _check(lse, "lse", torch.float32)
     _check(sel, "sel", torch.int32)
     B, nq, Hq, d = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
@@ -310,7 +315,7 @@ def sparse_attn_backward(q, k_cache, v_cache, g, sel, kv_len, dout, *, topk=None
              dq_norm_w=torch.empty(d, **f32) if need_norm_w_grad else None)
     ws, ws_bytes = _workspace(OP_SPARSE_ATTN_BACKWARD, desc, q.device, workspace)
     _call(lib().sala_sparse_attn_backward, ctypes.byref(desc), _ptr(q), _ptr(q_norm_w), _ptr(k_cache),
-          _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(dout), _ptr(r["dq"]), _ptr(r["dk_cache"]),
+          _ptr(v_cache), _ptr(g), _ptr(sel), _ptr(dout), _ptr(out), _ptr(lse), _ptr(r["dq"]), _ptr(r["dk_cache"]),
           _ptr(r["dv_cache"]), _ptr(r["dg"]), _ptr(r["dq_norm_w"]), _ptr(ws), ws_bytes, _stream(stream),
           what="sparse_attn_backward")
     return r

@@ -207,10 +207,13 @@ sala_status sala_block_select(const sala_sparse_desc* desc, const void* q, const
  * where q^ = RMSNorm(q) * q_norm_w and the cache holds already-normalised keys. The bf16 path
  * uses MFMA (bf16 operands, fp32 accumulation and fp32 online softmax).
  * q, gate, out: [B, n_q, Hq, d]; caches as in sala_kv_append; sel as from sala_block_select.
+ * lse: NULL, or [B, n_q, Hq] float receiving each row's log2-sum-exp2 of its scaled scores,
+ *   log2 sum_s exp2(scale * log2(e) * q^ . k_cache[s]) (the state a backward pass can reuse,
+ *   see sala_sparse_attn_backward); bf16 prefill (n_q > 1) only, else SALA_ERR_UNSUPPORTED.
  * Workspace: sala_workspace_bytes(SALA_OP_SPARSE_ATTN, desc). */
 sala_status sala_sparse_attn(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
                              const void* k_cache, const void* v_cache, const void* gate,
-                             const int32_t* sel, void* out, void* workspace,
+                             const int32_t* sel, void* out, float* lse, void* workspace,
                              size_t workspace_bytes, void* stream);
 
 /* Dense mode of the sparse layer ("MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模" §2.1: the
@@ -232,16 +235,18 @@ sala_status sala_dense_attn(const sala_sparse_desc* desc, const void* q, const f
  *     the cache contents (the normalised keys k^ and the values); every row is written, 0 for
  *     rows no query attends;
  *   dq_norm_w: [d] float or NULL to skip (computed as if all ones when q_norm_w is NULL).
- * The softmax statistics are recomputed (the forward keeps none). Products run on MFMA with bf16
+ * out, lse: the forward call's out and lse (both, or both NULL). Given, the softmax statistics
+ * come from them (lse as saved; D = rowsum(dout * out)); NULL, they are recomputed by rerunning
+ * the forward. Products run on MFMA with bf16
  * operands (q^ scale log2 e, dO = dout sigmoid(gate), P and dS) and fp32 accumulation. The
  * key/value gradients are accumulated key-block by key-block over the query blocks that chose
  * each block, in a fixed order: the result is deterministic. Nothing may alias.
  * Workspace: sala_workspace_bytes(SALA_OP_SPARSE_ATTN_BACKWARD, desc) bytes. */
 sala_status sala_sparse_attn_backward(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
                                       const void* k_cache, const void* v_cache, const void* gate,
-                                      const int32_t* sel, const void* dout, float* dq, float* dk_cache,
-                                      float* dv_cache, float* dg, float* dq_norm_w, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+                                      const int32_t* sel, const void* dout, const void* out, const float* lse,
+                                      float* dq, float* dk_cache, float* dv_cache, float* dg, float* dq_norm_w,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward of the key normalisation sala_kv_append applies to the n_q appended tokens (k^ =
  * RMSNorm(k_new) * k_norm_w, written at cache positions [kv_len - n_q, kv_len)). dk_cache is the

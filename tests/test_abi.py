@@ -115,7 +115,7 @@ def test_sparse_rejects(kw, expect):
     d = _sp(**kw)
     assert L.sala_kv_append(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == expect
     assert L.sala_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == expect
-    assert L.sala_sparse_attn(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+    assert L.sala_sparse_attn(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
                               None) == expect
     assert L.sala_workspace_bytes(S.OP_BLOCK_SELECT, ctypes.byref(d)) == ctypes.c_size_t(-1).value
 
@@ -133,7 +133,7 @@ def test_sparse_null_workspace_and_pool_range():
     assert L.sala_kv_pool(ctypes.byref(d), FAKE, FAKE, 2, 1, None) == 2
     assert L.sala_kv_pool(ctypes.byref(d), None, FAKE, 0, 1, None) == 1
     dd = _sp(n_q=1, kv_len=1000, kv_capacity=1024, n_heads=64, n_kv_heads=2)  # bf16 decode, group 32
-    assert L.sala_sparse_attn(ctypes.byref(dd), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+    assert L.sala_sparse_attn(ctypes.byref(dd), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
                               None) == 3
     assert S.workspace_bytes(S.OP_SPARSE_ATTN, _sp(n_q=1, kv_len=1000, kv_capacity=1024)) > 0
 
@@ -195,16 +195,22 @@ def test_sparse_backward_arguments():
                       kv_len=128, kv_capacity=128, topk=3, n_local=2)
     need = S.workspace_bytes(S.OP_SPARSE_ATTN_BACKWARD, d)
     assert need > 0
-    # q qw k v gate sel dout | dq dk dv dg dqw
-    args = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None]
+    # q qw k v gate sel dout | out lse | dq dk dv dg dqw
+    args = [FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None]
     assert L.sala_sparse_attn_backward(ctypes.byref(d), *args, FAKE, need - 1, None) == 4
     assert L.sala_sparse_attn_backward(ctypes.byref(d), *args, None, need, None) == 4
     bad = list(args)
     bad[5] = None  # sel
     assert L.sala_sparse_attn_backward(ctypes.byref(d), *bad, FAKE, need, None) == 1
+    half = list(args)
+    half[7] = FAKE  # the forward's out without its lse
+    assert L.sala_sparse_attn_backward(ctypes.byref(d), *half, FAKE, need, None) == 1
     dec = S.sparse_desc(batch=1, n_q=1, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
                         kv_len=128, kv_capacity=128, topk=3, n_local=2)
     assert L.sala_sparse_attn_backward(ctypes.byref(dec), *args, FAKE, need, None) == 3  # decode: not built
+    # the forward's lse output: bf16 prefill only
+    assert L.sala_sparse_attn(ctypes.byref(dec), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                              None) == 3
     f32 = S.sparse_desc(batch=1, n_q=128, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.float32,
                         kv_len=128, kv_capacity=128, topk=3, n_local=2)
     assert L.sala_sparse_attn_backward(ctypes.byref(f32), *args, FAKE, need, None) == 3

@@ -154,3 +154,45 @@ def test_sparse_attn_backward_repeatable(S):
     torch.cuda.synchronize()
     for n in ("dq", "dg", "dk_cache", "dv_cache"):
         assert torch.equal(a[n], b[n]), n
+
+
+def test_sparse_attn_backward_from_saved_forward(S):
+    """The backward given the forward's out and lse (no forward rerun) against the oracle and the
+    recomputing backward; the forward's lse against the log2-sum-exp2 of the oracle's scaled
+    scores over the selected keys (scipy)."""
+    import torch
+    from scipy.special import logsumexp
+
+    B, kv_len, n_q, Hq, Hkv, topk = 1, 2150, 2150, 4, 2, 6
+    c = _sparse_setup(S, 91, B, kv_len, n_q, Hq, Hkv, topk, True)
+    g = dev(c["g"], "bf16")
+    lse = torch.empty((B, n_q, Hq), dtype=torch.float32, device="cuda")
+    out = S.sparse_attn(c["qd"], c["kc"], c["vc"], g, c["sel"], kv_len, q_norm_w=c["wq"], lse=lse)
+    saved = S.sparse_attn_backward(c["qd"], c["kc"], c["vc"], g, c["sel"], kv_len, dev(c["dout"], "bf16"),
+                                   topk=topk, q_norm_w=c["wq"], need_norm_w_grad=True, out=out, lse=lse)
+    rerun = S.sparse_attn_backward(c["qd"], c["kc"], c["vc"], g, c["sel"], kv_len, dev(c["dout"], "bf16"),
+                                   topk=topk, q_norm_w=c["wq"], need_norm_w_grad=True)
+    ref = G.sparse_attention_grads(c["q"], c["k_hat"], c["v"], c["g"], c["sel_full"], c["dout"], q_norm_w=c["qw"],
+                                   q_positions=np.arange(c["p0"], kv_len))
+    errs = {}
+    for n, rn in (("dq", "dq"), ("dg", "dg"), ("dq_norm_w", "dq_norm_w")):
+        errs[n] = assert_rel(host(saved[n]), ref[rn], TOL, n)
+        assert_rel(host(saved[n]), host(rerun[n]), TOL, n + " vs rerun")
+    dk, dv = host(saved["dk_cache"]), host(saved["dv_cache"])
+    errs["dk_cache"] = assert_rel(dk[:, :, :kv_len].transpose(0, 2, 1, 3), ref["dk_hat"], TOL, "dk_cache")
+    errs["dv_cache"] = assert_rel(dv[:, :, :kv_len].transpose(0, 2, 1, 3), ref["dv"], TOL, "dv_cache")
+    print("  relative errors:", {n: f"{e:.2e}" for n, e in errs.items()}, flush=True)
+    # lse of a sample of rows: log2 sum over the selected causal keys of exp(scale * q^ . k^)
+    import oracle as O
+    qh = O.qk_norm(c["q"], c["qw"])
+    got = host(lse)
+    for t in (0, 63, 64, 1000, 2149):
+        i = t // 64
+        for h in range(Hq):
+            gk = h // (Hq // Hkv)
+            keys = np.concatenate([np.arange(j * 64, min(kv_len, (j + 1) * 64)) for j in c["sel_full"][0, gk, i]
+                                   if j >= 0])
+            keys = keys[keys <= t]
+            s = (c["k_hat"][0, keys, gk] @ qh[0, t, h]) / np.sqrt(128)
+            want = logsumexp(s) / np.log(2)
+            assert abs(got[0, t, h] - want) <= 2e-2 * max(1.0, abs(want)), (t, h, got[0, t, h], want)
