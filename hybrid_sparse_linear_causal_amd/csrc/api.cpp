@@ -93,6 +93,22 @@ sala_status check_linear_varlen(const sala_linear_desc* d, const int32_t* cu, co
   return check_varlen(d->batch, d->seq_len, cu, pos0, -1);
 }
 
+// the decode step of the sparse layer with per-sequence cache lengths: bf16, d = 128, one query
+// token per sequence, group <= 16, contexts within the two-level selection range
+sala_status check_sparse_decode_at(const sala_sparse_desc* d) {
+  const sala_status s = check_sparse(d);
+  if (s != SALA_OK) return s;
+  if (d->n_q != 1) return SALA_ERR_INVALID;
+  if (d->dtype != SALA_BF16 || d->head_dim != 128 || d->n_heads / d->n_kv_heads > 16) return SALA_ERR_UNSUPPORTED;
+  if (sala::block_select_decode_at_workspace(*d) == SIZE_MAX) return SALA_ERR_UNSUPPORTED;
+  return SALA_OK;
+}
+
+size_t sparse_decode_step_workspace(const sala_sparse_desc& d) {
+  const size_t a = (sala::block_select_decode_at_workspace(d) + 255) & ~(size_t)255;
+  return a + sala::sparse_decode_at_workspace(d);
+}
+
 bool all_aligned(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if (p && !aligned16(p)) return false;
@@ -152,6 +168,11 @@ size_t sala_workspace_bytes(int op, const void* desc) {
       if (check_sparse(d, false) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128) return SIZE_MAX;
       return sala::kv_norm_backward_workspace(*d);
     }
+    case SALA_OP_SPARSE_DECODE_STEP: {
+      const sala_sparse_desc* d = static_cast<const sala_sparse_desc*>(desc);
+      if (check_sparse_decode_at(d) != SALA_OK) return SIZE_MAX;
+      return sparse_decode_step_workspace(*d);
+    }
     case SALA_OP_LINEAR_BACKWARD: {
       const sala_linear_desc* d = static_cast<const sala_linear_desc*>(desc);
       if (check_linear(d) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128) return SIZE_MAX;
@@ -207,8 +228,47 @@ sala_status sala_linear_decode_step(const sala_linear_desc* desc, const void* q,
   if (desc->seq_len != 1) return SALA_ERR_INVALID;
   if (!q || !k || !v || !gate || !state || !out) return SALA_ERR_NULL;
   if (!all_aligned({q, k, v, gate, out, q_norm_w, k_norm_w, state})) return SALA_ERR_INVALID;
-  return hip_status(sala::launch_linear_decode(*desc, q, k, v, gate, q_norm_w, k_norm_w, state, out,
+  return hip_status(sala::launch_linear_decode(*desc, q, k, v, gate, q_norm_w, k_norm_w, state, out, nullptr,
                                                (hipStream_t)stream));
+}
+
+sala_status sala_linear_decode_step_at(const sala_linear_desc* desc, const int64_t* pos, const void* q,
+                                       const void* k, const void* v, const void* gate, const float* q_norm_w,
+                                       const float* k_norm_w, float* state, void* out, void* stream) {
+  sala_status s = check_linear(desc);
+  if (s != SALA_OK) return s;
+  if (desc->seq_len != 1) return SALA_ERR_INVALID;
+  if (!pos || !q || !k || !v || !gate || !state || !out) return SALA_ERR_NULL;
+  if (!all_aligned({q, k, v, gate, out, q_norm_w, k_norm_w, state}) || (reinterpret_cast<uintptr_t>(pos) & 7u))
+    return SALA_ERR_INVALID;
+  return hip_status(sala::launch_linear_decode(*desc, q, k, v, gate, q_norm_w, k_norm_w, state, out, pos,
+                                               (hipStream_t)stream));
+}
+
+sala_status sala_sparse_decode_step(const sala_sparse_desc* desc, const int64_t* kv_lens, const void* q,
+                                    const float* q_norm_w, const void* k_new, const void* v_new,
+                                    const float* k_norm_w, const void* gate, void* k_cache, void* v_cache,
+                                    float* k_pool, int32_t* sel, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  const sala_status s = check_sparse_decode_at(desc);
+  if (s != SALA_OK) return s;
+  if (!kv_lens || !q || !k_new || !v_new || !gate || !k_cache || !v_cache || !k_pool || !sel || !out)
+    return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_new, v_new, k_norm_w, gate, k_cache, v_cache, k_pool, sel, out, workspace}) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 7u))
+    return SALA_ERR_INVALID;
+  const size_t need = sparse_decode_step_workspace(*desc);
+  if (!workspace || workspace_bytes < need) return SALA_ERR_WORKSPACE;
+  const sala_sparse_desc& d = *desc;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e = sala::launch_kv_append(d, k_new, v_new, k_norm_w, k_cache, v_cache, k_pool, st, kv_lens);
+  if (e == hipSuccess) e = sala::launch_block_select_decode_at(d, kv_lens, q, q_norm_w, k_pool, sel, workspace, st);
+  if (e == hipSuccess) {
+    const size_t a = (sala::block_select_decode_at_workspace(d) + 255) & ~(size_t)255;
+    e = sala::launch_sparse_decode_at(d, kv_lens, q, q_norm_w, k_cache, v_cache, gate, sel, out,
+                                      static_cast<char*>(workspace) + a, st);
+  }
+  return hip_status(e);
 }
 
 sala_status sala_kv_append(const sala_sparse_desc* desc, const void* k_new, const void* v_new,

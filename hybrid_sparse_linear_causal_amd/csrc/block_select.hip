@@ -384,13 +384,24 @@ __device__ __forceinline__ void radix_threshold(const uint32_t* keys, int n, int
   need = remaining;
 }
 
+// the candidate count of sequence b when sequences sit at their own cache lengths kv_lens[b]
+// (clamped to [1, kv_max]): blocks 1 .. i - n_local of its query block i
+__device__ __forceinline__ long decode_candidates(const int64_t* kv_lens, int b, long kv_max, int n_local, long* i) {
+  long kv = kv_lens[b];
+  kv = kv < 1 ? 1 : (kv > kv_max ? kv_max : kv);
+  *i = (kv - 1) / 64;
+  return *i - n_local > 0 ? *i - n_local : 0;
+}
+
 // Level 1: grid (B*Hkv, nsl), NT threads. Slice s holds candidates j = j0 .. j0+n-1 with
 // j0 = 1 + s*DSL, n = min(DSL, nc - j0 + 1): scores q~ . k_pool[j] (8 lanes per pooled row),
-// then the slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered).
+// then the slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered). With
+// kv_lens, nc is each sequence's own count (at most the nc given).
 template <int DD>
 __global__ void __launch_bounds__(NT)
 decode_slice_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
-                    uint64_t* __restrict__ cand, long nblk_cap, long nc, int R) {
+                    uint64_t* __restrict__ cand, long nblk_cap, long nc, int R,
+                    const int64_t* __restrict__ kv_lens, int Hkv, long kv_max, int n_local) {
   constexpr int LPB = 8, FPL = DD / LPB, RPI = NT / LPB;  // rows per iteration
   __shared__ uint32_t keys[DSL];
   __shared__ int hist[256];
@@ -399,8 +410,13 @@ decode_slice_kernel(const float* __restrict__ qt, const float* __restrict__ kpoo
   __shared__ int s_need;
   const int bg = blockIdx.x, sl = blockIdx.y, nsl = gridDim.y;
   const int tid = threadIdx.x, sub = tid / LPB, part = tid % LPB;
+  if (kv_lens) {
+    long i;
+    const long ncb = decode_candidates(kv_lens, bg / Hkv, kv_max, n_local, &i);
+    nc = ncb < nc ? ncb : nc;
+  }
   const long j0 = 1 + (long)sl * DSL;
-  const int n = (int)min((long)DSL, nc - j0 + 1);
+  const int n = (int)max(0L, min((long)DSL, nc - j0 + 1));
   float qv[FPL];
 #pragma unroll
   for (int e = 0; e < FPL; ++e) qv[e] = qt[(long)bg * DD + part * FPL + e];
@@ -467,7 +483,8 @@ __device__ __forceinline__ void idx2key(uint32_t* keys, const uint32_t* idx, int
 template <int CAPB>
 __global__ void __launch_bounds__(NT)
 decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel, int nsl, int R,
-                    long i, int n_local, int topk, long nc) {
+                    long i, int n_local, int topk, long nc, const int64_t* __restrict__ kv_lens, int Hkv,
+                    long kv_max) {
   __shared__ uint32_t keys[CAPB];
   __shared__ uint32_t idx[CAPB];
   __shared__ uint32_t bits[DBITS];
@@ -477,6 +494,10 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   __shared__ int s_need;
   const int bg = blockIdx.x, tid = threadIdx.x;
   const int n = nsl * R;
+  if (kv_lens) {  // this sequence's query block and candidate count (at most the nc given)
+    const long ncb = decode_candidates(kv_lens, bg / Hkv, kv_max, n_local, &i);
+    nc = ncb < nc ? ncb : nc;
+  }
   int valid = 0;
   for (int t = tid; t < n; t += NT) {
     const uint64_t c = cand[(long)bg * n + t];
@@ -600,12 +621,12 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
     uint64_t* cand = reinterpret_cast<uint64_t*>(sc);
     if (d.head_dim == 128)
       hipLaunchKernelGGL(decode_slice_kernel<128>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand,
-                         (long)g.nblk_cap, nc, R);
+                         (long)g.nblk_cap, nc, R, nullptr, d.n_kv_heads, (long)d.kv_len, d.n_local);
     else
       hipLaunchKernelGGL(decode_slice_kernel<64>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand,
-                         (long)g.nblk_cap, nc, R);
+                         (long)g.nblk_cap, nc, R, nullptr, d.n_kv_heads, (long)d.kv_len, d.n_local);
     hipLaunchKernelGGL(decode_merge_kernel<DMERGE>, dim3(BG), dim3(NT), 0, st, cand, sel, nsl, R, i_max,
-                       d.n_local, d.topk, nc);
+                       d.n_local, d.topk, nc, nullptr, d.n_kv_heads, (long)d.kv_len);
     return hipGetLastError();
   }
   if (i_max - d.n_local >= 1) {
@@ -636,6 +657,57 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
   else
     hipLaunchKernelGGL((select_kernel<256, 4096>), dim3((unsigned)(BG * g.nqb)), dim3(256), 0, st, sc, sel,
                        (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
+  return hipGetLastError();
+}
+
+}  // namespace sala
+
+namespace sala {
+
+// ---- decode selection with each sequence at its own cache length (device array kv_lens,
+// clamped to [1, desc kv_len]): always the two-level path, sized for the longest context.
+// Returns false if that context is beyond the two-level range.
+static bool decode_at_plan(const sala_sparse_desc& d, long* nc, int* nsl, int* R) {
+  const long i_max = (d.kv_len - 1) / 64;
+  *nc = i_max - d.n_local > 0 ? i_max - d.n_local : 0;
+  *R = i_max >= d.n_local ? d.topk - d.n_local - 1 : d.topk - (int)(i_max + 1);
+  *nsl = (int)((*nc + DSL - 1) / DSL);
+  if (*nsl < 1) *nsl = 1;
+  if (*R < 1) *R = 1;
+  return *nsl <= DNSL_MAX && (long)*nsl * *R <= DMERGE && *nc / 32 + 1 <= DBITS;
+}
+
+size_t block_select_decode_at_workspace(const sala_sparse_desc& d) {
+  long nc; int nsl, R;
+  if (!decode_at_plan(d, &nc, &nsl, &R)) return SIZE_MAX;
+  const size_t bg = (size_t)d.batch * d.n_kv_heads;
+  const size_t qt = bg * d.head_dim * sizeof(float);
+  return ((qt + 255) & ~(size_t)255) + bg * (size_t)nsl * R * sizeof(uint64_t);
+}
+
+hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_t* kv_lens, const void* q,
+                                         const float* qw, const float* k_pool, int32_t* sel, void* ws,
+                                         hipStream_t st) {
+  long nc; int nsl, R;
+  if (!decode_at_plan(d, &nc, &nsl, &R)) return hipErrorInvalidValue;
+  const int BG = d.batch * d.n_kv_heads;
+  float* qt = static_cast<float*>(ws);
+  const size_t qt_bytes = (size_t)BG * d.head_dim * sizeof(float);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + ((qt_bytes + 255) & ~(size_t)255));
+  const long nblk_cap = d.kv_capacity / 64;
+  if (d.head_dim == 128) {
+    hipLaunchKernelGGL((qtilde_kernel<bf16_t, 128>), dim3(d.batch, 1), dim3(NT), 0, st, (const bf16_t*)q, qw, qt, 1,
+                       d.n_heads, d.n_kv_heads, (long)(d.kv_len - 1), d.norm_eps);
+    hipLaunchKernelGGL(decode_slice_kernel<128>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand, nblk_cap, nc, R,
+                       kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local);
+  } else {
+    hipLaunchKernelGGL((qtilde_kernel<bf16_t, 64>), dim3(d.batch, 1), dim3(NT), 0, st, (const bf16_t*)q, qw, qt, 1,
+                       d.n_heads, d.n_kv_heads, (long)(d.kv_len - 1), d.norm_eps);
+    hipLaunchKernelGGL(decode_slice_kernel<64>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand, nblk_cap, nc, R,
+                       kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local);
+  }
+  hipLaunchKernelGGL(decode_merge_kernel<DMERGE>, dim3(BG), dim3(NT), 0, st, cand, sel, nsl, R,
+                     (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens, d.n_kv_heads, (long)d.kv_len);
   return hipGetLastError();
 }
 

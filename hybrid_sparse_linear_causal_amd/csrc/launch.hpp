@@ -55,7 +55,7 @@ hipError_t launch_linear_prefill_varlen(const sala_linear_desc& d, const int32_t
                                         float* state_out, void* out, void* ws, hipStream_t st);
 hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const void* k,
                                 const void* v, const void* g, const float* qw, const float* kw,
-                                float* state, void* out, hipStream_t st);
+                                float* state, void* out, const int64_t* pos_b, hipStream_t st);
 size_t linear_backward_workspace(const sala_linear_desc& d);
 hipError_t launch_linear_backward(const sala_linear_desc& d, const void* q, const void* k, const void* v,
                                   const void* g, const float* qw, const float* kw, const float* state_in,
@@ -72,15 +72,25 @@ struct SparseGeom {
 };
 SparseGeom sparse_geom(const sala_sparse_desc& d);
 
+// kv_lens (device, [B], one appended token per sequence): per-sequence cache lengths
 hipError_t launch_kv_append(const sala_sparse_desc& d, const void* k_new, const void* v_new,
                             const float* kw, void* k_cache, void* v_cache, float* k_pool,
-                            hipStream_t st);
+                            hipStream_t st, const int64_t* kv_lens = nullptr);
 hipError_t launch_kv_pool(const sala_sparse_desc& d, const void* k_cache, float* k_pool,
                           int64_t blk_begin, int64_t blk_end, hipStream_t st);
 size_t block_select_workspace(const sala_sparse_desc& d);
 hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
                                const float* k_pool, int32_t* sel, void* ws, hipStream_t st);
 size_t sparse_attn_workspace(const sala_sparse_desc& d);
+// decode with each sequence at its own cache length (kv_lens: device [B] int64)
+size_t block_select_decode_at_workspace(const sala_sparse_desc& d);  // SIZE_MAX: context too long
+hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_t* kv_lens, const void* q,
+                                         const float* qw, const float* k_pool, int32_t* sel, void* ws,
+                                         hipStream_t st);
+size_t sparse_decode_at_workspace(const sala_sparse_desc& d);
+hipError_t launch_sparse_decode_at(const sala_sparse_desc& d, const int64_t* kv_lens, const void* q, const float* qw,
+                                   const void* k_cache, const void* v_cache, const void* g, const int32_t* sel,
+                                   void* out, void* ws, hipStream_t st);
 // packed variable-length batches (desc.batch = sequences, cu_seqlens / pos0 on the host)
 int64_t varlen_query_blocks(int nseq, const int32_t* cu_seqlens);
 size_t block_select_varlen_workspace(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0);

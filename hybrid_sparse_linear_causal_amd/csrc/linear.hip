@@ -650,11 +650,15 @@ __global__ void __launch_bounds__(256)
 linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                      const T* __restrict__ g, const float* __restrict__ qw,
                      const float* __restrict__ kw, float* __restrict__ state, T* __restrict__ out,
-                     long pos, float eps, RopeFreqs freqs) {
+                     long pos, const int64_t* __restrict__ pos_b, int H, float eps, RopeFreqs freqs) {
   constexpr int NR = DD / 16;  // rows per thread
   __shared__ float sq[DD], sk[DD];
   __shared__ float4 red[16][16];
   const int bh = blockIdx.x;
+  if (pos_b) {  // each sequence at its own position (negative values read as 0)
+    const long pb = pos_b[bh / H];
+    pos = pb > 0 ? pb : 0;
+  }
   const int j = threadIdx.x, r0 = j >> 4, c4 = j & 15;
   const long vec = (long)bh * DD;
   const int col = 64 * blockIdx.y + 4 * c4;
@@ -867,8 +871,8 @@ hipError_t launch_linear_prefill_varlen(const sala_linear_desc& d, const int32_t
 
 hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const void* k,
                                 const void* v, const void* g, const float* qw, const float* kw,
-                                float* state, void* out, hipStream_t st) {
-  const int BH = d.batch * d.n_heads, hd = d.head_dim;
+                                float* state, void* out, const int64_t* pos_b, hipStream_t st) {
+  const int BH = d.batch * d.n_heads, hd = d.head_dim, H = d.n_heads;
   const RopeFreqs fr = make_rope_freqs(hd, d.rope_base);
   const dim3 grid(BH, hd / 64);
   const long pos = (long)d.pos0;
@@ -876,20 +880,20 @@ hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const 
     if (hd == 128)
       hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 128>), grid, dim3(256), 0, st, (const bf16_t*)q,
                          (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, qw, kw, state, (bf16_t*)out,
-                         pos, d.norm_eps, fr);
+                         pos, pos_b, H, d.norm_eps, fr);
     else
       hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 64>), grid, dim3(256), 0, st, (const bf16_t*)q,
                          (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, qw, kw, state, (bf16_t*)out,
-                         pos, d.norm_eps, fr);
+                         pos, pos_b, H, d.norm_eps, fr);
   } else {
     if (hd == 128)
       hipLaunchKernelGGL((linear_decode_kernel<float, 128>), grid, dim3(256), 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (const float*)g, qw, kw, state, (float*)out,
-                         pos, d.norm_eps, fr);
+                         pos, pos_b, H, d.norm_eps, fr);
     else
       hipLaunchKernelGGL((linear_decode_kernel<float, 64>), grid, dim3(256), 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (const float*)g, qw, kw, state, (float*)out,
-                         pos, d.norm_eps, fr);
+                         pos, pos_b, H, d.norm_eps, fr);
   }
   return hipGetLastError();
 }

@@ -254,12 +254,17 @@ __global__ void __launch_bounds__(256)
 sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
                           const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
                           const int32_t* __restrict__ sel, float* __restrict__ part, int Hq,
-                          int Hkv, long kv_len, long cap, int topk, float eps, float qscale) {
+                          int Hkv, long kv_len, long cap, int topk, float eps, float qscale,
+                          const int64_t* __restrict__ kv_lens) {
   __shared__ __align__(16) bf16_t vts[4][D * VS];
   __shared__ float cm[4][16], cl[4][16];
   const int bg = blockIdx.x, split = blockIdx.y;
   const int b = bg / Hkv, gk = bg % Hkv, G = Hq / Hkv;
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
+  if (kv_lens) {  // this sequence's own cache length, clamped to [1, kv_len]
+    const long kb = kv_lens[b];
+    kv_len = kb < 1 ? 1 : (kb > kv_len ? kv_len : kb);
+  }
   const long p = kv_len - 1;
   const long row_base = (long)bg * cap;
   // the selection row (ascending, -1 padded; topk <= 256): lane x holds entries x + 64u
@@ -540,7 +545,8 @@ static hipError_t launch_attn(const sala_sparse_desc& d, const void* q, const fl
     hipLaunchKernelGGL(sparse_decode_bf16_kernel<DENSE>, dim3(d.batch * d.n_kv_heads, DEC_SPLIT), dim3(256), 0,
                        st, (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, sel,
                        part, d.n_heads, d.n_kv_heads, (long)d.kv_len, (long)d.kv_capacity, d.topk,
-                       d.norm_eps, qscale);
+                       d.norm_eps, qscale,
+                       nullptr);
     hipLaunchKernelGGL(sparse_decode_combine_kernel, dim3(d.batch * d.n_heads), dim3(D), 0, st,
                        part, (const bf16_t*)g, (bf16_t*)out, d.n_heads, d.n_kv_heads);
     return hipGetLastError();
@@ -589,6 +595,28 @@ hipError_t launch_sparse_attn_varlen(const sala_sparse_desc& d, const int32_t* c
                      (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, (const bf16_t*)g, sel,
                      (bf16_t*)out, nullptr, d.n_heads, d.n_kv_heads, (long)d.kv_capacity, d.topk, d.norm_eps, qscale,
                      geo);
+  return hipGetLastError();
+}
+
+}  // namespace sala
+
+namespace sala {
+
+size_t sparse_decode_at_workspace(const sala_sparse_desc& d) {
+  return (size_t)d.batch * d.n_kv_heads * DEC_SPLIT * 16 * (D + 2) * sizeof(float);
+}
+
+// decode attention with each sequence at its own cache length (device array kv_lens)
+hipError_t launch_sparse_decode_at(const sala_sparse_desc& d, const int64_t* kv_lens, const void* q, const float* qw,
+                                   const void* k_cache, const void* v_cache, const void* g, const int32_t* sel,
+                                   void* out, void* ws, hipStream_t st) {
+  const float qscale = sparse_geom(d).scale * 1.4426950408889634f;  // exp -> exp2
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL(sparse_decode_bf16_kernel<false>, dim3(d.batch * d.n_kv_heads, DEC_SPLIT), dim3(256), 0, st,
+                     (const bf16_t*)q, qw, (const bf16_t*)k_cache, (const bf16_t*)v_cache, sel, part, d.n_heads,
+                     d.n_kv_heads, (long)d.kv_len, (long)d.kv_capacity, d.topk, d.norm_eps, qscale, kv_lens);
+  hipLaunchKernelGGL(sparse_decode_combine_kernel, dim3(d.batch * d.n_heads), dim3(D), 0, st, part,
+                     (const bf16_t*)g, (bf16_t*)out, d.n_heads, d.n_kv_heads);
   return hipGetLastError();
 }
 

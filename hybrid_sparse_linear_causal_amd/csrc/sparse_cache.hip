@@ -52,16 +52,22 @@ __device__ __forceinline__ void store_row_part<float>(float* p, const float* f) 
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
 }
 
-// grid (B*Hkv, blocks touched by the new tokens); 256 threads.
+// grid (B*Hkv, blocks touched by the new tokens); 256 threads. kv_lens (one token per sequence
+// only): each sequence's own cache length, clamped to [1, kv_len].
 template <typename T, int DD>
 __global__ void __launch_bounds__(256)
 kv_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
                  const float* __restrict__ kw, T* __restrict__ k_cache, T* __restrict__ v_cache,
-                 float* __restrict__ k_pool, int n_q, int Hkv, long kv_len, long cap, float eps) {
+                 float* __restrict__ k_pool, int n_q, int Hkv, long kv_len, long cap, float eps,
+                 const int64_t* __restrict__ kv_lens) {
   using G = RowGeom<T, DD>;
   constexpr int EPL = G::EPL, LPR = G::LPR, RPP = G::RPP;
   __shared__ float psum[RPP][DD];
   const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
+  if (kv_lens) {
+    const long kb = kv_lens[b];
+    kv_len = kb < 1 ? 1 : (kb > kv_len ? kv_len : kb);
+  }
   const long q0 = kv_len - n_q;
   const long blk = q0 / 64 + blockIdx.y;
   const int j = threadIdx.x, r = j / LPR, seg = j % LPR;
@@ -141,14 +147,14 @@ kv_pool_kernel(const T* __restrict__ k_cache, float* __restrict__ k_pool, int Hk
 
 hipError_t launch_kv_append(const sala_sparse_desc& d, const void* k_new, const void* v_new,
                             const float* kw, void* k_cache, void* v_cache, float* k_pool,
-                            hipStream_t st) {
+                            hipStream_t st, const int64_t* kv_lens) {
   const long q0 = d.kv_len - d.n_q;
   const long nblk = (d.kv_len - 1) / 64 - q0 / 64 + 1;
   const dim3 grid(d.batch * d.n_kv_heads, (unsigned)nblk);
 #define SALA_APPEND(T, DD)                                                                        \
   hipLaunchKernelGGL((kv_append_kernel<T, DD>), grid, dim3(256), 0, st, (const T*)k_new,          \
                      (const T*)v_new, kw, (T*)k_cache, (T*)v_cache, k_pool, d.n_q, d.n_kv_heads,  \
-                     (long)d.kv_len, (long)d.kv_capacity, d.norm_eps)
+                     (long)d.kv_len, (long)d.kv_capacity, d.norm_eps, kv_lens)
   if (d.dtype == SALA_BF16) {
     if (d.head_dim == 128) SALA_APPEND(bf16_t, 128); else SALA_APPEND(bf16_t, 64);
   } else {

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_PKG, "libsala.so")
 
 SALA_F32, SALA_BF16 = 0, 1
 OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN, OP_DENSE_ATTN, OP_LINEAR_BACKWARD = 1, 2, 3, 4, 5
-OP_SPARSE_ATTN_BACKWARD, OP_KV_NORM_BACKWARD = 6, 7
+OP_SPARSE_ATTN_BACKWARD, OP_KV_NORM_BACKWARD, OP_SPARSE_DECODE_STEP = 6, 7, 8
 STATUS = {0: "ok", 1: "null pointer", 2: "invalid", 3: "unsupported", 4: "workspace", 5: "hip"}
 
 
@@ -59,6 +59,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.sala_linear_prefill.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 10 + [ctypes.c_size_t, _VP]
         L.sala_linear_decode_step.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 9
+        L.sala_linear_decode_step_at.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 10
+        L.sala_sparse_decode_step.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 13 + [ctypes.c_size_t, _VP]
         L.sala_linear_backward.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 17 + [ctypes.c_size_t, _VP]
         L.sala_sparse_attn_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 15 + [ctypes.c_size_t, _VP]
         L.sala_kv_norm_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 6 + [ctypes.c_size_t, _VP]
@@ -86,7 +88,7 @@ def lib():
                      "sala_block_select", "sala_sparse_attn", "sala_dense_attn",
                      "sala_sparse_layer_uses_dense", "sala_abi_version", "sala_last_hip_error",
                      "sala_linear_prefill_varlen", "sala_kv_append_varlen", "sala_block_select_varlen",
-                     "sala_sparse_attn_varlen"):
+                     "sala_sparse_attn_varlen", "sala_linear_decode_step_at", "sala_sparse_decode_step"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -219,6 +221,48 @@ def linear_decode_step(q, k, v, g, state, pos, *, rope_base=10000.0, eps=1e-6, q
           _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state), _ptr(out), _stream(stream),
           what="linear_decode_step")
     return out
+
+
+def linear_decode_step_at(q, k, v, g, state, pos, *, rope_base=10000.0, eps=1e-6, q_norm_w=None, k_norm_w=None,
+                          out=None, stream=None):
+    """As linear_decode_step with token b at position pos[b] (pos: device int64 tensor [B])."""
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, q.dtype)
+    _check(state, "state", torch.float32)
+    _check(pos, "pos", torch.int64)
+    B, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    desc = LinearDesc(B, 1, H, H, d, _dtype_code(q), 0, float(rope_base), float(eps))
+    _call(lib().sala_linear_decode_step_at, ctypes.byref(desc), _ptr(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+          _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state), _ptr(out), _stream(stream), what="linear_decode_step_at")
+    return out
+
+
+def sparse_decode_step(q, k_new, v_new, g, k_cache, v_cache, k_pool, kv_lens, kv_max, *, topk=64, n_local=2,
+                       eps=1e-6, scale=0.0, q_norm_w=None, k_norm_w=None, sel=None, out=None, workspace=None,
+                       stream=None):
+    """Sparse-layer decode step with sequence b's cache holding kv_lens[b] tokens once its new
+    token is in (kv_lens: device int64 [B], each <= kv_max). q, g [B, Hq, d]; k_new, v_new
+    [B, Hkv, d] bf16. Appends, selects (sel [B, Hkv, topk]) and attends; returns (out, sel)."""
+    for n, t in (("q", q), ("g", g), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                 ("v_cache", v_cache)):
+        _check(t, n, torch.bfloat16)
+    _check(k_pool, "k_pool", torch.float32)
+    _check(kv_lens, "kv_lens", torch.int64)
+    B, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    desc = sparse_desc(batch=B, n_q=1, n_heads=Hq, n_kv_heads=Hkv, head_dim=d, dtype=q.dtype, kv_len=kv_max,
+                       kv_capacity=cap, topk=topk, n_local=n_local, eps=eps, scale=scale)
+    if sel is None:
+        sel = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, ws_bytes = _workspace(OP_SPARSE_DECODE_STEP, desc, q.device, workspace)
+    _call(lib().sala_sparse_decode_step, ctypes.byref(desc), _ptr(kv_lens), _ptr(q), _ptr(q_norm_w), _ptr(k_new),
+          _ptr(v_new), _ptr(k_norm_w), _ptr(g), _ptr(k_cache), _ptr(v_cache), _ptr(k_pool), _ptr(sel), _ptr(out),
+          _ptr(ws), ws_bytes, _stream(stream), what="sparse_decode_step")
+    return out, sel
 
 
 def sparse_desc(*, batch, n_q, n_heads, n_kv_heads, head_dim, dtype, kv_len, kv_capacity, topk=64,

@@ -59,7 +59,8 @@ typedef enum {
   SALA_OP_DENSE_ATTN = 4,
   SALA_OP_LINEAR_BACKWARD = 5,
   SALA_OP_SPARSE_ATTN_BACKWARD = 6,
-  SALA_OP_KV_NORM_BACKWARD = 7
+  SALA_OP_KV_NORM_BACKWARD = 7,
+  SALA_OP_SPARSE_DECODE_STEP = 8
 } sala_op;
 
 /* Linear-attention layer shape.
@@ -184,6 +185,14 @@ sala_status sala_kv_append(const sala_sparse_desc* desc, const void* k_new, cons
 sala_status sala_kv_pool(const sala_sparse_desc* desc, const void* k_cache, float* k_pool,
                          int64_t block_begin, int64_t block_end, void* stream);
 
+/* Linear layer decode step with each sequence at its own position (same pages): as
+ * sala_linear_decode_step, with token b at position pos[b] (pos: DEVICE array [B] int64, read
+ * by the kernel, so a captured graph can replay with updated positions; negative values read as
+ * 0); desc->pos0 is ignored. */
+sala_status sala_linear_decode_step_at(const sala_linear_desc* desc, const int64_t* pos, const void* q,
+                                       const void* k, const void* v, const void* gate, const float* q_norm_w,
+                                       const float* k_norm_w, float* state, void* out, void* stream);
+
 /* Block selection for the sparse layer (same pages; sliding-window and global-anchor patterns
  * from "MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模" §1). For each query block i covered by
  * the call (decode: the block of the single query) and KV group g:
@@ -257,6 +266,23 @@ sala_status sala_sparse_attn_backward(const sala_sparse_desc* desc, const void* 
 sala_status sala_kv_norm_backward(const sala_sparse_desc* desc, const void* k_new, const float* k_norm_w,
                                   const float* dk_cache, float* dk_new, float* dk_norm_w, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Decode step of the sparse layer with each sequence at its own cache length (the pages'
+ * decoding against a cache that grows per sequence; "MiniCPM-SALA：融合稀疏与线性注意力实现高效长上下文建模"
+ * §1 and the sections cited at sala_kv_append / sala_block_select / sala_sparse_attn). One call
+ * runs, for every sequence b with L_b = kv_lens[b] (DEVICE array [B] int64, clamped to
+ * [1, desc->kv_len]): sala_kv_append of its token at position L_b - 1 (pooling the block it
+ * completes), sala_block_select for its query block (L_b - 1) / 64, and sala_sparse_attn
+ * over the cache's first L_b tokens. desc: n_q = 1, kv_len = the largest L_b (sizes the grids;
+ * contexts up to 16,384 candidate blocks, else UNSUPPORTED), bf16, d = 128, at most 16 query
+ * heads per KV head. q, gate, out: [B, Hq, d]; k_new, v_new: [B, Hkv, d]; caches and pool as in
+ * sala_kv_append; sel: [B, Hkv, topk] int32 receives the selection.
+ * Workspace: sala_workspace_bytes(SALA_OP_SPARSE_DECODE_STEP, desc). */
+sala_status sala_sparse_decode_step(const sala_sparse_desc* desc, const int64_t* kv_lens, const void* q,
+                                    const float* q_norm_w, const void* k_new, const void* v_new,
+                                    const float* k_norm_w, const void* gate, void* k_cache, void* v_cache,
+                                    float* k_pool, int32_t* sel, void* out, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /* The switch between the two modes (same section; the pages give no length, so the rule is the
  * one under which both modes give the same result): 1 when every query of the call would

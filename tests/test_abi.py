@@ -269,3 +269,34 @@ def test_varlen_arguments():
     sf = S.sparse_desc(batch=3, n_q=400, n_heads=4, n_kv_heads=2, head_dim=128, dtype=torch.float32, kv_len=0,
                        kv_capacity=512, topk=3, n_local=2)
     assert L.sala_kv_append_varlen(ctypes.byref(sf), *svl.args(), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == 3
+
+
+def test_decode_at_arguments():
+    """Argument errors of the decode calls with per-sequence positions (no device work)."""
+    import torch
+
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    d = S.LinearDesc(4, 1, 2, 2, 128, S.SALA_BF16, 0, 10000.0, 1e-6)
+    args = [FAKE] * 4 + [None, None] + [FAKE, FAKE]  # q k v gate | qw kw | state out
+    assert L.sala_linear_decode_step_at(ctypes.byref(d), None, *args, None) == 1
+    two = S.LinearDesc(4, 2, 2, 2, 128, S.SALA_BF16, 0, 10000.0, 1e-6)
+    assert L.sala_linear_decode_step_at(ctypes.byref(two), FAKE, *args, None) == 2  # one token per sequence
+    sd = S.sparse_desc(batch=3, n_q=1, n_heads=8, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16, kv_len=3000,
+                       kv_capacity=3072, topk=16, n_local=2)
+    need = S.workspace_bytes(S.OP_SPARSE_DECODE_STEP, sd)
+    assert need > 0
+    # q qw k_new v_new kw gate | k_cache v_cache k_pool sel out
+    sargs = [FAKE, None, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert L.sala_sparse_decode_step(ctypes.byref(sd), FAKE, *sargs, FAKE, need - 1, None) == 4
+    assert L.sala_sparse_decode_step(ctypes.byref(sd), None, *sargs, FAKE, need, None) == 1
+    pre = S.sparse_desc(batch=3, n_q=64, n_heads=8, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16, kv_len=3000,
+                        kv_capacity=3072, topk=16, n_local=2)
+    assert L.sala_sparse_decode_step(ctypes.byref(pre), FAKE, *sargs, FAKE, need, None) == 2
+    wide = S.sparse_desc(batch=3, n_q=1, n_heads=64, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16, kv_len=3000,
+                         kv_capacity=3072, topk=16, n_local=2)  # 32 query heads per KV head
+    assert L.sala_sparse_decode_step(ctypes.byref(wide), FAKE, *sargs, FAKE, need, None) == 3
+    huge = S.sparse_desc(batch=1, n_q=1, n_heads=8, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
+                         kv_len=64 * 20000, kv_capacity=64 * 20000, topk=16, n_local=2)  # beyond 16,384 blocks
+    assert S.lib().sala_workspace_bytes(S.OP_SPARSE_DECODE_STEP, ctypes.byref(huge)) == ctypes.c_size_t(-1).value
