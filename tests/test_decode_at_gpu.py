@@ -129,3 +129,76 @@ def test_sparse_decode_step_equals_one_position_path(S):
     torch.cuda.synchronize()
     assert torch.equal(sel_a, sel_b[:, :, 0]) and torch.equal(out_a, out_b[:, 0])
     assert torch.equal(kc, kc2) and torch.equal(kp, kp2)
+
+
+def test_decode_at_graph_replays_with_advancing_positions(S):
+    """One decode step (a linear layer at per-sequence positions, then the sparse layer at
+    per-sequence cache lengths) captured once as a HIP graph. The positions live in device
+    tensors, so the same graph serves later steps: each replay, after the positions and the new
+    tokens are updated in place, must equal the eager step on a copy of the caches and states."""
+    import torch
+
+    from hybrid_sparse_linear_causal_amd.inputs import device_normal
+
+    B, H, Hkv, d, topk = 2, 8, 2, 128, 8
+    lens = [500, 1300]
+    cap = 1408
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    for b, n in enumerate(lens):
+        kc[b, :, :n - 1] = device_normal(61, 5 + b, (Hkv, n - 1, d))
+        vc[b, :, :n - 1] = device_normal(61, 7 + b, (Hkv, n - 1, d))
+        S.kv_pool(kc[b:b + 1], kp[b:b + 1], n - 1, 0, (n - 1) // 64)
+    state = device_normal(62, 4, (B, H, d, d), dtype="f32")
+    lin_in = [torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    q, g = (torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    kn, vn = (torch.empty((B, Hkv, d), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    kvl = torch.tensor(lens, dtype=torch.int64, device="cuda")
+    pos = kvl - 1
+    lout, sout = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda"), torch.empty_like(q)
+    sel = torch.empty((B, Hkv, topk), dtype=torch.int32, device="cuda")
+    desc = S.sparse_desc(batch=B, n_q=1, n_heads=H, n_kv_heads=Hkv, head_dim=d, dtype=torch.bfloat16,
+                         kv_len=cap, kv_capacity=cap, topk=topk, n_local=2)
+    ws = torch.empty(S.workspace_bytes(S.OP_SPARSE_DECODE_STEP, desc), dtype=torch.uint8, device="cuda")
+
+    def step(st, k_c, v_c, k_p):
+        S.linear_decode_step_at(*lin_in, st, pos, out=lout)
+        S.sparse_decode_step(q, kn, vn, g, k_c, v_c, k_p, kvl, cap, topk=topk, sel=sel, out=sout, workspace=ws)
+
+    def new_tokens(t):
+        for i, x in enumerate(lin_in):
+            x.copy_(device_normal(70 + t, i, (B, H, d)))
+        q.copy_(device_normal(80 + t, 0, (B, H, d)))
+        g.copy_(device_normal(80 + t, 3, (B, H, d)))
+        kn.copy_(device_normal(80 + t, 1, (B, Hkv, d)))
+        vn.copy_(device_normal(80 + t, 2, (B, Hkv, d)))
+
+    new_tokens(0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    scratch = [state.clone(), kc.clone(), vc.clone(), kp.clone()]
+    with torch.cuda.stream(s):
+        step(*scratch)  # warm-up on copies, before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(state, kc, vc, kp)
+    ref_state, ref_kc, ref_vc, ref_kp = state.clone(), kc.clone(), vc.clone(), kp.clone()
+    for t in range(3):
+        new_tokens(t)
+        # eager reference on copies
+        step(ref_state, ref_kc, ref_vc, ref_kp)
+        torch.cuda.synchronize()
+        ref = [lout.clone(), sout.clone(), sel.clone()]
+        lout.zero_(); sout.zero_(); sel.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b_, n in zip([lout, sout, sel], ref, ("linear out", "sparse out", "sel")):
+            assert torch.equal(a, b_), f"step {t}: {n}"
+        assert torch.equal(state, ref_state) and torch.equal(kc, ref_kc) and torch.equal(kp, ref_kp)
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()  # eager work between replays
+        kvl += 1  # the next token of every sequence
+        pos += 1
