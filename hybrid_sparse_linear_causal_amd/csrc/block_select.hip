@@ -319,6 +319,7 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
 constexpr int DSL = 512;      // candidates per slice (level 1)
 constexpr int DNSL_MAX = 32;  // slices per row handled by the merge
 constexpr int DMERGE = 2048;  // slice winners the merge holds (nsl * R)
+constexpr int DMERGE_NT = 1024;  // merge threads
 constexpr int DBITS = DSL * DNSL_MAX / 32 + 1;  // bitmap words over candidate indices 0 .. nc
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, long j) {
@@ -421,20 +422,37 @@ decode_slice_kernel(const float* __restrict__ qt, const float* __restrict__ kpoo
 #pragma unroll
   for (int e = 0; e < FPL; ++e) qv[e] = qt[(long)bg * DD + part * FPL + e];
   const float* kb = kpool + ((long)bg * nblk_cap + j0) * DD + part * FPL;
-#pragma unroll 4
-  for (int it = 0; it < DSL / RPI; ++it) {
-    const int x = it * RPI + sub;
-    float sdot = 0.f;
-    if (x < n) {
-      const float* row = kb + (long)x * DD;
+  if (n > 0) {
+    // the rows stream in batches of BT iterations, the next batch's loads issued before the
+    // current batch is reduced (rows past the slice repeat its last row; their keys are never
+    // read)
+    constexpr int IT = DSL / RPI, BT = 4;
+    float4 buf[2][BT][FPL / 4];
+    auto load = [&](int bt, int slot) {
 #pragma unroll
-      for (int e = 0; e < FPL; e += 4) {
-        const float4 u = *reinterpret_cast<const float4*>(row + e);
-        sdot += u.x * qv[e] + u.y * qv[e + 1] + u.z * qv[e + 2] + u.w * qv[e + 3];
+      for (int u = 0; u < BT; ++u) {
+        const int x = (bt * BT + u) * RPI + sub;
+        const float* row = kb + (long)(x < n ? x : n - 1) * DD;
+#pragma unroll
+        for (int e = 0; e < FPL / 4; ++e) buf[slot][u][e] = *reinterpret_cast<const float4*>(row + 4 * e);
+      }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int bt = 0; bt < IT / BT; ++bt) {
+      if (bt + 1 < IT / BT) load(bt + 1, (bt + 1) & 1);
+#pragma unroll
+      for (int u = 0; u < BT; ++u) {
+        float sdot = 0.f;
+#pragma unroll
+        for (int e = 0; e < FPL / 4; ++e) {
+          const float4 w = buf[bt & 1][u][e];
+          sdot += w.x * qv[4 * e] + w.y * qv[4 * e + 1] + w.z * qv[4 * e + 2] + w.w * qv[4 * e + 3];
+        }
+        sdot = group_sum<LPB>(sdot);
+        if (part == 0) keys[(bt * BT + u) * RPI + sub] = score_key(sdot);
       }
     }
-    sdot = group_sum<LPB>(sdot);
-    if (part == 0) keys[x] = score_key(sdot);
   }
   __syncthreads();
   uint64_t* dst = cand + ((long)bg * nsl + sl) * R;
@@ -480,8 +498,8 @@ __device__ __forceinline__ void idx2key(uint32_t* keys, const uint32_t* idx, int
 // then the output row: forced block 0 (if outside the local range), the chosen candidates
 // ascending (a bitmap over candidate indices compacted in order), the forced local blocks
 // f_lo .. i, and -1 padding.
-template <int CAPB>
-__global__ void __launch_bounds__(NT)
+template <int CAPB, int NTM>
+__global__ void __launch_bounds__(NTM)
 decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel, int nsl, int R,
                     long i, int n_local, int topk, long nc, const int64_t* __restrict__ kv_lens, int Hkv,
                     long kv_max) {
@@ -489,7 +507,7 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   __shared__ uint32_t idx[CAPB];
   __shared__ uint32_t bits[DBITS];
   __shared__ int hist[256];
-  __shared__ int scan_tmp[NT / 64 + 1];
+  __shared__ int scan_tmp[NTM / 64 + 1];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int bg = blockIdx.x, tid = threadIdx.x;
@@ -499,39 +517,39 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
     nc = ncb < nc ? ncb : nc;
   }
   int valid = 0;
-  for (int t = tid; t < n; t += NT) {
+  for (int t = tid; t < n; t += NTM) {
     const uint64_t c = cand[(long)bg * n + t];
     keys[t] = (uint32_t)(c >> 32);
     idx[t] = 0xFFFFFFFFu - (uint32_t)c;
     valid += c != 0ull;
   }
   const int nw = (int)(nc / 32) + 1;  // bitmap words over indices 0 .. nc
-  for (int w = tid; w < nw; w += NT) bits[w] = 0u;
+  for (int w = tid; w < nw; w += NTM) bits[w] = 0u;
   int n_valid;
-  block_excl_scan<NT>(valid, scan_tmp, &n_valid);  // also orders the fills above
+  block_excl_scan<NTM>(valid, scan_tmp, &n_valid);  // also orders the fills above
   uint32_t T = 0, T2 = 0;
   int need = 0;
   const bool all = n_valid <= R;
   bool all_ties = true;
   if (!all) {
-    radix_threshold<NT>(keys, n, R, hist, &s_prefix, &s_need, T, need);
+    radix_threshold<NTM>(keys, n, R, hist, &s_prefix, &s_need, T, need);
     int ties = 0;
-    for (int t = tid; t < n; t += NT) ties += keys[t] == T;
+    for (int t = tid; t < n; t += NTM) ties += keys[t] == T;
     int ties_total;
-    block_excl_scan<NT>(ties, scan_tmp, &ties_total);
+    block_excl_scan<NTM>(ties, scan_tmp, &ties_total);
     all_ties = ties_total == need;  // the usual case: no surplus equal scores
     if (!all_ties) {
       // surplus ties: keep the `need` lowest indices. After idx2key the R largest keys are the
       // R - need keys above T (all ones) and the ties with the `need` largest ~index; indices
       // are distinct, so the R-th largest T2 separates them exactly.
       __syncthreads();
-      for (int t = tid; t < n; t += NT) idx2key(keys, idx, t, T);
+      for (int t = tid; t < n; t += NTM) idx2key(keys, idx, t, T);
       __syncthreads();
       int need2;
-      radix_threshold<NT>(keys, n, R, hist, &s_prefix, &s_need, T2, need2);
+      radix_threshold<NTM>(keys, n, R, hist, &s_prefix, &s_need, T2, need2);
     }
   }
-  for (int t = tid; t < n; t += NT) {
+  for (int t = tid; t < n; t += NTM) {
     bool pick;
     if (all) pick = keys[t] != 0u;
     else if (all_ties) pick = keys[t] >= T;
@@ -543,11 +561,11 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   const int head = f_lo > 0 ? 1 : 0;
   int32_t* out = sel + (long)bg * topk;
   // thread t owns bitmap words wpt*t .. wpt*t + wpt-1
-  const int wpt = (nw + NT - 1) / NT;
+  const int wpt = (nw + NTM - 1) / NTM;
   int c = 0;
   for (int w = wpt * tid; w < min(nw, wpt * tid + wpt); ++w) c += __popc(bits[w]);
   int cnt;
-  int pos = head + block_excl_scan<NT>(c, scan_tmp, &cnt);
+  int pos = head + block_excl_scan<NTM>(c, scan_tmp, &cnt);
   for (int w = wpt * tid; w < min(nw, wpt * tid + wpt); ++w) {
     uint32_t m = bits[w];
     while (m) {
@@ -559,9 +577,9 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   }
   if (tid == 0 && head) out[0] = 0;
   const int nloc = (int)(i - f_lo + 1);
-  for (int t = tid; t < nloc; t += NT)
+  for (int t = tid; t < nloc; t += NTM)
     if (head + cnt + t < topk) out[head + cnt + t] = (int32_t)(f_lo + t);
-  for (int t = head + cnt + nloc + tid; t < topk; t += NT) out[t] = -1;
+  for (int t = head + cnt + nloc + tid; t < topk; t += NTM) out[t] = -1;
 }
 
 }  // namespace
@@ -625,7 +643,7 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
     else
       hipLaunchKernelGGL(decode_slice_kernel<64>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand,
                          (long)g.nblk_cap, nc, R, nullptr, d.n_kv_heads, (long)d.kv_len, d.n_local);
-    hipLaunchKernelGGL(decode_merge_kernel<DMERGE>, dim3(BG), dim3(NT), 0, st, cand, sel, nsl, R, i_max,
+    hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nsl, R, i_max,
                        d.n_local, d.topk, nc, nullptr, d.n_kv_heads, (long)d.kv_len);
     return hipGetLastError();
   }
@@ -706,7 +724,7 @@ hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_
     hipLaunchKernelGGL(decode_slice_kernel<64>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand, nblk_cap, nc, R,
                        kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local);
   }
-  hipLaunchKernelGGL(decode_merge_kernel<DMERGE>, dim3(BG), dim3(NT), 0, st, cand, sel, nsl, R,
+  hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nsl, R,
                      (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens, d.n_kv_heads, (long)d.kv_len);
   return hipGetLastError();
 }

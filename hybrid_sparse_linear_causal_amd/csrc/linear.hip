@@ -645,32 +645,28 @@ linear_scan_f32_kernel(const float* __restrict__ qt, const float* __restrict__ k
 // grid (B*H, DD/64), 256 threads: one token's step for 64 state columns of one head. Thread
 // (row group r0 = j/16, column quad c4 = j%16) owns columns 64y + 4c4 .. +3 of rows r0 + 16m;
 // its state rows are loaded as float4 before the q/k preparation, so their latency overlaps it.
+// Decode step, grid (B*H, DD/64), 320 threads: wave 0 normalises and rotates q and k (their
+// loads are not queued behind the state's), waves 1-4 stream the 64-column slice of S; S is
+// updated in place and each wave-1..4 thread keeps a partial of o = q^ S for its rows.
 template <typename T, int DD>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(320)
 linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                      const T* __restrict__ g, const float* __restrict__ qw,
                      const float* __restrict__ kw, float* __restrict__ state, T* __restrict__ out,
                      long pos, const int64_t* __restrict__ pos_b, int H, float eps, RopeFreqs freqs) {
-  constexpr int NR = DD / 16;  // rows per thread
+  constexpr int NR = DD / 16;  // rows per state thread
+  constexpr int HALF = DD / 2;
   __shared__ float sq[DD], sk[DD];
   __shared__ float4 red[16][16];
   const int bh = blockIdx.x;
-  if (pos_b) {  // each sequence at its own position (negative values read as 0)
-    const long pb = pos_b[bh / H];
-    pos = pb > 0 ? pb : 0;
-  }
-  const int j = threadIdx.x, r0 = j >> 4, c4 = j & 15;
+  const int j = threadIdx.x;
   const long vec = (long)bh * DD;
-  const int col = 64 * blockIdx.y + 4 * c4;
-  float* Sp = state + (long)bh * DD * DD + col;
-  float4 sv[NR];
-#pragma unroll
-  for (int m = 0; m < NR; ++m) sv[m] = *reinterpret_cast<const float4*>(Sp + (long)(r0 + 16 * m) * DD);
-  float vc[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[vec + col + e]);
   if (j < 64) {
-    constexpr int HALF = DD / 2;
+    // ---- wave 0: q^, k^ = RoPE(RMSNorm(q, k) * w) into LDS
+    if (pos_b) {  // each sequence at its own position (negative values read as 0)
+      const long pb = pos_b[bh / H];
+      pos = pb > 0 ? pb : 0;
+    }
     const bool on = j < HALF;
     float a0 = 0, a1 = 0, b0 = 0, b1 = 0;
     if (on) {
@@ -691,8 +687,32 @@ linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
       sq[j] = x0 * cs - x1 * sn; sq[j + HALF] = x0 * sn + x1 * cs;
       sk[j] = y0 * cs - y1 * sn; sk[j + HALF] = y0 * sn + y1 * cs;
     }
+    __syncthreads();
+    __syncthreads();
+    // ---- o[c] = sum of the 16 row-group partials, gated
+    const int cc = j >> 2, e = j & 3;  // column 64y + 4cc + e
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float4 t = red[m][cc];
+      acc += e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w;
+    }
+    const long oc = vec + 64 * blockIdx.y + j;
+    const float gv = to_f32(g[oc]);
+    out[oc] = from_f32<T>(acc / (1.0f + expf(-gv)));
+    return;
   }
-  __syncthreads();
+  // ---- waves 1-4: the state slice (rows r0 + 16m, columns 64y + 4c4 .. +3)
+  const int js = j - 64, r0 = js >> 4, c4 = js & 15;
+  const int col = 64 * blockIdx.y + 4 * c4;
+  float* Sp = state + (long)bh * DD * DD + col;
+  float4 sv[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) sv[m] = *reinterpret_cast<const float4*>(Sp + (long)(r0 + 16 * m) * DD);
+  float vc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[vec + col + e]);
+  __syncthreads();  // q^, k^ ready
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int m = 0; m < NR; ++m) {
@@ -704,19 +724,7 @@ linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
     o.x += qr * s4.x; o.y += qr * s4.y; o.z += qr * s4.z; o.w += qr * s4.w;
   }
   red[r0][c4] = o;
-  __syncthreads();
-  if (j < 64) {
-    const int cc = j >> 2, e = j & 3;  // column 64y + 4cc + e
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float4 t = red[m][cc];
-      acc += e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w;
-    }
-    const long oc = vec + 64 * blockIdx.y + j;
-    const float gv = to_f32(g[oc]);
-    out[oc] = from_f32<T>(acc / (1.0f + expf(-gv)));
-  }
+  __syncthreads();  // partials ready
 }
 
 // The bf16 prefill over a geometry: segment sums (when some sequence has several segments),
@@ -876,22 +884,23 @@ hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const 
   const RopeFreqs fr = make_rope_freqs(hd, d.rope_base);
   const dim3 grid(BH, hd / 64);
   const long pos = (long)d.pos0;
+  const dim3 block(320);
   if (d.dtype == SALA_BF16) {
     if (hd == 128)
-      hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 128>), grid, dim3(256), 0, st, (const bf16_t*)q,
+      hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 128>), grid, block, 0, st, (const bf16_t*)q,
                          (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, qw, kw, state, (bf16_t*)out,
                          pos, pos_b, H, d.norm_eps, fr);
     else
-      hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 64>), grid, dim3(256), 0, st, (const bf16_t*)q,
+      hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 64>), grid, block, 0, st, (const bf16_t*)q,
                          (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, qw, kw, state, (bf16_t*)out,
                          pos, pos_b, H, d.norm_eps, fr);
   } else {
     if (hd == 128)
-      hipLaunchKernelGGL((linear_decode_kernel<float, 128>), grid, dim3(256), 0, st, (const float*)q,
+      hipLaunchKernelGGL((linear_decode_kernel<float, 128>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (const float*)g, qw, kw, state, (float*)out,
                          pos, pos_b, H, d.norm_eps, fr);
     else
-      hipLaunchKernelGGL((linear_decode_kernel<float, 64>), grid, dim3(256), 0, st, (const float*)q,
+      hipLaunchKernelGGL((linear_decode_kernel<float, 64>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (const float*)g, qw, kw, state, (float*)out,
                          pos, pos_b, H, d.norm_eps, fr);
   }
