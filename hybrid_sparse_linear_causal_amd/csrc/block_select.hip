@@ -394,14 +394,56 @@ __device__ __forceinline__ long decode_candidates(const int64_t* kv_lens, int b,
   return *i - n_local > 0 ? *i - n_local : 0;
 }
 
+// q~ of a single query token for KV group g (decode): the sum over the group's heads of
+// RMSNorm(q[b, h]) * w, with the arithmetic of qtilde_kernel for one token (16 lanes per head
+// row, heads summed in order), into qs[DD]. NT threads; hsum holds 16 head rows.
+template <typename T, int DD>
+__device__ __forceinline__ void decode_qtilde(const T* __restrict__ q, const float* __restrict__ qw, int b, int g,
+                                              int Hq, int Hkv, float eps, float (*hsum)[DD], float* qs) {
+  constexpr int EPL = 16 / (int)sizeof(T), LPR = DD / EPL, RPP = NT / LPR;
+  const int j = threadIdx.x, hr = j / LPR, seg = j % LPR;
+  const int G = Hq / Hkv;
+  float tot = 0.f;  // thread j < DD: running sum over the group's heads of dim j
+  for (int h0 = 0; h0 < G; h0 += RPP) {
+    const int hh = h0 + hr;
+    if (hh < G) {
+      const T* src = q + ((long)b * Hq + g * G + hh) * DD + seg * EPL;
+      float x[EPL];
+      if constexpr (sizeof(T) == 2) {
+        unpack8(*reinterpret_cast<const uint4*>(src), x);
+      } else {
+        const float4 u = *reinterpret_cast<const float4*>(src);
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+      ss = group_sum<LPR>(ss);
+      const float inv = 1.0f / sqrtf(ss / DD + eps);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) hsum[hr][seg * EPL + e] = x[e] * inv * 1.0f * (qw ? qw[seg * EPL + e] : 1.0f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) hsum[hr][seg * EPL + e] = 0.f;
+    }
+    __syncthreads();
+    if (j < DD)
+      for (int r = 0; r < RPP && h0 + r < G; ++r) tot += hsum[r][j];
+    __syncthreads();
+  }
+  if (j < DD) qs[j] = tot;
+  __syncthreads();
+}
+
 // Level 1: grid (B*Hkv, nsl), NT threads. Slice s holds candidates j = j0 .. j0+n-1 with
 // j0 = 1 + s*DSL, n = min(DSL, nc - j0 + 1): scores q~ . k_pool[j] (8 lanes per pooled row),
 // then the slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered). With
-// kv_lens, nc is each sequence's own count (at most the nc given).
-template <int DD>
+// kv_lens, nc is each sequence's own count (at most the nc given). q~ of the single query token
+// is computed here (decode_qtilde) from q [B, Hq, DD].
+template <typename QT, int DD>
 __global__ void __launch_bounds__(NT)
-decode_slice_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
-                    uint64_t* __restrict__ cand, long nblk_cap, long nc, int R,
+decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int Hq, float eps,
+                    const float* __restrict__ kpool, uint64_t* __restrict__ cand, long nblk_cap, long nc, int R,
                     const int64_t* __restrict__ kv_lens, int Hkv, long kv_max, int n_local) {
   constexpr int LPB = 8, FPL = DD / LPB, RPI = NT / LPB;  // rows per iteration
   __shared__ uint32_t keys[DSL];
@@ -409,8 +451,11 @@ decode_slice_kernel(const float* __restrict__ qt, const float* __restrict__ kpoo
   __shared__ int scan_tmp[NT / 64 + 1];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
+  __shared__ float hsum[NT / (DD / (16 / (int)sizeof(QT)))][DD];
+  __shared__ float qs[DD];
   const int bg = blockIdx.x, sl = blockIdx.y, nsl = gridDim.y;
   const int tid = threadIdx.x, sub = tid / LPB, part = tid % LPB;
+  decode_qtilde<QT, DD>(q, qw, bg / Hkv, bg % Hkv, Hq, Hkv, eps, hsum, qs);
   if (kv_lens) {
     long i;
     const long ncb = decode_candidates(kv_lens, bg / Hkv, kv_max, n_local, &i);
@@ -420,7 +465,7 @@ decode_slice_kernel(const float* __restrict__ qt, const float* __restrict__ kpoo
   const int n = (int)max(0L, min((long)DSL, nc - j0 + 1));
   float qv[FPL];
 #pragma unroll
-  for (int e = 0; e < FPL; ++e) qv[e] = qt[(long)bg * DD + part * FPL + e];
+  for (int e = 0; e < FPL; ++e) qv[e] = qs[part * FPL + e];
   const float* kb = kpool + ((long)bg * nblk_cap + j0) * DD + part * FPL;
   if (n > 0) {
     // the rows stream in batches of BT iterations, the next batch's loads issued before the
@@ -615,6 +660,22 @@ size_t block_select_workspace(const sala_sparse_desc& d) {
   return ((qt + 255) & ~(size_t)255) + sc;
 }
 
+// level 1 of the decode selection (q~ computed inside), for the descriptor's dtype and dim
+static void launch_decode_slice(const sala_sparse_desc& d, const void* q, const float* qw, const float* k_pool,
+                                uint64_t* cand, long nblk_cap, long nc, int R, int nsl, const int64_t* kv_lens,
+                                hipStream_t st) {
+  const dim3 grid(d.batch * d.n_kv_heads, nsl);
+#define SALA_SLICE(T, DD)                                                                                   \
+  hipLaunchKernelGGL((decode_slice_kernel<T, DD>), grid, dim3(NT), 0, st, (const T*)q, qw, d.n_heads, d.norm_eps, \
+                     k_pool, cand, nblk_cap, nc, R, kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local)
+  if (d.dtype == SALA_BF16) {
+    if (d.head_dim == 128) SALA_SLICE(bf16_t, 128); else SALA_SLICE(bf16_t, 64);
+  } else {
+    if (d.head_dim == 128) SALA_SLICE(float, 128); else SALA_SLICE(float, 64);
+  }
+#undef SALA_SLICE
+}
+
 hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
                                const float* k_pool, int32_t* sel, void* ws, hipStream_t st) {
   const SparseGeom g = sparse_geom(d);
@@ -623,6 +684,15 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
   float* qt = static_cast<float*>(ws);
   const size_t qt_bytes = (size_t)BG * g.nqb * d.head_dim * sizeof(float);
   float* sc = reinterpret_cast<float*>(static_cast<char*>(ws) + ((qt_bytes + 255) & ~(size_t)255));
+  const long i_max = g.qb0 + g.nqb - 1;
+  long nc; int nsl, R;
+  if (decode_two_level(d, &nc, &nsl, &R)) {
+    uint64_t* cand = reinterpret_cast<uint64_t*>(sc);
+    launch_decode_slice(d, q, qw, k_pool, cand, g.nblk_cap, nc, R, nsl, nullptr, st);
+    hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nsl, R,
+                       i_max, d.n_local, d.topk, nc, nullptr, d.n_kv_heads, (long)d.kv_len);
+    return hipGetLastError();
+  }
   const dim3 gq(d.batch, (unsigned)g.nqb);
 #define SALA_QT(T, DD)                                                                             \
   hipLaunchKernelGGL((qtilde_kernel<T, DD>), gq, dim3(NT), 0, st, (const T*)q, qw, qt, d.n_q,      \
@@ -633,20 +703,6 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
     if (d.head_dim == 128) SALA_QT(float, 128); else SALA_QT(float, 64);
   }
 #undef SALA_QT
-  const long i_max = g.qb0 + g.nqb - 1;
-  long nc; int nsl, R;
-  if (decode_two_level(d, &nc, &nsl, &R)) {
-    uint64_t* cand = reinterpret_cast<uint64_t*>(sc);
-    if (d.head_dim == 128)
-      hipLaunchKernelGGL(decode_slice_kernel<128>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand,
-                         (long)g.nblk_cap, nc, R, nullptr, d.n_kv_heads, (long)d.kv_len, d.n_local);
-    else
-      hipLaunchKernelGGL(decode_slice_kernel<64>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand,
-                         (long)g.nblk_cap, nc, R, nullptr, d.n_kv_heads, (long)d.kv_len, d.n_local);
-    hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nsl, R, i_max,
-                       d.n_local, d.topk, nc, nullptr, d.n_kv_heads, (long)d.kv_len);
-    return hipGetLastError();
-  }
   if (i_max - d.n_local >= 1) {
     if (g.nqb == 1) {
       const long ncand_end = i_max - d.n_local + 1;  // score blocks 0 .. i - n_local
@@ -709,21 +765,10 @@ hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_
   long nc; int nsl, R;
   if (!decode_at_plan(d, &nc, &nsl, &R)) return hipErrorInvalidValue;
   const int BG = d.batch * d.n_kv_heads;
-  float* qt = static_cast<float*>(ws);
   const size_t qt_bytes = (size_t)BG * d.head_dim * sizeof(float);
   uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + ((qt_bytes + 255) & ~(size_t)255));
   const long nblk_cap = d.kv_capacity / 64;
-  if (d.head_dim == 128) {
-    hipLaunchKernelGGL((qtilde_kernel<bf16_t, 128>), dim3(d.batch, 1), dim3(NT), 0, st, (const bf16_t*)q, qw, qt, 1,
-                       d.n_heads, d.n_kv_heads, (long)(d.kv_len - 1), d.norm_eps);
-    hipLaunchKernelGGL(decode_slice_kernel<128>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand, nblk_cap, nc, R,
-                       kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local);
-  } else {
-    hipLaunchKernelGGL((qtilde_kernel<bf16_t, 64>), dim3(d.batch, 1), dim3(NT), 0, st, (const bf16_t*)q, qw, qt, 1,
-                       d.n_heads, d.n_kv_heads, (long)(d.kv_len - 1), d.norm_eps);
-    hipLaunchKernelGGL(decode_slice_kernel<64>, dim3(BG, nsl), dim3(NT), 0, st, qt, k_pool, cand, nblk_cap, nc, R,
-                       kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local);
-  }
+  launch_decode_slice(d, q, qw, k_pool, cand, nblk_cap, nc, R, nsl, kv_lens, st);
   hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nsl, R,
                      (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens, d.n_kv_heads, (long)d.kv_len);
   return hipGetLastError();

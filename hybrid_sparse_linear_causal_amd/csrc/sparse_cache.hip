@@ -75,9 +75,11 @@ kv_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  const bool completes = (blk + 1) * 64 <= kv_len;  // the block is full once these tokens are in
   for (int t = r; t < 64; t += RPP) {
     const long p = blk * 64 + t;
     float x[EPL];
+    if (!completes && !(p >= q0 && p < kv_len)) continue;  // no pool to compute: new rows only
     if (p >= q0 && p < kv_len) {
       const long src = (((long)b * n_q + (p - q0)) * Hkv + g) * DD + seg * EPL;
       load_row_part<T>(k_new + src, x);
@@ -101,7 +103,7 @@ kv_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] += x[e];
   }
-  if ((blk + 1) * 64 > kv_len) return;  // block still incomplete: nothing to pool (uniform)
+  if (!completes) return;  // block still incomplete: nothing to pool (uniform)
 #pragma unroll
   for (int e = 0; e < EPL; ++e) psum[r][seg * EPL + e] = acc[e];
   __syncthreads();
