@@ -33,14 +33,7 @@ namespace sala {
 namespace {
 
 constexpr int D = 128;
-constexpr int KS = D + 8;    // K tile row stride (bf16): 272 B
-constexpr int VS = 64 + 8;   // V^T tile row stride (bf16): 144 B
 constexpr int DEC_SPLIT = 16;       // decode workgroups per (b, g)
-
-__device__ __forceinline__ uint32_t bf_half(const uint4& u, int e) {
-  const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
 
 // ---- work geometry of the prefill kernel: which (sequence b, KV group gk, query block r of
 // the call, head quad hq) a workgroup handles, where the call's query tokens of sequence b sit
@@ -249,6 +242,9 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
 
 // grid (B*Hkv, DEC_SPLIT); wave-global index wi = split*4 + wave takes sel entries
 // wi, wi + 4*DEC_SPLIT, ... Partial per workgroup: m[16], l[16], O[16][D] (fp32).
+// Each wave owns a V tile in LDS: its block's V rows arrive there by DMA, in the swizzled
+// row-major layout of the prefill kernel, and leave as V^T operands through transposing reads.
+constexpr int DEC_OSTR = D + 4;  // fp32 row stride of the O staging (rows at one column spread over banks)
 template <bool DENSE>
 __global__ void __launch_bounds__(256)
 sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw,
@@ -256,11 +252,18 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
                           const int32_t* __restrict__ sel, float* __restrict__ part, int Hq,
                           int Hkv, long kv_len, long cap, int topk, float eps, float qscale,
                           const int64_t* __restrict__ kv_lens) {
-  __shared__ __align__(16) bf16_t vts[4][D * VS];
+  __shared__ __align__(16) bf16_t vts[4][TILE];
   __shared__ float cm[4][16], cl[4][16];
   const int bg = blockIdx.x, split = blockIdx.y;
   const int b = bg / Hkv, gk = bg % Hkv, G = Hq / Hkv;
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
+  // the query rows first, so that their loads overlap those of the selection row
+  const bool ok = l16 < G;
+  uint4 qraw[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qraw[ks] = ok ? *reinterpret_cast<const uint4*>(q + ((long)b * Hq + gk * G + l16) * D + 32 * ks + 8 * lq)
+                  : make_uint4(0, 0, 0, 0);
   if (kv_lens) {  // this sequence's own cache length, clamped to [1, kv_len]
     const long kb = kv_lens[b];
     kv_len = kb < 1 ? 1 : (kb > kv_len ? kv_len : kb);
@@ -282,14 +285,11 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
   // Q^T fragments: column l16 = head gk*G + l16 (zero beyond the group)
   bf16x8 qf[4];
   {
-    const bool ok = l16 < G;
     float x[4][8];
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) u = *reinterpret_cast<const uint4*>(q + ((long)b * Hq + gk * G + l16) * D + 32 * ks + 8 * lq);
-      unpack8(u, x[ks]);
+      unpack8(qraw[ks], x[ks]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
     }
@@ -310,13 +310,12 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) OT[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int stride = 4 * DEC_SPLIT;
-  bf16_t* vt = vts[wave];  // this wave's own V^T tile: no workgroup barrier needed
+  bf16_t* vt = vts[wave];  // this wave's own V tile: no workgroup barrier needed
   for (int e = split * 4 + wave; e < nsel; e += stride) {
     const int su = e >> 6;
     const long blk = DENSE ? (long)e : (long)__shfl(su == 0 ? sv[0] : su == 1 ? sv[1] : su == 2 ? sv[2] : sv[3], e & 63, 64);
-    // both tiles of the block in flight at once: K in MFMA A layout (key 16kt + l16, dims
-    // 32ks + 8lq ..), V as 4 consecutive keys x 8 dims per lane for the transpose
-    uint4 kk[4][4], vv[4][4];
+    // K in MFMA A layout (key 16kt + l16, dims 32ks + 8lq ..) into registers
+    uint4 kk[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const long pk = blk * 64 + 16 * kt + l16;
@@ -325,14 +324,17 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
         kk[kt][ks] = pk < kv_len ? *reinterpret_cast<const uint4*>(kc + (row_base + pk) * D + 32 * ks + 8 * lq)
                                  : make_uint4(0, 0, 0, 0);
     }
+    // V rows by DMA into the wave's tile: piece I = rows 4I .. 4I+3, lane -> chunk position
+    // lane % 16 of row 4I + lane / 16, loading the source chunk the swizzle puts there. Rows
+    // past the cache are clamped to its last row: their probabilities are 0.
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const long pk = blk * 64 + 16 * mm + 4 * lq + u;
-        vv[mm][u] = pk < kv_len ? *reinterpret_cast<const uint4*>(vc + (row_base + pk) * D + 8 * l16)
-                                : make_uint4(0, 0, 0, 0);
-      }
+    for (int I = 0; I < 16; ++I) {
+      const int row = 4 * I + (lane >> 4);
+      const int chv = (lane & 15) ^ (2 * (row & 7));
+      long pk = blk * 64 + row;
+      if (pk >= kv_len) pk = kv_len - 1;
+      dma16(vc + (row_base + pk) * D + 8 * chv, lds_addr_u32(vt + I * 512));
+    }
     f32x4 ST[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -343,18 +345,6 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
       for (int c = 0; c < 4; ++c)
         if (blk * 64 + 16 * kt + 4 * lq + c > p) ST[kt][c] = -INFINITY;
     }
-    // V^T into the wave's tile (lane: keys 16mm + 4lq + u, dims 8 l16 + ee)
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
-#pragma unroll
-      for (int ee = 0; ee < 8; ++ee) {
-        uint2 w;
-        w.x = bf_half(vv[mm][0], ee) | (bf_half(vv[mm][1], ee) << 16);
-        w.y = bf_half(vv[mm][2], ee) | (bf_half(vv[mm][3], ee) << 16);
-        *reinterpret_cast<uint2*>(&vt[(8 * l16 + ee) * VS + 16 * mm + 4 * lq]) = w;
-      }
-    // a wave's LDS accesses complete in order: its reads below see these writes
-    __builtin_amdgcn_wave_barrier();
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -368,6 +358,7 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) OT[dt] *= alpha;
     m = mn;
+    wait_vmcnt<0>();  // the wave's V tile has landed (its DMA completes in issue order)
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       float pr[8];
@@ -379,26 +370,22 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
 #pragma unroll
       for (int u = 0; u < 8; ++u) lp += pr[u];
       const bf16x8 pf = as_bf16x8(pack8(pr));
+      // P^T slots: keys 32c + 4lq + u, then 32c + 16 + 4lq + u, as vt_frag orders V^T
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const bf16_t* vr = &vt[(16 * dt + l16) * VS + 32 * c + 4 * lq];
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + 16));
-        OT[dt] = mfma16x16x32(a, pf, OT[dt]);
-      }
+      for (int dt = 0; dt < 8; ++dt) OT[dt] = mfma16x16x32(vt_frag(vt, 32 * c, dt, l16, lq), pf, OT[dt]);
     }
-    // the tile is rewritten by this wave's next block: its reads must be done first
+    // the tile is rewritten by this wave's next block: its reads have been consumed above
     __builtin_amdgcn_wave_barrier();
   }
-  __syncthreads();  // every wave is done with its V^T tile (reused below)
-  // combine the 4 waves: O staged in the (now free) V^T area as fp32 [wave][head][D]
+  __syncthreads();  // every wave is done with its V tile (reused below)
+  // combine the 4 waves: O staged in the (now free) V area as fp32 [wave][head][DEC_OSTR]
   lp += __shfl_xor(lp, 16, 64);
   lp += __shfl_xor(lp, 32, 64);
   if (lq == 0) { cm[wave][l16] = m; cl[wave][l16] = lp; }
-  float* ost = reinterpret_cast<float*>(&vts[0][0]);  // 4*16*128 floats = 32 KB <= sizeof(vts)
+  float* ost = reinterpret_cast<float*>(&vts[0][0]);  // 4*16*DEC_OSTR floats = 33 KB <= sizeof(vts)
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ost[(wave * 16 + l16) * D + 16 * dt + 4 * lq + c] = OT[dt][c];
+    *reinterpret_cast<f32x4*>(&ost[(wave * 16 + l16) * DEC_OSTR + 16 * dt + 4 * lq]) = OT[dt];
   __syncthreads();
   float* dst = part + ((long)bg * DEC_SPLIT + split) * 16 * (D + 2);
   for (int idx = j; idx < 16 * D; idx += 256) {
@@ -410,7 +397,7 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
 #pragma unroll
     for (int wv = 0; wv < 4; ++wv) {
       const float sc = (cm[wv][hh] == -INFINITY) ? 0.f : exp2f(cm[wv][hh] - M);
-      o += ost[(wv * 16 + hh) * D + dd] * sc;
+      o += ost[(wv * 16 + hh) * DEC_OSTR + dd] * sc;
       l += cl[wv][hh] * sc;
     }
     dst[hh * (D + 2) + 2 + dd] = o;
