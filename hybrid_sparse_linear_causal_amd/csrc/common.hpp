@@ -110,6 +110,12 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 // ---- LDS tiles of 256-byte rows (64 or 128 bf16): 16-byte chunk c of row r is stored at chunk
 // position c ^ (r & 15), so 16 rows read at one column land in 16 different bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + 8 * (chunk ^ (row & 15)); }
+// Layout of tiles that are also read transposed: chunk c of row r at position c ^ 2(r & 7). The
+// transposing reads of 32 lanes (8 consecutive rows x 2 adjacent chunks) land on 16 different
+// positions, and row reads of 16 rows at one chunk stay free of bank conflicts as well
+// (measured with the LDS bank-conflict counter on gfx950); swz gives the transposing reads
+// two-way conflicts.
+__device__ __forceinline__ int swzv(int row, int chunk) { return row * 128 + 8 * (chunk ^ (2 * (row & 7))); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -122,12 +128,14 @@ __device__ __forceinline__ uint2 ds_read_tr(const bf16_t* p) {
   v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
   return __builtin_bit_cast(uint2, r);
 }
-// MFMA operand "column j = c0 + l16, k = rows k0 + 0..7" of a row-major swizzled tile, k0 and
-// c0 multiples of 4: two transposing reads (rows k0..k0+3, then k0+d1..k0+d1+3).
-__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* T, int k0, int d1, int c0, int l16) {
+// MFMA operand "column j = c0 + l16, k = rows k0 + 0..7" of a row-major tile in the swzv
+// layout, k0 and c0 multiples of 4: two transposing reads (rows k0..k0+3, then k0+d1..k0+d1+3).
+// Free of bank conflicts when the lanes of each 32 cover 8 consecutive rows (k0 = kb + 4 * lq,
+// d1 = 16).
+__device__ __forceinline__ bf16x8 tr_frag_v(const bf16_t* T, int k0, int d1, int c0, int l16) {
   const int row = k0 + (l16 >> 2), col = c0 + 4 * (l16 & 3);
-  const uint2 a = ds_read_tr(T + swz(row, col >> 3) + (col & 7));
-  const uint2 b = ds_read_tr(T + swz(row + d1, col >> 3) + (col & 7));
+  const uint2 a = ds_read_tr(T + swzv(row, col >> 3) + (col & 7));
+  const uint2 b = ds_read_tr(T + swzv(row + d1, col >> 3) + (col & 7));
   return as_bf16x8(a, b);
 }
 

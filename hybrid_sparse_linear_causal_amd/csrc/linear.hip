@@ -286,12 +286,12 @@ __device__ __forceinline__ void dma_chunk(const bf16_t* q, const bf16_t* k, cons
   for (int m = 0; m < 2; ++m) {
     const int I = 2 * wave + m;
     const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
-    const long off = row0 + (long)(min(t0 + row, n_valid - 1) - t0) * H * D + 8 * ch;
-    dma16(q + off, lds_addr_u32(T[0] + I * 512));
-    dma16(k + off, lds_addr_u32(T[1] + I * 512));
-    dma16(v + off, lds_addr_u32(T[2] + I * 512));
-    dma16(g + off, lds_addr_u32(T[3] + I * 512));
+    const int ch = (lane & 15) ^ (row & 15), chv = (lane & 15) ^ (2 * (row & 7));
+    const long src = row0 + (long)(min(t0 + row, n_valid - 1) - t0) * H * D;
+    dma16(q + src + 8 * ch, lds_addr_u32(T[0] + I * 512));
+    dma16(k + src + 8 * chv, lds_addr_u32(T[1] + I * 512));
+    dma16(v + src + 8 * chv, lds_addr_u32(T[2] + I * 512));
+    dma16(g + src + 8 * ch, lds_addr_u32(T[3] + I * 512));
   }
 }
 
@@ -386,8 +386,8 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       uint4 xq[2], xk[2];
       xq[0] = *reinterpret_cast<const uint4*>(&Qt[swz(tok, s8)]);
       xq[1] = *reinterpret_cast<const uint4*>(&Qt[swz(tok, s8 + 8)]);
-      xk[0] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8)]);
-      xk[1] = *reinterpret_cast<const uint4*>(&Kt[swz(tok, s8 + 8)]);
+      xk[0] = *reinterpret_cast<const uint4*>(&Kt[swzv(tok, s8)]);
+      xk[1] = *reinterpret_cast<const uint4*>(&Kt[swzv(tok, s8 + 8)]);
       float rc[8], rs[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -400,8 +400,8 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       if (c0 + tok >= t_end) { xk[0] = make_uint4(0, 0, 0, 0); xk[1] = xk[0]; }
       *reinterpret_cast<uint4*>(&Qt[swz(tok, s8)]) = xq[0];
       *reinterpret_cast<uint4*>(&Qt[swz(tok, s8 + 8)]) = xq[1];
-      *reinterpret_cast<uint4*>(&Kt[swz(tok, s8)]) = xk[0];
-      *reinterpret_cast<uint4*>(&Kt[swz(tok, s8 + 8)]) = xk[1];
+      *reinterpret_cast<uint4*>(&Kt[swzv(tok, s8)]) = xk[0];
+      *reinterpret_cast<uint4*>(&Kt[swzv(tok, s8 + 8)]) = xk[1];
     }
     __syncthreads();
 
@@ -423,7 +423,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           if (kt <= w4) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-              const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[swz(16 * kt + l16, 4 * ks + lq)]));
+              const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[swzv(16 * kt + l16, 4 * ks + lq)]));
               at[hh] = mfma16x16x32(kf, qfrag[ks], at[hh]);
             }
             if (kt == w4) {
@@ -441,7 +441,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         const bf16x8 pfrag = as_bf16x8(pb);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          acc[dt] = mfma16x16x32(tr_frag(Vt, 32 * c + 4 * lq, 16, 16 * dt, l16), pfrag, acc[dt]);
+          acc[dt] = mfma16x16x32(tr_frag_v(Vt, 32 * c + 4 * lq, 16, 16 * dt, l16), pfrag, acc[dt]);
       }
       // ---------------- inter-chunk: O^T += S^T Q~^T
 #pragma unroll
@@ -452,15 +452,16 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           acc[dt] = mfma16x16x32(sf, qfrag[ks], acc[dt]);
         }
     } else {
-      // ---------------- state update: S += K~^T V (dk rows 32*w4 .. +31, all dv)
+      // ---------------- state update: S += K~^T V (dk rows 32*w4 .. +31, all dv); the token
+      // index k runs over 32ks + 4lq + 0..3 and 32ks + 16 + 4lq + 0..3, the same for both operands
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 af[2];
 #pragma unroll
-        for (int it = 0; it < 2; ++it) af[it] = tr_frag(Kt, 32 * ks + 8 * lq, 4, 32 * w4 + 16 * it, l16);
+        for (int it = 0; it < 2; ++it) af[it] = tr_frag_v(Kt, 32 * ks + 4 * lq, 16, 32 * w4 + 16 * it, l16);
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
-          const bf16x8 bfr = tr_frag(Vt, 32 * ks + 8 * lq, 4, 16 * jt, l16);
+          const bf16x8 bfr = tr_frag_v(Vt, 32 * ks + 4 * lq, 16, 16 * jt, l16);
 #pragma unroll
           for (int it = 0; it < 2; ++it) acc[8 * it + jt] = mfma16x16x32(af[it], bfr, acc[8 * it + jt]);
         }

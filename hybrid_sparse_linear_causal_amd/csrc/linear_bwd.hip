@@ -114,7 +114,7 @@ constexpr int PL_DMA = 6;  // copy instructions per wave per chunk (3 tiles x 2 
 
 __device__ __forceinline__ long tok_of(bool rev, long u, int N) { return rev ? (long)N - 1 - u : u; }
 
-// DMA of one chunk's tiles (64 rows x 256 B each, swizzled rows as swz): wave w moves pieces
+// DMA of one chunk's tiles (64 rows x 256 B each, swizzled rows as swzv): wave w moves pieces
 // 2w, 2w+1 (rows 8w .. 8w+7) of each tile. Rows past the end are clamped to the last token in
 // order u (valid memory; the chunk kernel zeroes their B rows).
 template <int NT>
@@ -125,7 +125,7 @@ __device__ __forceinline__ void dma_tiles(const bf16_t* const (&src)[NT], long h
   for (int m = 0; m < 2; ++m) {
     const int I = 2 * wave + m;
     const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15);
+    const int ch = (lane & 15) ^ (2 * (row & 7));
     const long t = tok_of(rev, u0 + row < N ? u0 + row : (long)N - 1, N);
     const long off = head_off + t * tok_stride + 8 * ch;
 #pragma unroll
@@ -168,9 +168,9 @@ lplain_segsum_kernel(const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ C
     const bf16_t* Ct = L.t[c & 1][1];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 af = tr_frag(Bt, 32 * ks + 8 * lq, 4, 16 * wave, l16);
+      const bf16x8 af = tr_frag_v(Bt, 32 * ks + 4 * lq, 16, 16 * wave, l16);
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt) S[jt] = mfma16x16x32(af, tr_frag(Ct, 32 * ks + 8 * lq, 4, 16 * jt, l16), S[jt]);
+      for (int jt = 0; jt < 8; ++jt) S[jt] = mfma16x16x32(af, tr_frag_v(Ct, 32 * ks + 4 * lq, 16, 16 * jt, l16), S[jt]);
     }
   }
   float* dst = ws + ((long)bh * nseg + seg + 1) * D * D;
@@ -276,7 +276,7 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
       bf16x8 afrag[4];
       const int tl = 16 * w4 + l16;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) afrag[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&At[swz(tl, 4 * ks + lq)]));
+      for (int ks = 0; ks < 4; ++ks) afrag[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&At[swzv(tl, 4 * ks + lq)]));
       for (int c = 0; 2 * c <= w4; ++c) {
         f32x4 at[2];
 #pragma unroll
@@ -286,7 +286,7 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
           if (kt <= w4) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-              const bf16x8 bfr = as_bf16x8(*reinterpret_cast<const uint4*>(&Bt[swz(16 * kt + l16, 4 * ks + lq)]));
+              const bf16x8 bfr = as_bf16x8(*reinterpret_cast<const uint4*>(&Bt[swzv(16 * kt + l16, 4 * ks + lq)]));
               at[hh] = mfma16x16x32(bfr, afrag[ks], at[hh]);
             }
             if (kt == w4) {
@@ -304,7 +304,7 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
         const bf16x8 pfrag = as_bf16x8(pb);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          acc[dt] = mfma16x16x32(tr_frag(Ct, 32 * c + 4 * lq, 16, 16 * dt, l16), pfrag, acc[dt]);
+          acc[dt] = mfma16x16x32(tr_frag_v(Ct, 32 * c + 4 * lq, 16, 16 * dt, l16), pfrag, acc[dt]);
       }
       // inter-chunk: Y^T += S^T A^T
 #pragma unroll
@@ -315,15 +315,15 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
           acc[dt] = mfma16x16x32(sf, afrag[ks], acc[dt]);
         }
     } else {
-      // state: S += B^T C (dk rows 32*w4 .. +31, all dv)
+      // state: S += B^T C (dk rows 32*w4 .. +31, all dv; token order as in the output pass)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8 af[2];
 #pragma unroll
-        for (int it = 0; it < 2; ++it) af[it] = tr_frag(Bt, 32 * ks + 8 * lq, 4, 32 * w4 + 16 * it, l16);
+        for (int it = 0; it < 2; ++it) af[it] = tr_frag_v(Bt, 32 * ks + 4 * lq, 16, 32 * w4 + 16 * it, l16);
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
-          const bf16x8 cf = tr_frag(Ct, 32 * ks + 8 * lq, 4, 16 * jt, l16);
+          const bf16x8 cf = tr_frag_v(Ct, 32 * ks + 4 * lq, 16, 16 * jt, l16);
 #pragma unroll
           for (int it = 0; it < 2; ++it) acc[8 * it + jt] = mfma16x16x32(af[it], cf, acc[8 * it + jt]);
         }

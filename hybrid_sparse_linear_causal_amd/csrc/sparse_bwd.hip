@@ -37,34 +37,6 @@ constexpr int SB_NT = 512;
 constexpr int SB_QT = 2;   // 16-row query tiles per wave in the query-major kernels
 constexpr int SB_SL = 32;  // query blocks per dK/dV slice
 
-// K^T operand (rows dk = 16*dt + l16, k = keys in the permuted P^T order, as vt_frag) read by
-// transposing reads from a tile in the plain swz layout
-__device__ __forceinline__ bf16x8 ktr_frag(const bf16_t* T, int kb, int dt, int l16, int lq) {
-  const int row0 = kb + 4 * lq + (l16 >> 2);
-  const int col = 16 * dt + 4 * (l16 & 3);
-  const int ch = col >> 3, sub = col & 7;
-  const uint2 a = ds_read_tr(T + swz(row0, ch) + sub);
-  const uint2 b = ds_read_tr(T + swz(row0 + 16, ch) + sub);
-  return as_bf16x8(a, b);
-}
-
-// Layout of tiles read both by rows and transposed: 16-byte chunk c of row r sits at chunk
-// c ^ swt_of(r), swt_of(r) = 2(r & 7) + ((r >> 3) & 1). Over 16 aligned rows swt_of is a
-// permutation of 0..15 (a row read of 16 rows x 16 bytes touches 16 distinct chunk columns), and
-// over 8 aligned rows its upper three bits are distinct (a transposing read of 8 rows x 32 bytes
-// touches 8 distinct 32-byte column pairs): both kinds of read are free of bank conflicts.
-__device__ __forceinline__ int swt_of(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-__device__ __forceinline__ int swt(int row, int chunk) { return row * D + 8 * (chunk ^ swt_of(row)); }
-
-// as ktr_frag, for a tile in the swt layout
-__device__ __forceinline__ bf16x8 ktr_frag_t(const bf16_t* T, int kb, int dt, int l16, int lq) {
-  const int row0 = kb + 4 * lq + (l16 >> 2);
-  const int col = 16 * dt + 4 * (l16 & 3);
-  const int ch = col >> 3, sub = col & 7;
-  const uint2 a = ds_read_tr(T + swt(row0, ch) + sub);
-  const uint2 b = ds_read_tr(T + swt(row0 + 16, ch) + sub);
-  return as_bf16x8(a, b);
-}
 
 struct ItemGeom {
   int hq, r, gk, b, hl, h;
@@ -356,17 +328,18 @@ sbwd_dq_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw, const
 
 #pragma unroll
   for (int x = 0; x < 3; ++x)
-    if (x < nsel) dma_block(kc, vc, it.row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
+    if (x < nsel) dma_block<true>(kc, vc, it.row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
   if (nsel > 2) wait_vmcnt<2 * DMA_PER_WAVE>();
   else if (nsel > 1) wait_vmcnt<DMA_PER_WAVE>();
   else wait_vmcnt<0>();
   __syncthreads();
+  // K tiles in the swzv layout: read by rows for the scores and transposed for dq
   auto step = [&](int e, bool diag) {
-    if (e + 3 < nsel) dma_block(kc, vc, it.row_base, blk(e + 3), kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
+    if (e + 3 < nsel) dma_block<true>(kc, vc, it.row_base, blk(e + 3), kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
     const bf16_t* Ks = lds[e & 3][0];
     const bf16_t* Vs = lds[e & 3][1];
     f32x4 ST[4][SB_QT], PT[4][SB_QT];
-    scores<SB_QT>(Ks, qf, minit, ST, l16);
+    scores<SB_QT, true>(Ks, qf, minit, ST, l16);
     if (diag) mask_diag<SB_QT>(ST, l16, lq, qrow0);
     // dP^T[key][query] = V dO^T (A = V rows, k = dv)
 #pragma unroll
@@ -395,7 +368,7 @@ sbwd_dq_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw, const
       }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 a = ktr_frag(Ks, 32 * c, dt, l16, lq);
+        const bf16x8 a = vt_frag(Ks, 32 * c, dt, l16, lq);
 #pragma unroll
         for (int qt = 0; qt < SB_QT; ++qt) QT[dt][qt] = mfma16x16x32(a, sf[qt], QT[dt][qt]);
       }
@@ -545,7 +518,7 @@ struct DkvLds {
   int n;
 };
 
-// copies of one step: q~ and dO tiles in the swt layout (16 pieces of 1 KB each, wave w moves
+// copies of one step: q~ and dO tiles in the swzv layout (16 pieces of 1 KB each, wave w moves
 // 4w .. 4w+3 of both) and, by wave 0, the 1 KB stats rows
 __device__ __forceinline__ void dma_step(const bf16_t* qtb, const bf16_t* dob, const float* stb, long pad0,
                                          DkvLds& L, int bufi) {
@@ -554,7 +527,7 @@ __device__ __forceinline__ void dma_step(const bf16_t* qtb, const bf16_t* dob, c
   for (int m = 0; m < 4; ++m) {
     const int I = 4 * wave + m;
     const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ swt_of(row);
+    const int ch = (lane & 15) ^ (2 * (row & 7));
     const long off = (pad0 + row) * D + 8 * ch;
     dma16(qtb + off, lds_addr_u32(L.qd[bufi][0] + I * 512));
     dma16(dob + off, lds_addr_u32(L.qd[bufi][1] + I * 512));
@@ -644,8 +617,8 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          qa[qt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(Qs + swt(32 * qh + 16 * qt + l16, 4 * ks + lq)));
-          da[qt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(Ds + swt(32 * qh + 16 * qt + l16, 4 * ks + lq)));
+          qa[qt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(Qs + swzv(32 * qh + 16 * qt + l16, 4 * ks + lq)));
+          da[qt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(Ds + swzv(32 * qh + 16 * qt + l16, 4 * ks + lq)));
         }
       // C layout: query 32qh + 16qt + 4lq + e, key 16kt + l16; S starts at -lse2
       f32x4 S[2], P[2];
@@ -663,7 +636,7 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
         }
       bf16x8 tv[8];  // dO^T fragments of this half, read while the products run
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) tv[dt] = ktr_frag_t(Ds, 32 * qh, dt, l16, lq);
+      for (int dt = 0; dt < 8; ++dt) tv[dt] = vt_frag(Ds, 32 * qh, dt, l16, lq);
       float pv[8], dsv[8];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
@@ -679,7 +652,7 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
       const bf16x8 pf = as_bf16x8(pack8(pv)), sf = as_bf16x8(pack8(dsv));
       bf16x8 tk[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) tk[dt] = ktr_frag_t(Qs, 32 * qh, dt, l16, lq);
+      for (int dt = 0; dt < 8; ++dt) tk[dt] = vt_frag(Qs, 32 * qh, dt, l16, lq);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) dVT[dt] = mfma16x16x32(tv[dt], pf, dVT[dt]);
 #pragma unroll

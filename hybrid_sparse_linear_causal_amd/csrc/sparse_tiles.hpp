@@ -14,11 +14,8 @@ constexpr int SP_D = 128;  // head dim of the bf16 paths
 constexpr int TILE = 64 * SP_D;  // bf16 elements per 64-row tile
 constexpr int NSTAGE = 4;       // LDS ring depth (blocks resident or in flight)
 
-// V tiles use their own swizzle: chunk c of row r sits at chunk position c ^ 2(r & 7). The
-// transposing reads of 32 lanes touch 8 consecutive rows x 2 adjacent chunks; this puts those
-// 16 chunks at 16 different positions, so they never share a bank (the K swizzle would put two
-// rows on the same banks).
-__device__ __forceinline__ int swzv(int row, int chunk) { return row * 128 + 8 * (chunk ^ (2 * (row & 7))); }
+// V tiles use the swzv layout (transposing reads); K tiles use swz, or swzv where they are also
+// read transposed (template parameter KV of the DMA and the scores).
 
 // Issue the DMA of one 64-key block (K and V tiles, 16 KB each = 16 pieces of 1 KB) into a
 // stage. With 8 waves each wave moves pieces 2w and 2w+1 (rows 8w .. 8w+7) of both tiles:
@@ -26,6 +23,7 @@ __device__ __forceinline__ int swzv(int row, int chunk) { return row * 128 + 8 *
 // so it loads the source chunk that the tile's swizzle puts there. Rows at or beyond kv_len
 // are clamped to the last valid row: they are causally masked (K) or weighted 0 (V).
 constexpr int DMA_PER_WAVE = 4;
+template <bool KV = false>
 __device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, long row_base,
                                           long blk, long kv_len, bf16_t* Ks, bf16_t* Vs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -33,7 +31,7 @@ __device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, lo
   for (int m = 0; m < 2; ++m) {
     const int I = 2 * wave + m;                 // 1 KB piece: rows 4I .. 4I+3
     const int row = 4 * I + (lane >> 4);
-    const int chk = (lane & 15) ^ (row & 15);   // K source chunk stored at this position
+    const int chk = (lane & 15) ^ (KV ? 2 * (row & 7) : (row & 15));  // K source chunk stored here
     const int chv = (lane & 15) ^ (2 * (row & 7));
     long p = blk * 64 + row;
     if (p >= kv_len) p = kv_len - 1;
@@ -62,7 +60,7 @@ __device__ __forceinline__ bf16x8 vt_frag(const bf16_t* Vs, int kb, int dt, int 
 
 // S^T[kt][qt] = K[kt] Q^T[qt] - m[qt] (scores in log2 units: scale*log2(e) is folded into q;
 // the running reference m enters as the accumulator's initial value, minit = -m)
-template <int QT>
+template <int QT, bool KV = false>
 __device__ __forceinline__ void scores(const bf16_t* Ks, const bf16x8 (&qf)[QT][4], const f32x4 (&minit)[QT],
                                        f32x4 (&ST)[4][QT], int l16) {
   const int lq = (threadIdx.x & 63) >> 4;
@@ -73,7 +71,8 @@ __device__ __forceinline__ void scores(const bf16_t* Ks, const bf16x8 (&qf)[QT][
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int kt = kp; kt < kp + 2; ++kt) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + swz(16 * kt + l16, 4 * ks + lq)));
+        const int off = KV ? swzv(16 * kt + l16, 4 * ks + lq) : swz(16 * kt + l16, 4 * ks + lq);
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(Ks + off));
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) ST[kt][qt] = mfma16x16x32(a, qf[qt][ks], ks == 0 ? minit[qt] : ST[kt][qt]);
       }
