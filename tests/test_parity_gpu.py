@@ -238,7 +238,9 @@ def test_block_select_planted_needles_and_ties(S):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,topk", [(2, 32, 2, 64 * 50 + 13, 16), (1, 16, 1, 64 * 50, 64),
-                                             (2, 8, 2, 64 * 3 + 1, 8), (1, 4, 1, 40, 4)])
+                                             (2, 8, 2, 64 * 3 + 1, 8), (1, 4, 1, 40, 4),
+                                             # more blocks than the 64 decode waves of a KV group
+                                             (1, 16, 2, 64 * 300 + 3, 160)])
 def test_sparse_decode(S, B, Hq, Hkv, L, topk):
     """Decode at p = L - 1 over a synthetic cache of already-normalised keys (the same bits on
     both sides): append the new token, select, attend."""
@@ -356,11 +358,14 @@ def test_dense_attn_prefill(S, B, N, Hq, Hkv, dtype):
     assert_rel(host(out), ref, TOL[dtype], "dense out")
 
 
-def test_dense_attn_decode(S):
-    """One decode token over a cache of already-normalised keys, every block attended."""
+@pytest.mark.parametrize("L", [64 * 30 + 7, 64 * 150 + 7])
+def test_dense_attn_decode(S, L):
+    """One decode token over a cache of already-normalised keys, every block attended (151
+    blocks: some decode waves take three blocks in turn, reusing their LDS tile)."""
     import torch
 
-    B, Hq, Hkv, d, L = 2, 32, 2, 128, 64 * 30 + 7
+    B, Hq, Hkv, d = 2, 32, 2, 128
+    print(f"dense_attn_decode L={L}", flush=True)
     cap = ((L + 63) // 64) * 64
     kc_h = host_normal(51, 5, (B, Hkv, L - 1, d), "bf16")
     vc_h = host_normal(51, 6, (B, Hkv, L - 1, d), "bf16")
