@@ -274,24 +274,28 @@ struct OutLds {
 };
 static_assert(sizeof(OutLds) == 163840, "output-pass LDS plan");
 
-// DMA the four raw tiles of a chunk: 64 pieces of 1 KB, 8 per wave (wave w: pieces 2w, 2w+1
-// of each tile, rows 8w .. 8w+7). Rows past the sequence end are clamped to its last row
+// DMA of one raw tile X (0 q, 1 k, 2 v, 3 g) of a chunk: 16 pieces of 1 KB shared by NW waves
+// (NW 8: wave w moves pieces 2w, 2w+1; NW 4: waves 0-3 move pieces 4w .. 4w+3); q and g in the
+// swz layout, k and v in swzv. The CU's vector memory path takes one 1 KB copy per 16 cycles
+// and a wave stalls at issue while it is backed up (64 copies issued at once held the state
+// waves for 1,900 cycles), so the next chunk's q and k are issued at the start of a chunk by
+// every wave and its v and g after the prep by the output waves, which would otherwise wait
+// for the state waves at the barrier. Rows past the sequence end are clamped to its last row
 // (finite values; k rows past the end are zeroed by the prep, so they contribute nothing).
 constexpr int OUT_NT = 512;  // 8 waves: 0-3 produce outputs, 4-7 update the state
+template <int X, int NW>
 __device__ __forceinline__ void dma_chunk(const bf16_t* q, const bf16_t* k, const bf16_t* v,
                                           const bf16_t* g, long row0, int t0, int n_valid, int H,
                                           bf16_t (*T)[CH * D]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bf16_t* src = X == 0 ? q : X == 1 ? k : X == 2 ? v : g;
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int I = 2 * wave + m;
+  for (int m = 0; m < 16 / NW; ++m) {
+    const int I = (16 / NW) * wave + m;
     const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (row & 15), chv = (lane & 15) ^ (2 * (row & 7));
-    const long src = row0 + (long)(min(t0 + row, n_valid - 1) - t0) * H * D;
-    dma16(q + src + 8 * ch, lds_addr_u32(T[0] + I * 512));
-    dma16(k + src + 8 * chv, lds_addr_u32(T[1] + I * 512));
-    dma16(v + src + 8 * chv, lds_addr_u32(T[2] + I * 512));
-    dma16(g + src + 8 * ch, lds_addr_u32(T[3] + I * 512));
+    const int ch = (X == 1 || X == 2) ? (lane & 15) ^ (2 * (row & 7)) : (lane & 15) ^ (row & 15);
+    const long off = row0 + (long)(min(t0 + row, n_valid - 1) - t0) * H * D + 8 * ch;
+    dma16(src + off, lds_addr_u32(T[X] + I * 512));
   }
 }
 
@@ -319,7 +323,13 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const long head_off = (it.tok0 * H + h) * D;
   const long tok_stride = (long)H * D;
 
-  dma_chunk(q, k, v, g, head_off + (long)t_begin * tok_stride, t_begin, N, H, L.t[0]);
+  {
+    const long r0 = head_off + (long)t_begin * tok_stride;
+    dma_chunk<0, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
+    dma_chunk<1, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
+    dma_chunk<2, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
+    dma_chunk<3, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
+  }
 
   // acc: state waves keep S[dk][dv] (C layout, dk rows 32*w4 .. +31) in acc[8*it + jt];
   // output waves use acc[0..7] for their O^T tiles. One array, so the roles share registers.
@@ -359,14 +369,16 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     wk[8 + e] = HAS_W && kw ? kw[64 + 8 * s8 + e] : 1.0f;
   }
 
-  // RoPE phases of this thread's token (in revolutions, reduced to [-1/2, 1/2]): exact at the
-  // segment start (fp64 reduction) and advanced by frac(64 f) per chunk in fp32, set up once
-  // (indexing the argument block per lane compiles to memory loads)
-  float ph[8], dph[8];
+  // RoPE of this thread's token: cos/sin of its 8 angles, exact at the segment start (fp64
+  // reduction) and advanced by the rotation of 64 positions per chunk, as the segment-sum pass
+  // does (so both passes rotate k identically); set up once (indexing the argument block per
+  // lane compiles to memory loads)
+  float rc[8], rs[8], ac[8], as[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    ph[e] = rope_rev((double)(pos0 + t_begin + tok), freqs.f[8 * s8 + e]);
-    dph[e] = rope_rev(64.0, freqs.f[8 * s8 + e]);
+    sincos_rev(rope_rev((double)(pos0 + t_begin + tok), freqs.f[8 * s8 + e]), &rs[e], &rc[e]);
+    ac[e] = freqs.c64[8 * s8 + e];
+    as[e] = freqs.s64[8 * s8 + e];
   }
 
   wait_vmcnt<0>();
@@ -378,9 +390,14 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* Vt = L.t[buf][2];
     const bf16_t* Gt = L.t[buf][3];
     // the next chunk's tiles stream into the other buffer (free since the last barrier) for
-    // the whole of this chunk
-    if (c0 + CH < t_end)
-      dma_chunk(q, k, v, g, head_off + (long)(c0 + CH) * tok_stride, c0 + CH, N, H, L.t[buf ^ 1]);
+    // the rest of this chunk: q and k now, v and g after the prep
+    const bool next = c0 + CH < t_end;
+    const long nrow0 = head_off + (long)(c0 + CH) * tok_stride;
+    bf16_t (*nbuf)[CH * D] = L.t[buf ^ 1];
+    if (next) {
+      dma_chunk<0, 8>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
+      dma_chunk<1, 8>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
+    }
     // ---------------- prep in place: QK-norm + RoPE (rows past the end: k~ = 0)
     {
       uint4 xq[2], xk[2];
@@ -388,13 +405,6 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       xq[1] = *reinterpret_cast<const uint4*>(&Qt[swz(tok, s8 + 8)]);
       xk[0] = *reinterpret_cast<const uint4*>(&Kt[swzv(tok, s8)]);
       xk[1] = *reinterpret_cast<const uint4*>(&Kt[swzv(tok, s8 + 8)]);
-      float rc[8], rs[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sincos_rev(ph[e], &rs[e], &rc[e]);
-        const float x = ph[e] + dph[e];
-        ph[e] = x - rintf(x);
-      }
       norm_rope_w(xq, wq, eps, rc, rs);
       norm_rope_w(xk, wk, eps, rc, rs);
       if (c0 + tok >= t_end) { xk[0] = make_uint4(0, 0, 0, 0); xk[1] = xk[0]; }
@@ -402,6 +412,16 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       *reinterpret_cast<uint4*>(&Qt[swz(tok, s8 + 8)]) = xq[1];
       *reinterpret_cast<uint4*>(&Kt[swzv(tok, s8)]) = xk[0];
       *reinterpret_cast<uint4*>(&Kt[swzv(tok, s8 + 8)]) = xk[1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float c = rc[e], s = rs[e];
+        rc[e] = c * ac[e] - s * as[e];
+        rs[e] = s * ac[e] + c * as[e];
+      }
+    }
+    if (next && out_wave) {
+      dma_chunk<2, 4>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
+      dma_chunk<3, 4>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
     }
     __syncthreads();
 
