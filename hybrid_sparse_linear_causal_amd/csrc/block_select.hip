@@ -44,22 +44,33 @@ qtilde_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __re
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
     if (h < Hq) {
-      for (long p = p_lo; p < p_hi; ++p) {
-        const T* src = q + (((long)b * n_q + (p - q0)) * Hq + h) * DD + seg * EPL;
-        float x[EPL];
-        if constexpr (sizeof(T) == 2) {
-          unpack8(*reinterpret_cast<const uint4*>(src), x);
-        } else {
-          const float4 u = *reinterpret_cast<const float4*>(src);
-          x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+      // 8 tokens' loads in flight before any of them is reduced
+      for (long p0 = p_lo; p0 < p_hi; p0 += 8) {
+        uint4 raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const long p = p0 + u;
+          raw[u] = p < p_hi ? *reinterpret_cast<const uint4*>(q + (((long)b * n_q + (p - q0)) * Hq + h) * DD + seg * EPL)
+                            : make_uint4(0, 0, 0, 0);
         }
-        float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
-        ss = group_sum<LPR>(ss);
-        const float inv = 1.0f / sqrtf(ss / DD + eps);
+        for (int u = 0; u < 8; ++u) {
+          if (p0 + u >= p_hi) break;  // uniform over the workgroup
+          float x[EPL];
+          if constexpr (sizeof(T) == 2) {
+            unpack8(raw[u], x);
+          } else {
+            x[0] = __uint_as_float(raw[u].x); x[1] = __uint_as_float(raw[u].y);
+            x[2] = __uint_as_float(raw[u].z); x[3] = __uint_as_float(raw[u].w);
+          }
+          float ss = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += x[e] * inv;
+          for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+          ss = group_sum<LPR>(ss);
+          const float inv = 1.0f / sqrtf(ss / DD + eps);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] += x[e] * inv;
+        }
       }
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
