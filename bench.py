@@ -143,8 +143,8 @@ def main():
                     help="stack_256k: the headline line; segmented_1m: 1M-token prefill in segments + decode")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
-              f"multi-GPU path; the sharding design is described in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no "
+              f"multi-GPU path; each GPU would run its own heads or sequences independently.", file=sys.stderr)
         sys.exit(2)
     if args.workload == "segmented_1m":
         segmented_1m(args)

@@ -128,7 +128,7 @@ const char* sala_status_str(sala_status s) {
     case SALA_OK: return "ok";
     case SALA_ERR_NULL: return "a required pointer is NULL";
     case SALA_ERR_INVALID: return "invalid sizes, parameters or alignment";
-    case SALA_ERR_UNSUPPORTED: return "shape or dtype not supported by this build";
+    case SALA_ERR_UNSUPPORTED: return "shape or dtype not supported by this library";
     case SALA_ERR_WORKSPACE: return "workspace missing or too small";
     case SALA_ERR_HIP: return "HIP kernel launch failed";
   }

@@ -45,7 +45,7 @@ typedef enum {
   SALA_OK = 0,
   SALA_ERR_NULL = 1,        /* a required pointer is NULL */
   SALA_ERR_INVALID = 2,     /* inconsistent or out-of-range sizes / parameters / alignment */
-  SALA_ERR_UNSUPPORTED = 3, /* valid, but not a shape or dtype this build implements */
+  SALA_ERR_UNSUPPORTED = 3, /* valid, but not a shape or dtype this library implements */
   SALA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than sala_workspace_bytes() */
   SALA_ERR_HIP = 5          /* a kernel launch failed */
 } sala_status;
@@ -66,7 +66,7 @@ typedef enum {
 /* Linear-attention layer shape.
  *   batch      B >= 1
  *   seq_len    N tokens in this call (prefill: N >= 0; decode: must be 1)
- *   n_heads    H query heads; n_kv_heads must equal n_heads in this build
+ *   n_heads    H query heads; n_kv_heads must equal n_heads (grouped linear heads: SALA_ERR_UNSUPPORTED)
  *   head_dim   d: 64 or 128 (bf16 prefill needs 128)
  *   dtype      sala_dtype of q, k, v, gate and out
  *   pos0       position of the first token of the call (>= 0); RoPE uses p = pos0 + t
