@@ -313,7 +313,8 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
   bf16_t* vt = vts[wave];  // this wave's own V tile: no workgroup barrier needed
   for (int e = split * 4 + wave; e < nsel; e += stride) {
     const int su = e >> 6;
-    const long blk = DENSE ? (long)e : (long)__shfl(su == 0 ? sv[0] : su == 1 ? sv[1] : su == 2 ? sv[2] : sv[3], e & 63, 64);
+    long blk = DENSE ? (long)e : (long)__shfl(su == 0 ? sv[0] : su == 1 ? sv[1] : su == 2 ? sv[2] : sv[3], e & 63, 64);
+    if (blk < 0) blk = 0;  // a malformed row (-1 before its end) must not read before the cache
     // K in MFMA A layout (key 16kt + l16, dims 32ks + 8lq ..) into registers
     uint4 kk[4][4];
 #pragma unroll

@@ -215,7 +215,10 @@ sala_status sala_block_select(const sala_sparse_desc* desc, const void* q, const
  *   out[t,h] = softmax_s(scale * q^ . k_cache[s]) . v_cache[s] * sigmoid(gate[t, h])
  * where q^ = RMSNorm(q) * q_norm_w and the cache holds already-normalised keys. The bf16 path
  * uses MFMA (bf16 operands, fp32 accumulation and fp32 online softmax).
- * q, gate, out: [B, n_q, Hq, d]; caches as in sala_kv_append; sel as from sala_block_select.
+ * q, gate, out: [B, n_q, Hq, d]; caches as in sala_kv_append; sel as from sala_block_select:
+ *   ascending block indices of 0 .. i ending with i, then -1. Other contents are not checked on
+ *   the device: they give unspecified outputs, but every read stays inside the caches (indices
+ *   are clamped to the cache rows that exist).
  * lse: NULL, or [B, n_q, Hq] float receiving each row's log2-sum-exp2 of its scaled scores,
  *   log2 sum_s exp2(scale * log2(e) * q^ . k_cache[s]) (the state a backward pass can reuse,
  *   see sala_sparse_attn_backward); bf16 prefill (n_q > 1) only, else SALA_ERR_UNSUPPORTED.
