@@ -645,11 +645,13 @@ static long select_row_len(const sala_sparse_desc& d) {
   return g.qb0 + g.nqb;  // blocks 0 .. i_max
 }
 
-// decode (one query block) uses the two-level selection while the candidates fit DNSL_MAX
-// slices; it needs nsl * R composites per row instead of the score row
+// decode (a single query token) uses the two-level selection while the candidates fit
+// DNSL_MAX slices; it needs nsl * R composites per row instead of the score row. The slice
+// kernel forms q~ from the one token of each sequence, so a call with several query tokens in
+// one block (a short continued prompt) takes the q~ kernel's block mean and the score-row path.
 static bool decode_two_level(const sala_sparse_desc& d, long* nc_out, int* nsl_out, int* r_out) {
   const SparseGeom g = sparse_geom(d);
-  if (g.nqb != 1) return false;
+  if (d.n_q != 1 || g.nqb != 1) return false;
   const long i = g.qb0;
   const long nc = i - d.n_local > 0 ? i - d.n_local : 0;
   const long f_lo = i - d.n_local + 1 > 0 ? i - d.n_local + 1 : 0;

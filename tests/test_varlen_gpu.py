@@ -63,6 +63,9 @@ def _sparse_full(seed, F, Hq, Hkv, d):
 @pytest.mark.parametrize("new,prefix,Hq,Hkv,topk", [
     ([200, 0, 640, 64, 1, 333], [0, 64, 128, 0, 192, 640], 4, 2, 4),
     ([1500, 130], [0, 256], 32, 2, 8),                  # a full GQA group of 16 heads
+    # continuations of a few tokens inside one query block after a cached prefix: the block
+    # mean of their queries selects (not the single-token decode path)
+    ([10, 64, 2, 1], [640, 640, 1280, 704], 8, 2, 4),
 ])
 def test_sparse_layer_varlen(S, new, prefix, Hq, Hkv, topk):
     """Prefixes appended first (one varlen call from position 0), then the new tokens appended,
