@@ -66,3 +66,27 @@ def check_selection(gpu_sel, ref_sel, scores_fn, topk, n_local, first_block=0):
                     assert sc[j] >= s_r - MARGIN, (b, g, i, j, sc[j], s_r)
                 by_margin += 1
     return by_margin
+
+
+def oracle_decode_on_selection(q_hat, k_cache_hat, v_cache, k_hat_new, v_new, sel_row, scale):
+    """The oracle's sparse attention (O.sparse_attention) for one decode query over the blocks
+    of a given selection row (the GPU's), for the query heads of one KV group.
+
+    q_hat [G, d] (normalised queries); k_cache_hat, v_cache [p, d]: the normalised keys and the
+    values of positions 0 .. p-1; k_hat_new, v_new [d]: the token at position p (the query's own).
+    The selected blocks are gathered in ascending order and renumbered 0 .. m-1; the query's
+    own block is the last of them, so the oracle's token-level causal mask applies unchanged at
+    the query's renumbered position. Returns o [G, d] (before the gate)."""
+    p = k_cache_hat.shape[0]
+    blks = [int(j) for j in sel_row if j >= 0]
+    assert blks == sorted(set(blks)) and blks[-1] == p // 64, (blks, p)
+    old = np.concatenate([np.arange(j * 64, min(p, j * 64 + 64)) for j in blks])
+    K = np.concatenate([np.asarray(k_cache_hat)[old].astype(np.float64), np.asarray(k_hat_new, np.float64)[None]])
+    V = np.concatenate([np.asarray(v_cache)[old].astype(np.float64), np.asarray(v_new, np.float64)[None]])
+    m = len(blks)
+    sel_c = np.full((1, 1, m, len(sel_row)), -1, dtype=np.int64)
+    sel_c[0, 0, m - 1, :m] = np.arange(m)
+    q_pos = (m - 1) * 64 + (p - blks[-1] * 64)
+    assert q_pos == K.shape[0] - 1
+    return O.sparse_attention(np.asarray(q_hat, np.float64)[None, None], K[None, :, None], V[None, :, None],
+                              sel_c, 64, scale, q_positions=[q_pos])[0, 0]

@@ -1,10 +1,10 @@
 """GPU parity of the backward entry points against the gradient oracle (float64 autograd of the
 forward definitions, oracle/sala_oracle_grad.py) on the same bf16-representable seeded inputs.
 
-Tolerance: max|gpu - ref| <= 2e-2 * max|ref| per gradient. The kernels feed MFMA with bf16
-operands (the normalised, rotated q and k, dO = dout * sigmoid(g), the intra-chunk score tile
-and the chunk-entry state), each a relative rounding of at most 2^-9, and every gradient passes
-through two such products, plus the fp32 norm / RoPE / gate transposes; 2e-2 bounds that
+Tolerance: max|gpu - ref| <= 1e-2 * max|ref| per gradient, the bf16 bar of the forward. The
+kernels feed MFMA with bf16 operands (the normalised, rotated q and k, dO = dout * sigmoid(g),
+the intra-chunk score tile and the chunk-entry state), each a relative rounding of at most 2^-9,
+and every gradient passes through two such products plus the fp32 norm / RoPE / gate transposes
 (measured errors are listed in the test output)."""
 
 import numpy as np
@@ -16,7 +16,7 @@ from sala_testutil import assert_rel, dev, host
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-2
+TOL = 1e-2
 
 
 @pytest.fixture(scope="module")
@@ -195,4 +195,4 @@ def test_sparse_attn_backward_from_saved_forward(S):
             keys = keys[keys <= t]
             s = (c["k_hat"][0, keys, gk] @ qh[0, t, h]) / np.sqrt(128)
             want = logsumexp(s) / np.log(2)
-            assert abs(got[0, t, h] - want) <= 2e-2 * max(1.0, abs(want)), (t, h, got[0, t, h], want)
+            assert abs(got[0, t, h] - want) <= 1e-2 * max(1.0, abs(want)), (t, h, got[0, t, h], want)

@@ -24,7 +24,7 @@ from sala_testutil import assert_rel, check_selection, host
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-2  # the backward tolerance (bf16 operands in two products per gradient)
+TOL = 1e-2  # the bf16 bar, for the forward and the backward alike
 
 
 @pytest.fixture(scope="module")

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from sala_testutil import assert_rel, check_selection, host
+from sala_testutil import assert_rel, check_selection, host, oracle_decode_on_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,8 @@ def test_decode_full_size(S):
                              Dw.n_local, first_block=i)
         if nm == 0:
             assert_rel(host(out[b:b + 1, 0, gk * G:(gk + 1) * G]), ref["out"], 1e-2, f"decode {(b, gk)}")
+        # rows accepted by the margin rule included: the oracle's attention on the GPU's selection
+        o2 = oracle_decode_on_selection(O.qk_norm(qs)[0], kch[0, 0], vch[0, 0], O.qk_norm(kns[0, 0]),
+                                        vns[0, 0], gsel[b, gk, 0], 1.0 / math.sqrt(d))
+        assert_rel(host(out[b:b + 1, 0, gk * G:(gk + 1) * G]), (o2 * O.sigmoid(gs[0]))[None], 1e-2,
+                   f"decode {(b, gk)} on the gpu selection")

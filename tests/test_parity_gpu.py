@@ -8,7 +8,7 @@ import pytest
 
 import oracle as O
 from hybrid_sparse_linear_causal_amd.inputs import host_normal
-from sala_testutil import assert_rel, check_selection, dev, host
+from sala_testutil import assert_rel, check_selection, dev, host, oracle_decode_on_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -280,18 +280,14 @@ def test_sparse_decode(S, B, Hq, Hkv, L, topk):
     nm = check_selection(gsel, ref["sel"][:, :, None], scores, topk, n_local, first_block=i)
     if nm == 0:
         assert_rel(host(out)[:, 0], ref["out"], 1e-2, "decode out")
-    else:  # rerun the oracle's attention on the GPU's selection
-        o2 = np.empty_like(ref["out"])
-        for b in range(B):
-            for gg in range(Hkv):
-                K = np.concatenate([kc_h[b, gg], O.qk_norm(kn[b, 0, gg])[None]]).astype(np.float64)
-                V = np.concatenate([vc_h[b, gg], vn[b, 0, gg][None]]).astype(np.float64)
-                keys = np.concatenate([np.arange(j * 64, min(L, j * 64 + 64)) for j in gsel[b, gg, 0] if j >= 0])
-                for h in range(gg * G, (gg + 1) * G):
-                    s = K[keys] @ qh[b, h] / np.sqrt(d)
-                    w = np.exp(s - s.max())
-                    o2[b, h] = (w / w.sum()) @ V[keys] * O.sigmoid(g[b, 0, h])
-        assert_rel(host(out)[:, 0], o2, 1e-2, "decode out (gpu selection)")
+    # the oracle's attention on the GPU's selection, always
+    o2 = np.empty_like(ref["out"])
+    for b in range(B):
+        for gg in range(Hkv):
+            o2[b, gg * G:(gg + 1) * G] = oracle_decode_on_selection(
+                qh[b, gg * G:(gg + 1) * G], kc_h[b, gg], vc_h[b, gg], O.qk_norm(kn[b, 0, gg]), vn[b, 0, gg],
+                gsel[b, gg, 0], 1.0 / np.sqrt(d))
+    assert_rel(host(out)[:, 0], o2 * O.sigmoid(g[:, 0]), 1e-2, "decode out (gpu selection)")
 
 
 def test_decode_select_exact_ties_across_slices(S):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from sala_testutil import assert_rel, check_selection, dev, host
+from sala_testutil import assert_rel, check_selection, dev, host, oracle_decode_on_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -161,3 +161,10 @@ def test_sparse_segmented_1m_context_sampled(S):
                          first_block=i)
     if nm == 0:
         assert_rel(host(out[:, 0, gk * G:(gk + 1) * G]), ref["out"], 1e-2, "decode at 1M")
+    # rows accepted by the margin rule included: the oracle's attention on the GPU's selection
+    o2 = oracle_decode_on_selection(O.qk_norm(qd[:, 0, gk * G:(gk + 1) * G].float().cpu().numpy())[0], kch[0, 0],
+                                    vch[0, 0], O.qk_norm(kd[0, 0, gk].float().cpu().numpy()),
+                                    vd[0, 0, gk].float().cpu().numpy(), sel.cpu().numpy()[0, gk, 0], 1.0 / math.sqrt(d))
+    assert_rel(host(out[:, 0, gk * G:(gk + 1) * G]),
+               (o2 * O.sigmoid(gd[0, 0, gk * G:(gk + 1) * G].float().cpu().numpy()))[None], 1e-2,
+               "decode at 1M on the gpu selection")
