@@ -5,10 +5,34 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "sala.h"
 
+// Scratch memory of sala_sparse_decode_step_noalloc: one copy per device the library runs on,
+// held until the process ends. Host code never uses this name as an address (on the host it is
+// a stand-in symbol); it uses the device address looked up per device below.
+static __device__ __align__(256) unsigned char scratch[SALA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// per-device address of `scratch`, looked up once per device with that device current
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
 
 thread_local int g_last_hip_error = 0;
 
@@ -269,6 +293,35 @@ sala_status sala_sparse_decode_step(const sala_sparse_desc* desc, const int64_t*
                                       static_cast<char*>(workspace) + a, st);
   }
   return hip_status(e);
+}
+
+sala_status sala_sparse_decode_step_noalloc(const sala_sparse_desc* desc, const int64_t* kv_lens, const void* q,
+                                            const float* q_norm_w, const void* k_new, const void* v_new,
+                                            const float* k_norm_w, const void* gate, void* k_cache, void* v_cache,
+                                            float* k_pool, int32_t* sel, void* out, void* stream) {
+  const sala_status s = check_sparse_decode_at(desc);
+  if (s != SALA_OK) return s;
+  if (!kv_lens || !q || !k_new || !v_new || !gate || !k_cache || !v_cache || !k_pool || !sel || !out)
+    return SALA_ERR_NULL;
+  if (!all_aligned({q, q_norm_w, k_new, v_new, k_norm_w, gate, k_cache, v_cache, k_pool, sel, out}) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 7u))
+    return SALA_ERR_INVALID;
+  if (sparse_decode_step_workspace(*desc) > SALA_NOALLOC_SCRATCH_BYTES) return SALA_ERR_WORKSPACE;
+  // the scratch copy of the device the work runs on: the stream's, which must be current
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return hip_status(e);
+    if (sdev != dev) return SALA_ERR_INVALID;
+  }
+  void* ws = nullptr;
+  e = scratch_address(dev, &ws);
+  if (e != hipSuccess) return hip_status(e);
+  return sala_sparse_decode_step(desc, kv_lens, q, q_norm_w, k_new, v_new, k_norm_w, gate, k_cache, v_cache, k_pool,
+                                 sel, out, ws, SALA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 sala_status sala_kv_append(const sala_sparse_desc* desc, const void* k_new, const void* v_new,

@@ -61,6 +61,7 @@ def lib():
         L.sala_linear_decode_step.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 9
         L.sala_linear_decode_step_at.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 10
         L.sala_sparse_decode_step.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 13 + [ctypes.c_size_t, _VP]
+        L.sala_sparse_decode_step_noalloc.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 13
         L.sala_linear_backward.argtypes = [ctypes.POINTER(LinearDesc)] + [_VP] * 17 + [ctypes.c_size_t, _VP]
         L.sala_sparse_attn_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 15 + [ctypes.c_size_t, _VP]
         L.sala_kv_norm_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 6 + [ctypes.c_size_t, _VP]
@@ -88,7 +89,8 @@ def lib():
                      "sala_block_select", "sala_sparse_attn", "sala_dense_attn",
                      "sala_sparse_layer_uses_dense", "sala_abi_version", "sala_last_hip_error",
                      "sala_linear_prefill_varlen", "sala_kv_append_varlen", "sala_block_select_varlen",
-                     "sala_sparse_attn_varlen", "sala_linear_decode_step_at", "sala_sparse_decode_step"):
+                     "sala_sparse_attn_varlen", "sala_linear_decode_step_at", "sala_sparse_decode_step",
+                     "sala_sparse_decode_step_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -262,6 +264,30 @@ def sparse_decode_step(q, k_new, v_new, g, k_cache, v_cache, k_pool, kv_lens, kv
     _call(lib().sala_sparse_decode_step, ctypes.byref(desc), _ptr(kv_lens), _ptr(q), _ptr(q_norm_w), _ptr(k_new),
           _ptr(v_new), _ptr(k_norm_w), _ptr(g), _ptr(k_cache), _ptr(v_cache), _ptr(k_pool), _ptr(sel), _ptr(out),
           _ptr(ws), ws_bytes, _stream(stream), what="sparse_decode_step")
+    return out, sel
+
+
+def sparse_decode_step_noalloc(q, k_new, v_new, g, k_cache, v_cache, k_pool, kv_lens, kv_max, *, topk=64,
+                               n_local=2, eps=1e-6, scale=0.0, q_norm_w=None, k_norm_w=None, sel=None, out=None,
+                               stream=None):
+    """sparse_decode_step with the library's static scratch array instead of a workspace (nothing
+    is allocated by the library; sel and out are allocated here only when not given)."""
+    for n, t in (("q", q), ("g", g), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                 ("v_cache", v_cache)):
+        _check(t, n, torch.bfloat16)
+    _check(k_pool, "k_pool", torch.float32)
+    _check(kv_lens, "kv_lens", torch.int64)
+    B, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    desc = sparse_desc(batch=B, n_q=1, n_heads=Hq, n_kv_heads=Hkv, head_dim=d, dtype=q.dtype, kv_len=kv_max,
+                       kv_capacity=cap, topk=topk, n_local=n_local, eps=eps, scale=scale)
+    if sel is None:
+        sel = torch.empty((B, Hkv, topk), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _call(lib().sala_sparse_decode_step_noalloc, ctypes.byref(desc), _ptr(kv_lens), _ptr(q), _ptr(q_norm_w),
+          _ptr(k_new), _ptr(v_new), _ptr(k_norm_w), _ptr(g), _ptr(k_cache), _ptr(v_cache), _ptr(k_pool), _ptr(sel),
+          _ptr(out), _stream(stream), what="sparse_decode_step_noalloc")
     return out, sel
 
 

@@ -287,6 +287,26 @@ sala_status sala_sparse_decode_step(const sala_sparse_desc* desc, const int64_t*
                                     float* k_pool, int32_t* sel, void* out, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* Scratch bytes of sala_sparse_decode_step_noalloc (a static device array per device). */
+#define SALA_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc): sala_sparse_decode_step with its scratch memory taken
+ * from a static device array of SALA_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * device it runs on until the process ends, instead of a caller workspace. The library allocates
+ * nothing during the call. Arguments, layouts and results are those of sala_sparse_decode_step
+ * without the workspace. The work runs on the current device; a non-NULL stream must belong to
+ * it (else SALA_ERR_INVALID). SALA_ERR_WORKSPACE: the call needs more than
+ * SALA_NOALLOC_SCRATCH_BYTES (sala_workspace_bytes(SALA_OP_SPARSE_DECODE_STEP, desc) bytes;
+ * 2.4 MB for batch 8, 2 KV heads and a 1M-token context). Every call on a device shares its array
+ * and leaves it holding that call's partial results; the kernels write every scratch byte they
+ * read, so nothing carries over, but calls that overlap in time on one device (other streams,
+ * other threads) race on it and must be serialised by the caller. */
+sala_status sala_sparse_decode_step_noalloc(const sala_sparse_desc* desc, const int64_t* kv_lens, const void* q,
+                                            const float* q_norm_w, const void* k_new, const void* v_new,
+                                            const float* k_norm_w, const void* gate, void* k_cache, void* v_cache,
+                                            float* k_pool, int32_t* sel, void* out, void* stream);
+
 /* The switch between the two modes (same section; the pages give no length, so the rule is the
  * one under which both modes give the same result): 1 when every query of the call would
  * select all of its causal blocks (kv_len <= topk * 64, so sala_dense_attn equals block

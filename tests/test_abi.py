@@ -297,6 +297,15 @@ def test_decode_at_arguments():
     wide = S.sparse_desc(batch=3, n_q=1, n_heads=64, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16, kv_len=3000,
                          kv_capacity=3072, topk=16, n_local=2)  # 32 query heads per KV head
     assert L.sala_sparse_decode_step(ctypes.byref(wide), FAKE, *sargs, FAKE, need, None) == 3
+    # the variant without workspace: the same argument errors, and calls needing more scratch than
+    # its static array (8 MiB) are refused before any device call
+    assert L.sala_sparse_decode_step_noalloc(ctypes.byref(sd), None, *sargs, None) == 1
+    assert L.sala_sparse_decode_step_noalloc(ctypes.byref(pre), FAKE, *sargs, None) == 2
+    assert L.sala_sparse_decode_step_noalloc(ctypes.byref(wide), FAKE, *sargs, None) == 3
+    big = S.sparse_desc(batch=64, n_q=1, n_heads=32, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
+                        kv_len=1 << 20, kv_capacity=1 << 20, topk=64, n_local=2)
+    assert S.workspace_bytes(S.OP_SPARSE_DECODE_STEP, big) > (8 << 20)
+    assert L.sala_sparse_decode_step_noalloc(ctypes.byref(big), FAKE, *sargs, None) == 4
     huge = S.sparse_desc(batch=1, n_q=1, n_heads=8, n_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
                          kv_len=64 * 20000, kv_capacity=64 * 20000, topk=16, n_local=2)  # beyond 16,384 blocks
     assert S.lib().sala_workspace_bytes(S.OP_SPARSE_DECODE_STEP, ctypes.byref(huge)) == ctypes.c_size_t(-1).value
