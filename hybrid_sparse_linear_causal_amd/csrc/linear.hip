@@ -61,6 +61,10 @@ struct LinUniform {
     *nslots = nseg;
     return (long)x * nseg;
   }
+  // the slot run of KV head kvh of the item's sequence (segment sums and scan run per KV head)
+  __device__ __forceinline__ long kv_slot(const LinItem& it, int Hkv, int kvh) const {
+    return ((long)it.s * Hkv + kvh) * nseg;
+  }
 };
 // packed sequences (tensors [T, H, d]): aux0 = prefix of the per-sequence segment counts;
 // item0 = H * aux0 (output pass) or H * (aux0[s] - s) (segment sums)
@@ -86,6 +90,9 @@ struct LinVarlen {
     const int s = x / H, h = x % H;
     *nslots = t.aux0[s + 1] - t.aux0[s];
     return (long)H * t.aux0[s] + (long)h * *nslots;
+  }
+  __device__ __forceinline__ long kv_slot(const LinItem& it, int Hkv, int kvh) const {
+    return (long)Hkv * t.aux0[it.s] + (long)kvh * it.nseg;
   }
 };
 
@@ -283,18 +290,22 @@ static_assert(sizeof(OutLds) == 163840, "output-pass LDS plan");
 // for the state waves at the barrier. Rows past the sequence end are clamped to its last row
 // (finite values; k rows past the end are zeroed by the prep, so they contribute nothing).
 constexpr int OUT_NT = 512;  // 8 waves: 0-3 produce outputs, 4-7 update the state
+// q and g rows start at row0 (H heads per token), k and v rows at kv_row0 (Hkv heads per token).
 template <int X, int NW>
 __device__ __forceinline__ void dma_chunk(const bf16_t* q, const bf16_t* k, const bf16_t* v,
-                                          const bf16_t* g, long row0, int t0, int n_valid, int H,
-                                          bf16_t (*T)[CH * D]) {
+                                          const bf16_t* g, long row0, long kv_row0, int t0, int n_valid, int H,
+                                          int Hkv, bf16_t (*T)[CH * D]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr bool KV = X == 1 || X == 2;
   const bf16_t* src = X == 0 ? q : X == 1 ? k : X == 2 ? v : g;
+  const long r0 = KV ? kv_row0 : row0;
+  const long stride = (long)(KV ? Hkv : H) * D;
 #pragma unroll
   for (int m = 0; m < 16 / NW; ++m) {
     const int I = (16 / NW) * wave + m;
     const int row = 4 * I + (lane >> 4);
-    const int ch = (X == 1 || X == 2) ? (lane & 15) ^ (2 * (row & 7)) : (lane & 15) ^ (row & 15);
-    const long off = row0 + (long)(min(t0 + row, n_valid - 1) - t0) * H * D + 8 * ch;
+    const int ch = KV ? (lane & 15) ^ (2 * (row & 7)) : (lane & 15) ^ (row & 15);
+    const long off = r0 + (long)(min(t0 + row, n_valid - 1) - t0) * stride + 8 * ch;
     dma16(src + off, lds_addr_u32(T[X] + I * 512));
   }
 }
@@ -305,14 +316,18 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                   const bf16_t* __restrict__ v, const bf16_t* __restrict__ g,
                   const float* __restrict__ qw, const float* __restrict__ kw,
                   const float* __restrict__ state_in, const float* __restrict__ ws,
-                  float* __restrict__ state_out, bf16_t* __restrict__ out, int H, int seg_len, float eps,
-                  RopeFreqs freqs, Geo geo) {
+                  float* __restrict__ state_out, bf16_t* __restrict__ out, int H, int Hkv, int seg_len,
+                  float eps, RopeFreqs freqs, Geo geo) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   OutLds& L = *reinterpret_cast<OutLds*>(lds_raw);
   const LinItem it = geo.item(blockIdx.x, H, false);
   const int seg = it.seg, nseg = it.nseg, h = it.h, N = it.n;
   const long pos0 = it.pos0;
-  const long bh = (long)it.s * H + h;  // state index
+  // query head h reads (and, as every head of its group does, carries forward) the state of KV
+  // head kvh; only the group's first head writes state_out
+  const int G = H / Hkv, kvh = h / G;
+  const long bh = (long)it.s * Hkv + kvh;  // state index
+  const long kv_slot = geo.kv_slot(it, Hkv, kvh);
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
   const bool out_wave = wave < 4;
@@ -322,13 +337,15 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int t_end = min(N, t_begin + seg_len);
   const long head_off = (it.tok0 * H + h) * D;
   const long tok_stride = (long)H * D;
+  const long kv_off = (it.tok0 * Hkv + kvh) * D;
+  const long kv_stride = (long)Hkv * D;
 
   {
-    const long r0 = head_off + (long)t_begin * tok_stride;
-    dma_chunk<0, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
-    dma_chunk<1, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
-    dma_chunk<2, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
-    dma_chunk<3, 8>(q, k, v, g, r0, t_begin, N, H, L.t[0]);
+    const long r0 = head_off + (long)t_begin * tok_stride, k0 = kv_off + (long)t_begin * kv_stride;
+    dma_chunk<0, 8>(q, k, v, g, r0, k0, t_begin, N, H, Hkv, L.t[0]);
+    dma_chunk<1, 8>(q, k, v, g, r0, k0, t_begin, N, H, Hkv, L.t[0]);
+    dma_chunk<2, 8>(q, k, v, g, r0, k0, t_begin, N, H, Hkv, L.t[0]);
+    dma_chunk<3, 8>(q, k, v, g, r0, k0, t_begin, N, H, Hkv, L.t[0]);
   }
 
   // acc: state waves keep S[dk][dv] (C layout, dk rows 32*w4 .. +31) in acc[8*it + jt];
@@ -337,7 +354,10 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
   for (int x = 0; x < 16; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (!out_wave) {
-    const float* src = (nseg == 1) ? (state_in ? state_in + bh * D * D : nullptr) : ws + (it.slot + seg) * D * D;
+    // grouped heads read the entering state from the workspace even with one segment: the
+    // group's first head may write state_out over state_in while the others still read it
+    const float* src = (nseg == 1 && G == 1) ? (state_in ? state_in + bh * D * D : nullptr)
+                                             : ws + (kv_slot + seg) * D * D;
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
@@ -392,11 +412,11 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     // the next chunk's tiles stream into the other buffer (free since the last barrier) for
     // the rest of this chunk: q and k now, v and g after the prep
     const bool next = c0 + CH < t_end;
-    const long nrow0 = head_off + (long)(c0 + CH) * tok_stride;
+    const long nrow0 = head_off + (long)(c0 + CH) * tok_stride, nkv0 = kv_off + (long)(c0 + CH) * kv_stride;
     bf16_t (*nbuf)[CH * D] = L.t[buf ^ 1];
     if (next) {
-      dma_chunk<0, 8>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
-      dma_chunk<1, 8>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
+      dma_chunk<0, 8>(q, k, v, g, nrow0, nkv0, c0 + CH, N, H, Hkv, nbuf);
+      dma_chunk<1, 8>(q, k, v, g, nrow0, nkv0, c0 + CH, N, H, Hkv, nbuf);
     }
     // ---------------- prep in place: QK-norm + RoPE (rows past the end: k~ = 0)
     {
@@ -420,8 +440,8 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       }
     }
     if (next && out_wave) {
-      dma_chunk<2, 4>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
-      dma_chunk<3, 4>(q, k, v, g, nrow0, c0 + CH, N, H, nbuf);
+      dma_chunk<2, 4>(q, k, v, g, nrow0, nkv0, c0 + CH, N, H, Hkv, nbuf);
+      dma_chunk<3, 4>(q, k, v, g, nrow0, nkv0, c0 + CH, N, H, Hkv, nbuf);
     }
     __syncthreads();
 
@@ -540,7 +560,7 @@ linear_out_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     __syncthreads();
     buf ^= 1;
   }
-  if (!out_wave && seg == nseg - 1 && state_out) {
+  if (!out_wave && seg == nseg - 1 && state_out && h % G == 0) {
     float* dst = state_out + bh * D * D;
 #pragma unroll
     for (int it = 0; it < 2; ++it)
@@ -571,7 +591,7 @@ linear_scan_kernel(const float* __restrict__ state_in, float* __restrict__ ws, i
   const int e = blockIdx.y * 256 + threadIdx.x;
   int nslots;
   const long slot = geo.scan_item(bh, H, &nslots);
-  if (e >= dd || nslots <= 1) return;
+  if (e >= dd || nslots < 1) return;
   float acc = state_in ? state_in[(long)bh * dd + e] : 0.f;
   float* p = ws + slot * dd + e;
   p[0] = acc;
@@ -583,22 +603,27 @@ linear_scan_kernel(const float* __restrict__ state_in, float* __restrict__ ws, i
 
 // ------------------------------------------------------------------ fp32 path (plain scan)
 
-// q~ and k~ for every (b, t, h): RMS norm, weight, RoPE (angle reduced in fp64, accurate
-// fp32 sin/cos). One wave per row; lane i < d/2 owns dims i and i + d/2.
+// q~ for every (b, t, h) and k~ for every (b, t, kv head): RMS norm, weight, RoPE (angle reduced
+// in fp64, accurate fp32 sin/cos). One wave per (b, t, h) query row, which also handles the key
+// row (b, t, h) when h < Hkv; lane i < d/2 owns dims i and i + d/2.
 __global__ void __launch_bounds__(64)
 linear_prep_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                        const float* __restrict__ qw, const float* __restrict__ kw,
-                       float* __restrict__ qt, float* __restrict__ kt, int N, int H, int d,
+                       float* __restrict__ qt, float* __restrict__ kt, int N, int H, int Hkv, int d,
                        long pos0, float eps, RopeFreqs freqs) {
   const long row = blockIdx.x;  // (b*N + t)*H + h
-  const int t = (int)((row / H) % N);
+  const int h = (int)(row % H);
+  const long bt = row / H;
+  const int t = (int)(bt % N);
+  const bool has_k = h < Hkv;
+  const long krow = bt * Hkv + h;
   const int i = threadIdx.x;
   const int half = d / 2;
   const bool on = i < half;
   float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
   if (on) {
     a[0] = q[row * d + i]; a[1] = q[row * d + i + half];
-    b[0] = k[row * d + i]; b[1] = k[row * d + i + half];
+    if (has_k) { b[0] = k[krow * d + i]; b[1] = k[krow * d + i + half]; }
   }
   const float sq = group_sum<64>(a[0] * a[0] + a[1] * a[1]);
   const float sk = group_sum<64>(b[0] * b[0] + b[1] * b[1]);
@@ -613,145 +638,170 @@ linear_prep_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
   sincosf(ang, &sn, &cs);
   qt[row * d + i] = x0 * cs - x1 * sn;
   qt[row * d + i + half] = x0 * sn + x1 * cs;
-  kt[row * d + i] = y0 * cs - y1 * sn;
-  kt[row * d + i + half] = y0 * sn + y1 * cs;
+  if (has_k) {
+    kt[krow * d + i] = y0 * cs - y1 * sn;
+    kt[krow * d + i + half] = y0 * sn + y1 * cs;
+  }
 }
 
-// One workgroup of d threads per (b, h); thread c owns state column c (all d rows), so the
-// readout o[c] = sum_i q~[i] S[i][c] needs no cross-thread reduction. Tokens in order.
+// One workgroup of d threads per (b, KV head); thread c owns state column c (all d rows), so
+// the readout o[c] = sum_i q~[i] S[i][c] needs no cross-thread reduction. Tokens in order; each
+// token updates the state once and reads it out for every query head of the group.
 template <int DD>
 __global__ void __launch_bounds__(DD)
 linear_scan_f32_kernel(const float* __restrict__ qt, const float* __restrict__ kt,
                        const float* __restrict__ v, const float* __restrict__ g,
                        const float* __restrict__ state_in, float* __restrict__ state_out,
-                       float* __restrict__ out, int N, int H) {
-  constexpr int TB = 32;  // tokens staged per step
-  __shared__ float sq[TB][DD], sk[TB][DD];
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+                       float* __restrict__ out, int N, int H, int Hkv) {
+  constexpr int QR = 64;  // query rows staged per step (TB tokens x G heads)
+  __shared__ float sq[QR][DD], sk[QR][DD];
+  const int bkv = blockIdx.x, b = bkv / Hkv, kvh = bkv % Hkv;
+  const int G = H / Hkv, TB = G >= QR ? 1 : QR / G;
   const int c = threadIdx.x;
   float S[DD];
 #pragma unroll
-  for (int r = 0; r < DD; ++r) S[r] = state_in ? state_in[((long)bh * DD + r) * DD + c] : 0.f;
+  for (int r = 0; r < DD; ++r) S[r] = state_in ? state_in[((long)bkv * DD + r) * DD + c] : 0.f;
   for (int t0 = 0; t0 < N; t0 += TB) {
     const int nt = min(TB, N - t0);
     __syncthreads();
     for (int u = 0; u < nt; ++u) {
-      const long row = ((long)b * N + t0 + u) * H + h;
-      sq[u][c] = qt[row * DD + c];
-      sk[u][c] = kt[row * DD + c];
+      const long bt = (long)b * N + t0 + u;
+      sk[u][c] = kt[(bt * Hkv + kvh) * DD + c];
+      for (int hg = 0; hg < G; ++hg) sq[u * G + hg][c] = qt[(bt * H + kvh * G + hg) * DD + c];
     }
     __syncthreads();
     for (int u = 0; u < nt; ++u) {
-      const long row = ((long)b * N + t0 + u) * H + h;
-      const float vc = v[row * DD + c];
-      float o = 0.f;
+      const long bt = (long)b * N + t0 + u;
+      const float vc = v[(bt * Hkv + kvh) * DD + c];
 #pragma unroll
-      for (int r = 0; r < DD; ++r) {
-        S[r] += sk[u][r] * vc;
-        o += sq[u][r] * S[r];
+      for (int r = 0; r < DD; ++r) S[r] += sk[u][r] * vc;
+      for (int hg = 0; hg < G; ++hg) {
+        const long row = bt * H + kvh * G + hg;
+        float o = 0.f;
+#pragma unroll
+        for (int r = 0; r < DD; ++r) o += sq[u * G + hg][r] * S[r];
+        out[row * DD + c] = o / (1.0f + expf(-g[row * DD + c]));
       }
-      out[row * DD + c] = o / (1.0f + expf(-g[row * DD + c]));
     }
   }
   if (state_out) {
 #pragma unroll
-    for (int r = 0; r < DD; ++r) state_out[((long)bh * DD + r) * DD + c] = S[r];
+    for (int r = 0; r < DD; ++r) state_out[((long)bkv * DD + r) * DD + c] = S[r];
   }
 }
 
 // ------------------------------------------------------------------ decode step
 
-// grid (B*H, d/32): each workgroup owns 32 state columns of one (b, h). Thread j: column
-// 32*blockIdx.y + j%32, rows j/32 + 8m. q~, k~ (norm + RoPE at pos) computed by wave 0.
-// grid (B*H, DD/64), 256 threads: one token's step for 64 state columns of one head. Thread
-// (row group r0 = j/16, column quad c4 = j%16) owns columns 64y + 4c4 .. +3 of rows r0 + 16m;
-// its state rows are loaded as float4 before the q/k preparation, so their latency overlaps it.
-// Decode step, grid (B*H, DD/64), 320 threads: wave 0 normalises and rotates q and k (their
-// loads are not queued behind the state's), waves 1-4 stream the 64-column slice of S; S is
-// updated in place and each wave-1..4 thread keeps a partial of o = q^ S for its rows.
+// Decode step, grid (B*Hkv, DD/64), 320 threads: one KV head's 64-column slice of S. Wave 0
+// normalises and rotates k and the group's queries (their loads are not queued behind the
+// state's); waves 1-4 stream the slice, update it in place once, and keep per-row partials of
+// o = q^ S for each query head of the group in turn, which wave 0 sums, gates and stores.
+constexpr int DEC_GMAX = 64;  // query heads per KV head
 template <typename T, int DD>
 __global__ void __launch_bounds__(320)
 linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                      const T* __restrict__ g, const float* __restrict__ qw,
                      const float* __restrict__ kw, float* __restrict__ state, T* __restrict__ out,
-                     long pos, const int64_t* __restrict__ pos_b, int H, float eps, RopeFreqs freqs) {
+                     long pos, const int64_t* __restrict__ pos_b, int H, int Hkv, float eps, RopeFreqs freqs) {
   constexpr int NR = DD / 16;  // rows per state thread
   constexpr int HALF = DD / 2;
-  __shared__ float sq[DD], sk[DD];
+  __shared__ float sq[DEC_GMAX][DD], sk[DD];
   __shared__ float4 red[16][16];
-  const int bh = blockIdx.x;
+  const int bkv = blockIdx.x, b = bkv / Hkv, kvh = bkv % Hkv, G = H / Hkv;
   const int j = threadIdx.x;
-  const long vec = (long)bh * DD;
+  const long kvec = (long)bkv * DD;                  // k, v of this KV head
+  const long qvec = ((long)b * H + kvh * G) * DD;    // the group's first query head
+  const int js = j - 64, r0 = js >> 4, c4 = js & 15;
+  const int col = 64 * blockIdx.y + 4 * c4;
+  float* Sp = state + (long)bkv * DD * DD + col;
+  float4 sv[NR];
+  float vc[4];
   if (j < 64) {
-    // ---- wave 0: q^, k^ = RoPE(RMSNorm(q, k) * w) into LDS
+    // ---- wave 0: k^ and the group's q^ = RoPE(RMSNorm(.) * w) into LDS
     if (pos_b) {  // each sequence at its own position (negative values read as 0)
-      const long pb = pos_b[bh / H];
+      const long pb = pos_b[b];
       pos = pb > 0 ? pb : 0;
     }
     const bool on = j < HALF;
-    float a0 = 0, a1 = 0, b0 = 0, b1 = 0;
+    float cs = 1.f, sn = 0.f;
     if (on) {
-      a0 = to_f32(q[vec + j]); a1 = to_f32(q[vec + j + HALF]);
-      b0 = to_f32(k[vec + j]); b1 = to_f32(k[vec + j + HALF]);
-    }
-    const float ssq = group_sum<64>(a0 * a0 + a1 * a1);
-    const float ssk = group_sum<64>(b0 * b0 + b1 * b1);
-    if (on) {
-      const float iq = 1.0f / sqrtf(ssq / DD + eps), ik = 1.0f / sqrtf(ssk / DD + eps);
-      float x0 = a0 * iq, x1 = a1 * iq, y0 = b0 * ik, y1 = b1 * ik;
-      if (qw) { x0 *= qw[j]; x1 *= qw[j + HALF]; }
-      if (kw) { y0 *= kw[j]; y1 *= kw[j + HALF]; }
       const double rev = (double)pos * freqs.f[j];
       const float ang = (float)((rev - rint(rev)) * 6.283185307179586);
-      float sn, cs;
       sincosf(ang, &sn, &cs);
-      sq[j] = x0 * cs - x1 * sn; sq[j + HALF] = x0 * sn + x1 * cs;
+    }
+    float b0 = 0, b1 = 0;
+    if (on) { b0 = to_f32(k[kvec + j]); b1 = to_f32(k[kvec + j + HALF]); }
+    const float ssk = group_sum<64>(b0 * b0 + b1 * b1);
+    if (on) {
+      const float ik = 1.0f / sqrtf(ssk / DD + eps);
+      float y0 = b0 * ik, y1 = b1 * ik;
+      if (kw) { y0 *= kw[j]; y1 *= kw[j + HALF]; }
       sk[j] = y0 * cs - y1 * sn; sk[j + HALF] = y0 * sn + y1 * cs;
     }
-    __syncthreads();
-    __syncthreads();
-    // ---- o[c] = sum of the 16 row-group partials, gated
-    const int cc = j >> 2, e = j & 3;  // column 64y + 4cc + e
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float4 t = red[m][cc];
-      acc += e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w;
+    for (int hg = 0; hg < G; ++hg) {
+      float a0 = 0, a1 = 0;
+      if (on) { a0 = to_f32(q[qvec + (long)hg * DD + j]); a1 = to_f32(q[qvec + (long)hg * DD + j + HALF]); }
+      const float ssq = group_sum<64>(a0 * a0 + a1 * a1);
+      if (on) {
+        const float iq = 1.0f / sqrtf(ssq / DD + eps);
+        float x0 = a0 * iq, x1 = a1 * iq;
+        if (qw) { x0 *= qw[j]; x1 *= qw[j + HALF]; }
+        sq[hg][j] = x0 * cs - x1 * sn; sq[hg][j + HALF] = x0 * sn + x1 * cs;
+      }
     }
-    const long oc = vec + 64 * blockIdx.y + j;
-    const float gv = to_f32(g[oc]);
-    out[oc] = from_f32<T>(acc / (1.0f + expf(-gv)));
-    return;
+  } else {
+    // ---- waves 1-4: the state slice (rows r0 + 16m, columns 64y + 4c4 .. +3), loaded while
+    // wave 0 prepares q^ and k^
+#pragma unroll
+    for (int m = 0; m < NR; ++m) sv[m] = *reinterpret_cast<const float4*>(Sp + (long)(r0 + 16 * m) * DD);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[kvec + col + e]);
   }
-  // ---- waves 1-4: the state slice (rows r0 + 16m, columns 64y + 4c4 .. +3)
-  const int js = j - 64, r0 = js >> 4, c4 = js & 15;
-  const int col = 64 * blockIdx.y + 4 * c4;
-  float* Sp = state + (long)bh * DD * DD + col;
-  float4 sv[NR];
-#pragma unroll
-  for (int m = 0; m < NR; ++m) sv[m] = *reinterpret_cast<const float4*>(Sp + (long)(r0 + 16 * m) * DD);
-  float vc[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[vec + col + e]);
   __syncthreads();  // q^, k^ ready
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (j >= 64) {
 #pragma unroll
-  for (int m = 0; m < NR; ++m) {
-    const int r = r0 + 16 * m;
-    const float kr = sk[r], qr = sq[r];
-    float4 s4 = sv[m];
-    s4.x += kr * vc[0]; s4.y += kr * vc[1]; s4.z += kr * vc[2]; s4.w += kr * vc[3];
-    *reinterpret_cast<float4*>(Sp + (long)r * DD) = s4;
-    o.x += qr * s4.x; o.y += qr * s4.y; o.z += qr * s4.z; o.w += qr * s4.w;
+    for (int m = 0; m < NR; ++m) {
+      const int r = r0 + 16 * m;
+      const float kr = sk[r];
+      float4 s4 = sv[m];
+      s4.x += kr * vc[0]; s4.y += kr * vc[1]; s4.z += kr * vc[2]; s4.w += kr * vc[3];
+      *reinterpret_cast<float4*>(Sp + (long)r * DD) = s4;
+      sv[m] = s4;
+    }
   }
-  red[r0][c4] = o;
-  __syncthreads();  // partials ready
+  for (int hg = 0; hg < G; ++hg) {
+    if (j >= 64) {
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const float qr = sq[hg][r0 + 16 * m];
+        o.x += qr * sv[m].x; o.y += qr * sv[m].y; o.z += qr * sv[m].z; o.w += qr * sv[m].w;
+      }
+      red[r0][c4] = o;
+    }
+    __syncthreads();  // partials ready
+    if (j < 64) {
+      // ---- o[c] = sum of the 16 row-group partials, gated
+      const int cc = j >> 2, e = j & 3;  // column 64y + 4cc + e
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const float4 t = red[m][cc];
+        acc += e == 0 ? t.x : e == 1 ? t.y : e == 2 ? t.z : t.w;
+      }
+      const long oc = qvec + (long)hg * DD + 64 * blockIdx.y + j;
+      const float gv = to_f32(g[oc]);
+      out[oc] = from_f32<T>(acc / (1.0f + expf(-gv)));
+    }
+    if (hg + 1 < G) __syncthreads();  // the partials are rewritten for the next head
+  }
 }
 
 // The bf16 prefill over a geometry: segment sums (when some sequence has several segments),
 // their scan, then the output pass. GS is the segment-sum geometry, GO the output/scan one.
 template <class GS, class GO>
-hipError_t run_linear_bf16(const GS& gs, const GO& go, long n_ss, long n_out, long n_bh, bool scan, int H, int seg,
+hipError_t run_linear_bf16(const GS& gs, const GO& go, long n_ss, long n_out, long n_bh, bool scan, int H, int Hkv,
+                           int seg,
                            const void* q, const void* k, const void* v, const void* g, const float* qw,
                            const float* kw, const float* state_in, float* state_out, void* out, void* ws, float eps,
                            const RopeFreqs& fr, hipStream_t st) {
@@ -776,20 +826,20 @@ hipError_t run_linear_bf16(const GS& gs, const GO& go, long n_ss, long n_out, lo
     if (n_ss > 0) {
       if (kw)
         hipLaunchKernelGGL((linear_segsum_kernel<true, GS>), dim3((unsigned)n_ss), dim3(SS_NT), sizeof(SegLds), st, kb,
-                           vb, kw, wsf, H, seg, eps, fr, gs);
+                           vb, kw, wsf, Hkv, seg, eps, fr, gs);
       else
         hipLaunchKernelGGL((linear_segsum_kernel<false, GS>), dim3((unsigned)n_ss), dim3(SS_NT), sizeof(SegLds), st, kb,
-                           vb, kw, wsf, H, seg, eps, fr, gs);
+                           vb, kw, wsf, Hkv, seg, eps, fr, gs);
     }
-    hipLaunchKernelGGL((linear_scan_kernel<GO>), dim3((unsigned)n_bh, D * D / 256), dim3(256), 0, st, state_in, wsf, H,
-                       D * D, go);
+    hipLaunchKernelGGL((linear_scan_kernel<GO>), dim3((unsigned)n_bh, D * D / 256), dim3(256), 0, st, state_in, wsf,
+                       Hkv, D * D, go);
   }
   if (qw || kw)
     hipLaunchKernelGGL((linear_out_kernel<true, GO>), dim3((unsigned)n_out), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
-                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, H, seg, eps, fr, go);
+                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, H, Hkv, seg, eps, fr, go);
   else
     hipLaunchKernelGGL((linear_out_kernel<false, GO>), dim3((unsigned)n_out), dim3(OUT_NT), sizeof(OutLds), st, qb, kb,
-                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, H, seg, eps, fr, go);
+                       vb, gb, qw, kw, state_in, wsf, state_out, (bf16_t*)out, H, Hkv, seg, eps, fr, go);
   return hipGetLastError();
 }
 
@@ -801,8 +851,8 @@ size_t linear_prefill_workspace(const sala_linear_desc& d) {
   if (d.dtype == SALA_F32) return 2ull * d.batch * d.seq_len * d.n_heads * d.head_dim * sizeof(float);
   const int seg = linear_segment_len(d);
   const long nseg = (d.seq_len + seg - 1) / seg;
-  if (nseg <= 1) return 0;
-  return (size_t)d.batch * d.n_heads * nseg * d.head_dim * d.head_dim * sizeof(float);
+  if (nseg <= 1 && d.n_kv_heads == d.n_heads) return 0;
+  return (size_t)d.batch * d.n_kv_heads * nseg * d.head_dim * d.head_dim * sizeof(float);
 }
 
 int linear_segment_len(const sala_linear_desc& d) {
@@ -817,11 +867,11 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
                                  const void* v, const void* g, const float* qw, const float* kw,
                                  const float* state_in, float* state_out, void* out, void* ws,
                                  hipStream_t st) {
-  const int B = d.batch, N = d.seq_len, H = d.n_heads, hd = d.head_dim;
+  const int B = d.batch, N = d.seq_len, H = d.n_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   if (N == 0) {
     // no tokens: state passes through
     if (state_out && state_out != state_in) {
-      const long n = (long)B * H * hd * hd;
+      const long n = (long)B * Hkv * hd * hd;
       const unsigned nb = (unsigned)std::min<long>((n + 255) / 256, 4096);
       hipLaunchKernelGGL(copy_or_zero_kernel, dim3(nb), dim3(256), 0, st, state_in, state_out, n);
       return hipGetLastError();
@@ -833,21 +883,21 @@ hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const
     float* qt = static_cast<float*>(ws);
     float* kt = qt + (size_t)B * N * H * hd;
     hipLaunchKernelGGL(linear_prep_f32_kernel, dim3((unsigned)((long)B * N * H)), dim3(64), 0, st,
-                       (const float*)q, (const float*)k, qw, kw, qt, kt, N, H, hd, (long)d.pos0,
+                       (const float*)q, (const float*)k, qw, kw, qt, kt, N, H, Hkv, hd, (long)d.pos0,
                        d.norm_eps, fr);
     if (hd == 64)
-      hipLaunchKernelGGL(linear_scan_f32_kernel<64>, dim3(B * H), dim3(64), 0, st, qt, kt,
-                         (const float*)v, (const float*)g, state_in, state_out, (float*)out, N, H);
+      hipLaunchKernelGGL(linear_scan_f32_kernel<64>, dim3(B * Hkv), dim3(64), 0, st, qt, kt,
+                         (const float*)v, (const float*)g, state_in, state_out, (float*)out, N, H, Hkv);
     else
-      hipLaunchKernelGGL(linear_scan_f32_kernel<128>, dim3(B * H), dim3(128), 0, st, qt, kt,
-                         (const float*)v, (const float*)g, state_in, state_out, (float*)out, N, H);
+      hipLaunchKernelGGL(linear_scan_f32_kernel<128>, dim3(B * Hkv), dim3(128), 0, st, qt, kt,
+                         (const float*)v, (const float*)g, state_in, state_out, (float*)out, N, H, Hkv);
     return hipGetLastError();
   }
   const int seg = linear_segment_len(d);
   const int nseg = (N + seg - 1) / seg;
   const LinUniform geo{N, (long)d.pos0, nseg};
-  return run_linear_bf16(geo, geo, (long)B * H * (nseg - 1), (long)B * H * nseg, (long)B * H, nseg > 1, H, seg, q, k,
-                         v, g, qw, kw, state_in, state_out, out, ws, d.norm_eps, fr, st);
+  return run_linear_bf16(geo, geo, (long)B * Hkv * (nseg - 1), (long)B * H * nseg, (long)B * Hkv, nseg > 1 || Hkv < H,
+                         H, Hkv, seg, q, k, v, g, qw, kw, state_in, state_out, out, ws, d.norm_eps, fr, st);
 }
 
 // segment length of a packed batch: chosen for its total token count, as for one sequence
@@ -861,14 +911,14 @@ size_t linear_prefill_varlen_workspace(const sala_linear_desc& d, const int32_t*
   const int seg = varlen_segment_len(d);
   size_t slots = 0;
   for (int s = 0; s < d.batch; ++s) slots += (cu_seqlens[s + 1] - cu_seqlens[s] + seg - 1) / seg;
-  return (size_t)d.n_heads * slots * d.head_dim * d.head_dim * sizeof(float);
+  return (size_t)d.n_kv_heads * slots * d.head_dim * d.head_dim * sizeof(float);
 }
 
 hipError_t launch_linear_prefill_varlen(const sala_linear_desc& d, const int32_t* cu_seqlens, const int64_t* pos0,
                                         const void* q, const void* k, const void* v, const void* g,
                                         const float* qw, const float* kw, const float* state_in,
                                         float* state_out, void* out, void* ws, hipStream_t st) {
-  const int H = d.n_heads, nseq = d.batch;
+  const int H = d.n_heads, Hkv = d.n_kv_heads, nseq = d.batch;
   const RopeFreqs fr = make_rope_freqs(d.head_dim, d.rope_base);
   const int seg = varlen_segment_len(d);
   LinVarlen ss{make_varlen_table(nseq, cu_seqlens, pos0)};
@@ -880,9 +930,9 @@ hipError_t launch_linear_prefill_varlen(const sala_linear_desc& d, const int32_t
     any_multi = any_multi || ns > 1;
     // a sequence without tokens: its state passes through
     if (n == 0 && state_out && state_out != state_in) {
-      const long off = (long)s * H * D * D;
+      const long off = (long)s * Hkv * D * D;
       hipLaunchKernelGGL(copy_or_zero_kernel, dim3(64), dim3(256), 0, st, state_in ? state_in + off : nullptr,
-                         state_out + off, (long)H * D * D);
+                         state_out + off, (long)Hkv * D * D);
     }
   }
   LinVarlen ou = ss;
@@ -891,39 +941,39 @@ hipError_t launch_linear_prefill_varlen(const sala_linear_desc& d, const int32_t
     // segment-sum items: every segment but the last of each sequence with tokens
     int skip = 0;
     for (int x = 0; x < s; ++x) skip += ss.t.n[x] > 0;
-    ss.t.item0[s] = H * (ss.t.aux0[s] - skip);
+    ss.t.item0[s] = Hkv * (ss.t.aux0[s] - skip);
   }
   if (ou.t.item0[nseq] == 0) return hipGetLastError();
-  return run_linear_bf16(ss, ou, ss.t.item0[nseq], ou.t.item0[nseq], nseq * H, any_multi, H, seg, q, k, v, g, qw,
-                         kw, state_in, state_out, out, ws, d.norm_eps, fr, st);
+  return run_linear_bf16(ss, ou, ss.t.item0[nseq], ou.t.item0[nseq], nseq * Hkv, any_multi || Hkv < H, H, Hkv, seg, q,
+                         k, v, g, qw, kw, state_in, state_out, out, ws, d.norm_eps, fr, st);
 }
 
 hipError_t launch_linear_decode(const sala_linear_desc& d, const void* q, const void* k,
                                 const void* v, const void* g, const float* qw, const float* kw,
                                 float* state, void* out, const int64_t* pos_b, hipStream_t st) {
-  const int BH = d.batch * d.n_heads, hd = d.head_dim, H = d.n_heads;
+  const int H = d.n_heads, Hkv = d.n_kv_heads, hd = d.head_dim;
   const RopeFreqs fr = make_rope_freqs(hd, d.rope_base);
-  const dim3 grid(BH, hd / 64);
+  const dim3 grid(d.batch * Hkv, hd / 64);
   const long pos = (long)d.pos0;
   const dim3 block(320);
   if (d.dtype == SALA_BF16) {
     if (hd == 128)
       hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 128>), grid, block, 0, st, (const bf16_t*)q,
                          (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, qw, kw, state, (bf16_t*)out,
-                         pos, pos_b, H, d.norm_eps, fr);
+                         pos, pos_b, H, Hkv, d.norm_eps, fr);
     else
       hipLaunchKernelGGL((linear_decode_kernel<bf16_t, 64>), grid, block, 0, st, (const bf16_t*)q,
                          (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, qw, kw, state, (bf16_t*)out,
-                         pos, pos_b, H, d.norm_eps, fr);
+                         pos, pos_b, H, Hkv, d.norm_eps, fr);
   } else {
     if (hd == 128)
       hipLaunchKernelGGL((linear_decode_kernel<float, 128>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (const float*)g, qw, kw, state, (float*)out,
-                         pos, pos_b, H, d.norm_eps, fr);
+                         pos, pos_b, H, Hkv, d.norm_eps, fr);
     else
       hipLaunchKernelGGL((linear_decode_kernel<float, 64>), grid, block, 0, st, (const float*)q,
                          (const float*)k, (const float*)v, (const float*)g, qw, kw, state, (float*)out,
-                         pos, pos_b, H, d.norm_eps, fr);
+                         pos, pos_b, H, Hkv, d.norm_eps, fr);
   }
   return hipGetLastError();
 }
