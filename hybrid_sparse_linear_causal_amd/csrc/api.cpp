@@ -52,8 +52,11 @@ sala_status check_linear(const sala_linear_desc* d) {
   if (d->dtype != SALA_F32 && d->dtype != SALA_BF16) return SALA_ERR_INVALID;
   if (!(d->rope_base > 0.f) || !isfinite(d->rope_base)) return SALA_ERR_INVALID;
   if (!(d->norm_eps >= 0.f) || !isfinite(d->norm_eps)) return SALA_ERR_INVALID;
-  if (d->n_heads % d->n_kv_heads != 0) return SALA_ERR_INVALID;
-  if (d->n_kv_heads != d->n_heads) return SALA_ERR_UNSUPPORTED;  // GQA linear layers: not built
+  if (d->n_heads % d->n_kv_heads != 0 || d->reserved_ != 0) return SALA_ERR_INVALID;
+  if (d->n_heads / d->n_kv_heads > 64) return SALA_ERR_UNSUPPORTED;
+  // the chunked evaluation is built for 64-token chunks; 128 and 256 are chunk sizes of the
+  // method that are not built here
+  if (d->chunk != 0 && d->chunk != 64) return (d->chunk == 128 || d->chunk == 256) ? SALA_ERR_UNSUPPORTED : SALA_ERR_INVALID;
   // sizes must stay within 64-bit element offsets and 32-bit grid dimensions
   const double elems = (double)d->batch * d->seq_len * d->n_heads * d->head_dim;
   if (elems > 9.0e15 || (double)d->batch * d->seq_len * d->n_heads > 2.0e9) return SALA_ERR_INVALID;
@@ -199,7 +202,8 @@ size_t sala_workspace_bytes(int op, const void* desc) {
     }
     case SALA_OP_LINEAR_BACKWARD: {
       const sala_linear_desc* d = static_cast<const sala_linear_desc*>(desc);
-      if (check_linear(d) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128) return SIZE_MAX;
+      if (check_linear(d) != SALA_OK || d->dtype != SALA_BF16 || d->head_dim != 128 || d->n_kv_heads != d->n_heads)
+        return SIZE_MAX;
       return sala::linear_backward_workspace(*d);
     }
     default: return SIZE_MAX;
@@ -232,7 +236,7 @@ sala_status sala_linear_backward(const sala_linear_desc* desc, const void* q, co
   sala_status s = check_linear(desc);
   if (s != SALA_OK) return s;
   const sala_linear_desc& d = *desc;
-  if (d.dtype != SALA_BF16 || d.head_dim != 128) return SALA_ERR_UNSUPPORTED;
+  if (d.dtype != SALA_BF16 || d.head_dim != 128 || d.n_kv_heads != d.n_heads) return SALA_ERR_UNSUPPORTED;
   if (d.seq_len > 0 && (!q || !k || !v || !gate || !dout || !dq || !dk || !dv || !dg)) return SALA_ERR_NULL;
   if (!all_aligned({q, k, v, gate, q_norm_w, k_norm_w, state_in, dout, dstate_out, dq, dk, dv, dg, dq_norm_w,
                     dk_norm_w, dstate_in, workspace}))
@@ -426,15 +430,15 @@ sala_status sala_kv_pool(const sala_sparse_desc* desc, const void* k_cache, floa
 }
 
 sala_status sala_block_select(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
-                              const float* k_pool, int32_t* sel, void* workspace,
+                              const float* k_pool, int32_t* sel, float* sel_scores, void* workspace,
                               size_t workspace_bytes, void* stream) {
   sala_status s = check_sparse(desc);
   if (s != SALA_OK) return s;
   if (!q || !k_pool || !sel) return SALA_ERR_NULL;
-  if (!all_aligned({q, q_norm_w, k_pool, sel, workspace})) return SALA_ERR_INVALID;
+  if (!all_aligned({q, q_norm_w, k_pool, sel, sel_scores, workspace})) return SALA_ERR_INVALID;
   const size_t need = sala::block_select_workspace(*desc);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SALA_ERR_WORKSPACE;
-  return hip_status(sala::launch_block_select(*desc, q, q_norm_w, k_pool, sel, workspace,
+  return hip_status(sala::launch_block_select(*desc, q, q_norm_w, k_pool, sel, sel_scores, workspace,
                                               (hipStream_t)stream));
 }
 

@@ -25,6 +25,11 @@ namespace {
 
 constexpr int NT = 256;
 
+// the score a monotone key was made from (inverse of score_key)
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // grid (B, nqb); q~[b][g][r][DD] (fp32) = sum_{h in g} mean_t RMSNorm(q[t, h]) * w
 template <typename T, int DD>
 __global__ void __launch_bounds__(NT)
@@ -206,8 +211,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 // memory (correct, slower).
 template <int NTS, int CAP>
 __global__ void __launch_bounds__(NTS)
-select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, long qb0, int RL,
-              int topk, int n_local) {
+select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, float* __restrict__ sel_sc, int nqb,
+              long qb0, int RL, int topk, int n_local) {
   __shared__ uint32_t keys[CAP];
   __shared__ int hist[256];
   __shared__ int scan_tmp[NTS / 64 + 1];
@@ -218,6 +223,7 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
   const long i = qb0 + r;
   const float* srow = sc + row * RL;
   int32_t* out = sel + row * topk;
+  float* out_sc = sel_sc ? sel_sc + row * topk : nullptr;
   const int tid = threadIdx.x, lane = tid & 63;
   const long nc = i - n_local > 0 ? i - n_local : 0;             // candidates j = 1..nc
   const long f_lo = i - n_local + 1 > 0 ? i - n_local + 1 : 0;   // forced local range [f_lo, i]
@@ -315,11 +321,17 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, int nqb, 
     int eqb = eq_before;
     for (long jj = a; jj < e_end; ++jj)
       if (picked(jj, eqb)) {
-        if (pos < topk) out[pos] = (int32_t)jj;  // bounded even if the count were off
+        if (pos < topk) {  // bounded even if the count were off
+          out[pos] = (int32_t)jj;
+          if (out_sc) out_sc[pos] = (jj == 0 || jj >= f_lo) ? INFINITY : srow[jj];  // forced: +inf
+        }
         ++pos;
       }
   }
-  for (int k = total + tid; k < topk; k += NTS) out[k] = -1;
+  for (int k = total + tid; k < topk; k += NTS) {
+    out[k] = -1;
+    if (out_sc) out_sc[k] = -INFINITY;
+  }
 }
 
 // ---- decode selection (one query block per row, long candidate ranges): two levels.
@@ -556,7 +568,8 @@ __device__ __forceinline__ void idx2key(uint32_t* keys, const uint32_t* idx, int
 // f_lo .. i, and -1 padding.
 template <int CAPB, int NTM>
 __global__ void __launch_bounds__(NTM)
-decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel, int nsl, int R,
+decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel, float* __restrict__ sel_sc, int nsl,
+                    int R,
                     long i, int n_local, int topk, long nc, const int64_t* __restrict__ kv_lens, int Hkv,
                     long kv_max) {
   __shared__ uint32_t keys[CAPB];
@@ -566,6 +579,7 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   __shared__ int scan_tmp[NTM / 64 + 1];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
+  __shared__ int32_t s_row[256];  // the emitted row (topk <= 256), for placing the scores
   const int bg = blockIdx.x, tid = threadIdx.x;
   const int n = nsl * R;
   if (kv_lens) {  // this sequence's query block and candidate count (at most the nc given)
@@ -611,6 +625,7 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
     else if (all_ties) pick = keys[t] >= T;
     else pick = keys[t] >= T2;
     if (pick && idx[t] <= (uint32_t)nc) atomicOr(&bits[idx[t] >> 5], 1u << (idx[t] & 31));
+    if (!pick) idx[t] = 0xFFFFFFFFu;  // (for the scores below: only chosen candidates keep an index)
   }
   __syncthreads();
   const long f_lo = i - n_local + 1 > 0 ? i - n_local + 1 : 0;
@@ -627,7 +642,7 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
     while (m) {
       const int b = __ffs(m) - 1;
       m &= m - 1;
-      if (pos < topk) out[pos] = 32 * w + b;
+      if (pos < topk) { out[pos] = 32 * w + b; s_row[pos] = 32 * w + b; }
       ++pos;
     }
   }
@@ -636,6 +651,27 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   for (int t = tid; t < nloc; t += NTM)
     if (head + cnt + t < topk) out[head + cnt + t] = (int32_t)(f_lo + t);
   for (int t = head + cnt + nloc + tid; t < topk; t += NTM) out[t] = -1;
+  if (sel_sc) {
+    // each chosen candidate finds its place in the emitted (ascending) row and writes its
+    // score there; forced blocks get +inf, padding -inf
+    float* osc = sel_sc + (long)bg * topk;
+    __syncthreads();
+    const int nch = min(cnt, topk - head);
+    for (int t = tid; t < n; t += NTM) {
+      const uint32_t j = idx[t];
+      if (j == 0xFFFFFFFFu || j > (uint32_t)nc) continue;
+      int lo = head, hi = head + nch;  // binary search in s_row[head .. head + nch)
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((uint32_t)s_row[mid] < j) lo = mid + 1; else hi = mid;
+      }
+      if (lo < head + nch && (uint32_t)s_row[lo] == j) osc[lo] = key_score((uint32_t)(cand[(long)bg * n + t] >> 32));
+    }
+    if (tid == 0 && head) osc[0] = INFINITY;
+    for (int t = tid; t < nloc; t += NTM)
+      if (head + cnt + t < topk) osc[head + cnt + t] = INFINITY;
+    for (int t = head + cnt + nloc + tid; t < topk; t += NTM) osc[t] = -INFINITY;
+  }
 }
 
 }  // namespace
@@ -690,7 +726,7 @@ static void launch_decode_slice(const sala_sparse_desc& d, const void* q, const 
 }
 
 hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
-                               const float* k_pool, int32_t* sel, void* ws, hipStream_t st) {
+                               const float* k_pool, int32_t* sel, float* sel_sc, void* ws, hipStream_t st) {
   const SparseGeom g = sparse_geom(d);
   const int BG = d.batch * d.n_kv_heads;
   const long RL = select_row_len(d);
@@ -702,8 +738,8 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
   if (decode_two_level(d, &nc, &nsl, &R)) {
     uint64_t* cand = reinterpret_cast<uint64_t*>(sc);
     launch_decode_slice(d, q, qw, k_pool, cand, g.nblk_cap, nc, R, nsl, nullptr, st);
-    hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nsl, R,
-                       i_max, d.n_local, d.topk, nc, nullptr, d.n_kv_heads, (long)d.kv_len);
+    hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, sel_sc,
+                       nsl, R, i_max, d.n_local, d.topk, nc, nullptr, d.n_kv_heads, (long)d.kv_len);
     return hipGetLastError();
   }
   const dim3 gq(d.batch, (unsigned)g.nqb);
@@ -739,10 +775,10 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
   // long rows (decode past the two-level range, prefill beyond 4,096 candidate blocks): 1024
   // threads and 16,384 keys in LDS per row; shorter rows: 256 threads, 4,096 keys
   if (g.nqb == 1 || RL > 4096)
-    hipLaunchKernelGGL((select_kernel<1024, 16384>), dim3((unsigned)(BG * g.nqb)), dim3(1024), 0, st, sc, sel,
+    hipLaunchKernelGGL((select_kernel<1024, 16384>), dim3((unsigned)(BG * g.nqb)), dim3(1024), 0, st, sc, sel, sel_sc,
                        (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
   else
-    hipLaunchKernelGGL((select_kernel<256, 4096>), dim3((unsigned)(BG * g.nqb)), dim3(256), 0, st, sc, sel,
+    hipLaunchKernelGGL((select_kernel<256, 4096>), dim3((unsigned)(BG * g.nqb)), dim3(256), 0, st, sc, sel, sel_sc,
                        (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
   return hipGetLastError();
 }
@@ -782,8 +818,8 @@ hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_
   uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + ((qt_bytes + 255) & ~(size_t)255));
   const long nblk_cap = d.kv_capacity / 64;
   launch_decode_slice(d, q, qw, k_pool, cand, nblk_cap, nc, R, nsl, kv_lens, st);
-  hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nsl, R,
-                     (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens, d.n_kv_heads, (long)d.kv_len);
+  hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nullptr,
+                     nsl, R, (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens, d.n_kv_heads, (long)d.kv_len);
   return hipGetLastError();
 }
 

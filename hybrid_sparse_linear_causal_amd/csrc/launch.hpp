@@ -80,7 +80,7 @@ hipError_t launch_kv_pool(const sala_sparse_desc& d, const void* k_cache, float*
                           int64_t blk_begin, int64_t blk_end, hipStream_t st);
 size_t block_select_workspace(const sala_sparse_desc& d);
 hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
-                               const float* k_pool, int32_t* sel, void* ws, hipStream_t st);
+                               const float* k_pool, int32_t* sel, float* sel_sc, void* ws, hipStream_t st);
 size_t sparse_attn_workspace(const sala_sparse_desc& d);
 // decode with each sequence at its own cache length (kv_lens: device [B] int64)
 size_t block_select_decode_at_workspace(const sala_sparse_desc& d);  // SIZE_MAX: context too long

@@ -61,7 +61,7 @@ hipError_t launch_block_select_varlen(const sala_sparse_desc& d, const int32_t* 
     if (n == 0) continue;
     const hipError_t e =
         launch_block_select(seq_desc(d, cu, pos0, s), static_cast<const char*>(q) + (size_t)cu[s] * qrow * eb, qw,
-                            k_pool + s * pool_seq, sel + qb_row * d.n_kv_heads * d.topk, ws, st);
+                            k_pool + s * pool_seq, sel + qb_row * d.n_kv_heads * d.topk, nullptr, ws, st);
     if (e != hipSuccess) return e;
     qb_row += (n + 63) / 64;
   }

@@ -35,7 +35,8 @@ class SalaError(RuntimeError):
 class LinearDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("pos0", ctypes.c_int64), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+                ("pos0", ctypes.c_int64), ("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float),
+                ("chunk", ctypes.c_int32), ("reserved_", ctypes.c_int32)]
 
 
 class SparseDesc(ctypes.Structure):
@@ -67,7 +68,7 @@ def lib():
         L.sala_kv_norm_backward.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 6 + [ctypes.c_size_t, _VP]
         L.sala_kv_append.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7
         L.sala_kv_pool.argtypes = [ctypes.POINTER(SparseDesc), _VP, _VP, ctypes.c_int64, ctypes.c_int64, _VP]
-        L.sala_block_select.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 5 + [ctypes.c_size_t, _VP]
+        L.sala_block_select.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 6 + [ctypes.c_size_t, _VP]
         L.sala_sparse_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 9 + [ctypes.c_size_t, _VP]
         L.sala_dense_attn.argtypes = [ctypes.POINTER(SparseDesc)] + [_VP] * 7 + [ctypes.c_size_t, _VP]
         L.sala_sparse_layer_uses_dense.argtypes = [ctypes.POINTER(SparseDesc)]
@@ -150,29 +151,32 @@ def _workspace(op, desc, device, workspace):
     return torch.empty(need, dtype=torch.uint8, device=device), need
 
 
-def linear_desc(q, pos0, rope_base, eps):
+def linear_desc(q, pos0, rope_base, eps, n_kv_heads=None, chunk=64):
     B, N, H, d = q.shape
-    return LinearDesc(B, N, H, H, d, _dtype_code(q), int(pos0), float(rope_base), float(eps))
+    return LinearDesc(B, N, H, n_kv_heads or H, d, _dtype_code(q), int(pos0), float(rope_base), float(eps),
+                      int(chunk), 0)
 
 
 def linear_prefill(q, k, v, g, *, pos0=0, rope_base=10000.0, eps=1e-6, state_in=None,
-                   state_out=None, q_norm_w=None, k_norm_w=None, out=None, workspace=None,
+                   state_out=None, q_norm_w=None, k_norm_w=None, out=None, workspace=None, chunk=64,
                    stream=None):
-    """q, k, v, g: [B, N, H, d] (bf16 or f32); returns (out, state_out [B, H, d, d] f32)."""
+    """q, g: [B, N, H, d]; k, v: [B, N, Hkv, d] (bf16 or f32, Hkv dividing H); returns
+    (out, state_out [B, Hkv, d, d] f32)."""
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _check(t, n, q.dtype)
     B, N, H, d = q.shape
-    for n, t in (("k", k), ("v", v), ("g", g)):
-        if tuple(t.shape) != (B, N, H, d):
-            raise SalaError(2, f"{n} shape {tuple(t.shape)} != {(B, N, H, d)}")
+    Hkv = k.shape[2]
+    for n, t, hh in (("k", k, Hkv), ("v", v, Hkv), ("g", g, H)):
+        if tuple(t.shape) != (B, N, hh, d):
+            raise SalaError(2, f"{n} shape {tuple(t.shape)} != {(B, N, hh, d)}")
     if out is None:
         out = torch.empty_like(q)
     if state_out is None:
-        state_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+        state_out = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=q.device)
     for n, t in (("state_in", state_in), ("state_out", state_out), ("q_norm_w", q_norm_w),
                  ("k_norm_w", k_norm_w)):
         _check(t, n, torch.float32)
-    desc = linear_desc(q, pos0, rope_base, eps)
+    desc = linear_desc(q, pos0, rope_base, eps, Hkv, chunk)
     ws, ws_bytes = _workspace(OP_LINEAR_PREFILL, desc, q.device, workspace)
     _call(lib().sala_linear_prefill, ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
           _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(ws),
@@ -211,14 +215,15 @@ def linear_backward(q, k, v, g, dout, *, pos0=0, rope_base=10000.0, eps=1e-6, st
 
 def linear_decode_step(q, k, v, g, state, pos, *, rope_base=10000.0, eps=1e-6, q_norm_w=None,
                        k_norm_w=None, out=None, stream=None):
-    """q, k, v, g: [B, H, d]; state [B, H, d, d] f32 updated in place; returns out [B, H, d]."""
+    """q, g: [B, H, d]; k, v: [B, Hkv, d]; state [B, Hkv, d, d] f32 updated in place; returns
+    out [B, H, d]."""
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _check(t, n, q.dtype)
     _check(state, "state", torch.float32)
     B, H, d = q.shape
     if out is None:
         out = torch.empty_like(q)
-    desc = LinearDesc(B, 1, H, H, d, _dtype_code(q), int(pos), float(rope_base), float(eps))
+    desc = LinearDesc(B, 1, H, k.shape[1], d, _dtype_code(q), int(pos), float(rope_base), float(eps), 64, 0)
     _call(lib().sala_linear_decode_step, ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
           _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state), _ptr(out), _stream(stream),
           what="linear_decode_step")
@@ -235,7 +240,7 @@ def linear_decode_step_at(q, k, v, g, state, pos, *, rope_base=10000.0, eps=1e-6
     B, H, d = q.shape
     if out is None:
         out = torch.empty_like(q)
-    desc = LinearDesc(B, 1, H, H, d, _dtype_code(q), 0, float(rope_base), float(eps))
+    desc = LinearDesc(B, 1, H, k.shape[1], d, _dtype_code(q), 0, float(rope_base), float(eps), 64, 0)
     _call(lib().sala_linear_decode_step_at, ctypes.byref(desc), _ptr(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
           _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state), _ptr(out), _stream(stream), what="linear_decode_step_at")
     return out
@@ -324,8 +329,9 @@ def kv_pool(k_cache, k_pool, kv_len, blk_begin, blk_end, *, stream=None):
 
 
 def block_select(q, k_pool, kv_len, kv_capacity, *, n_kv_heads, topk=64, n_local=2, eps=1e-6,
-                 q_norm_w=None, sel=None, workspace=None, stream=None):
-    """q [B, n_q, Hq, d]; returns sel [B, Hkv, nqb, topk] int32."""
+                 q_norm_w=None, sel=None, sel_scores=None, workspace=None, stream=None):
+    """q [B, n_q, Hq, d]; returns sel [B, Hkv, nqb, topk] int32. sel_scores: optional f32 tensor
+    of sel's shape receiving each entry's block score (+inf forced, -inf padding)."""
     _check(q, "q")
     _check(k_pool, "k_pool", torch.float32)
     B, nq, Hq, d = q.shape
@@ -336,8 +342,9 @@ def block_select(q, k_pool, kv_len, kv_capacity, *, n_kv_heads, topk=64, n_local
     if sel is None:
         sel = torch.empty((B, n_kv_heads, nqb, topk), dtype=torch.int32, device=q.device)
     ws, ws_bytes = _workspace(OP_BLOCK_SELECT, desc, q.device, workspace)
+    _check(sel_scores, "sel_scores", torch.float32)
     _call(lib().sala_block_select, ctypes.byref(desc), _ptr(q), _ptr(q_norm_w), _ptr(k_pool),
-          _ptr(sel), _ptr(ws), ws_bytes, _stream(stream), what="block_select")
+          _ptr(sel), _ptr(sel_scores), _ptr(ws), ws_bytes, _stream(stream), what="block_select")
     return sel
 
 
@@ -499,11 +506,11 @@ def linear_prefill_varlen(q, k, v, g, vl, *, rope_base=10000.0, eps=1e-6, state_
     if out is None:
         out = torch.empty_like(q)
     if state_out is None:
-        state_out = torch.empty((vl.nseq, H, d, d), dtype=torch.float32, device=q.device)
+        state_out = torch.empty((vl.nseq, k.shape[1], d, d), dtype=torch.float32, device=q.device)
     for n, t in (("state_in", state_in), ("state_out", state_out), ("q_norm_w", q_norm_w),
                  ("k_norm_w", k_norm_w)):
         _check(t, n, torch.float32)
-    desc = LinearDesc(vl.nseq, T, H, H, d, SALA_BF16, 0, float(rope_base), float(eps))
+    desc = LinearDesc(vl.nseq, T, H, k.shape[1], d, SALA_BF16, 0, float(rope_base), float(eps), 64, 0)
     ws, ws_bytes = _varlen_workspace(OP_LINEAR_PREFILL, desc, vl, q.device, workspace)
     _call(lib().sala_linear_prefill_varlen, ctypes.byref(desc), *vl.args(), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
           _ptr(q_norm_w), _ptr(k_norm_w), _ptr(state_in), _ptr(state_out), _ptr(out), _ptr(ws), ws_bytes,

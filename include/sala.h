@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define SALA_ABI_VERSION 5
+#define SALA_ABI_VERSION 6
 
 /* sequences per call of the packed variable-length (varlen) entry points */
 #define SALA_VARLEN_MAX_SEQS 64
@@ -66,12 +66,20 @@ typedef enum {
 /* Linear-attention layer shape.
  *   batch      B >= 1
  *   seq_len    N tokens in this call (prefill: N >= 0; decode: must be 1)
- *   n_heads    H query heads; n_kv_heads must equal n_heads (grouped linear heads: SALA_ERR_UNSUPPORTED)
+ *   n_heads    H query heads
+ *   n_kv_heads Hkv key/value heads, dividing H (at most 64 query heads per KV head): query head h
+ *              reads the state of KV head h / (H / Hkv); the state is per KV head. Hkv = H is
+ *              plain multi-head linear attention
  *   head_dim   d: 64 or 128 (bf16 prefill needs 128)
  *   dtype      sala_dtype of q, k, v, gate and out
  *   pos0       position of the first token of the call (>= 0); RoPE uses p = pos0 + t
  *   rope_base  RoPE base (theta_i = rope_base^(-2i/d)), > 0
- *   norm_eps   QK-norm epsilon, >= 0 */
+ *   norm_eps   QK-norm epsilon, >= 0
+ *   chunk      tokens per chunk of the chunked evaluation: 64 (0 selects 64). The result does not
+ *              depend on it in exact arithmetic (the chunked form equals the recurrence); 128
+ *              and 256 are valid chunk sizes that this library does not build
+ *              (SALA_ERR_UNSUPPORTED); other values are SALA_ERR_INVALID
+ *   reserved_  must be 0 */
 typedef struct {
   int32_t batch;
   int32_t seq_len;
@@ -82,6 +90,8 @@ typedef struct {
   int64_t pos0;
   float rope_base;
   float norm_eps;
+  int32_t chunk;
+  int32_t reserved_;
 } sala_linear_desc;
 
 /* Block-sparse layer shape.
@@ -123,10 +133,10 @@ typedef struct {
  *   q^ = RoPE_p(RMSNorm(q_t) * q_norm_w), k^ = RoPE_p(RMSNorm(k_t) * k_norm_w)
  *   S  <- S + k^^T v_t           (S[i][j] += k^[i] v[j])
  *   out_t = (q^ S) * sigmoid(g_t)
- * Inputs  q, k, v, gate, out: [B, N, H, d] (token-major, dtype);
+ * Inputs  q, gate, out: [B, N, H, d]; k, v: [B, N, Hkv, d] (token-major, dtype);
  *         q_norm_w, k_norm_w: [d] float or NULL (= all ones);
- *         state_in: [B, H, d, d] float (S[i][j], row i = key dim) or NULL (= zeros).
- * Outputs out: [B, N, H, d]; state_out: [B, H, d, d] float, or NULL to skip. state_out may
+ *         state_in: [B, Hkv, d, d] float (S[i][j], row i = key dim) or NULL (= zeros).
+ * Outputs out: [B, N, H, d]; state_out: [B, Hkv, d, d] float, or NULL to skip. state_out may
  *         alias state_in. The bf16 path evaluates the recurrence in 64-token chunks on MFMA
  *         (bf16 operands, fp32 accumulation, fp32 state); the f32 path is a plain fp32 scan.
  * Workspace: sala_workspace_bytes(SALA_OP_LINEAR_PREFILL, desc) bytes (may be 0). */
@@ -136,8 +146,9 @@ sala_status sala_linear_prefill(const sala_linear_desc* desc, const void* q, con
                                 void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Linear layer decode step: one token per sequence at position desc->pos0 (same pages).
- * desc->seq_len must be 1. q, k, v, gate, out: [B, H, d]; state: [B, H, d, d] float, updated
- * in place (S <- S + k^^T v, then out = (q^ S) * sigmoid(g)). */
+ * desc->seq_len must be 1. q, gate, out: [B, H, d]; k, v: [B, Hkv, d]; state: [B, Hkv, d, d]
+ * float, updated in place (S <- S + k^^T v once per KV head, then out = (q^ S) * sigmoid(g) for
+ * each query head of its group). */
 sala_status sala_linear_decode_step(const sala_linear_desc* desc, const void* q, const void* k,
                                     const void* v, const void* gate, const float* q_norm_w,
                                     const float* k_norm_w, float* state, void* out, void* stream);
@@ -151,7 +162,8 @@ sala_status sala_linear_decode_step(const sala_linear_desc* desc, const void* q,
  *   dq_norm_w, dk_norm_w: [d] float, or NULL to skip (computed as if the weight were all ones
  *   when the matching input weight is NULL);
  *   dstate_in: [B, H, d, d] float, or NULL to skip.
- * Inputs q, k, v, gate, dout: [B, N, H, d] bf16 (desc->dtype must be SALA_BF16, head_dim 128);
+ * Inputs q, k, v, gate, dout: [B, N, H, d] bf16 (desc->dtype must be SALA_BF16, head_dim 128,
+ * n_kv_heads = n_heads: grouped heads are SALA_ERR_UNSUPPORTED here);
  * q_norm_w, k_norm_w, state_in, dstate_out as in sala_linear_prefill (NULL = ones / zeros).
  * The gradients are chunked causal linear attentions over the normalised, rotated q and k (two
  * of them in reverse token order) on MFMA with bf16 operands and fp32 accumulation; the norm,
@@ -204,9 +216,11 @@ sala_status sala_linear_decode_step_at(const sala_linear_desc* desc, const int64
  * Output sel: [B, Hkv, nqb, topk] int32, ascending block indices, padded with -1, where
  * nqb = (kv_len - 1) / 64 - (kv_len - n_q) / 64 + 1 (row r is query block
  * (kv_len - n_q) / 64 + r). Scores are fp32. q: [B, n_q, Hq, d]; k_pool as in sala_kv_append.
+ * sel_scores: NULL, or [B, Hkv, nqb, topk] float receiving, beside each entry of sel, the score
+ * of a chosen candidate block, +INFINITY for a forced block and -INFINITY for padding.
  * Workspace: sala_workspace_bytes(SALA_OP_BLOCK_SELECT, desc). */
 sala_status sala_block_select(const sala_sparse_desc* desc, const void* q, const float* q_norm_w,
-                              const float* k_pool, int32_t* sel, void* workspace,
+                              const float* k_pool, int32_t* sel, float* sel_scores, void* workspace,
                               size_t workspace_bytes, void* stream);
 
 /* Block-sparse softmax attention with output gate (same pages). For each query token t (at

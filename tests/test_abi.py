@@ -32,7 +32,7 @@ def test_abi_version_and_status_strings():
     from hybrid_sparse_linear_causal_amd import sala as S
 
     L = S.lib()
-    assert L.sala_abi_version() == 5
+    assert L.sala_abi_version() == 6
     for code in range(6):
         assert L.sala_status_str(code)
     assert L.sala_last_hip_error() == 0
@@ -61,8 +61,10 @@ FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(batch=0), 2), (dict(seq_len=-1), 2), (dict(head_dim=96), 3), (dict(dtype=7), 2),
-    (dict(n_kv_heads=1), 3), (dict(n_kv_heads=3), 2), (dict(rope_base=0.0), 2),
+    (dict(n_kv_heads=3), 2), (dict(n_heads=130, n_kv_heads=2), 3), (dict(rope_base=0.0), 2),
     (dict(norm_eps=-1.0), 2), (dict(pos0=-5), 2), (dict(head_dim=64), 3),
+    # chunk sizes: 64 (or 0) built; 128 and 256 valid but not built; anything else invalid
+    (dict(chunk=128), 3), (dict(chunk=256), 3), (dict(chunk=100), 2), (dict(chunk=-64), 2), (dict(reserved_=1), 2),
 ])
 def test_linear_prefill_rejects(kw, expect):
     from hybrid_sparse_linear_causal_amd import sala as S
@@ -92,6 +94,22 @@ def test_linear_prefill_null_and_alignment_and_workspace():
                                  None, need, None) == 4
 
 
+def test_linear_grouped_heads_sizes():
+    """Grouped (GQA) linear heads: the segment-state workspace is per KV head; the backward
+    supports plain multi-head layers only."""
+    from hybrid_sparse_linear_causal_amd import sala as S
+
+    L = S.lib()
+    mha = _lin(seq_len=1 << 16, n_heads=32, n_kv_heads=32)
+    gqa = _lin(seq_len=1 << 16, n_heads=32, n_kv_heads=2)
+    assert S.workspace_bytes(S.OP_LINEAR_PREFILL, gqa) * 16 == S.workspace_bytes(S.OP_LINEAR_PREFILL, mha)
+    assert L.sala_workspace_bytes(S.OP_LINEAR_BACKWARD, ctypes.byref(gqa)) == ctypes.c_size_t(-1).value
+    args = [FAKE] * 4 + [None, None, None, FAKE, None] + [FAKE] * 4 + [None, None, None]
+    assert L.sala_linear_backward(ctypes.byref(gqa), *args, FAKE, 1 << 40, None) == 3
+    assert L.sala_linear_prefill(ctypes.byref(_lin(chunk=256)), FAKE, FAKE, FAKE, FAKE, None, None, None, None,
+                                 FAKE, FAKE, 1 << 30, None) == 3
+
+
 def test_linear_decode_rejects():
     from hybrid_sparse_linear_causal_amd import sala as S
 
@@ -114,7 +132,7 @@ def test_sparse_rejects(kw, expect):
     L = S.lib()
     d = _sp(**kw)
     assert L.sala_kv_append(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == expect
-    assert L.sala_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == expect
+    assert L.sala_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, FAKE, 1 << 40, None) == expect
     assert L.sala_sparse_attn(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
                               None) == expect
     assert L.sala_workspace_bytes(S.OP_BLOCK_SELECT, ctypes.byref(d)) == ctypes.c_size_t(-1).value
@@ -125,10 +143,10 @@ def test_sparse_null_workspace_and_pool_range():
 
     L = S.lib()
     d = _sp()
-    assert L.sala_block_select(ctypes.byref(d), None, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert L.sala_block_select(ctypes.byref(d), None, None, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
     need = S.workspace_bytes(S.OP_BLOCK_SELECT, d)
     assert need > 0
-    assert L.sala_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, need - 1, None) == 4
+    assert L.sala_block_select(ctypes.byref(d), FAKE, None, FAKE, FAKE, None, FAKE, need - 1, None) == 4
     assert L.sala_kv_pool(ctypes.byref(d), FAKE, FAKE, 0, 3, None) == 2  # 3*64 > kv_len
     assert L.sala_kv_pool(ctypes.byref(d), FAKE, FAKE, 2, 1, None) == 2
     assert L.sala_kv_pool(ctypes.byref(d), None, FAKE, 0, 1, None) == 1

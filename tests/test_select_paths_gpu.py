@@ -111,3 +111,74 @@ def test_decode_select_beyond_two_level(S, L, topk):
                                     gsel[0, 0, 0], 1.0 / math.sqrt(d))
     e = assert_rel(host(out)[0, 0], o2 * O.sigmoid(g[0, 0]), 1e-2, "decode out on the gpu selection")
     print(f"  margin rows {nm}, rel err {e:.2e}", flush=True)
+
+
+def _check_scores(sel, scores, ref_score, first_block, n_local, what):
+    """sel_scores beside sel: +inf for forced blocks, -inf for padding, and the candidate's score
+    (fp32, against the oracle's float64 q~ . k_bar) for chosen candidates."""
+    B, G, R, K = sel.shape
+    errs = []
+    for b in range(B):
+        for g in range(G):
+            for r in range(R):
+                i = first_block + r
+                forced = {0} | set(range(max(0, i - n_local + 1), i + 1))
+                row_ref = []
+                for x in range(K):
+                    j = int(sel[b, g, r, x])
+                    if j < 0:
+                        assert scores[b, g, r, x] == -np.inf, (what, b, g, i, x)
+                    elif j in forced:
+                        assert scores[b, g, r, x] == np.inf, (what, b, g, i, x)
+                    else:
+                        row_ref.append((scores[b, g, r, x], ref_score(b, g, i, j)))
+                if row_ref:
+                    got, want = np.array(row_ref).T
+                    errs.append(np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30))
+    assert errs and max(errs) <= 1e-4, (what, max(errs) if errs else None)
+    return max(errs)
+
+
+def test_selection_scores(S):
+    """The optional scores output on the three selection paths: prefill rows (score tiles and the
+    per-row radix select), a decode row inside the two-level range (slice winners merged), and a
+    decode row past it (score row and the long-row select)."""
+    import torch
+
+    d, n_local = 128, 2
+    # prefill: 40 query blocks, 2 KV groups of 4 heads, top-6
+    B, N, Hq, Hkv, topk = 1, 64 * 40 + 17, 8, 2, 6
+    q = host_normal(970, 0, (B, N, Hq, d))
+    k = host_normal(970, 1, (B, N, Hkv, d))
+    cap = ((N + 63) // 64) * 64
+    kc = torch.zeros((B, Hkv, cap, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+    S.kv_append(dev(k, "bf16"), dev(k, "bf16"), kc, vc, kp, N, n_heads=Hq)
+    nqb = (N + 63) // 64
+    scores = torch.empty((B, Hkv, nqb, topk), dtype=torch.float32, device="cuda")
+    sel = S.block_select(dev(q, "bf16"), kp, N, cap, n_kv_heads=Hkv, topk=topk, n_local=n_local, sel_scores=scores)
+    qt = O.query_block_tilde(O.qk_norm(q), 64, Hkv)
+    kb = O.pool_keys(O.qk_norm(k), 64)
+    e = _check_scores(sel.cpu().numpy(), scores.cpu().numpy(), lambda b, g, i, j: float(qt[b, g, i] @ kb[b, g, j]), 0,
+                      n_local, "prefill")
+    print(f"  prefill rel err {e:.2e}", flush=True)
+    # decode rows: two-level (4,000 blocks, top-16) and beyond it (5,000 blocks, top-256)
+    for L, topk in ((64 * 4000 + 9, 16), (64 * 5000 + 9, 256)):
+        B, Hq, Hkv = 2, 8, 2
+        kc_h = host_normal(971, 5, (B, Hkv, L, d))
+        qd = host_normal(971, 0, (B, 1, Hq, d))
+        kc = torch.zeros((B, Hkv, cap := ((L + 63) // 64) * 64, d), dtype=torch.bfloat16, device="cuda")
+        kc[:, :, :L] = dev(kc_h, "bf16")
+        kp = torch.zeros((B, Hkv, cap // 64, d), dtype=torch.float32, device="cuda")
+        S.kv_pool(kc, kp, L, 0, (L - 1) // 64)
+        scores = torch.empty((B, Hkv, 1, topk), dtype=torch.float32, device="cuda")
+        sel = S.block_select(dev(qd, "bf16"), kp, L, cap, n_kv_heads=Hkv, topk=topk, n_local=n_local,
+                             sel_scores=scores)
+        qh = O.qk_norm(qd[:, 0])
+        G = Hq // Hkv
+        kbd = O.pool_keys(kc_h.transpose(0, 2, 1, 3), 64)
+        e = _check_scores(sel.cpu().numpy(), scores.cpu().numpy(),
+                          lambda b, g, i, j: float(qh[b, g * G:(g + 1) * G].sum(axis=0) @ kbd[b, g, j]),
+                          (L - 1) // 64, n_local, f"decode L={L}")
+        print(f"  decode L={L} top-{topk} rel err {e:.2e}", flush=True)
