@@ -130,6 +130,63 @@ def stored_traffic(kernel, launches_per_profile=1):
     return (rec["fetch_kb"] * rec["fetch_scale"] + rec["write_kb"] * rec["write_scale"]) * 1024.0
 
 
+def measured_peaks(torch):
+    """Ceilings measured on this GPU by the committed peak kernels (libsala_peaks.so, built from
+    hybrid_sparse_linear_causal_amd/csrc/peaks/peaks.hip): the best over a few grid sizes of a
+    4 GiB streaming read (16-byte loads) and of a loop of independent bf16 MFMA 16x16x32
+    products, timed with HIP events."""
+    import ctypes
+
+    path = os.path.join(ROOT, "hybrid_sparse_linear_causal_amd", "libsala_peaks.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    lib.sala_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.sala_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sala_peak_mfma32.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")  # >= the largest grid * 256
+
+    def call(rc):
+        if rc != 0:
+            raise RuntimeError(f"peak kernel launch failed ({rc})")
+
+    read = {}
+    for wgs in (1024, 2048, 4096, 8192):
+        ms = _time_events(torch, lambda: call(lib.sala_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), wgs, st)), 5)
+        read[wgs] = nbytes / (ms * 1e-3) / 1e9
+    del buf
+    iters = 2048
+    mfma, mfma32 = {}, {}
+    for wgs in (256, 512, 1024, 2048, 4096):
+        ms = _time_events(torch, lambda: call(lib.sala_peak_mfma(sink.data_ptr(), iters, wgs, st)), 3)
+        mfma[wgs] = wgs * 4 * 8 * iters * 16384 / (ms * 1e-3) / 1e12
+        ms = _time_events(torch, lambda: call(lib.sala_peak_mfma32(sink.data_ptr(), iters, wgs, st)), 3)
+        mfma32[wgs] = wgs * 4 * 4 * iters * 32768 / (ms * 1e-3) / 1e12
+    return {"hbm_read_gbs": max(read.values()), "bf16_mfma_tflops": max(mfma.values()),
+            "bf16_mfma_32x32x16_tflops": max(mfma32.values()),
+            "hbm_read_gbs_by_grid": read, "bf16_mfma_tflops_by_grid": mfma, "bf16_mfma_32x32x16_tflops_by_grid": mfma32,
+            "method": "libsala_peaks.so: 4 GiB streaming read (uint4 loads, 4 in flight per lane); "
+                      "8 independent v_mfma_f32_16x16x32_bf16 (4 of v_mfma_f32_32x32x16_bf16) chains per "
+                      "wave; best over grid sizes"}
+
+
+def stored_mfma_busy(kernel):
+    """MFMA busy fraction of `kernel` from the committed rocprofv3 counter summary
+    (profiles/pmc_mfma.json: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x CUs x 4 SIMDs, and
+    the executed bf16 MFMA flops), or None if missing or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", "pmc_mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(kernel)
+    if not rec or rec.get("source_sha256") != kernel_source_sha(rec["sources"]):
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac", "executed_flops_per_launch", "counters", "command") if k in rec}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,16 +307,31 @@ def main():
             e["end"] = ev(); e["end"].record()
         return e
 
+    # the decode step's calls with their algorithmic HBM bytes: a linear layer reads and writes
+    # its fp32 state (plus q, k, v, g, out); the append writes the new k, v and, as the token
+    # completes a block, reads its 64 keys and writes the pooled key; the selection reads the
+    # pooled keys of every candidate block; the attention reads the selected blocks' K and V
+    n_cand = (L - 1) // 64 - Dw.n_local  # candidate blocks 1 .. i - n_local
+    bytes_lin = B * H * d * d * 4 * 2 + B * H * d * 2 * 5
+    bytes_app = B * Hkv * (2 * d * 2 + 64 * d * 2 + d * 4)
+    bytes_sel = B * Hkv * n_cand * d * 4 + B * H * d * 2
+    bytes_att = B * Hkv * Dw.topk * 64 * d * 2 * 2 + B * H * d * 2 * 3
+
+    def dlin_call(Dr):
+        q, k, v, g = Dr["qkvg"]
+        return lambda: S.linear_decode_step(q, k, v, g, Dr["state"], L - 1, rope_base=W.rope_base, eps=W.norm_eps,
+                                            out=Dr["out"])
+
+    decode_calls = [(f"linear_layer_{li}", dlin_call(Dr), bytes_lin) for li, Dr in enumerate(dl)] + [
+        ("kv_append", lambda: S.kv_append(dkn, dvn, dkc, dvc, dkp, L, eps=W.norm_eps, n_heads=H), bytes_app),
+        ("block_select", lambda: S.block_select(dq, dkp, L, L, n_kv_heads=Hkv, topk=Dw.topk, n_local=Dw.n_local,
+                                                eps=W.norm_eps, sel=dsel, workspace=ws_dsel), bytes_sel),
+        ("sparse_attn", lambda: S.sparse_attn(dq, dkc, dvc, dg, dsel, L, n_local=Dw.n_local, eps=W.norm_eps,
+                                              out=dsout, workspace=ws_datt), bytes_att)]
+
     def decode_step():
-        for Dr in dl:
-            q, k, v, g = Dr["qkvg"]
-            S.linear_decode_step(q, k, v, g, Dr["state"], L - 1, rope_base=W.rope_base, eps=W.norm_eps,
-                                 out=Dr["out"])
-        S.kv_append(dkn, dvn, dkc, dvc, dkp, L, eps=W.norm_eps, n_heads=H)
-        S.block_select(dq, dkp, L, L, n_kv_heads=Hkv, topk=Dw.topk, n_local=Dw.n_local, eps=W.norm_eps,
-                       sel=dsel, workspace=ws_dsel)
-        S.sparse_attn(dq, dkc, dvc, dg, dsel, L, n_local=Dw.n_local, eps=W.norm_eps, out=dsout,
-                      workspace=ws_datt)
+        for _, fn, _ in decode_calls:
+            fn()
 
     for _ in range(args.warmup):
         step(False)
@@ -286,11 +358,8 @@ def main():
     att_tflops = flops_attn / (t_att * 1e-3) / 1e12
     lin_bytes = N * H * d * 2 * 5  # q, k, v, g in; out
     lin_gbs = lin_bytes / (sum(t_lin) / 3 * 1e-3) / 1e9
-    dec_bytes_lin = B * H * d * d * 4 * 2 + B * H * d * 2 * 5
-    n_cand = (L - 1) // 64 - Dw.n_local  # candidate blocks 1 .. i - n_local
-    dec_bytes_sp = (B * Hkv * (n_cand + 1) * d * 4 + B * Hkv * Dw.topk * 64 * d * 2 * 2
-                    + B * H * d * 2 * 3 + B * Hkv * 64 * d * 2)
-    dec_gbs = (3 * dec_bytes_lin + dec_bytes_sp) / (t_dec * 1e-3) / 1e9
+    dec_bytes = sum(b for _, _, b in decode_calls)
+    dec_gbs = dec_bytes / (t_dec * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -321,15 +390,29 @@ def main():
             "sparse_layer_ms": t_sparse,
             "sparse_layer_tokens_per_s": N / (t_sparse * 1e-3),
             "sparse_parts_ms": {"kv_append": t_app, "block_select": t_sel, "attention": t_att},
-            "decode_step_us": t_dec * 1e3,
-            "decode_us_per_token": t_dec * 1e3 / B,
-            "decode_parts_us": {"linear_x3": t_dlin * 1e3, "append_select": t_dsel * 1e3,
-                                "attention": t_datt * 1e3},
-            "decode_hbm_frac": dec_gbs / HBM_PEAK_GBS,
+            "decode_step_in_stack_us": t_dec * 1e3,
+            "decode_parts_in_stack_us": {"linear_x3": t_dlin * 1e3, "append_select": t_dsel * 1e3,
+                                         "attention": t_datt * 1e3},
+            "decode_in_stack_hbm_frac": dec_gbs / HBM_PEAK_GBS,
+            "decode_bytes_per_step": dec_bytes,
         },
     }
+    peaks = measured_peaks(torch)
+    result["measured_peaks"] = peaks
+    r = result["roofline"]
+    r["peak_measured"] = peaks["bf16_mfma_tflops"]
+    r["frac_of_measured"] = att_tflops / peaks["bf16_mfma_tflops"]
+    r["mfma_busy_counters"] = stored_mfma_busy("sparse_prefill_bf16_kernel")
+    result["breakdown"]["linear_layer_hbm_frac_of_measured"] = lin_gbs / peaks["hbm_read_gbs"]
+    result["linear_layer_tokens_per_s"] = result["breakdown"]["linear_layer_tokens_per_s"]
+    result["sparse_layer_tokens_per_s"] = result["breakdown"]["sparse_layer_tokens_per_s"]
     if not args.no_extras:
-        result["breakdown"].update(extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d))
+        ex = extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv, d, peaks)
+        result["breakdown"].update(ex)
+        # the decode headline: the step with the last-level cache flushed before it
+        result["decode_step_us"] = ex["decode_cold_step_us_median"]
+        result["decode_us_per_token"] = ex["decode_cold_step_us_median"] / B
+        result["decode_hbm_frac"] = dec_bytes / (ex["decode_cold_step_us_median"] * 1e-6) / 1e9 / HBM_PEAK_GBS
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_sample(W)
     print(json.dumps(result))
@@ -348,9 +431,10 @@ def _time_events(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d):
+def extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv, d, peaks):
     """Per-configuration layer times (32K linear, 128K sparse), the decode step as one graph
-    replay, and the decode step with the 256 MB last-level cache flushed before each step."""
+    replay, and the decode step with the 256 MB last-level cache flushed before each step (whole
+    and call by call, with each call's HBM rate)."""
     from hybrid_sparse_linear_causal_amd.inputs import WORKLOADS, device_normal
 
     res = {}
@@ -444,12 +528,31 @@ def extra_measurements(S, torch, W, decode_step, dl, B, L, H, Hkv, d):
         e1.record()
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
+    # the same, call by call: events between the calls of each flushed step
+    per = {name: [] for name, _, _ in decode_calls}
+    for r in range(10):
+        flush.fill_(r)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(decode_calls) + 1)]
+        evs[0].record()
+        for x, (_, fn, _) in enumerate(decode_calls):
+            fn()
+            evs[x + 1].record()
+        torch.cuda.synchronize()
+        for x, (name, _, _) in enumerate(decode_calls):
+            per[name].append(evs[x].elapsed_time(evs[x + 1]) * 1e3)
     for Dr, s0 in zip(dl, saved):
         Dr["state"].copy_(s0)
+    calls = {}
+    for name, _, byts in decode_calls:
+        v = sorted(per[name])[len(per[name]) // 2]
+        gbs = byts / (v * 1e-6) / 1e9
+        calls[name] = {"us": v, "bytes": byts, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                       "frac_of_measured_read": gbs / peaks["hbm_read_gbs"]}
     cold.sort()
-    res["decode_graph_step_us"] = us_graph
-    res["decode_graph_us_per_token"] = us_graph / B
+    res["decode_graph_step_us_warm"] = us_graph
+    res["decode_graph_us_per_token_warm"] = us_graph / B
     res["decode_cold_step_us_median"] = cold[len(cold) // 2]
+    res["decode_cold_calls"] = calls
     return res
 
 

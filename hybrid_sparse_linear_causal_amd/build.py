@@ -1,7 +1,8 @@
 """Build libsala.so (HIP for gfx950) in-tree with hipcc.
 
 Every source under csrc/ is compiled for --offload-arch=gfx950 into _build/ and linked into
-hybrid_sparse_linear_causal_amd/libsala.so. Packed-fp32 VALU instructions are disabled for
+hybrid_sparse_linear_causal_amd/libsala.so; csrc/peaks/peaks.hip (the measured-ceiling kernels
+of bench.py) becomes libsala_peaks.so. Packed-fp32 VALU instructions are disabled for
 the device code (-Xclang -target-feature -Xclang -packed-fp32-ops).
 
     python -m hybrid_sparse_linear_causal_amd.build
@@ -65,7 +66,23 @@ def build(verbose=False, jobs=8):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_peaks(hipcc)
     return LIB
+
+
+PEAKS_SRC = os.path.join(CSRC, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "libsala_peaks.so")
+
+
+def build_peaks(hipcc=None):
+    """The measured-ceiling kernels bench.py uses (libsala_peaks.so; not part of libsala)."""
+    hipcc = hipcc or _hipcc()
+    tmp = PEAKS_LIB + ".tmp"
+    r = subprocess.run([hipcc, *COMMON, *DEVICE_FLAGS, "-shared", PEAKS_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PEAKS_SRC}:\n{r.stderr}")
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
 
 
 if __name__ == "__main__":
