@@ -2,7 +2,9 @@
 
 Every source under csrc/ is compiled for --offload-arch=gfx950 into _build/ and linked into
 hybrid_sparse_linear_causal_amd/libsala.so; csrc/peaks/peaks.hip (the measured-ceiling kernels
-of bench.py) becomes libsala_peaks.so. Packed-fp32 VALU instructions are disabled for
+of bench.py) becomes libsala_peaks.so; libsala_asan.so is the same library with its host code
+built with AddressSanitizer and UndefinedBehaviorSanitizer (for the argument-check tests on the
+CPU). Packed-fp32 VALU instructions are disabled for
 the device code (-Xclang -target-feature -Xclang -packed-fp32-ops).
 
     python -m hybrid_sparse_linear_causal_amd.build
@@ -67,7 +69,48 @@ def build(verbose=False, jobs=8):
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
     build_peaks(hipcc)
+    build_asan(jobs)
     return LIB
+
+
+ASAN_BUILD = os.path.join(PKG, "_build_asan")
+ASAN_LIB = os.path.join(PKG, "libsala_asan.so")
+# host code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer (the device code is
+# built as usual); for the argument-checking tests on the CPU, run with the clang ASan runtime
+# preloaded (asan_runtime())
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime():
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    return path if path and os.path.exists(path) else None
+
+
+def build_asan(jobs=8):
+    """libsala_asan.so: the library with sanitizer-instrumented host code."""
+    hipcc = _hipcc()
+    os.makedirs(ASAN_BUILD, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(ASAN_BUILD, os.path.basename(src) + ".o")
+        lang = ["-x", "hip"] if src.endswith(".cpp") else []
+        r = subprocess.run([hipcc, *COMMON, *lang, *DEVICE_FLAGS, *ASAN_FLAGS, "-c", src, "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized host) failed for {src}:\n{r.stderr}")
+        return obj
+
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, sources()))
+    tmp = ASAN_LIB + ".tmp"
+    r = subprocess.run([hipcc, f"--offload-arch={ARCH}", "-shared", *ASAN_FLAGS, "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized host) failed:\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
 
 
 PEAKS_SRC = os.path.join(CSRC, "peaks", "peaks.hip")

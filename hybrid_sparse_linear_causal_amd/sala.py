@@ -18,7 +18,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsala.so")
+# SALA_LIBRARY may name another build of the library (the sanitizer-instrumented one in the tests)
+LIB_PATH = os.environ.get("SALA_LIBRARY") or os.path.join(_PKG, "libsala.so")
 
 SALA_F32, SALA_BF16 = 0, 1
 OP_LINEAR_PREFILL, OP_BLOCK_SELECT, OP_SPARSE_ATTN, OP_DENSE_ATTN, OP_LINEAR_BACKWARD = 1, 2, 3, 4, 5

@@ -10,7 +10,7 @@ import pytest
 
 from conftest import ROOT
 
-LIB = os.path.join(ROOT, "hybrid_sparse_linear_causal_amd", "libsala.so")
+LIB = os.environ.get("SALA_LIBRARY") or os.path.join(ROOT, "hybrid_sparse_linear_causal_amd", "libsala.so")
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libsala.so not built")
 
 
