@@ -12,10 +12,10 @@
 // Kernels: (1) qtilde_kernel — one pass over q; (2) prefill: score_tile_kernel (64x64 fp32
 // tiles of q~ k_pool^T), then select_kernel — per row an exact radix select on monotone uint32
 // keys of the scores and ordered compaction, so the output is ascending and deterministic;
-// (3) decode (one query block): decode_slice_kernel scores slices of 512 candidates and keeps
-// each slice's best (radix threshold, ties to the lower index), decode_merge_kernel selects
-// among the slice winners and emits them ascending through a bitmap; very long ranges fall
-// back to score_row_kernel + select_kernel.
+// (3) decode (one query block): decode_slice_kernel scores slices of 512 candidates (chunks of
+// 32 dealt round-robin) and keeps each slice's best (radix threshold, ties to the lower index),
+// decode_merge_kernel selects among the slice winners and emits them ascending through a
+// bitmap; very long ranges fall back to score_row_kernel + select_kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -419,50 +419,69 @@ __device__ __forceinline__ long decode_candidates(const int64_t* kv_lens, int b,
 
 // q~ of a single query token for KV group g (decode): the sum over the group's heads of
 // RMSNorm(q[b, h]) * w, with the arithmetic of qtilde_kernel for one token (16 lanes per head
-// row, heads summed in order), into qs[DD]. NT threads; hsum holds 16 head rows.
-template <typename T, int DD>
+// row, heads summed in order), into qs[DD]. NT threads; hsum holds 16 head rows. `issued` runs
+// once the first rows' loads are issued (the caller's own loads queue behind them, so waiting
+// for the q rows does not wait for those).
+template <typename T, int DD, class F>
 __device__ __forceinline__ void decode_qtilde(const T* __restrict__ q, const float* __restrict__ qw, int b, int g,
-                                              int Hq, int Hkv, float eps, float (*hsum)[DD], float* qs) {
+                                              int Hq, int Hkv, float eps, float (*hsum)[DD], float* qs, F&& issued) {
   constexpr int EPL = 16 / (int)sizeof(T), LPR = DD / EPL, RPP = NT / LPR;
   const int j = threadIdx.x, hr = j / LPR, seg = j % LPR;
   const int G = Hq / Hkv;
+  // rows past the group read the group's last head (in bounds) and count as zero; the loads
+  // are unconditional so that the caller's loads issued after the first ones can stay in flight
+  auto ld = [&](int h0) {
+    const int hh = min(h0 + hr, G - 1);
+    return *reinterpret_cast<const uint4*>(q + ((long)b * Hq + g * G + hh) * DD + seg * EPL);
+  };
   float tot = 0.f;  // thread j < DD: running sum over the group's heads of dim j
-  for (int h0 = 0; h0 < G; h0 += RPP) {
-    const int hh = h0 + hr;
-    if (hh < G) {
-      const T* src = q + ((long)b * Hq + g * G + hh) * DD + seg * EPL;
-      float x[EPL];
-      if constexpr (sizeof(T) == 2) {
-        unpack8(*reinterpret_cast<const uint4*>(src), x);
-      } else {
-        const float4 u = *reinterpret_cast<const float4*>(src);
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-      }
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
-      ss = group_sum<LPR>(ss);
-      const float inv = 1.0f / sqrtf(ss / DD + eps);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) hsum[hr][seg * EPL + e] = x[e] * inv * 1.0f * (qw ? qw[seg * EPL + e] : 1.0f);
+  auto heads = [&](uint4 raw, int h0) {
+    const bool valid = h0 + hr < G;
+    float x[EPL];
+    if constexpr (sizeof(T) == 2) {
+      unpack8(raw, x);
     } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) hsum[hr][seg * EPL + e] = 0.f;
+      x[0] = __uint_as_float(raw.x); x[1] = __uint_as_float(raw.y);
+      x[2] = __uint_as_float(raw.z); x[3] = __uint_as_float(raw.w);
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+    ss = group_sum<LPR>(ss);
+    const float inv = valid ? 1.0f / sqrtf(ss / DD + eps) : 0.f;
+    float wv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) wv[e] = 1.0f;
+    if (qw) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) wv[e] = qw[seg * EPL + e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) hsum[hr][seg * EPL + e] = x[e] * inv * 1.0f * wv[e];
     __syncthreads();
     if (j < DD)
       for (int r = 0; r < RPP && h0 + r < G; ++r) tot += hsum[r][j];
     __syncthreads();
-  }
+  };
+  const uint4 first = ld(0);
+  issued();
+  __builtin_amdgcn_sched_barrier(0);  // keep the caller's loads ahead of the wait for `first`
+  heads(first, 0);
+  for (int h0 = RPP; h0 < G; h0 += RPP) heads(ld(h0), h0);
   if (j < DD) qs[j] = tot;
   __syncthreads();
 }
 
-// Level 1: grid (B*Hkv, nsl), NT threads. Slice s holds candidates j = j0 .. j0+n-1 with
-// j0 = 1 + s*DSL, n = min(DSL, nc - j0 + 1): scores q~ . k_pool[j] (8 lanes per pooled row),
-// then the slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered). With
-// kv_lens, nc is each sequence's own count (at most the nc given). q~ of the single query token
-// is computed here (decode_qtilde) from q [B, Hq, DD].
+// Level 1: grid (B*Hkv, nsl), NT threads. The candidates 1 .. nc are cut into chunks of RPI = 32
+// consecutive blocks, dealt round-robin to the slices: slice s holds chunks s, s + nsl, s + 2nsl,
+// ... (at most DSL / 32 of them), so local position x of the slice is candidate
+// j = 1 + ((x / 32) * nsl + s) * 32 + x % 32. Local positions rise with j and the valid ones
+// form a prefix 0 .. n-1 (only the last chunk of the range can be partial, and it is the last
+// chunk of its slice). At each step the nsl slices of a row read adjacent chunks, which spreads
+// the stream over the memory channels. Scores q~ . k_pool[j] (8 lanes per pooled row), then the
+// slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered). With kv_lens, nc
+// is each sequence's own count (at most the nc given). q~ of the single query token is computed
+// here (decode_qtilde) from q [B, Hq, DD], while the first rows' loads are in flight.
 template <typename QT, int DD>
 __global__ void __launch_bounds__(NT)
 decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int Hq, float eps,
@@ -476,36 +495,44 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   __shared__ int s_need;
   __shared__ float hsum[NT / (DD / (16 / (int)sizeof(QT)))][DD];
   __shared__ float qs[DD];
+  static_assert(RPI == 32, "chunks of 32 candidates: one step of the workgroup");
+  constexpr int IT = DSL / RPI, BT = 4;
   const int bg = blockIdx.x, sl = blockIdx.y, nsl = gridDim.y;
   const int tid = threadIdx.x, sub = tid / LPB, part = tid % LPB;
-  decode_qtilde<QT, DD>(q, qw, bg / Hkv, bg % Hkv, Hq, Hkv, eps, hsum, qs);
   if (kv_lens) {
     long i;
     const long ncb = decode_candidates(kv_lens, bg / Hkv, kv_max, n_local, &i);
     nc = ncb < nc ? ncb : nc;
   }
-  const long j0 = 1 + (long)sl * DSL;
-  const int n = (int)max(0L, min((long)DSL, nc - j0 + 1));
+  // local position x -> candidate index, and the count of valid positions
+  auto cand_of = [&](int x) -> long { return 1 + ((long)(x / RPI) * nsl + sl) * RPI + x % RPI; };
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < IT; ++c) n += (int)max(0L, min((long)RPI, nc - ((long)c * nsl + sl) * RPI));
+  // lane `part` of a row reads its floats 4*part + 32e .. +3 (e < FPL/4): the 8 lanes of a row
+  // read 128 contiguous bytes per load
+  const float* kb = kpool + (long)bg * nblk_cap * DD + 4 * part;
+  // the rows stream in batches of BT chunks, the next batch's loads issued before the current
+  // batch is reduced (positions past the slice repeat its last row, or its first chunk's row
+  // when it has none: always rows of the pool, whose keys are never read)
+  float4 buf[2][BT][FPL / 4];
+  auto load = [&](int bt, int slot) {
+#pragma unroll
+    for (int u = 0; u < BT; ++u) {
+      const int x = (bt * BT + u) * RPI + sub;
+      const float* row = kb + cand_of(x < n ? x : (n > 0 ? n - 1 : 0)) * DD;
+#pragma unroll
+      for (int e = 0; e < FPL / 4; ++e) buf[slot][u][e] = *reinterpret_cast<const float4*>(row + 4 * LPB * e);
+    }
+  };
+  decode_qtilde<QT, DD>(q, qw, bg / Hkv, bg % Hkv, Hq, Hkv, eps, hsum, qs, [&] { load(0, 0); });
   float qv[FPL];
 #pragma unroll
-  for (int e = 0; e < FPL; ++e) qv[e] = qs[part * FPL + e];
-  const float* kb = kpool + ((long)bg * nblk_cap + j0) * DD + part * FPL;
+  for (int e = 0; e < FPL; ++e) qv[e] = qs[4 * LPB * (e / 4) + 4 * part + e % 4];
   if (n > 0) {
-    // the rows stream in batches of BT iterations, the next batch's loads issued before the
-    // current batch is reduced (rows past the slice repeat its last row; their keys are never
-    // read)
-    constexpr int IT = DSL / RPI, BT = 4;
-    float4 buf[2][BT][FPL / 4];
-    auto load = [&](int bt, int slot) {
-#pragma unroll
-      for (int u = 0; u < BT; ++u) {
-        const int x = (bt * BT + u) * RPI + sub;
-        const float* row = kb + (long)(x < n ? x : n - 1) * DD;
-#pragma unroll
-        for (int e = 0; e < FPL / 4; ++e) buf[slot][u][e] = *reinterpret_cast<const float4*>(row + 4 * e);
-      }
-    };
-    load(0, 0);
+    // the lane's partial dot products of its IT rows; reduced over the 8 lanes of each row after
+    // the stream (a transposing butterfly: 8 + 4 + 2 exchanges leave each lane two full sums)
+    float pd[IT];
 #pragma unroll
     for (int bt = 0; bt < IT / BT; ++bt) {
       if (bt + 1 < IT / BT) load(bt + 1, (bt + 1) & 1);
@@ -517,15 +544,29 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
           const float4 w = buf[bt & 1][u][e];
           sdot += w.x * qv[4 * e] + w.y * qv[4 * e + 1] + w.z * qv[4 * e + 2] + w.w * qv[4 * e + 3];
         }
-        sdot = group_sum<LPB>(sdot);
-        if (part == 0) keys[(bt * BT + u) * RPI + sub] = score_key(sdot);
+        pd[bt * BT + u] = sdot;
       }
     }
+    static_assert(IT == 16 && LPB == 8, "butterfly shape");
+    const bool hb = part & 4, hc = part & 2, hd = part & 1;
+    float a8[8], a4[4], a2[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      a8[k] = (hb ? pd[8 + k] : pd[k]) + __shfl_xor(hb ? pd[k] : pd[8 + k], 4, 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      a4[k] = (hc ? a8[4 + k] : a8[k]) + __shfl_xor(hc ? a8[k] : a8[4 + k], 2, 64);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      a2[k] = (hd ? a4[2 + k] : a4[k]) + __shfl_xor(hd ? a4[k] : a4[2 + k], 1, 64);
+    const int it0 = (hb ? 8 : 0) + (hc ? 4 : 0) + (hd ? 2 : 0);  // this lane's rows it0, it0 + 1
+#pragma unroll
+    for (int k = 0; k < 2; ++k) keys[(it0 + k) * RPI + sub] = score_key(a2[k]);
   }
   __syncthreads();
   uint64_t* dst = cand + ((long)bg * nsl + sl) * R;
   if (n <= R) {
-    for (int t = tid; t < R; t += NT) dst[t] = t < n ? composite(keys[t], j0 + t) : 0ull;
+    for (int t = tid; t < R; t += NT) dst[t] = t < n ? composite(keys[t], cand_of(t)) : 0ull;
     return;
   }
   uint32_t T;
@@ -551,7 +592,7 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
     if (x >= n) continue;
     const uint32_t key = keys[x];
     const bool pick = key > T || (key == T && (eqb++) < need);
-    if (pick && pos < R) dst[pos++] = composite(key, j0 + x);
+    if (pick && pos < R) dst[pos++] = composite(key, cand_of(x));
   }
 }
 
