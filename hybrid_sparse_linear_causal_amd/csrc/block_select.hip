@@ -183,12 +183,7 @@ __device__ __forceinline__ void hist_add(int* hist, uint32_t dgt, bool match, in
 template <int NTS>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -264,12 +259,7 @@ select_kernel(const float* __restrict__ sc, int32_t* __restrict__ sel, float* __
         int v[4], sum = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) { v[e] = hist[255 - 4 * lane - e]; sum += v[e]; }
-        int incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(sum);
         const uint64_t hit = __ballot(incl >= remaining);
         const int L = __ffsll((unsigned long long)hit) - 1;  // first lane reaching the count
         if (hit == 0 && lane == 0) { s_prefix = prefix; s_need = remaining; }  // unreachable
@@ -380,12 +370,7 @@ __device__ __forceinline__ void radix_threshold(const uint32_t* keys, int n, int
       int v[4], sum = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) { v[e] = hist[255 - 4 * lane - e]; sum += v[e]; }
-      int incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
+      const int incl = wave_incl_scan(sum);
       const uint64_t hit = __ballot(incl >= remaining);
       const int L = __ffsll((unsigned long long)hit) - 1;
       if (lane == L) {

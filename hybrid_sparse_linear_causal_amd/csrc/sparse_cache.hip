@@ -72,38 +72,44 @@ kv_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
   const long blk = q0 / 64 + blockIdx.y;
   const int j = threadIdx.x, r = j / LPR, seg = j % LPR;
   const long row_base = ((long)b * Hkv + g) * cap;  // cache row of (b, g, position 0)
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  constexpr int NIT = 64 / RPP;  // rows of the block per thread
   const bool completes = (blk + 1) * 64 <= kv_len;  // the block is full once these tokens are in
-  for (int t = r; t < 64; t += RPP) {
-    const long p = blk * 64 + t;
-    float x[EPL];
-    if (!completes && !(p >= q0 && p < kv_len)) continue;  // no pool to compute: new rows only
+  // a block that completes is pooled: its cached rows are all loaded first (the rows that the
+  // new tokens replace are read too, in bounds, and overwritten below), so that the loads
+  // overlap instead of waiting one by one
+  float xs[NIT][EPL];
+  if (completes) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      load_row_part<T>(k_cache + (row_base + blk * 64 + r + it * RPP) * DD + seg * EPL, xs[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const long p = blk * 64 + r + it * RPP;
     if (p >= q0 && p < kv_len) {
       const long src = (((long)b * n_q + (p - q0)) * Hkv + g) * DD + seg * EPL;
+      float x[EPL], vv[EPL];
       load_row_part<T>(k_new + src, x);
+      load_row_part<T>(v_new + src, vv);
       float ss = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
       ss = group_sum<LPR>(ss);
       const float inv = 1.0f / sqrtf(ss / DD + eps);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] *= inv * (kw ? kw[seg * EPL + e] : 1.0f);
-      store_row_part<T>(k_cache + (row_base + p) * DD + seg * EPL, x);
-      float vv[EPL];
-      load_row_part<T>(v_new + src, vv);
+      for (int e = 0; e < EPL; ++e) xs[it][e] = x[e] * inv * (kw ? kw[seg * EPL + e] : 1.0f);
+      store_row_part<T>(k_cache + (row_base + p) * DD + seg * EPL, xs[it]);
       store_row_part<T>(v_cache + (row_base + p) * DD + seg * EPL, vv);
-    } else if (p < q0) {
-      load_row_part<T>(k_cache + (row_base + p) * DD + seg * EPL, x);  // already cached
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] = 0.f;
     }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += x[e];
   }
   if (!completes) return;  // block still incomplete: nothing to pool (uniform)
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += xs[it][e];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) psum[r][seg * EPL + e] = acc[e];
   __syncthreads();
