@@ -434,7 +434,8 @@ def _time_events(torch, fn, reps):
 def extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv, d, peaks):
     """Per-configuration layer times (32K linear, 128K sparse), the decode step as one graph
     replay, and the decode step with the 256 MB last-level cache flushed before each step (whole
-    and call by call, with each call's HBM rate)."""
+    and call by call, with each call's HBM rate; flushed by reading, and for comparison by
+    writing)."""
     from hybrid_sparse_linear_causal_amd.inputs import WORKLOADS, device_normal
 
     res = {}
@@ -517,21 +518,41 @@ def extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv,
     with torch.cuda.graph(graph):
         decode_step()
     us_graph = _time_events(torch, graph.replay, 20) * 1e3
-    # last-level-cache-cold decode: 512 MB written between steps, outside the timed region
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold = []
-    for r in range(10):
-        flush.fill_(r)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        decode_step()
-        e1.record()
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1) * 1e3)
+    # last-level-cache-cold decode: between steps (outside the timed region) a 1 GiB buffer, four
+    # times the 256 MB last-level cache, is read through, which leaves the caches holding only
+    # clean lines of other data. A second series writes 512 MB instead: then every cache line
+    # the step brings in first evicts a dirty line of the flush, whose write-back the step pays.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush.fill_(0)
+    fl32 = flush.view(torch.float32)
+    sink = torch.empty(1, dtype=torch.float32, device="cuda")
+    dirty = flush[: 512 << 20]
+
+    def flush_read(r):
+        torch.sum(fl32, dim=0, keepdim=True, out=sink)
+
+    def flush_write(r):
+        dirty.fill_(r)
+
+    def cold_steps(flush_fn):
+        ts = []
+        for r in range(10):
+            flush_fn(r)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            decode_step()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    cold = cold_steps(flush_read)
+    cold_dirty = cold_steps(flush_write)
     # the same, call by call: events between the calls of each flushed step
     per = {name: [] for name, _, _ in decode_calls}
     for r in range(10):
-        flush.fill_(r)
+        flush_read(r)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(decode_calls) + 1)]
         evs[0].record()
         for x, (_, fn, _) in enumerate(decode_calls):
@@ -548,10 +569,11 @@ def extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv,
         gbs = byts / (v * 1e-6) / 1e9
         calls[name] = {"us": v, "bytes": byts, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                        "frac_of_measured_read": gbs / peaks["hbm_read_gbs"]}
-    cold.sort()
     res["decode_graph_step_us_warm"] = us_graph
     res["decode_graph_us_per_token_warm"] = us_graph / B
-    res["decode_cold_step_us_median"] = cold[len(cold) // 2]
+    res["decode_cold_step_us_median"] = cold
+    res["decode_cold_flush"] = "1 GiB read between steps (clean caches)"
+    res["decode_cold_step_us_dirty_flush"] = cold_dirty
     res["decode_cold_calls"] = calls
     return res
 
