@@ -487,7 +487,7 @@ BwdPlan bwd_plan(const sala_linear_desc& d) {
   BwdPlan p;
   const long nrows = (long)d.batch * d.seq_len * d.n_heads;
   const size_t act = (size_t)nrows * D;
-  p.seg = linear_segment_len(d);
+  p.seg = linear_segment_len(d, 2048, 4096);
   p.nseg = (int)((d.seq_len + p.seg - 1) / p.seg);
   p.ew_blocks = (int)std::min<long>((nrows + EW_ROWS - 1) / EW_ROWS, EW_BLOCKS_MAX);
   const size_t bh = (size_t)d.batch * d.n_heads;
