@@ -42,8 +42,8 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
 }
 
 // ---- linear layer
-// linear prefill segment length: B*H*N / target_wgs rounded up to a power of two in
-// [64, max_seg] (the forward's defaults; the backward keeps 2,048 workgroups and 4,096 tokens)
+// linear segment length (forward and backward): B*H*N / target_wgs rounded up to a power of two
+// in [64, max_seg]
 int linear_segment_len(const sala_linear_desc& d, int target_wgs = 512, int max_seg = 8192);
 size_t linear_prefill_workspace(const sala_linear_desc& d);
 hipError_t launch_linear_prefill(const sala_linear_desc& d, const void* q, const void* k,

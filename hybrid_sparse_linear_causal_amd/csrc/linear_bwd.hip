@@ -139,6 +139,9 @@ struct PlainSegLds {
 struct PlainLds {
   bf16_t t[2][3][CH * D];  // [buffer][A, B, C]
   bf16_t st[D * D];        // S^T [dv][dk] bf16: the state entering the chunk
+  float nw[D];             // NORM passes: the norm weight (1 where none)
+  double nf[D / 2];        // NORM passes: the RoPE frequencies (revolutions per position)
+  float wacc[4][D];        // NORM passes: per output wave, the norm-weight gradient sums
 };
 
 // per (b, h, segment s < last): sum over the segment of B^T C into workspace slot s + 1
@@ -198,13 +201,17 @@ lplain_scan_kernel(const float* __restrict__ S0, float* __restrict__ ws, int nsl
 // outputs of query tiles 0-3, waves 4-7 carry S (dk rows 32(w-4) .. +31) and publish S^T.
 // TRANS: the entering states (S0 and the segment slots) are stored transposed, i.e. this pass's
 // state is the transpose of another pass's (the slots are then that pass's). GATE: instead of
-// Y, the output is dg = dout * Y * sigmoid'(g) (Y is the layer's pre-gate output).
-template <bool REV, bool TRANS, bool GATE>
+// Y, the output is dg = dout * Y * sigmoid'(g) (Y is the layer's pre-gate output). NORM: Y is
+// dx~ of x = q or k (raw rows xr, norm weight xw); the output is dx, through the transposes of
+// RoPE and RMSNorm, and the workgroup's sums of n * (RoPE^T dx~) over its rows (the norm-weight
+// gradient) go to wpart[blockIdx.x][wsel][D].
+template <bool REV, bool TRANS, bool GATE, bool NORM>
 __global__ void __launch_bounds__(PL_NT)
 lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ C,
                     const float* __restrict__ S0, const float* __restrict__ ws, float* __restrict__ S_final,
                     float* __restrict__ Y, const bf16_t* __restrict__ gate, const bf16_t* __restrict__ dout, int N,
-                    int H, int seg_len, int nseg) {
+                    int H, int seg_len, int nseg, const bf16_t* __restrict__ xr, const float* __restrict__ xw,
+                    float eps, long pos0, RopeFreqs fr, float* __restrict__ wpart, int wsel) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   PlainLds& L = *reinterpret_cast<PlainLds*>(lds_raw);
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
@@ -217,6 +224,12 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
   const long head_off = ((long)b * N * H + h) * D, tok_stride = (long)H * D;
   const bf16_t* src[3] = {A, Bm, C};
   dma_tiles(src, head_off, tok_stride, u_begin, N, REV, L.t[0]);
+  if (NORM) {
+    // published by the barrier before the chunk loop
+    for (int x = j; x < D; x += PL_NT) L.nw[x] = xw ? xw[x] : 1.0f;
+    for (int x = j; x < D / 2; x += PL_NT) L.nf[x] = fr.f[x];
+    for (int x = j; x < 4 * D; x += PL_NT) (&L.wacc[0][0])[x] = 0.f;
+  }
 
   f32x4 acc[16];
 #pragma unroll
@@ -260,6 +273,13 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
         gv[dt] = *reinterpret_cast<const uint2*>(gate + off + 16 * dt);
         dov[dt] = *reinterpret_cast<const uint2*>(dout + off + 16 * dt);
       }
+    }
+    uint2 xv8[8];  // NORM: this lane's raw x (dims 16dt + 4lq .. +3), used after the final wait
+    if (NORM && out_wave) {
+      const long u = u0 + 16 * w4 + l16;
+      const long off = head_off + tok_of(REV, u < u_end ? u : u_end - 1, N) * tok_stride + 4 * lq;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) xv8[dt] = *reinterpret_cast<const uint2*>(xr + off + 16 * dt);
     }
     if (u0 + CH < u_end) dma_tiles(src, head_off, tok_stride, u0 + CH, N, REV, L.t[buf ^ 1]);
     const int nvalid = u_end - u0 < CH ? (int)(u_end - u0) : CH;
@@ -344,7 +364,78 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
     }
     // the next chunk's tiles must have landed before the barrier; outputs go out after the wait
     wait_vmcnt<0>();
-    if (out_wave) {
+    if (NORM && out_wave) {
+      // dx from dx~ = acc: u = RoPE^T dx~, dn = u w, dx = (dn - n mean(dn n)) / rms(x), n = x / rms(x);
+      // the 4 lanes lq of a row hold its 128 dims; dims i and i + 64 (dt and dt + 4) are RoPE pairs
+      const long u = u0 + 16 * w4 + l16;
+      const bool ok = u < u_end;
+      const long tk = tok_of(REV, ok ? u : u_end - 1, N);
+      // x element e of piece dt, unpacked where it is used (fewer live registers)
+      auto xe = [&](int dt, int e) -> float {
+        const uint32_t w = (e < 2) ? xv8[dt].x : xv8[dt].y;
+        return bf2f((e & 1) ? (w >> 16) : (w & 0xffffu));
+      };
+      float ss = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(xe(dt, e), xe(dt, e), ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+      // acc becomes dn = (RoPE^T dx~) w in place; wv = n (RoPE^T dx~), the row's norm-weight
+      // gradient terms (dims 16dt + 4lq + e at 4dt + e; 0 for rows past the end)
+      float dot = 0.f, wv[32];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * dt + 4 * lq + e;
+          float sn, cs;
+          sincos_rev(rope_rev((double)(pos0 + tk), L.nf[i]), &sn, &cs);
+          const float ya = acc[dt][e], yb = acc[dt + 4][e];
+          const float ua = cs * ya + sn * yb, ub = -sn * ya + cs * yb;  // RoPE^T
+          const float na = xe(dt, e) * inv, nb = xe(dt + 4, e) * inv;
+          wv[4 * dt + e] = ok ? na * ua : 0.f;
+          wv[4 * (dt + 4) + e] = ok ? nb * ub : 0.f;
+          acc[dt][e] = ua * L.nw[i];
+          acc[dt + 4][e] = ub * L.nw[i + 64];
+          dot = fmaf(acc[dt][e], na, fmaf(acc[dt + 4][e], nb, dot));
+        }
+      dot += __shfl_xor(dot, 16, 64);
+      dot += __shfl_xor(dot, 32, 64);
+      dot *= 1.0f / D;
+      // sum wv over the wave's 16 rows (lanes l16 of each lq) by a transposing butterfly: after
+      // the exchanges at distances 8, 4, 2, 1 lane l16 holds the sums of entries 2 l16 and
+      // 2 l16 + 1, which it alone adds into the wave's LDS row (same lane every chunk)
+      {
+        float a16[16], a8[8], a4[4], a2[2];
+        const bool h3 = l16 & 8, h2 = l16 & 4, h1 = l16 & 2, h0 = l16 & 1;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) a16[k] = (h3 ? wv[16 + k] : wv[k]) + __shfl_xor(h3 ? wv[k] : wv[16 + k], 8, 64);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a8[k] = (h2 ? a16[8 + k] : a16[k]) + __shfl_xor(h2 ? a16[k] : a16[8 + k], 4, 64);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a4[k] = (h1 ? a8[4 + k] : a8[k]) + __shfl_xor(h1 ? a8[k] : a8[4 + k], 2, 64);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) a2[k] = (h0 ? a4[2 + k] : a4[k]) + __shfl_xor(h0 ? a4[k] : a4[2 + k], 1, 64);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int kk = 2 * l16 + k;  // entry 4dt + e: dim 16dt + 4lq + e
+          L.wacc[w4][16 * (kk >> 2) + 4 * lq + (kk & 3)] += a2[k];
+        }
+      }
+      if (ok) {
+        float* yp = Y + head_off + tk * tok_stride + 4 * lq;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (acc[dt][e] - xe(dt, e) * inv * dot) * inv;
+          *reinterpret_cast<f32x4*>(yp + 16 * dt) = o;
+        }
+      }
+    } else if (out_wave) {
       const long u = u0 + 16 * w4 + l16;  // lane: query u, dims 16dt + 4lq .. +3
       if (u < u_end) {
         float* yp = Y + head_off + tok_of(REV, u, N) * tok_stride + 4 * lq;
@@ -369,6 +460,12 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
     __syncthreads();
     buf ^= 1;
   }
+  if (NORM) {
+    // the workgroup's weight-gradient sums: the four output waves' rows in order (the loop
+    // ended with a barrier, after the last LDS accumulation)
+    for (int dd = j; dd < D; dd += PL_NT)
+      wpart[((long)blockIdx.x * 2 + wsel) * D + dd] = ((L.wacc[0][dd] + L.wacc[1][dd]) + L.wacc[2][dd]) + L.wacc[3][dd];
+  }
   if (!out_wave && seg == nseg - 1 && S_final) {
     float* dst = S_final + (long)bh * D * D;
 #pragma unroll
@@ -378,84 +475,6 @@ lplain_chunk_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bm,
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[(32 * w4 + 16 * it + 4 * lq + e) * D + 16 * jt + l16] = acc[8 * it + jt][e];
   }
-}
-
-// the transposes of the norm and RoPE for q or k, in place on dx (which holds dx~ on entry):
-// u = RoPE^T dx~, dn = u w, dx = (dn - n mean(dn n)) / rms; adds n u to the weight sums
-__device__ __forceinline__ void norm_rope_bwd(float* __restrict__ dx, const bf16_t* __restrict__ x,
-                                              const float* __restrict__ w, int s8, float eps, const float (&c)[8],
-                                              const float (&s)[8], bool ok, float (&wsum)[16]) {
-  float xv[16], n[16], y[16], inv;
-  load16(x, s8, xv);
-  norm_rope_fwd(xv, w, s8, eps, c, s, n, y, inv);
-  float dy[16];
-  const f32x4 a0 = *reinterpret_cast<const f32x4*>(dx + 8 * s8), a1 = *reinterpret_cast<const f32x4*>(dx + 8 * s8 + 4);
-  const f32x4 b0 = *reinterpret_cast<const f32x4*>(dx + 64 + 8 * s8), b1 = *reinterpret_cast<const f32x4*>(dx + 64 + 8 * s8 + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    dy[e] = a0[e]; dy[4 + e] = a1[e]; dy[8 + e] = b0[e]; dy[12 + e] = b1[e];
-  }
-  float dn[16];
-  float dot = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float ua = c[e] * dy[e] + s[e] * dy[8 + e];   // RoPE^T
-    const float ub = -s[e] * dy[e] + c[e] * dy[8 + e];
-    const float wa = w ? w[8 * s8 + e] : 1.0f, wb = w ? w[64 + 8 * s8 + e] : 1.0f;
-    if (ok) {
-      wsum[e] = fmaf(n[e], ua, wsum[e]);
-      wsum[8 + e] = fmaf(n[8 + e], ub, wsum[8 + e]);
-    }
-    dn[e] = ua * wa;
-    dn[8 + e] = ub * wb;
-    dot = fmaf(dn[e], n[e], fmaf(dn[8 + e], n[8 + e], dot));
-  }
-  dot = group_sum8_dpp(dot) * (1.0f / D);
-  f32x4 o[4];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) o[e / 4][e % 4] = (dn[e] - n[e] * dot) * inv;
-  if (ok) {
-    *reinterpret_cast<f32x4*>(dx + 8 * s8) = o[0];
-    *reinterpret_cast<f32x4*>(dx + 8 * s8 + 4) = o[1];
-    *reinterpret_cast<f32x4*>(dx + 64 + 8 * s8) = o[2];
-    *reinterpret_cast<f32x4*>(dx + 64 + 8 * s8 + 4) = o[3];
-  }
-}
-
-// dq, dk (in place, from dq~ and dk~); per-block partial sums of the norm-weight gradients into
-// wpart[block][2][D] (q then k)
-__global__ void __launch_bounds__(EW_NT)
-lbwd_post_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ qw,
-                 const float* __restrict__ kw, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ wpart,
-                 long nrows, int N, int H, long pos0, float eps, RopeFreqs fr) {
-  __shared__ float red[EW_ROWS][2][D];
-  const int s8 = threadIdx.x & 7, rl = threadIdx.x >> 3;
-  float wq_sum[16], wk_sum[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) wq_sum[e] = wk_sum[e] = 0.f;
-  for (long r0 = (long)blockIdx.x * EW_ROWS; r0 < nrows; r0 += (long)gridDim.x * EW_ROWS) {
-    const long row = r0 + (long)rl < nrows ? r0 + (long)rl : nrows - 1;
-    const bool ok = r0 + (long)rl < nrows;
-    const long pos = pos0 + (row / H) % N;
-    const long base = row * D;
-    float c[8], s[8];
-    rope_cs(pos, s8, fr, c, s);
-    norm_rope_bwd(dq + base, q + base, qw, s8, eps, c, s, ok, wq_sum);
-    norm_rope_bwd(dk + base, k + base, kw, s8, eps, c, s, ok, wk_sum);
-  }
-  // block partial sums of the weight gradients over its rows
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    red[rl][0][8 * s8 + e] = wq_sum[e];
-    red[rl][0][64 + 8 * s8 + e] = wq_sum[8 + e];
-    red[rl][1][8 * s8 + e] = wk_sum[e];
-    red[rl][1][64 + 8 * s8 + e] = wk_sum[8 + e];
-  }
-  __syncthreads();
-  const int which = threadIdx.x >> 7, dim = threadIdx.x & 127;
-  float a = 0.f;
-  for (int r = 0; r < EW_ROWS; ++r) a += red[r][which][dim];
-  wpart[((long)blockIdx.x * 2 + which) * D + dim] = a;
 }
 
 // dw_q, dw_k = sums of the per-block partials: one block per output (q dims, then k dims), a
@@ -487,7 +506,7 @@ BwdPlan bwd_plan(const sala_linear_desc& d) {
   BwdPlan p;
   const long nrows = (long)d.batch * d.seq_len * d.n_heads;
   const size_t act = (size_t)nrows * D;
-  p.seg = linear_segment_len(d, 2048, 4096);
+  p.seg = linear_segment_len(d);
   p.nseg = (int)((d.seq_len + p.seg - 1) / p.seg);
   p.ew_blocks = (int)std::min<long>((nrows + EW_ROWS - 1) / EW_ROWS, EW_BLOCKS_MAX);
   const size_t bh = (size_t)d.batch * d.n_heads;
@@ -497,19 +516,20 @@ BwdPlan bwd_plan(const sala_linear_desc& d) {
   p.off_kh = take(act * 2);
   p.off_do = take(act * 2);
   p.off_slots = take(p.nseg > 1 ? bh * p.nseg * D * D * 4 : 0);
-  p.off_wpart = take((size_t)p.ew_blocks * 2 * D * 4);
+  p.off_wpart = take(bh * p.nseg * 2 * D * 4);  // one partial per chunk-pass workgroup
   p.total = off;
   return p;
 }
 
 // one plain pass; with SEGSUM false the segment slots of an earlier pass (whose state this
 // pass's is the transpose of) are reused as they are
-template <bool REV, bool TRANS, bool GATE>
+template <bool REV, bool TRANS, bool GATE, bool NORM>
 hipError_t run_plain(const bf16_t* A, const bf16_t* Bm, const bf16_t* C, const float* S0, float* S_final, float* Y,
                      const bf16_t* gate, const bf16_t* dout, float* slots, bool segsum, int B, int N, int H, int seg,
-                     int nseg, hipStream_t st) {
+                     int nseg, const bf16_t* xr, const float* xw, float eps, long pos0, const RopeFreqs& fr,
+                     float* wpart, int wsel, hipStream_t st) {
   static const hipError_t attr_ok = [] {
-    const hipError_t e0 = hipFuncSetAttribute((const void*)lplain_chunk_kernel<REV, TRANS, GATE>,
+    const hipError_t e0 = hipFuncSetAttribute((const void*)lplain_chunk_kernel<REV, TRANS, GATE, NORM>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PlainLds));
     const hipError_t e1 = hipFuncSetAttribute((const void*)lplain_segsum_kernel<REV>,
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(PlainSegLds));
@@ -521,8 +541,8 @@ hipError_t run_plain(const bf16_t* A, const bf16_t* Bm, const bf16_t* C, const f
                        Bm, C, slots, N, H, seg, nseg);
     hipLaunchKernelGGL(lplain_scan_kernel, dim3(B * H, D * D / 256), dim3(256), 0, st, S0, slots, nseg);
   }
-  hipLaunchKernelGGL((lplain_chunk_kernel<REV, TRANS, GATE>), dim3(B * H * nseg), dim3(PL_NT), sizeof(PlainLds), st, A,
-                     Bm, C, S0, slots, S_final, Y, gate, dout, N, H, seg, nseg);
+  hipLaunchKernelGGL((lplain_chunk_kernel<REV, TRANS, GATE, NORM>), dim3(B * H * nseg), dim3(PL_NT), sizeof(PlainLds), st,
+                     A, Bm, C, S0, slots, S_final, Y, gate, dout, N, H, seg, nseg, xr, xw, eps, pos0, fr, wpart, wsel);
   return hipGetLastError();
 }
 
@@ -562,23 +582,26 @@ hipError_t launch_linear_backward(const sala_linear_desc& d, const void* q, cons
   hipLaunchKernelGGL(lbwd_prep_kernel, dim3(p.ew_blocks), dim3(EW_NT), 0, st, qb, kb, gb, db, qw, kw, qh, kh, dO, nrows,
                      N, H, (long)d.pos0, d.norm_eps, fr);
   hipError_t e;
-  // dg (from o), dq~ (state = the o pass's, transposed), dv and dS_in, dk~ (state = the dv
-  // pass's, transposed)
-  if ((e = run_plain<false, false, true>(qh, kh, vb, state_in, nullptr, dg, gb, db, slots, true, B, N, H, p.seg,
-                                         p.nseg, st)) != hipSuccess)
+  // dg (from o), dq (from dq~, whose state is the o pass's, transposed), dv and dS_in, dk (from
+  // dk~, whose state is the dv pass's, transposed); the dq and dk passes apply the transposes of
+  // RoPE and RMSNorm to their rows and leave per-workgroup norm-weight partials
+  const long p0 = (long)d.pos0;
+  const float eps = d.norm_eps;
+  if ((e = run_plain<false, false, true, false>(qh, kh, vb, state_in, nullptr, dg, gb, db, slots, true, B, N, H, p.seg,
+                                                p.nseg, nullptr, nullptr, eps, p0, fr, nullptr, 0, st)) != hipSuccess)
     return e;
-  if ((e = run_plain<false, true, false>(dO, vb, kh, state_in, nullptr, dq, nullptr, nullptr, slots, false, B, N, H,
-                                         p.seg, p.nseg, st)) != hipSuccess)
+  if ((e = run_plain<false, true, false, true>(dO, vb, kh, state_in, nullptr, dq, nullptr, nullptr, slots, false, B, N,
+                                               H, p.seg, p.nseg, qb, qw, eps, p0, fr, wpart, 0, st)) != hipSuccess)
     return e;
-  if ((e = run_plain<true, false, false>(kh, qh, dO, dstate_out, dstate_in, dv, nullptr, nullptr, slots, true, B, N,
-                                         H, p.seg, p.nseg, st)) != hipSuccess)
+  if ((e = run_plain<true, false, false, false>(kh, qh, dO, dstate_out, dstate_in, dv, nullptr, nullptr, slots, true, B,
+                                                N, H, p.seg, p.nseg, nullptr, nullptr, eps, p0, fr, nullptr, 0, st)) !=
+      hipSuccess)
     return e;
-  if ((e = run_plain<true, true, false>(vb, dO, qh, dstate_out, nullptr, dk, nullptr, nullptr, slots, false, B, N, H,
-                                        p.seg, p.nseg, st)) != hipSuccess)
+  if ((e = run_plain<true, true, false, true>(vb, dO, qh, dstate_out, nullptr, dk, nullptr, nullptr, slots, false, B, N,
+                                              H, p.seg, p.nseg, kb, kw, eps, p0, fr, wpart, 1, st)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL(lbwd_post_kernel, dim3(p.ew_blocks), dim3(EW_NT), 0, st, qb, kb, qw, kw, dq, dk, wpart, nrows, N,
-                     H, (long)d.pos0, d.norm_eps, fr);
-  if (dqw || dkw) hipLaunchKernelGGL(lbwd_wsum_kernel, dim3(2 * D), dim3(256), 0, st, wpart, p.ew_blocks, dqw, dkw);
+  if (dqw || dkw)
+    hipLaunchKernelGGL(lbwd_wsum_kernel, dim3(2 * D), dim3(256), 0, st, wpart, B * H * p.nseg, dqw, dkw);
   return hipGetLastError();
 }
 
