@@ -16,8 +16,10 @@
 //      lse2, D, dg, and q~ and dO in bf16, head-major and padded to whole query blocks;
 //   2. dq (query-major, same grid): S, P, dP, dS per selected block, dq^ on MFMA, then the
 //      RMSNorm transpose and per-workgroup sums of the norm-weight gradient;
-//   3. the selection inverted: a bitmap [key block][query block], per key block the count of
-//      query blocks that chose it, cut into slices of at most SB_SL query blocks;
+//   3. the selection inverted: a bitmap [key block][query block]; for every range of SB_RW
+//      query blocks and every key block, the query blocks of the range that chose it, cut into
+//      slices of at most SB_SL, numbered range by range (so the workgroups running at one time
+//      gather q~ and dO of one range of query blocks, which the caches then hold);
 //   4. dK, dV (key-major, one workgroup per slice): for each query block of the slice and
 //      each head of the group, S and dP for the 64 keys, then dV^T += dO^T P, dK^T += q~^T dS
 //      on MFMA; one fp32 partial per slice;
@@ -36,6 +38,8 @@ constexpr int D = 128;
 constexpr int SB_NT = 512;
 constexpr int SB_QT = 2;   // 16-row query tiles per wave in the query-major kernels
 constexpr int SB_SL = 32;  // query blocks per dK/dV slice
+constexpr int SB_RWW = 8;  // bitmap words (32 query blocks each) per query-block range
+constexpr int SB_RW = 32 * SB_RWW;
 
 
 struct ItemGeom {
@@ -478,16 +482,21 @@ sbwd_bitmap_kernel(const int32_t* __restrict__ sel, uint32_t* __restrict__ bm, i
 
 // per (b, g): slice offsets soff[blk] = sum over earlier key blocks of ceil(count / SB_SL)
 __global__ void __launch_bounds__(1024)
-sbwd_slices_kernel(const uint32_t* __restrict__ bm, int* __restrict__ soff, int nkb, int words) {
+sbwd_slices_kernel(const uint32_t* __restrict__ bm, int* __restrict__ soff, int nkb, int words, int nw) {
+  // entry e = w * nkb + kb: the query blocks of range w that chose key block kb; soff[e] = the
+  // first slice of the entry (entries in order), soff[nw * nkb] = the slice count
   __shared__ int part[1024];
   const long bg = blockIdx.x;
+  const int ne = nw * nkb;
   int carry = 0;
-  for (int c0 = 0; c0 < nkb; c0 += 1024) {
-    const int blk = c0 + threadIdx.x;
+  for (int c0 = 0; c0 < ne; c0 += 1024) {
+    const int e = c0 + threadIdx.x;
     int ns = 0;
-    if (blk < nkb) {
+    if (e < ne) {
+      const int w = e / nkb, blk = e % nkb;
+      const int w1 = min(words, (w + 1) * SB_RWW);
       int cnt = 0;
-      for (int w = 0; w < words; ++w) cnt += __popc(bm[(bg * nkb + blk) * words + w]);
+      for (int x = w * SB_RWW; x < w1; ++x) cnt += __popc(bm[(bg * nkb + blk) * words + x]);
       ns = (cnt + SB_SL - 1) / SB_SL;
     }
     part[threadIdx.x] = ns;
@@ -498,11 +507,11 @@ sbwd_slices_kernel(const uint32_t* __restrict__ bm, int* __restrict__ soff, int 
       part[threadIdx.x] += v;
       __syncthreads();
     }
-    if (blk < nkb) soff[bg * (nkb + 1) + blk] = carry + part[threadIdx.x] - ns;
+    if (e < ne) soff[bg * (ne + 1) + e] = carry + part[threadIdx.x] - ns;
     carry += part[1023];
     __syncthreads();
   }
-  if (threadIdx.x == 0) soff[bg * (nkb + 1) + nkb] = carry;
+  if (threadIdx.x == 0) soff[bg * (ne + 1) + ne] = carry;
 }
 
 // ---- 4. dK, dV per slice: workgroups of four waves, two per CU, so that one workgroup's
@@ -539,25 +548,26 @@ __global__ void __launch_bounds__(SB_KV_NT, 2)
 sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, const bf16_t* __restrict__ qtb,
                 const bf16_t* __restrict__ dob, const float* __restrict__ stb, const uint32_t* __restrict__ bm,
                 const int* __restrict__ soff, float* __restrict__ part, int Hq, int Hkv, long qb0, int nqb,
-                long kv_len, long cap, int nkb, int words, int maxsl) {
+                long kv_len, long cap, int nkb, int words, int nw, int maxsl) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   DkvLds& L = *reinterpret_cast<DkvLds*>(lds_raw);
   const int bg = blockIdx.x / maxsl, s = blockIdx.x % maxsl;
-  const int* so = soff + (long)bg * (nkb + 1);
-  if (s >= so[nkb]) return;
-  // key block of slice s: the last blk with so[blk] <= s
-  int lo = 0, hi = nkb - 1;
+  const int ne = nw * nkb;
+  const int* so = soff + (long)bg * (ne + 1);
+  if (s >= so[ne]) return;
+  // entry of slice s: the last e with so[e] <= s (range w = e / nkb, key block e % nkb)
+  int lo = 0, hi = ne - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (so[mid] <= s) lo = mid; else hi = mid - 1;
   }
-  const int kb = lo, rank0 = (s - so[kb]) * SB_SL;
+  const int kb = lo % nkb, wr = lo / nkb, rank0 = (s - so[lo]) * SB_SL;
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
   const int G = Hq / Hkv, b = bg / Hkv, gk = bg % Hkv;
   if (j == 0) {
     const uint32_t* rowp = bm + ((long)bg * nkb + kb) * words;
     int seen = 0, n = 0;
-    for (int w = 0; w < words && n < SB_SL; ++w) {
+    for (int w = wr * SB_RWW; w < min(words, (wr + 1) * SB_RWW) && n < SB_SL; ++w) {
       uint32_t bits = rowp[w];
       while (bits && n < SB_SL) {
         const int bit = __builtin_ctz(bits);
@@ -674,18 +684,20 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
 // for capacity rows past kv_len's last block)
 __global__ void __launch_bounds__(256)
 sbwd_reduce_kernel(const float* __restrict__ part, const int* __restrict__ soff, float* __restrict__ dk,
-                   float* __restrict__ dv, long cap, int nkb, int maxsl) {
+                   float* __restrict__ dv, long cap, int nkb, int nw, int maxsl) {
   const long nbc = cap / 64;
   const int bg = (int)(blockIdx.x / nbc), kb = (int)(blockIdx.x % nbc);
-  const int s0 = kb < nkb ? soff[(long)bg * (nkb + 1) + kb] : 0;
-  const int s1 = kb < nkb ? soff[(long)bg * (nkb + 1) + kb + 1] : 0;
+  const int ne = nw * nkb;
+  const int* so = soff + (long)bg * (ne + 1);
   for (int x = threadIdx.x; x < 64 * D / 4; x += 256) {
     f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = ak;
-    for (int sl = s0; sl < s1; ++sl) {
-      const float* src = part + ((long)bg * maxsl + sl) * 2 * 64 * D;
-      ak += *reinterpret_cast<const f32x4*>(src + 4 * x);
-      av += *reinterpret_cast<const f32x4*>(src + 64 * D + 4 * x);
-    }
+    // the key block's slices, range by range
+    for (int w = 0; kb < nkb && w < nw; ++w)
+      for (int sl = so[w * nkb + kb]; sl < so[w * nkb + kb + 1]; ++sl) {
+        const float* src = part + ((long)bg * maxsl + sl) * 2 * 64 * D;
+        ak += *reinterpret_cast<const f32x4*>(src + 4 * x);
+        av += *reinterpret_cast<const f32x4*>(src + 64 * D + 4 * x);
+      }
     const long o = ((long)bg * cap + (long)kb * 64) * D + 4 * x;
     *reinterpret_cast<f32x4*>(dk + o) = ak;
     *reinterpret_cast<f32x4*>(dv + o) = av;
@@ -771,7 +783,7 @@ sbwd_knorm_kernel(const bf16_t* __restrict__ k, const float* __restrict__ kw, co
 constexpr int KN_BLOCKS_MAX = 2048;
 
 struct SbwdPlan {
-  long nqb, nkb, words, maxsl, nwg;
+  long nqb, nkb, words, nw, maxsl, nwg;
   size_t off_qt, off_do, off_st, off_bm, off_soff, off_part, off_wpart, total;
 };
 
@@ -783,7 +795,9 @@ SbwdPlan sbwd_plan(const sala_sparse_desc& d) {
   p.nqb = gm.nqb;
   p.nkb = (d.kv_len + 63) / 64;
   p.words = (p.nqb + 31) / 32;
-  p.maxsl = (p.nqb * d.topk + SB_SL - 1) / SB_SL + p.nkb;
+  p.nw = (p.words + SB_RWW - 1) / SB_RWW;
+  // slices: sum over (range, key block) of ceil(count / SB_SL) <= pairs / SB_SL + entries
+  p.maxsl = (p.nqb * d.topk + SB_SL - 1) / SB_SL + std::min(p.nw * p.nkb, p.nqb * (long)d.topk);
   p.nwg = BG * p.nqb * ((G + 3) / 4);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += (bytes + 255) & ~size_t(255); return o; };
@@ -792,7 +806,7 @@ SbwdPlan sbwd_plan(const sala_sparse_desc& d) {
   p.off_do = take(prow * D * 2);
   p.off_st = take(prow * 4 * 4);
   p.off_bm = take((size_t)BG * p.nkb * p.words * 4);
-  p.off_soff = take((size_t)BG * (p.nkb + 1) * 4);
+  p.off_soff = take((size_t)BG * (p.nw * p.nkb + 1) * 4);
   p.off_part = take((size_t)BG * p.maxsl * 2 * 64 * D * 4);
   p.off_wpart = take((size_t)p.nwg * D * 4);
   p.total = off;
@@ -845,16 +859,17 @@ hipError_t launch_sparse_attn_backward(const sala_sparse_desc& d, const void* q,
                      nbm);
   hipLaunchKernelGGL(sbwd_bitmap_kernel, dim3((unsigned)(BG * p.nqb)), dim3(256), 0, st, sel, bm, (int)p.nqb, d.topk,
                      (int)p.nkb, (int)p.words);
-  hipLaunchKernelGGL(sbwd_slices_kernel, dim3((unsigned)BG), dim3(1024), 0, st, bm, soff, (int)p.nkb, (int)p.words);
+  hipLaunchKernelGGL(sbwd_slices_kernel, dim3((unsigned)BG), dim3(1024), 0, st, bm, soff, (int)p.nkb, (int)p.words,
+                     (int)p.nw);
   static const hipError_t attr_ok = hipFuncSetAttribute((const void*)sbwd_dkv_kernel,
                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                                         (int)sizeof(DkvLds));
   if (attr_ok != hipSuccess) return attr_ok;
   hipLaunchKernelGGL(sbwd_dkv_kernel, dim3((unsigned)(BG * p.maxsl)), dim3(SB_KV_NT), sizeof(DkvLds), st, kb, vb, qtb,
                      dob, stb, bm, soff, part, d.n_heads, d.n_kv_heads, (long)gm.qb0, (int)p.nqb, (long)d.kv_len,
-                     (long)d.kv_capacity, (int)p.nkb, (int)p.words, (int)p.maxsl);
+                     (long)d.kv_capacity, (int)p.nkb, (int)p.words, (int)p.nw, (int)p.maxsl);
   hipLaunchKernelGGL(sbwd_reduce_kernel, dim3((unsigned)(BG * (d.kv_capacity / 64))), dim3(256), 0, st, part, soff,
-                     dk_cache, dv_cache, (long)d.kv_capacity, (int)p.nkb, (int)p.maxsl);
+                     dk_cache, dv_cache, (long)d.kv_capacity, (int)p.nkb, (int)p.nw, (int)p.maxsl);
   return hipGetLastError();
 }
 
