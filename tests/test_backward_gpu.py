@@ -114,6 +114,7 @@ def _sparse_setup(S, seed, B, kv_len, n_q, Hq, Hkv, topk, with_w):
     (1, 2150, 2150, 2, 1, 6, False),    # 34 query blocks: block 0 chosen by 34 > one slice; ragged tail; 2 heads
     (1, 640, 256, 4, 2, 4, True),       # queries continue a cached prefix of 384 tokens
     (2, 384, 384, 32, 2, 3, False),     # a 16-head GQA group (4 head quads), batch 2
+    (1, 17000, 17000, 2, 1, 4, True),   # 266 query blocks: two ranges of the dK/dV slices (256 query blocks each)
 ])
 def test_sparse_attn_backward(S, B, kv_len, n_q, Hq, Hkv, topk, with_w):
     print(f"sparse_attn_backward B={B} kv_len={kv_len} n_q={n_q} Hq={Hq} Hkv={Hkv} topk={topk} w={with_w}",
