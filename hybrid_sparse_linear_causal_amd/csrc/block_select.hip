@@ -341,10 +341,13 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, long j) {
 
 // Exact threshold of the R largest of n keys in LDS (1 <= R < n): T = the R-th largest key and
 // need = how many keys equal to T belong to the R largest. Four 8-bit radix passes; histogram
-// updates by hist_add.
-template <int NTH>
+// updates by hist_add. EARLY: when the digit bucket that holds the R-th largest is needed whole
+// (the usual case after two passes over distinct scores), stop there with T = the largest key
+// below that bucket and need = 0, so that the R largest are exactly the keys above T (a caller
+// that keeps keys == T by count still takes none, as need is 0).
+template <int NTH, bool EARLY>
 __device__ __forceinline__ void radix_threshold(const uint32_t* keys, int n, int R, int* hist,
-                                                uint32_t* s_prefix, int* s_need, uint32_t& T,
+                                                uint32_t* s_prefix, int* s_need, int* s_cnt, uint32_t& T,
                                                 int& need) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0, pmask = 0;
@@ -382,12 +385,18 @@ __device__ __forceinline__ void radix_threshold(const uint32_t* keys, int n, int
         }
         *s_prefix = prefix | ((uint32_t)(255 - 4 * lane - e) << shift);
         *s_need = remaining - cum;
+        *s_cnt = v[e];
       }
     }
     __syncthreads();
     prefix = *s_prefix;
     remaining = *s_need;
     pmask |= 255u << shift;
+    if (EARLY && pass < 3 && *s_cnt == remaining && prefix != 0u) {  // uniform: read after the barrier
+      T = prefix - 1u;  // the low bits of prefix are 0: every key of the bucket is above T
+      need = 0;
+      return;
+    }
   }
   T = prefix;
   need = remaining;
@@ -478,6 +487,7 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   __shared__ int scan_tmp[NT / 64 + 1];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
+  __shared__ int s_cnt;
   __shared__ float hsum[NT / (DD / (16 / (int)sizeof(QT)))][DD];
   __shared__ float qs[DD];
   static_assert(RPI == 32, "chunks of 32 candidates: one step of the workgroup");
@@ -556,7 +566,7 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   }
   uint32_t T;
   int need;
-  radix_threshold<NT>(keys, n, R, hist, &s_prefix, &s_need, T, need);
+  radix_threshold<NT, true>(keys, n, R, hist, &s_prefix, &s_need, &s_cnt, T, need);
   // keys above T, then the first `need` keys equal to T in index order: thread t owns
   // positions PER*t .. PER*t + PER-1
   constexpr int PER = DSL / NT;
@@ -605,6 +615,7 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   __shared__ int scan_tmp[NTM / 64 + 1];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
+  __shared__ int s_cnt;
   __shared__ int32_t s_row[256];  // the emitted row (topk <= 256), for placing the scores
   const int bg = blockIdx.x, tid = threadIdx.x;
   const int n = nsl * R;
@@ -628,7 +639,7 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   const bool all = n_valid <= R;
   bool all_ties = true;
   if (!all) {
-    radix_threshold<NTM>(keys, n, R, hist, &s_prefix, &s_need, T, need);
+    radix_threshold<NTM, true>(keys, n, R, hist, &s_prefix, &s_need, &s_cnt, T, need);
     int ties = 0;
     for (int t = tid; t < n; t += NTM) ties += keys[t] == T;
     int ties_total;
@@ -642,7 +653,7 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
       for (int t = tid; t < n; t += NTM) idx2key(keys, idx, t, T);
       __syncthreads();
       int need2;
-      radix_threshold<NTM>(keys, n, R, hist, &s_prefix, &s_need, T2, need2);
+      radix_threshold<NTM, false>(keys, n, R, hist, &s_prefix, &s_need, &s_cnt, T2, need2);
     }
   }
   for (int t = tid; t < n; t += NTM) {
