@@ -93,34 +93,51 @@ qtilde_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __re
 }
 
 // Prefill scores: grid (B*Hkv, ceil(nqb/64), ceil(RL/64)); 64x64 tile, 4x4 per thread.
-// sc[bg][r][j] = q~[bg][r] . k_pool[bg][j] for j <= qb0 + r - n_local (others untouched).
+// sc[bg][r][j] = q~[bg][r] . k_pool[bg][j] for j <= qb0 + r - n_local (others untouched). The
+// tiles sit row-major in LDS with rows DD + 4 floats apart, so the 16 lanes that read one dims
+// quad of 16 different rows hit 16 different bank quads; each thread reads its 4 rows and 4
+// candidates a dims quad at a time (8 float4 reads per 64 FMAs) and sums over the dims in order.
 template <int DD>
 __global__ void __launch_bounds__(NT)
 score_tile_kernel(const float* __restrict__ qt, const float* __restrict__ kpool,
                   float* __restrict__ sc, int nqb, long qb0, int RL, long nblk_cap, int n_local) {
-  __shared__ float sq[64][DD + 1];
-  __shared__ float sk[64][DD + 1];
+  constexpr int ST = DD + 4;
+  __shared__ __align__(16) float sq[64 * ST];
+  __shared__ __align__(16) float sk[64 * ST];
   const int bg = blockIdx.x;
   const int r0 = blockIdx.y * 64, j0 = blockIdx.z * 64;
   const long i_max = qb0 + min(nqb, r0 + 64) - 1;
   if (j0 > i_max - n_local) return;  // whole tile above the candidate range
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < 64 * DD; idx += NT) {
-    const int rr = idx / DD, dd = idx % DD;
-    sq[rr][dd] = (r0 + rr < nqb) ? qt[((long)bg * nqb + r0 + rr) * DD + dd] : 0.f;
-    sk[rr][dd] = (j0 + rr < RL) ? kpool[((long)bg * nblk_cap + j0 + rr) * DD + dd] : 0.f;
+  for (int idx = tid; idx < 64 * DD / 4; idx += NT) {
+    const int rr = idx / (DD / 4), d4 = idx % (DD / 4);
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&sq[rr * ST + 4 * d4]) =
+        (r0 + rr < nqb) ? *reinterpret_cast<const float4*>(&qt[((long)bg * nqb + r0 + rr) * DD + 4 * d4]) : zero;
+    *reinterpret_cast<float4*>(&sk[rr * ST + 4 * d4]) =
+        (j0 + rr < RL) ? *reinterpret_cast<const float4*>(&kpool[((long)bg * nblk_cap + j0 + rr) * DD + 4 * d4]) : zero;
   }
   __syncthreads();
   const int ty = tid / 16, tx = tid % 16;
   float acc[4][4] = {};
-  for (int dd = 0; dd < DD; ++dd) {
-    float a[4], c[4];
+  for (int dd = 0; dd < DD; dd += 4) {
+    float4 a[4], c[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) { a[u] = sq[ty * 4 + u][dd]; c[u] = sk[tx * 4 + u][dd]; }
+    for (int u = 0; u < 4; ++u) {
+      a[u] = *reinterpret_cast<const float4*>(&sq[(ty * 4 + u) * ST + dd]);
+      c[u] = *reinterpret_cast<const float4*>(&sk[(tx * 4 + u) * ST + dd]);
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) acc[u][w] += a[u] * c[w];
+      for (int w = 0; w < 4; ++w) {
+        float t = acc[u][w];
+        t += a[u].x * c[w].x;
+        t += a[u].y * c[w].y;
+        t += a[u].z * c[w].z;
+        t += a[u].w * c[w].w;
+        acc[u][w] = t;
+      }
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
