@@ -133,8 +133,8 @@ def stored_traffic(kernel, launches_per_profile=1):
 def measured_peaks(torch):
     """Ceilings measured on this GPU by the committed peak kernels (libsala_peaks.so, built from
     hybrid_sparse_linear_causal_amd/csrc/peaks/peaks.hip): the best over a few grid sizes of a
-    4 GiB streaming read (16-byte loads) and of a loop of independent bf16 MFMA 16x16x32
-    products, timed with HIP events."""
+    4 GiB streaming read (16-byte loads), a 2 GiB copy (bytes read plus written) and of loops of
+    independent bf16 MFMA products, timed with HIP events."""
     import ctypes
 
     path = os.path.join(ROOT, "hybrid_sparse_linear_causal_amd", "libsala_peaks.so")
@@ -142,6 +142,7 @@ def measured_peaks(torch):
         raise RuntimeError(f"{path} not built (run __graft_entry__.build())")
     lib = ctypes.CDLL(path)
     lib.sala_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.sala_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     lib.sala_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.sala_peak_mfma32.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -157,7 +158,14 @@ def measured_peaks(torch):
     for wgs in (1024, 2048, 4096, 8192):
         ms = _time_events(torch, lambda: call(lib.sala_peak_read(buf.data_ptr(), nbytes, sink.data_ptr(), wgs, st)), 5)
         read[wgs] = nbytes / (ms * 1e-3) / 1e9
-    del buf
+    # copy: 2 GiB read and 2 GiB written (bytes moved = both)
+    half = nbytes // 2
+    dst = buf[half // 4:]
+    copy = {}
+    for wgs in (1024, 2048, 4096, 8192):
+        ms = _time_events(torch, lambda: call(lib.sala_peak_copy(buf.data_ptr(), dst.data_ptr(), half, wgs, st)), 5)
+        copy[wgs] = 2 * half / (ms * 1e-3) / 1e9
+    del buf, dst
     iters = 2048
     mfma, mfma32 = {}, {}
     for wgs in (256, 512, 1024, 2048, 4096):
@@ -165,10 +173,12 @@ def measured_peaks(torch):
         mfma[wgs] = wgs * 4 * 8 * iters * 16384 / (ms * 1e-3) / 1e12
         ms = _time_events(torch, lambda: call(lib.sala_peak_mfma32(sink.data_ptr(), iters, wgs, st)), 3)
         mfma32[wgs] = wgs * 4 * 4 * iters * 32768 / (ms * 1e-3) / 1e12
-    return {"hbm_read_gbs": max(read.values()), "bf16_mfma_tflops": max(mfma.values()),
-            "bf16_mfma_32x32x16_tflops": max(mfma32.values()),
-            "hbm_read_gbs_by_grid": read, "bf16_mfma_tflops_by_grid": mfma, "bf16_mfma_32x32x16_tflops_by_grid": mfma32,
-            "method": "libsala_peaks.so: 4 GiB streaming read (uint4 loads, 4 in flight per lane); "
+    return {"hbm_read_gbs": max(read.values()), "hbm_copy_gbs": max(copy.values()),
+            "bf16_mfma_tflops": max(mfma.values()), "bf16_mfma_32x32x16_tflops": max(mfma32.values()),
+            "hbm_read_gbs_by_grid": read, "hbm_copy_gbs_by_grid": copy, "bf16_mfma_tflops_by_grid": mfma,
+            "bf16_mfma_32x32x16_tflops_by_grid": mfma32,
+            "method": "libsala_peaks.so: 4 GiB streaming read (uint4 loads, 4 in flight per lane); 2 GiB copy "
+                      "(read + written bytes); "
                       "8 independent v_mfma_f32_16x16x32_bf16 (4 of v_mfma_f32_32x32x16_bf16) chains per "
                       "wave; best over grid sizes"}
 
@@ -568,7 +578,8 @@ def extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv,
         v = sorted(per[name])[len(per[name]) // 2]
         gbs = byts / (v * 1e-6) / 1e9
         calls[name] = {"us": v, "bytes": byts, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-                       "frac_of_measured_read": gbs / peaks["hbm_read_gbs"]}
+                       "frac_of_measured_read": gbs / peaks["hbm_read_gbs"],
+                       "frac_of_measured_copy": gbs / peaks["hbm_copy_gbs"]}
     res["decode_graph_step_us_warm"] = us_graph
     res["decode_graph_us_per_token_warm"] = us_graph / B
     res["decode_cold_step_us_median"] = cold

@@ -1,5 +1,6 @@
 // Ceilings of the GPU the library runs on, measured by bench.py next to the published peaks:
-// a streaming read of device memory (16-byte loads, several in flight per lane) and loops of
+// a streaming read of device memory (16-byte loads, several in flight per lane), a streaming
+// copy (the same loads, each word stored to a second buffer) and loops of
 // independent bf16 MFMA products (v_mfma_f32_16x16x32_bf16, the instruction of the attention
 // and linear kernels, and v_mfma_f32_32x32x16_bf16). Built as libsala_peaks.so, separate from libsala; not part of its ABI.
 #include <hip/hip_runtime.h>
@@ -25,6 +26,20 @@ __global__ void __launch_bounds__(256) read_kernel(const uint4* __restrict__ src
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   sink[(long)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// grid-stride copy of n16 16-byte words, 4 loads in flight per lane before their stores
+__global__ void __launch_bounds__(256) copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, long n16) {
+  const long stride = (long)gridDim.x * 256;
+  long i = (long)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    dst[i] = a;
+    dst[i + stride] = b;
+    dst[i + 2 * stride] = c;
+    dst[i + 3 * stride] = d;
+  }
+  for (; i < n16; i += stride) dst[i] = src[i];
 }
 
 // 8 independent accumulators per wave, `iters` rounds of 8 products each
@@ -87,6 +102,16 @@ int sala_peak_read(const void* src, size_t bytes, void* sink, int wgs, void* str
   if (!src || !sink || wgs < 1 || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15)) return 2;
   hipLaunchKernelGGL(read_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (long)(bytes / 16),
                      (uint32_t*)sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+// Copy `bytes` (a multiple of 16; both buffers 16-byte aligned, not overlapping) from src to dst.
+int sala_peak_copy(const void* src, void* dst, size_t bytes, int wgs, void* stream) {
+  if (!src || !dst || wgs < 1 || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) ||
+      (reinterpret_cast<uintptr_t>(dst) & 15))
+    return 2;
+  hipLaunchKernelGGL(copy_kernel, dim3(wgs), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, (uint4*)dst,
+                     (long)(bytes / 16));
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
