@@ -274,7 +274,15 @@ def main():
                           kv_capacity=L, topk=Dw.topk, n_local=Dw.n_local)
     ws_dsel = torch.empty(S.workspace_bytes(S.OP_BLOCK_SELECT, ddesc), dtype=torch.uint8, device=dev)
     ws_datt = torch.empty(S.workspace_bytes(S.OP_SPARSE_ATTN, ddesc), dtype=torch.uint8, device=dev)
+    ws_dstep = torch.empty(S.workspace_bytes(S.OP_SPARSE_DECODE_STEP, ddesc), dtype=torch.uint8, device=dev)
+    dkvl = torch.full((B,), L, dtype=torch.int64, device=dev)  # every sequence at L tokens after the append
     dsout = torch.empty_like(dq)
+
+    def sparse_decode_step():
+        # append, select and attend in one call (three launches)
+        S.sparse_decode_step(dq[:, 0], dkn[:, 0], dvn[:, 0], dg[:, 0], dkc, dvc, dkp, dkvl, L, topk=Dw.topk,
+                             n_local=Dw.n_local, eps=W.norm_eps, sel=dsel[:, :, 0], out=dsout[:, 0],
+                             workspace=ws_dstep)
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -306,13 +314,7 @@ def main():
                                  out=Dr["out"])
         if record:
             e["dlin"] = ev(); e["dlin"].record()
-        S.kv_append(dkn, dvn, dkc, dvc, dkp, L, eps=W.norm_eps, n_heads=H)
-        S.block_select(dq, dkp, L, L, n_kv_heads=Hkv, topk=Dw.topk, n_local=Dw.n_local, eps=W.norm_eps,
-                       sel=dsel, workspace=ws_dsel)
-        if record:
-            e["dsel"] = ev(); e["dsel"].record()
-        S.sparse_attn(dq, dkc, dvc, dg, dsel, L, n_local=Dw.n_local, eps=W.norm_eps, out=dsout,
-                      workspace=ws_datt)
+        sparse_decode_step()
         if record:
             e["end"] = ev(); e["end"].record()
         return e
@@ -333,6 +335,9 @@ def main():
                                             out=Dr["out"])
 
     decode_calls = [(f"linear_layer_{li}", dlin_call(Dr), bytes_lin) for li, Dr in enumerate(dl)] + [
+        ("sparse_decode_step", sparse_decode_step, bytes_app + bytes_sel + bytes_att)]
+    # the sparse layer's decode as three separate calls (same results), for comparison
+    sparse_parts = [
         ("kv_append", lambda: S.kv_append(dkn, dvn, dkc, dvc, dkp, L, eps=W.norm_eps, n_heads=H), bytes_app),
         ("block_select", lambda: S.block_select(dq, dkp, L, L, n_kv_heads=Hkv, topk=Dw.topk, n_local=Dw.n_local,
                                                 eps=W.norm_eps, sel=dsel, workspace=ws_dsel), bytes_sel),
@@ -360,8 +365,8 @@ def main():
     t_lin = [avg("t0", "lin0"), avg("lin0", "lin1"), avg("lin1", "lin2")]
     t_app, t_sel, t_att = avg("lin2", "append"), avg("append", "select"), avg("select", "attn")
     t_sparse = t_app + t_sel + t_att
-    t_dlin, t_dsel, t_datt = avg("attn", "dlin"), avg("dlin", "dsel"), avg("dsel", "end")
-    t_dec = t_dlin + t_dsel + t_datt
+    t_dlin, t_dsp = avg("attn", "dlin"), avg("dlin", "end")
+    t_dec = t_dlin + t_dsp
     t_prefill = sum(t_lin) + t_sparse
 
     flops_attn = sparse_prefill_flops(N, H, d, W.topk)
@@ -401,8 +406,7 @@ def main():
             "sparse_layer_tokens_per_s": N / (t_sparse * 1e-3),
             "sparse_parts_ms": {"kv_append": t_app, "block_select": t_sel, "attention": t_att},
             "decode_step_in_stack_us": t_dec * 1e3,
-            "decode_parts_in_stack_us": {"linear_x3": t_dlin * 1e3, "append_select": t_dsel * 1e3,
-                                         "attention": t_datt * 1e3},
+            "decode_parts_in_stack_us": {"linear_x3": t_dlin * 1e3, "sparse_decode_step": t_dsp * 1e3},
             "decode_in_stack_hbm_frac": dec_gbs / HBM_PEAK_GBS,
             "decode_bytes_per_step": dec_bytes,
         },
@@ -417,7 +421,7 @@ def main():
     result["linear_layer_tokens_per_s"] = result["breakdown"]["linear_layer_tokens_per_s"]
     result["sparse_layer_tokens_per_s"] = result["breakdown"]["sparse_layer_tokens_per_s"]
     if not args.no_extras:
-        ex = extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv, d, peaks)
+        ex = extra_measurements(S, torch, W, decode_step, decode_calls, sparse_parts, dl, B, L, H, Hkv, d, peaks)
         result["breakdown"].update(ex)
         # the decode headline: the step with the last-level cache flushed before it
         result["decode_step_us"] = ex["decode_cold_step_us_median"]
@@ -441,7 +445,7 @@ def _time_events(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv, d, peaks):
+def extra_measurements(S, torch, W, decode_step, decode_calls, sparse_parts, dl, B, L, H, Hkv, d, peaks):
     """Per-configuration layer times (32K linear, 128K sparse), the decode step as one graph
     replay, and the decode step with the 256 MB last-level cache flushed before each step (whole
     and call by call, with each call's HBM rate; flushed by reading, and for comparison by
@@ -559,33 +563,39 @@ def extra_measurements(S, torch, W, decode_step, decode_calls, dl, B, L, H, Hkv,
 
     cold = cold_steps(flush_read)
     cold_dirty = cold_steps(flush_write)
-    # the same, call by call: events between the calls of each flushed step
-    per = {name: [] for name, _, _ in decode_calls}
-    for r in range(10):
-        flush_read(r)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(decode_calls) + 1)]
-        evs[0].record()
-        for x, (_, fn, _) in enumerate(decode_calls):
-            fn()
-            evs[x + 1].record()
-        torch.cuda.synchronize()
-        for x, (name, _, _) in enumerate(decode_calls):
-            per[name].append(evs[x].elapsed_time(evs[x + 1]) * 1e3)
+    def cold_calls(call_list):
+        # call by call: events between the calls of each flushed step
+        per = {name: [] for name, _, _ in call_list}
+        for r in range(10):
+            flush_read(r)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(call_list) + 1)]
+            evs[0].record()
+            for x, (_, fn, _) in enumerate(call_list):
+                fn()
+                evs[x + 1].record()
+            torch.cuda.synchronize()
+            for x, (name, _, _) in enumerate(call_list):
+                per[name].append(evs[x].elapsed_time(evs[x + 1]) * 1e3)
+        calls = {}
+        for name, _, byts in call_list:
+            v = sorted(per[name])[len(per[name]) // 2]
+            gbs = byts / (v * 1e-6) / 1e9
+            calls[name] = {"us": v, "bytes": byts, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                           "frac_of_measured_read": gbs / peaks["hbm_read_gbs"],
+                           "frac_of_measured_copy": gbs / peaks["hbm_copy_gbs"]}
+        return calls
+
+    calls = cold_calls(decode_calls)
+    parts = cold_calls(sparse_parts)
     for Dr, s0 in zip(dl, saved):
         Dr["state"].copy_(s0)
-    calls = {}
-    for name, _, byts in decode_calls:
-        v = sorted(per[name])[len(per[name]) // 2]
-        gbs = byts / (v * 1e-6) / 1e9
-        calls[name] = {"us": v, "bytes": byts, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-                       "frac_of_measured_read": gbs / peaks["hbm_read_gbs"],
-                       "frac_of_measured_copy": gbs / peaks["hbm_copy_gbs"]}
     res["decode_graph_step_us_warm"] = us_graph
     res["decode_graph_us_per_token_warm"] = us_graph / B
     res["decode_cold_step_us_median"] = cold
     res["decode_cold_flush"] = "1 GiB read between steps (clean caches)"
     res["decode_cold_step_us_dirty_flush"] = cold_dirty
     res["decode_cold_calls"] = calls
+    res["decode_cold_sparse_as_three_calls"] = parts
     return res
 
 

@@ -131,9 +131,12 @@ sala_status check_sparse_decode_at(const sala_sparse_desc* d) {
   return SALA_OK;
 }
 
+// the decode step's workspace: the selection's, then the attention's partials
+size_t step_select_bytes(const sala_sparse_desc& d) {
+  return (sala::block_select_decode_at_workspace(d) + 255) & ~(size_t)255;
+}
 size_t sparse_decode_step_workspace(const sala_sparse_desc& d) {
-  const size_t a = (sala::block_select_decode_at_workspace(d) + 255) & ~(size_t)255;
-  return a + sala::sparse_decode_at_workspace(d);
+  return step_select_bytes(d) + sala::sparse_decode_at_workspace(d);
 }
 
 bool all_aligned(std::initializer_list<const void*> ps) {
@@ -289,13 +292,14 @@ sala_status sala_sparse_decode_step(const sala_sparse_desc* desc, const int64_t*
   if (!workspace || workspace_bytes < need) return SALA_ERR_WORKSPACE;
   const sala_sparse_desc& d = *desc;
   const hipStream_t st = (hipStream_t)stream;
-  hipError_t e = sala::launch_kv_append(d, k_new, v_new, k_norm_w, k_cache, v_cache, k_pool, st, kv_lens);
-  if (e == hipSuccess) e = sala::launch_block_select_decode_at(d, kv_lens, q, q_norm_w, k_pool, sel, workspace, st);
-  if (e == hipSuccess) {
-    const size_t a = (sala::block_select_decode_at_workspace(d) + 255) & ~(size_t)255;
+  // the append rides in the selection's first kernel: it writes only the query's own block
+  // (cache rows and pooled key), which is never a candidate
+  char* ws = static_cast<char*>(workspace);
+  const sala::DecodeAppendPtrs app{k_new, v_new, k_norm_w, k_cache, v_cache, k_pool};
+  hipError_t e = sala::launch_block_select_decode_at(d, kv_lens, q, q_norm_w, k_pool, sel, ws, st, &app);
+  if (e == hipSuccess)
     e = sala::launch_sparse_decode_at(d, kv_lens, q, q_norm_w, k_cache, v_cache, gate, sel, out,
-                                      static_cast<char*>(workspace) + a, st);
-  }
+                                      ws + step_select_bytes(d), st);
   return hip_status(e);
 }
 

@@ -17,6 +17,7 @@
 // decode_merge_kernel selects among the slice winners and emits them ascending through a
 // bitmap; very long ranges fall back to score_row_kernel + select_kernel.
 #include "common.hpp"
+#include "kv_append.hpp"
 #include "launch.hpp"
 
 namespace sala {
@@ -493,11 +494,25 @@ __device__ __forceinline__ void decode_qtilde(const T* __restrict__ q, const flo
 // slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered). With kv_lens, nc
 // is each sequence's own count (at most the nc given). q~ of the single query token is computed
 // here (decode_qtilde) from q [B, Hq, DD], while the first rows' loads are in flight.
-template <typename QT, int DD>
+// APPEND (the decode step): the grid has one more row of workgroups, y = 0, that append each
+// sequence's new token to its cache (append_block) instead; the slices are y - 1. The append
+// writes the cache rows and the pooled key of the query's own block only, and no slice reads
+// those: the candidates end n_local blocks before it.
+template <typename QT>
+struct DecodeAppend {
+  const QT* k_new;
+  const QT* v_new;
+  const float* kw;
+  QT* k_cache;
+  QT* v_cache;
+  float* k_pool;
+  long cap;
+};
+template <typename QT, int DD, bool APPEND>
 __global__ void __launch_bounds__(NT)
 decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int Hq, float eps,
                     const float* __restrict__ kpool, uint64_t* __restrict__ cand, long nblk_cap, long nc, int R,
-                    const int64_t* __restrict__ kv_lens, int Hkv, long kv_max, int n_local) {
+                    const int64_t* __restrict__ kv_lens, int Hkv, long kv_max, int n_local, DecodeAppend<QT> ap) {
   constexpr int LPB = 8, FPL = DD / LPB, RPI = NT / LPB;  // rows per iteration
   __shared__ uint32_t keys[DSL];
   __shared__ int hist[256];
@@ -509,7 +524,13 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   __shared__ float qs[DD];
   static_assert(RPI == 32, "chunks of 32 candidates: one step of the workgroup");
   constexpr int IT = DSL / RPI, BT = 4;
-  const int bg = blockIdx.x, sl = blockIdx.y, nsl = gridDim.y;
+  if (APPEND && blockIdx.y == 0) {
+    static_assert(sizeof(hsum) == sizeof(float) * RowGeom<QT, DD>::RPP * DD, "append partial sums fit hsum");
+    append_block<QT, DD>(ap.k_new, ap.v_new, ap.kw, ap.k_cache, ap.v_cache, ap.k_pool, 1, Hkv, kv_max, ap.cap, eps,
+                         kv_lens, blockIdx.x, 0, hsum);
+    return;
+  }
+  const int bg = blockIdx.x, sl = blockIdx.y - (APPEND ? 1 : 0), nsl = gridDim.y - (APPEND ? 1 : 0);
   const int tid = threadIdx.x, sub = tid / LPB, part = tid % LPB;
   if (kv_lens) {
     long i;
@@ -769,8 +790,9 @@ static void launch_decode_slice(const sala_sparse_desc& d, const void* q, const 
                                 hipStream_t st) {
   const dim3 grid(d.batch * d.n_kv_heads, nsl);
 #define SALA_SLICE(T, DD)                                                                                   \
-  hipLaunchKernelGGL((decode_slice_kernel<T, DD>), grid, dim3(NT), 0, st, (const T*)q, qw, d.n_heads, d.norm_eps, \
-                     k_pool, cand, nblk_cap, nc, R, kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local)
+  hipLaunchKernelGGL((decode_slice_kernel<T, DD, false>), grid, dim3(NT), 0, st, (const T*)q, qw, d.n_heads,     \
+                     d.norm_eps, k_pool, cand, nblk_cap, nc, R, kv_lens, d.n_kv_heads, (long)d.kv_len, d.n_local, \
+                     DecodeAppend<T>{})
   if (d.dtype == SALA_BF16) {
     if (d.head_dim == 128) SALA_SLICE(bf16_t, 128); else SALA_SLICE(bf16_t, 64);
   } else {
@@ -864,14 +886,23 @@ size_t block_select_decode_at_workspace(const sala_sparse_desc& d) {
 
 hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_t* kv_lens, const void* q,
                                          const float* qw, const float* k_pool, int32_t* sel, void* ws,
-                                         hipStream_t st) {
+                                         hipStream_t st, const DecodeAppendPtrs* app) {
   long nc; int nsl, R;
   if (!decode_at_plan(d, &nc, &nsl, &R)) return hipErrorInvalidValue;
   const int BG = d.batch * d.n_kv_heads;
   const size_t qt_bytes = (size_t)BG * d.head_dim * sizeof(float);
   uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + ((qt_bytes + 255) & ~(size_t)255));
   const long nblk_cap = d.kv_capacity / 64;
-  launch_decode_slice(d, q, qw, k_pool, cand, nblk_cap, nc, R, nsl, kv_lens, st);
+  if (app) {
+    // bf16, d = 128 only (the decode step's shapes): the append rides along as grid row 0
+    const DecodeAppend<bf16_t> ap{(const bf16_t*)app->k_new, (const bf16_t*)app->v_new, app->kw,
+                                  (bf16_t*)app->k_cache, (bf16_t*)app->v_cache, app->k_pool, (long)d.kv_capacity};
+    hipLaunchKernelGGL((decode_slice_kernel<bf16_t, 128, true>), dim3(BG, nsl + 1), dim3(NT), 0, st,
+                       (const bf16_t*)q, qw, d.n_heads, d.norm_eps, k_pool, cand, nblk_cap, nc, R, kv_lens,
+                       d.n_kv_heads, (long)d.kv_len, d.n_local, ap);
+  } else {
+    launch_decode_slice(d, q, qw, k_pool, cand, nblk_cap, nc, R, nsl, kv_lens, st);
+  }
   hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nullptr,
                      nsl, R, (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens, d.n_kv_heads, (long)d.kv_len);
   return hipGetLastError();

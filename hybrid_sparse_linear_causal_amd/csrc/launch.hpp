@@ -86,9 +86,19 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
 size_t sparse_attn_workspace(const sala_sparse_desc& d);
 // decode with each sequence at its own cache length (kv_lens: device [B] int64)
 size_t block_select_decode_at_workspace(const sala_sparse_desc& d);  // SIZE_MAX: context too long
+// the one-token append that the decode step runs inside the selection's first kernel
+struct DecodeAppendPtrs {
+  const void* k_new;
+  const void* v_new;
+  const float* kw;
+  void* k_cache;
+  void* v_cache;
+  float* k_pool;
+};
+// app: also append (bf16, d = 128)
 hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_t* kv_lens, const void* q,
                                          const float* qw, const float* k_pool, int32_t* sel, void* ws,
-                                         hipStream_t st);
+                                         hipStream_t st, const DecodeAppendPtrs* app = nullptr);
 size_t sparse_decode_at_workspace(const sala_sparse_desc& d);
 hipError_t launch_sparse_decode_at(const sala_sparse_desc& d, const int64_t* kv_lens, const void* q, const float* qw,
                                    const void* k_cache, const void* v_cache, const void* g, const int32_t* sel,

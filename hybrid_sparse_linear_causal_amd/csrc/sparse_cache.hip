@@ -7,6 +7,7 @@
 // 注意力实现高效长上下文建模" §1 — sparse attention still keeps the full KV cache. The pooled
 // (mean) key per block is the block representative the selection scores against.
 #include "common.hpp"
+#include "kv_append.hpp"
 #include "launch.hpp"
 
 namespace sala {
@@ -23,101 +24,16 @@ SparseGeom sparse_geom(const sala_sparse_desc& d) {
 
 namespace {
 
-// Elements a lane moves per 16-byte access and lanes per head row.
-template <typename T, int DD> struct RowGeom {
-  static constexpr int EPL = 16 / (int)sizeof(T);
-  static constexpr int LPR = DD / EPL;  // lanes per row (<= 64)
-  static constexpr int RPP = 256 / LPR; // rows per 256-thread pass
-};
-
-template <typename T>
-__device__ __forceinline__ void load_row_part(const T* p, float* f);
-template <>
-__device__ __forceinline__ void load_row_part<bf16_t>(const bf16_t* p, float* f) {
-  unpack8(*reinterpret_cast<const uint4*>(p), f);
-}
-template <>
-__device__ __forceinline__ void load_row_part<float>(const float* p, float* f) {
-  const float4 u = *reinterpret_cast<const float4*>(p);
-  f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
-}
-template <typename T>
-__device__ __forceinline__ void store_row_part(T* p, const float* f);
-template <>
-__device__ __forceinline__ void store_row_part<bf16_t>(bf16_t* p, const float* f) {
-  *reinterpret_cast<uint4*>(p) = pack8(f);
-}
-template <>
-__device__ __forceinline__ void store_row_part<float>(float* p, const float* f) {
-  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
-}
-
-// grid (B*Hkv, blocks touched by the new tokens); 256 threads. kv_lens (one token per sequence
-// only): each sequence's own cache length, clamped to [1, kv_len].
+// grid (B*Hkv, blocks touched by the new tokens); 256 threads
 template <typename T, int DD>
 __global__ void __launch_bounds__(256)
 kv_append_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
                  const float* __restrict__ kw, T* __restrict__ k_cache, T* __restrict__ v_cache,
                  float* __restrict__ k_pool, int n_q, int Hkv, long kv_len, long cap, float eps,
                  const int64_t* __restrict__ kv_lens) {
-  using G = RowGeom<T, DD>;
-  constexpr int EPL = G::EPL, LPR = G::LPR, RPP = G::RPP;
-  __shared__ float psum[RPP][DD];
-  const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
-  if (kv_lens) {
-    const long kb = kv_lens[b];
-    kv_len = kb < 1 ? 1 : (kb > kv_len ? kv_len : kb);
-  }
-  const long q0 = kv_len - n_q;
-  const long blk = q0 / 64 + blockIdx.y;
-  const int j = threadIdx.x, r = j / LPR, seg = j % LPR;
-  const long row_base = ((long)b * Hkv + g) * cap;  // cache row of (b, g, position 0)
-  constexpr int NIT = 64 / RPP;  // rows of the block per thread
-  const bool completes = (blk + 1) * 64 <= kv_len;  // the block is full once these tokens are in
-  // a block that completes is pooled: its cached rows are all loaded first (the rows that the
-  // new tokens replace are read too, in bounds, and overwritten below), so that the loads
-  // overlap instead of waiting one by one
-  float xs[NIT][EPL];
-  if (completes) {
-#pragma unroll
-    for (int it = 0; it < NIT; ++it)
-      load_row_part<T>(k_cache + (row_base + blk * 64 + r + it * RPP) * DD + seg * EPL, xs[it]);
-  }
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const long p = blk * 64 + r + it * RPP;
-    if (p >= q0 && p < kv_len) {
-      const long src = (((long)b * n_q + (p - q0)) * Hkv + g) * DD + seg * EPL;
-      float x[EPL], vv[EPL];
-      load_row_part<T>(k_new + src, x);
-      load_row_part<T>(v_new + src, vv);
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
-      ss = group_sum<LPR>(ss);
-      const float inv = 1.0f / sqrtf(ss / DD + eps);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) xs[it][e] = x[e] * inv * (kw ? kw[seg * EPL + e] : 1.0f);
-      store_row_part<T>(k_cache + (row_base + p) * DD + seg * EPL, xs[it]);
-      store_row_part<T>(v_cache + (row_base + p) * DD + seg * EPL, vv);
-    }
-  }
-  if (!completes) return;  // block still incomplete: nothing to pool (uniform)
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += xs[it][e];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) psum[r][seg * EPL + e] = acc[e];
-  __syncthreads();
-  for (int dd = j; dd < DD; dd += 256) {
-    float s = 0.f;
-    for (int rr = 0; rr < RPP; ++rr) s += psum[rr][dd];
-    k_pool[(((long)b * Hkv + g) * (cap / 64) + blk) * DD + dd] = s * (1.0f / 64.0f);
-  }
+  __shared__ float psum[RowGeom<T, DD>::RPP][DD];
+  append_block<T, DD>(k_new, v_new, kw, k_cache, v_cache, k_pool, n_q, Hkv, kv_len, cap, eps, kv_lens, blockIdx.x,
+                      blockIdx.y, psum);
 }
 
 // grid (B*Hkv, blk_end - blk_begin); mean of the 64 cached keys of each block
