@@ -717,45 +717,67 @@ linear_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* 
   float4 sv[NR];
   float vc[4];
   if (j < 64) {
-    // ---- wave 0: k^ and the group's q^ = RoPE(RMSNorm(.) * w) into LDS
-    if (pos_b) {  // each sequence at its own position (negative values read as 0)
-      const long pb = pos_b[b];
-      pos = pb > 0 ? pb : 0;
-    }
+    // ---- wave 0: k^ and the group's q^ = RoPE(RMSNorm(.) * w) into LDS. Every load of the
+    // wave is issued before the first use, so that their latencies overlap: k, the frequency
+    // and the first QPRE query heads unconditionally (lanes past the rotation pairs and heads
+    // past the group read valid elements that are then ignored), the optional position and
+    // weights last.
+    constexpr int QPRE = 4;
     const bool on = j < HALF;
+    const int jj = j & (HALF - 1);
+    float b0 = to_f32(k[kvec + jj]), b1 = to_f32(k[kvec + jj + HALF]);
+    const double fj = freqs.f[jj];
+    float a0[QPRE], a1[QPRE];
+#pragma unroll
+    for (int u = 0; u < QPRE; ++u) {
+      const long qo = qvec + (long)(u < G ? u : G - 1) * DD + jj;
+      a0[u] = to_f32(q[qo]);
+      a1[u] = to_f32(q[qo + HALF]);
+    }
+    long pb = pos;
+    if (pos_b) pb = pos_b[b];
+    float kw0 = 1.f, kw1 = 1.f, qw0 = 1.f, qw1 = 1.f;
+    if (kw) { kw0 = kw[jj]; kw1 = kw[jj + HALF]; }
+    if (qw) { qw0 = qw[jj]; qw1 = qw[jj + HALF]; }
+    if (!on) b0 = b1 = 0.f;
+    if (pos_b) pos = pb > 0 ? pb : 0;  // each sequence at its own position (negative values read as 0)
     float cs = 1.f, sn = 0.f;
     if (on) {
-      const double rev = (double)pos * freqs.f[j];
+      const double rev = (double)pos * fj;
       const float ang = (float)((rev - rint(rev)) * 6.283185307179586);
       sincosf(ang, &sn, &cs);
     }
-    float b0 = 0, b1 = 0;
-    if (on) { b0 = to_f32(k[kvec + j]); b1 = to_f32(k[kvec + j + HALF]); }
     const float ssk = group_sum<64>(b0 * b0 + b1 * b1);
     if (on) {
       const float ik = 1.0f / sqrtf(ssk / DD + eps);
       float y0 = b0 * ik, y1 = b1 * ik;
-      if (kw) { y0 *= kw[j]; y1 *= kw[j + HALF]; }
+      if (kw) { y0 *= kw0; y1 *= kw1; }
       sk[j] = y0 * cs - y1 * sn; sk[j + HALF] = y0 * sn + y1 * cs;
     }
-    for (int hg = 0; hg < G; ++hg) {
-      float a0 = 0, a1 = 0;
-      if (on) { a0 = to_f32(q[qvec + (long)hg * DD + j]); a1 = to_f32(q[qvec + (long)hg * DD + j + HALF]); }
-      const float ssq = group_sum<64>(a0 * a0 + a1 * a1);
+    auto qhead = [&](float x0, float x1, int hg) {
+      const float ssq = group_sum<64>(x0 * x0 + x1 * x1);
       if (on) {
         const float iq = 1.0f / sqrtf(ssq / DD + eps);
-        float x0 = a0 * iq, x1 = a1 * iq;
-        if (qw) { x0 *= qw[j]; x1 *= qw[j + HALF]; }
+        x0 *= iq; x1 *= iq;
+        if (qw) { x0 *= qw0; x1 *= qw1; }
         sq[hg][j] = x0 * cs - x1 * sn; sq[hg][j + HALF] = x0 * sn + x1 * cs;
       }
+    };
+#pragma unroll
+    for (int u = 0; u < QPRE; ++u)
+      if (u < G) qhead(on ? a0[u] : 0.f, on ? a1[u] : 0.f, u);
+    for (int hg = QPRE; hg < G; ++hg) {
+      float x0 = 0, x1 = 0;
+      if (on) { x0 = to_f32(q[qvec + (long)hg * DD + j]); x1 = to_f32(q[qvec + (long)hg * DD + j + HALF]); }
+      qhead(x0, x1, hg);
     }
   } else {
-    // ---- waves 1-4: the state slice (rows r0 + 16m, columns 64y + 4c4 .. +3), loaded while
-    // wave 0 prepares q^ and k^
-#pragma unroll
-    for (int m = 0; m < NR; ++m) sv[m] = *reinterpret_cast<const float4*>(Sp + (long)(r0 + 16 * m) * DD);
+    // ---- waves 1-4: v, then the state slice (rows r0 + 16m, columns 64y + 4c4 .. +3), loaded
+    // while wave 0 prepares q^ and k^; each row is used as soon as it has arrived
 #pragma unroll
     for (int e = 0; e < 4; ++e) vc[e] = to_f32(v[kvec + col + e]);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) sv[m] = *reinterpret_cast<const float4*>(Sp + (long)(r0 + 16 * m) * DD);
   }
   __syncthreads();  // q^, k^ ready
   if (j >= 64) {
