@@ -254,6 +254,7 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
                           const int64_t* __restrict__ kv_lens) {
   __shared__ __align__(16) bf16_t vts[4][TILE];
   __shared__ float cm[4][16], cl[4][16];
+  __shared__ float csc[4][16], cM[16], cL[16];
   const int bg = blockIdx.x, split = blockIdx.y;
   const int b = bg / Hkv, gk = bg % Hkv, G = Hq / Hkv;
   const int j = threadIdx.x, lane = j & 63, wave = j >> 6, l16 = lane & 15, lq = lane >> 4;
@@ -388,22 +389,34 @@ sparse_decode_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict_
   for (int dt = 0; dt < 8; ++dt)
     *reinterpret_cast<f32x4*>(&ost[(wave * 16 + l16) * DEC_OSTR + 16 * dt + 4 * lq]) = OT[dt];
   __syncthreads();
-  float* dst = part + ((long)bg * DEC_SPLIT + split) * 16 * (D + 2);
-  for (int idx = j; idx < 16 * D; idx += 256) {
-    const int hh = idx / D, dd = idx % D;
+  // per head (threads 0..15): the workgroup's reference M, the waves' scales and the sum
+  if (j < 16) {
     float M = -INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, cm[wv][hh]);
-    float o = 0.f, l = 0.f;
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, cm[wv][j]);
+    float l = 0.f;
 #pragma unroll
     for (int wv = 0; wv < 4; ++wv) {
-      const float sc = (cm[wv][hh] == -INFINITY) ? 0.f : exp2f(cm[wv][hh] - M);
-      o += ost[(wv * 16 + hh) * DEC_OSTR + dd] * sc;
-      l += cl[wv][hh] * sc;
+      const float sc = (cm[wv][j] == -INFINITY) ? 0.f : exp2f(cm[wv][j] - M);
+      csc[wv][j] = sc;
+      l += cl[wv][j] * sc;
     }
-    dst[hh * (D + 2) + 2 + dd] = o;
-    if (dd == 0) { dst[hh * (D + 2)] = M; dst[hh * (D + 2) + 1] = l; }
+    cM[j] = M;
+    cL[j] = l;
   }
+  __syncthreads();
+  // thread j: dim j % D of heads j / D + 2it (independent LDS reads, issued together)
+  float* dst = part + ((long)bg * DEC_SPLIT + split) * 16 * (D + 2);
+  const int dd = j % D;
+#pragma unroll
+  for (int it = 0; it < 16 * D / 256; ++it) {
+    const int hh = j / D + 2 * it;
+    float o = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) o += ost[(wv * 16 + hh) * DEC_OSTR + dd] * csc[wv][hh];
+    dst[hh * (D + 2) + 2 + dd] = o;
+  }
+  if (j < 16) { dst[j * (D + 2)] = cM[j]; dst[j * (D + 2) + 1] = cL[j]; }
 }
 
 // grid (B*Hkv*G): one workgroup of D threads per (b, head); combine the DEC_SPLIT partials
