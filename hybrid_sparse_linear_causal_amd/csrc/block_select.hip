@@ -357,6 +357,66 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, long j) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }
 
+// ---- bitonic networks over the 64 lanes of a wave (64-bit values). Composites key << 32 | ~j
+// are distinct, so sorting them orders candidates by score with ties to the lower index; empty
+// slots (0) sort last.
+
+// the value of lane l ^ m (m a power of two, constant after unrolling): DPP moves within rows of
+// 16 lanes for m <= 8 (quad permutations for 1 and 2, shifts by 4 either way, a rotation by 8);
+// for 16 and 32 the row swaps of gfx950 with x as both operands (the 16-lane swap exchanges the
+// odd rows of the first with the even rows of the second, the 32-lane swap the upper half of the
+// first with the lower half of the second, so one of the two results holds each lane's partner)
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int m) {
+  if (m == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  }
+  if (m == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+  const int v = (int)x;
+  if (m == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  if (m == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  if (m == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, false);  // row_shl:4 (lane + 4)
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4 (lane - 4)
+    return (uint32_t)((threadIdx.x & 4) ? dn : up);
+  }
+  if (m == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  return (uint32_t)__shfl_xor(v, m, 64);
+}
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+  const uint32_t lo = xor_lane((uint32_t)x, m), hi = xor_lane((uint32_t)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+// one compare-exchange of a network over the 64 lanes: pairs (l, l ^ m); keep_max: this lane
+// keeps the larger of the pair
+__device__ __forceinline__ uint64_t cmp_x(uint64_t x, int m, bool keep_max) {
+  const uint64_t y = shfl_xor64(x, m);
+  return ((x < y) == keep_max) ? y : x;
+}
+// sort the wave's 64 values: descending (lane 0 the largest) or ascending
+__device__ __forceinline__ uint64_t wave_sort64(uint64_t x, bool descending) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k *= 2)
+#pragma unroll
+    for (int m = k / 2; m > 0; m /= 2) {
+      const bool desc = ((l & k) == 0) == descending;  // this block's direction (all of it at k = 64)
+      x = cmp_x(x, m, ((l & m) == 0) == desc);
+    }
+  return x;
+}
+// a bitonic sequence over the 64 lanes, sorted descending
+__device__ __forceinline__ uint64_t wave_merge_desc(uint64_t x) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 32; m > 0; m /= 2) x = cmp_x(x, m, (l & m) == 0);
+  return x;
+}
+
+
 // Exact threshold of the R largest of n keys in LDS (1 <= R < n): T = the R-th largest key and
 // need = how many keys equal to T belong to the R largest. Four 8-bit radix passes; histogram
 // updates by hist_add. EARLY: when the digit bucket that holds the R-th largest is needed whole
@@ -491,7 +551,8 @@ __device__ __forceinline__ void decode_qtilde(const T* __restrict__ q, const flo
 // form a prefix 0 .. n-1 (only the last chunk of the range can be partial, and it is the last
 // chunk of its slice). At each step the nsl slices of a row read adjacent chunks, which spreads
 // the stream over the memory channels. Scores q~ . k_pool[j] (8 lanes per pooled row), then the
-// slice's best R as composites into cand[bg][s][0..R) (0-padded, unordered). With kv_lens, nc
+// slice's best R as composites into cand[bg][s][0..R) (0-padded; sorted, largest first, when
+// R <= 64, else unordered). With kv_lens, nc
 // is each sequence's own count (at most the nc given). q~ of the single query token is computed
 // here (decode_qtilde) from q [B, Hq, DD], while the first rows' loads are in flight.
 // APPEND (the decode step): the grid has one more row of workgroups, y = 0, that append each
@@ -522,6 +583,7 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   __shared__ int s_cnt;
   __shared__ float hsum[NT / (DD / (16 / (int)sizeof(QT)))][DD];
   __shared__ float qs[DD];
+  __shared__ uint64_t s_win[64];
   static_assert(RPI == 32, "chunks of 32 candidates: one step of the workgroup");
   constexpr int IT = DSL / RPI, BT = 4;
   if (APPEND && blockIdx.y == 0) {
@@ -598,8 +660,21 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   }
   __syncthreads();
   uint64_t* dst = cand + ((long)bg * nsl + sl) * R;
+  // R <= 64: the winners go to LDS first and leave sorted, largest first (wave 0)
+  const bool sorted = R <= 64;
+  auto emit_sorted = [&] {
+    __syncthreads();
+    if (tid < 64) {
+      const uint64_t v = wave_sort64(tid < R ? s_win[tid] : 0ull, true);
+      if (tid < R) dst[tid] = v;
+    }
+  };
   if (n <= R) {
-    for (int t = tid; t < R; t += NT) dst[t] = t < n ? composite(keys[t], cand_of(t)) : 0ull;
+    for (int t = tid; t < R; t += NT) {
+      const uint64_t v = t < n ? composite(keys[t], cand_of(t)) : 0ull;
+      if (sorted) s_win[t] = v; else dst[t] = v;
+    }
+    if (sorted) emit_sorted();
     return;
   }
   uint32_t T;
@@ -625,8 +700,13 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
     if (x >= n) continue;
     const uint32_t key = keys[x];
     const bool pick = key > T || (key == T && (eqb++) < need);
-    if (pick && pos < R) dst[pos++] = composite(key, cand_of(x));
+    if (pick && pos < R) {
+      const uint64_t v = composite(key, cand_of(x));
+      if (sorted) s_win[pos] = v; else dst[pos] = v;
+      ++pos;
+    }
   }
+  if (sorted) emit_sorted();
 }
 
 // Second-stage keys for surplus ties at threshold T: keys above T become 0xFFFFFFFF (always
@@ -749,6 +829,74 @@ decode_merge_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel
   }
 }
 
+// Level 2, R <= 64 (at most 32 slices, each slice's winners sorted largest first; the ordinary
+// merge's arguments and output): wave w reads slice 2w forwards and slice 2w+1 backwards
+// (ascending), keeps the larger of each lane pair (the 64 largest of both, as a bitonic sequence)
+// and sorts them; the waves' lists are then halved pairwise the same way through LDS until wave
+// 0 holds the 64 largest in descending order. The first R that are not empty are chosen; wave 0
+// sorts them by block index and emits the row.
+template <int NTM>
+__global__ void __launch_bounds__(NTM)
+decode_merge64_kernel(const uint64_t* __restrict__ cand, int32_t* __restrict__ sel, float* __restrict__ sel_sc, int nsl,
+                      int R, long i, int n_local, int topk, long nc, const int64_t* __restrict__ kv_lens, int Hkv,
+                      long kv_max) {
+  constexpr int NW = NTM / 64;
+  static_assert(2 * NW >= DNSL_MAX, "two slices per wave");
+  __shared__ uint64_t lists[2][NW][64];
+  const int bg = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  if (kv_lens) {  // this sequence's query block and candidate count (at most the nc given)
+    const long ncb = decode_candidates(kv_lens, bg / Hkv, kv_max, n_local, &i);
+    nc = ncb < nc ? ncb : nc;
+  }
+  const uint64_t* src = cand + (long)bg * nsl * R;
+  const uint64_t a = (2 * w < nsl && l < R) ? src[(long)(2 * w) * R + l] : 0ull;
+  const uint64_t b = (2 * w + 1 < nsl && 63 - l < R) ? src[(long)(2 * w + 1) * R + 63 - l] : 0ull;
+  uint64_t c = wave_merge_desc(a > b ? a : b);
+  int cur = 0;
+  lists[cur][w][l] = c;
+  __syncthreads();
+#pragma unroll
+  for (int n = NW / 2; n >= 1; n /= 2) {
+    if (w < n) {
+      const uint64_t u = lists[cur][2 * w][l], v = lists[cur][2 * w + 1][63 - l];
+      c = wave_merge_desc(u > v ? u : v);
+      lists[cur ^ 1][w][l] = c;
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (w != 0) return;
+  // wave 0: c = the 64 largest composites, descending
+  const uint32_t j = 0xFFFFFFFFu - (uint32_t)c;
+  const bool pick = l < R && c != 0ull && j <= (uint32_t)nc;
+  const int cnt = __popcll(__ballot(pick));
+  // ascending by block index (the chosen first), the score key carried along
+  const uint64_t byidx = wave_sort64(pick ? ((uint64_t)j << 32) | (c >> 32) : ~0ull, false);
+  const long f_lo = i - n_local + 1 > 0 ? i - n_local + 1 : 0;
+  const int head = f_lo > 0 ? 1 : 0;
+  const int nloc = (int)(i - f_lo + 1);
+  int32_t* out = sel + (long)bg * topk;
+  float* osc = sel_sc ? sel_sc + (long)bg * topk : nullptr;
+  // row: forced block 0, the chosen (ascending), the forced local blocks f_lo .. i, -1 padding
+  if (l < cnt && head + l < topk) {
+    out[head + l] = (int32_t)(byidx >> 32);
+    if (osc) osc[head + l] = key_score((uint32_t)byidx);
+  }
+  if (l == 0 && head) {
+    out[0] = 0;
+    if (osc) osc[0] = INFINITY;
+  }
+  for (int t = l; t < nloc; t += 64)
+    if (head + cnt + t < topk) {
+      out[head + cnt + t] = (int32_t)(f_lo + t);
+      if (osc) osc[head + cnt + t] = INFINITY;
+    }
+  for (int t = head + cnt + nloc + l; t < topk; t += 64) {
+    out[t] = -1;
+    if (osc) osc[t] = -INFINITY;
+  }
+}
+
 }  // namespace
 
 static long select_row_len(const sala_sparse_desc& d) {
@@ -784,6 +932,18 @@ size_t block_select_workspace(const sala_sparse_desc& d) {
   return ((qt + 255) & ~(size_t)255) + sc;
 }
 
+// level 2 of the decode selection: the register networks while R <= 64, else the radix merge
+static void launch_decode_merge(const uint64_t* cand, int32_t* sel, float* sel_sc, int nsl, int R, long i, int n_local,
+                                int topk, long nc, const int64_t* kv_lens, int Hkv, long kv_max, int BG,
+                                hipStream_t st) {
+  if (R <= 64 && nsl <= DNSL_MAX)
+    hipLaunchKernelGGL((decode_merge64_kernel<DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, sel_sc, nsl,
+                       R, i, n_local, topk, nc, kv_lens, Hkv, kv_max);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, sel_sc,
+                       nsl, R, i, n_local, topk, nc, kv_lens, Hkv, kv_max);
+}
+
 // level 1 of the decode selection (q~ computed inside), for the descriptor's dtype and dim
 static void launch_decode_slice(const sala_sparse_desc& d, const void* q, const float* qw, const float* k_pool,
                                 uint64_t* cand, long nblk_cap, long nc, int R, int nsl, const int64_t* kv_lens,
@@ -814,8 +974,8 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
   if (decode_two_level(d, &nc, &nsl, &R)) {
     uint64_t* cand = reinterpret_cast<uint64_t*>(sc);
     launch_decode_slice(d, q, qw, k_pool, cand, g.nblk_cap, nc, R, nsl, nullptr, st);
-    hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, sel_sc,
-                       nsl, R, i_max, d.n_local, d.topk, nc, nullptr, d.n_kv_heads, (long)d.kv_len);
+    launch_decode_merge(cand, sel, sel_sc, nsl, R, i_max, d.n_local, d.topk, nc, nullptr, d.n_kv_heads,
+                        (long)d.kv_len, BG, st);
     return hipGetLastError();
   }
   const dim3 gq(d.batch, (unsigned)g.nqb);
@@ -903,8 +1063,8 @@ hipError_t launch_block_select_decode_at(const sala_sparse_desc& d, const int64_
   } else {
     launch_decode_slice(d, q, qw, k_pool, cand, nblk_cap, nc, R, nsl, kv_lens, st);
   }
-  hipLaunchKernelGGL((decode_merge_kernel<DMERGE, DMERGE_NT>), dim3(BG), dim3(DMERGE_NT), 0, st, cand, sel, nullptr,
-                     nsl, R, (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens, d.n_kv_heads, (long)d.kv_len);
+  launch_decode_merge(cand, sel, nullptr, nsl, R, (long)((d.kv_len - 1) / 64), d.n_local, d.topk, nc, kv_lens,
+                      d.n_kv_heads, (long)d.kv_len, BG, st);
   return hipGetLastError();
 }
 
