@@ -551,8 +551,8 @@ __device__ __forceinline__ void decode_qtilde(const T* __restrict__ q, const flo
 // form a prefix 0 .. n-1 (only the last chunk of the range can be partial, and it is the last
 // chunk of its slice). At each step the nsl slices of a row read adjacent chunks, which spreads
 // the stream over the memory channels. Scores q~ . k_pool[j] (8 lanes per pooled row), then the
-// slice's best R as composites into cand[bg][s][0..R) (0-padded; sorted, largest first, when
-// R <= 64, else unordered). With kv_lens, nc
+// slice's best R as composites into cand[bg][s][0..R) (0-padded; when R <= 64 chosen by bitonic
+// networks and sorted largest first, else by a radix threshold and unordered). With kv_lens, nc
 // is each sequence's own count (at most the nc given). q~ of the single query token is computed
 // here (decode_qtilde) from q [B, Hq, DD], while the first rows' loads are in flight.
 // APPEND (the decode step): the grid has one more row of workgroups, y = 0, that append each
@@ -583,7 +583,7 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   __shared__ int s_cnt;
   __shared__ float hsum[NT / (DD / (16 / (int)sizeof(QT)))][DD];
   __shared__ float qs[DD];
-  __shared__ uint64_t s_win[64];
+  __shared__ uint64_t s_lists[2][4][64];
   static_assert(RPI == 32, "chunks of 32 candidates: one step of the workgroup");
   constexpr int IT = DSL / RPI, BT = 4;
   if (APPEND && blockIdx.y == 0) {
@@ -660,21 +660,33 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
   }
   __syncthreads();
   uint64_t* dst = cand + ((long)bg * nsl + sl) * R;
-  // R <= 64: the winners go to LDS first and leave sorted, largest first (wave 0)
-  const bool sorted = R <= 64;
-  auto emit_sorted = [&] {
+  if (R <= 64) {
+    // the 64 largest composites by bitonic networks (exact: composites are distinct): wave w
+    // sorts positions 128w .. +63 (descending) and 128w + 64 .. +127 (ascending), keeps the
+    // larger of each lane pair and sorts them; two halvings through LDS leave the slice's 64
+    // largest, descending, in wave 0, whose first R are the winners
+    static_assert(NT == 256 && DSL == 4 * 128, "four waves of 128 positions");
+    const int w = tid >> 6, l = tid & 63;
+    auto comp = [&](int x) -> uint64_t { return x < n ? composite(keys[x], cand_of(x)) : 0ull; };
+    const uint64_t a = wave_sort64(comp(128 * w + l), true), b = wave_sort64(comp(128 * w + 64 + l), false);
+    uint64_t c = wave_merge_desc(a > b ? a : b);
+    s_lists[0][w][l] = c;
     __syncthreads();
-    if (tid < 64) {
-      const uint64_t v = wave_sort64(tid < R ? s_win[tid] : 0ull, true);
-      if (tid < R) dst[tid] = v;
+    if (w < 2) {
+      const uint64_t u = s_lists[0][2 * w][l], v = s_lists[0][2 * w + 1][63 - l];
+      c = wave_merge_desc(u > v ? u : v);
+      s_lists[1][w][l] = c;
     }
-  };
+    __syncthreads();
+    if (w == 0) {
+      const uint64_t u = s_lists[1][0][l], v = s_lists[1][1][63 - l];
+      c = wave_merge_desc(u > v ? u : v);
+      if (l < R) dst[l] = c;
+    }
+    return;
+  }
   if (n <= R) {
-    for (int t = tid; t < R; t += NT) {
-      const uint64_t v = t < n ? composite(keys[t], cand_of(t)) : 0ull;
-      if (sorted) s_win[t] = v; else dst[t] = v;
-    }
-    if (sorted) emit_sorted();
+    for (int t = tid; t < R; t += NT) dst[t] = t < n ? composite(keys[t], cand_of(t)) : 0ull;
     return;
   }
   uint32_t T;
@@ -700,13 +712,8 @@ decode_slice_kernel(const QT* __restrict__ q, const float* __restrict__ qw, int 
     if (x >= n) continue;
     const uint32_t key = keys[x];
     const bool pick = key > T || (key == T && (eqb++) < need);
-    if (pick && pos < R) {
-      const uint64_t v = composite(key, cand_of(x));
-      if (sorted) s_win[pos] = v; else dst[pos] = v;
-      ++pos;
-    }
+    if (pick && pos < R) dst[pos++] = composite(key, cand_of(x));
   }
-  if (sorted) emit_sorted();
 }
 
 // Second-stage keys for surplus ties at threshold T: keys above T become 0xFFFFFFFF (always
