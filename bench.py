@@ -166,6 +166,36 @@ def measured_peaks(torch):
         ms = _time_events(torch, lambda: call(lib.sala_peak_copy(buf.data_ptr(), dst.data_ptr(), half, wgs, st)), 5)
         copy[wgs] = 2 * half / (ms * 1e-3) / 1e9
     del buf, dst
+    # cold ceilings at the decode step's sizes (a linear layer's state traffic as a 16.8 MB copy,
+    # the selection's pooled keys as a 134 MB read, the attention's K/V as a 33.5 MB read): each
+    # transfer after a 1 GiB read outside the timed region, HIP events, median of 5, best grid
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    fsink = torch.empty(1, dtype=torch.float32, device="cuda")
+    buf = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+
+    def cold_us(fn):
+        ts = []
+        for _ in range(5):
+            torch.sum(flush, dim=0, keepdim=True, out=fsink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return sorted(ts)[2]
+
+    half_gib = 512 << 20
+    cold = {
+        "copy_16.8MB": min(cold_us(lambda w=w: call(lib.sala_peak_copy(buf.data_ptr(), buf.data_ptr() + half_gib,
+                                                                       16 << 20, w, st))) for w in (256, 512, 1024)),
+        "read_134MB": min(cold_us(lambda w=w: call(lib.sala_peak_read(buf.data_ptr(), 128 << 20, sink.data_ptr(), w,
+                                                                      st))) for w in (256, 512, 1024)),
+        "read_33.5MB": min(cold_us(lambda w=w: call(lib.sala_peak_read(buf.data_ptr(), 32 << 20, sink.data_ptr(), w,
+                                                                       st))) for w in (256, 512, 1024)),
+        "empty_region": cold_us(lambda: None),
+    }
+    del flush, buf
     iters = 2048
     mfma, mfma32 = {}, {}
     for wgs in (256, 512, 1024, 2048, 4096):
@@ -176,9 +206,10 @@ def measured_peaks(torch):
     return {"hbm_read_gbs": max(read.values()), "hbm_copy_gbs": max(copy.values()),
             "bf16_mfma_tflops": max(mfma.values()), "bf16_mfma_32x32x16_tflops": max(mfma32.values()),
             "hbm_read_gbs_by_grid": read, "hbm_copy_gbs_by_grid": copy, "bf16_mfma_tflops_by_grid": mfma,
-            "bf16_mfma_32x32x16_tflops_by_grid": mfma32,
+            "bf16_mfma_32x32x16_tflops_by_grid": mfma32, "cold_at_decode_sizes_us": cold,
             "method": "libsala_peaks.so: 4 GiB streaming read (uint4 loads, 4 in flight per lane); 2 GiB copy "
-                      "(read + written bytes); "
+                      "(read + written bytes); the same kernels at the decode step's sizes after a 1 GiB read "
+                      "(event-timed like the decode calls; empty_region is an event pair around nothing); "
                       "8 independent v_mfma_f32_16x16x32_bf16 (4 of v_mfma_f32_32x32x16_bf16) chains per "
                       "wave; best over grid sizes"}
 

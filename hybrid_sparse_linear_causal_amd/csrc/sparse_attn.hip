@@ -427,6 +427,10 @@ sparse_decode_combine_kernel(const float* __restrict__ part, const bf16_t* __res
   const int G = Hq / Hkv;
   const int bg = blockIdx.x / G, hh = blockIdx.x % G;
   const int b = bg / Hkv, gk = bg % Hkv, dd = threadIdx.x;
+  const long off = ((long)b * Hq + gk * G + hh) * D + dd;
+  // the gate first: its load then overlaps those of the partials instead of following them
+  const bf16_t gate = g[off];
+  __builtin_amdgcn_sched_barrier(0);
   const float* src = part + ((long)bg * DEC_SPLIT * 16 + hh) * (D + 2);
   float ms[DEC_SPLIT], ls[DEC_SPLIT], os[DEC_SPLIT];
 #pragma unroll
@@ -446,8 +450,7 @@ sparse_decode_combine_kernel(const float* __restrict__ part, const bf16_t* __res
     o += os[s] * w;
     l += ls[s] * w;
   }
-  const long off = ((long)b * Hq + gk * G + hh) * D + dd;
-  out[off] = f2bf(o / l * fast_sigmoid(bf2f(g[off])));
+  out[off] = f2bf(o / l * fast_sigmoid(bf2f(gate)));
 }
 
 // ------------------------------------------------------------------ fp32 path

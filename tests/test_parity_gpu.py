@@ -240,7 +240,11 @@ def test_block_select_planted_needles_and_ties(S):
 @pytest.mark.parametrize("B,Hq,Hkv,L,topk", [(2, 32, 2, 64 * 50 + 13, 16), (1, 16, 1, 64 * 50, 64),
                                              (2, 8, 2, 64 * 3 + 1, 8), (1, 4, 1, 40, 4),
                                              # more blocks than the 64 decode waves of a KV group
-                                             (1, 16, 2, 64 * 300 + 3, 160)])
+                                             (1, 16, 2, 64 * 300 + 3, 160),
+                                             # 64 and 65 chosen beside the 3 forced blocks, over 4 slices:
+                                             # the largest top-k of the lane-network selection, and the
+                                             # smallest of the radix one
+                                             (1, 8, 1, 64 * 2000 + 7, 67), (1, 8, 1, 64 * 2000 + 7, 68)])
 def test_sparse_decode(S, B, Hq, Hkv, L, topk):
     """Decode at p = L - 1 over a synthetic cache of already-normalised keys (the same bits on
     both sides): append the new token, select, attend."""
