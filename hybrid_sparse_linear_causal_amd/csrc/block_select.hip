@@ -13,9 +13,11 @@
 // tiles of q~ k_pool^T), then select_kernel — per row an exact radix select on monotone uint32
 // keys of the scores and ordered compaction, so the output is ascending and deterministic;
 // (3) decode (one query block): decode_slice_kernel scores slices of 512 candidates (chunks of
-// 32 dealt round-robin) and keeps each slice's best (radix threshold, ties to the lower index),
-// decode_merge_kernel selects among the slice winners and emits them ascending through a
-// bitmap; very long ranges fall back to score_row_kernel + select_kernel.
+// 32 dealt round-robin) and keeps each slice's best as score/index composites (up to 64 of them
+// by bitonic networks across the lanes, sorted; more by a radix threshold, ties to the lower
+// index); decode_merge64_kernel (networks over the sorted lists) or decode_merge_kernel (radix,
+// a bitmap for the ascending order) selects among the slice winners and emits the row; very long
+// ranges fall back to score_row_kernel + select_kernel.
 #include "common.hpp"
 #include "kv_append.hpp"
 #include "launch.hpp"
