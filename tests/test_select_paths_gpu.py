@@ -140,9 +140,10 @@ def _check_scores(sel, scores, ref_score, first_block, n_local, what):
 
 
 def test_selection_scores(S):
-    """The optional scores output on the three selection paths: prefill rows (score tiles and the
-    per-row radix select), a decode row inside the two-level range (slice winners merged), and a
-    decode row past it (score row and the long-row select)."""
+    """The optional scores output on the selection paths: prefill rows (score tiles and the
+    per-row radix select), decode rows inside the two-level range (slice winners merged by lane
+    networks, and by radix thresholds), and a decode row past it (score row and the long-row
+    select)."""
     import torch
 
     d, n_local = 128, 2
@@ -163,8 +164,9 @@ def test_selection_scores(S):
     e = _check_scores(sel.cpu().numpy(), scores.cpu().numpy(), lambda b, g, i, j: float(qt[b, g, i] @ kb[b, g, j]), 0,
                       n_local, "prefill")
     print(f"  prefill rel err {e:.2e}", flush=True)
-    # decode rows: two-level (4,000 blocks, top-16) and beyond it (5,000 blocks, top-256)
-    for L, topk in ((64 * 4000 + 9, 16), (64 * 5000 + 9, 256)):
+    # decode rows: two-level with the lane-network levels (4,000 blocks, top-16) and with the radix
+    # levels (3,000 blocks, top-100), and beyond the two-level range (5,000 blocks, top-256)
+    for L, topk in ((64 * 4000 + 9, 16), (64 * 3000 + 9, 100), (64 * 5000 + 9, 256)):
         B, Hq, Hkv = 2, 8, 2
         kc_h = host_normal(971, 5, (B, Hkv, L, d))
         qd = host_normal(971, 0, (B, 1, Hq, d))
