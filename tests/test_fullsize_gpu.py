@@ -163,3 +163,13 @@ def test_decode_full_size(S):
                                         vns[0, 0], gsel[b, gk, 0], 1.0 / math.sqrt(d))
         assert_rel(host(out[b:b + 1, 0, gk * G:(gk + 1) * G]), (o2 * O.sigmoid(gs[0]))[None], 1e-2,
                    f"decode {(b, gk)} on the gpu selection")
+    # the decode step's single call (append in the selection's first kernel, selection levels,
+    # attention, combine) over the same cache: appending the same token at the same position
+    # again leaves the cache and pooled keys as they are, so the row and output must be the
+    # three calls' bit for bit
+    kvl = torch.full((B,), L, dtype=torch.int64, device="cuda")
+    out_s, sel_s = S.sparse_decode_step(q[:, 0], kn[:, 0], vn[:, 0], g[:, 0], kc, vc, kp, kvl, L, topk=Dw.topk,
+                                        n_local=Dw.n_local)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_s, sel[:, :, 0]), "decode step selection"
+    assert torch.equal(out_s, out[:, 0]), "decode step output"
