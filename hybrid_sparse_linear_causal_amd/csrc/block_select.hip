@@ -18,9 +18,12 @@
 // index); decode_merge64_kernel (networks over the sorted lists) or decode_merge_kernel (radix,
 // a bitmap for the ascending order) selects among the slice winners and emits the row; very long
 // ranges fall back to score_row_kernel + select_kernel.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kv_append.hpp"
 #include "launch.hpp"
+#include "varlen.hpp"
 
 namespace sala {
 
@@ -33,14 +36,14 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// grid (B, nqb); q~[b][g][r][DD] (fp32) = sum_{h in g} mean_t RMSNorm(q[t, h]) * w
+// q~ of query block r of one sequence's call, by a workgroup of NT threads: for each KV group g,
+// q~[g] = sum_{h in g} mean_t RMSNorm(q[t, h]) * w over the call's tokens t of the block, stored
+// at qt_r[g * g_stride .. + DD). q: the sequence's first call token, [n_q, Hq, DD].
 template <typename T, int DD>
-__global__ void __launch_bounds__(NT)
-qtilde_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __restrict__ qt,
-              int n_q, int Hq, int Hkv, long q0, float eps) {
+__device__ __forceinline__ void qtilde_block(const T* __restrict__ q, const float* __restrict__ qw,
+                                             float* __restrict__ qt_r, long g_stride, int n_q, int Hq, int Hkv,
+                                             long q0, long r, float eps, float (*hsum)[DD]) {
   constexpr int EPL = 16 / (int)sizeof(T), LPR = DD / EPL, RPP = NT / LPR;
-  __shared__ float hsum[64][DD];  // per-head sums for up to 64 heads
-  const int b = blockIdx.x, r = blockIdx.y;
   const int j = threadIdx.x, hr = j / LPR, seg = j % LPR;
   // tokens of this query block inside the call: positions [64*(q0/64 + r), +64) clipped
   const long blk = q0 / 64 + r;
@@ -58,7 +61,7 @@ qtilde_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __re
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const long p = p0 + u;
-          raw[u] = p < p_hi ? *reinterpret_cast<const uint4*>(q + (((long)b * n_q + (p - q0)) * Hq + h) * DD + seg * EPL)
+          raw[u] = p < p_hi ? *reinterpret_cast<const uint4*>(q + ((p - q0) * Hq + h) * DD + seg * EPL)
                             : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
@@ -91,8 +94,33 @@ qtilde_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __re
     const int g = idx / DD, dd = idx % DD;
     float s = 0.f;
     for (int hh = 0; hh < G; ++hh) s += hsum[g * G + hh][dd];
-    qt[(((long)b * Hkv + g) * gridDim.y + r) * DD + dd] = s;
+    qt_r[g * g_stride + dd] = s;
   }
+}
+
+// grid (B, nqb); q~[b][g][r][DD] (fp32)
+template <typename T, int DD>
+__global__ void __launch_bounds__(NT)
+qtilde_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __restrict__ qt,
+              int n_q, int Hq, int Hkv, long q0, float eps) {
+  __shared__ float hsum[64][DD];  // per-head sums for up to 64 heads
+  const int b = blockIdx.x, r = blockIdx.y, nqb = gridDim.y;
+  qtilde_block<T, DD>(q + (long)b * n_q * Hq * DD, qw, qt + ((long)b * Hkv * nqb + r) * DD, (long)nqb * DD, n_q, Hq,
+                      Hkv, q0, r, eps, hsum);
+}
+
+// Packed batch: grid (sum of the sequences' query blocks); item x of sequence s (t.item0 the
+// prefix of their query-block counts) is its query block x - t.item0[s]; sequence s's q~ sits at
+// qt + Hkv * t.item0[s] * DD as [g][r][DD], the layout of a one-sequence call.
+template <typename T, int DD>
+__global__ void __launch_bounds__(NT)
+qtilde_varlen_kernel(const T* __restrict__ q, const float* __restrict__ qw, float* __restrict__ qt, int Hq, int Hkv,
+                     float eps, VarlenTable t) {
+  __shared__ float hsum[64][DD];
+  const int s = vl_seq(t, blockIdx.x), r = blockIdx.x - t.item0[s];
+  const long nqb = t.item0[s + 1] - t.item0[s];
+  qtilde_block<T, DD>(q + (long)t.tok0[s] * Hq * DD, qw, qt + ((long)Hkv * t.item0[s] + r) * DD, nqb * DD, t.n[s],
+                      Hq, Hkv, t.pos0[s], r, eps, hsum);
 }
 
 // Prefill scores: grid (B*Hkv, ceil(nqb/64), ceil(RL/64)); 64x64 tile, 4x4 per thread.
@@ -970,6 +998,9 @@ static void launch_decode_slice(const sala_sparse_desc& d, const void* q, const 
 #undef SALA_SLICE
 }
 
+static hipError_t launch_select_rows(const sala_sparse_desc& d, const float* qt, const float* k_pool, int32_t* sel,
+                                     float* sel_sc, float* sc, hipStream_t st);
+
 hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const float* qw,
                                const float* k_pool, int32_t* sel, float* sel_sc, void* ws, hipStream_t st) {
   const SparseGeom g = sparse_geom(d);
@@ -997,6 +1028,17 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
     if (d.head_dim == 128) SALA_QT(float, 128); else SALA_QT(float, 64);
   }
 #undef SALA_QT
+  return launch_select_rows(d, qt, k_pool, sel, sel_sc, sc, st);
+}
+
+// the scores and the forced + top-k rows of a call whose q~ is already in qt (layout of
+// qtilde_kernel); sc: the score workspace
+static hipError_t launch_select_rows(const sala_sparse_desc& d, const float* qt, const float* k_pool, int32_t* sel,
+                                     float* sel_sc, float* sc, hipStream_t st) {
+  const SparseGeom g = sparse_geom(d);
+  const int BG = d.batch * d.n_kv_heads;
+  const long RL = select_row_len(d);
+  const long i_max = g.qb0 + g.nqb - 1;
   if (i_max - d.n_local >= 1) {
     if (g.nqb == 1) {
       const long ncand_end = i_max - d.n_local + 1;  // score blocks 0 .. i - n_local
@@ -1026,6 +1068,96 @@ hipError_t launch_block_select(const sala_sparse_desc& d, const void* q, const f
     hipLaunchKernelGGL((select_kernel<256, 4096>), dim3((unsigned)(BG * g.nqb)), dim3(256), 0, st, sc, sel, sel_sc,
                        (int)g.nqb, (long)g.qb0, (int)RL, d.topk, d.n_local);
   return hipGetLastError();
+}
+
+// ---- packed batches (desc.batch = sequences; cu_seqlens, pos0 host arrays). The q~ of every
+// prefill sequence comes from one launch over all their query blocks (its grid would be small
+// for a short sequence alone); the scores and rows then run sequence by sequence with the
+// sequence's own cache row, cache length and query blocks. A sequence of a single decode token
+// (the two-level selection) runs as a one-sequence call, which forms its q~ itself.
+namespace {
+
+sala_sparse_desc select_seq_desc(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0, int s) {
+  sala_sparse_desc x = d;
+  x.batch = 1;
+  x.n_q = cu[s + 1] - cu[s];
+  x.kv_len = pos0[s] + x.n_q;
+  return x;
+}
+
+// query blocks of each sequence that takes the q~ kernel (0 for the others) and their sum
+long varlen_qtilde_blocks(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0, int* nqb_of) {
+  long tot = 0;
+  for (int s = 0; s < d.batch; ++s) {
+    nqb_of[s] = 0;
+    if (cu[s + 1] == cu[s]) continue;
+    const sala_sparse_desc x = select_seq_desc(d, cu, pos0, s);
+    long nc;
+    int nsl, R;
+    if (decode_two_level(x, &nc, &nsl, &R)) continue;
+    nqb_of[s] = (int)sparse_geom(x).nqb;
+    tot += nqb_of[s];
+  }
+  return tot;
+}
+
+}  // namespace
+
+size_t block_select_varlen_workspace(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0) {
+  int nqb_of[SALA_VARLEN_MAX_SEQS];
+  const long nq = varlen_qtilde_blocks(d, cu, pos0, nqb_of);
+  size_t per = 0;  // the largest one-sequence workspace (its own q~ part included)
+  for (int s = 0; s < d.batch; ++s)
+    if (cu[s + 1] > cu[s]) per = std::max(per, block_select_workspace(select_seq_desc(d, cu, pos0, s)));
+  const size_t qt = (size_t)nq * d.n_kv_heads * d.head_dim * sizeof(float);
+  return ((qt + 255) & ~(size_t)255) + per;
+}
+
+hipError_t launch_block_select_varlen(const sala_sparse_desc& d, const int32_t* cu, const int64_t* pos0,
+                                      const void* q, const float* qw, const float* k_pool, int32_t* sel, void* ws,
+                                      hipStream_t st) {
+  const size_t eb = d.dtype == SALA_BF16 ? 2 : 4, qrow = (size_t)d.n_heads * d.head_dim;
+  const size_t pool_seq = (size_t)d.n_kv_heads * d.head_dim * (d.kv_capacity / 64);
+  int nqb_of[SALA_VARLEN_MAX_SEQS];
+  const long nq = varlen_qtilde_blocks(d, cu, pos0, nqb_of);
+  float* qt = static_cast<float*>(ws);
+  const size_t qt_bytes = (size_t)nq * d.n_kv_heads * d.head_dim * sizeof(float);
+  char* rest = static_cast<char*>(ws) + ((qt_bytes + 255) & ~(size_t)255);
+  if (nq > 0) {
+    VarlenTable t = make_varlen_table(d.batch, cu, pos0);
+    for (int s = 0; s < d.batch; ++s) t.item0[s + 1] = t.item0[s] + nqb_of[s];
+#define SALA_QTV(T, DD)                                                                                      \
+  hipLaunchKernelGGL((qtilde_varlen_kernel<T, DD>), dim3((unsigned)nq), dim3(NT), 0, st, (const T*)q, qw, qt, \
+                     d.n_heads, d.n_kv_heads, d.norm_eps, t)
+    if (d.dtype == SALA_BF16) {
+      if (d.head_dim == 128) SALA_QTV(bf16_t, 128); else SALA_QTV(bf16_t, 64);
+    } else {
+      if (d.head_dim == 128) SALA_QTV(float, 128); else SALA_QTV(float, 64);
+    }
+#undef SALA_QTV
+  }
+  long qb_row = 0, qt_blk = 0;  // query blocks of the earlier sequences: all, and those in qt
+  for (int s = 0; s < d.batch; ++s) {
+    const int n = cu[s + 1] - cu[s];
+    if (n == 0) continue;
+    const sala_sparse_desc x = select_seq_desc(d, cu, pos0, s);
+    int32_t* sel_s = sel + qb_row * d.n_kv_heads * d.topk;
+    const float* pool_s = k_pool + s * pool_seq;
+    hipError_t e;
+    if (nqb_of[s] == 0) {
+      e = launch_block_select(x, static_cast<const char*>(q) + (size_t)cu[s] * qrow * eb, qw, pool_s, sel_s, nullptr,
+                              rest, st);
+    } else {
+      // past its q~ part, the one-sequence workspace layout holds the scores
+      const size_t own_qt = (size_t)d.n_kv_heads * nqb_of[s] * d.head_dim * sizeof(float);
+      float* sc = reinterpret_cast<float*>(rest + ((own_qt + 255) & ~(size_t)255));
+      e = launch_select_rows(x, qt + qt_blk * d.n_kv_heads * d.head_dim, pool_s, sel_s, nullptr, sc, st);
+      qt_blk += nqb_of[s];
+    }
+    if (e != hipSuccess) return e;
+    qb_row += (n + 63) / 64;
+  }
+  return hipSuccess;
 }
 
 }  // namespace sala
