@@ -116,23 +116,59 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   const int h = gk * G + (head_ok ? hl : 0);
   const long i = qb0 + r;
   const long row_base = ((long)b * Hkv + gk) * cap;
-  if (!DENSE) {
-    const int32_t* srow = sel + it.sel_row * topk;
-    if (j < topk) s_sel[j] = srow[j];
+  // the loads first: the selection row (oldest, so that waiting for it leaves the query loads
+  // in flight), then this wave's query rows (row addresses clamped into the call: rows past it
+  // are zeroed after the load)
+  int selv = -1;
+  if (!DENSE && j < topk) selv = sel[it.sel_row * topk + j];
+  uint4 qraw[PF_QT][4];
+  bool qok[PF_QT];
+#pragma unroll
+  for (int qt = 0; qt < PF_QT; ++qt) {
+    const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
+    qok[qt] = head_ok && t < n_q;
+    const long tc = t < n_q ? t : n_q - 1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qraw[qt][ks] = *reinterpret_cast<const uint4*>(q + ((it.tok0 + tc) * Hq + h) * D + 32 * ks + 8 * lq);
   }
+  if (!DENSE && j < topk) s_sel[j] = selv;
+  __syncthreads();
+  // the blocks attended: the selection (ascending, -1 padded, ends with block i), or every
+  // block 0 .. i. nsel = the index of the row's first -1 (or topk).
+  int nsel = 0;
+  if (DENSE) nsel = (int)(i + 1);
+  else {
+    nsel = topk;
+#pragma unroll
+    for (int u = 3; u >= 0; --u) {
+      const int x = lane + 64 * u;
+      const unsigned long long bad = __ballot(x < topk && s_sel[x] < 0);
+      if (bad) nsel = 64 * u + (int)__builtin_ctzll(bad);
+    }
+  }
+  auto blk = [&](int x) -> long { return DENSE ? (long)x : (long)s_sel[x]; };
+  // the query-norm weights this lane applies, loaded before the copies are issued
+  float qwv[4][8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qwv[ks][e] = qw ? qw[32 * ks + 8 * lq + e] : 1.0f;
+  // the first three blocks' copies, issued before the query rows are normalised
+#pragma unroll
+  for (int x = 0; x < 3; ++x)
+    if (x < nsel) dma_block(kc, vc, row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
 
   // ---- Q^T fragments (B operand: k = dim, n = query); normalised, scaled by scale*log2(e)
   bf16x8 qf[PF_QT][4];
 #pragma unroll
   for (int qt = 0; qt < PF_QT; ++qt) {
-    const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
-    const bool ok = head_ok && t < n_q;
     float x[4][8];
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (ok) u = *reinterpret_cast<const uint4*>(q + ((it.tok0 + t) * Hq + h) * D + 32 * ks + 8 * lq);
+      uint4 u = qraw[qt][ks];
+      if (!qok[qt]) u = make_uint4(0, 0, 0, 0);
       unpack8(u, x[ks]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
@@ -144,20 +180,13 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     for (int ks = 0; ks < 4; ++ks) {
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = x[ks][e] * inv * (qw ? qw[32 * ks + 8 * lq + e] : 1.0f);
+      for (int e = 0; e < 8; ++e) y[e] = x[ks][e] * inv * qwv[ks][e];
       uint4 u = pack8(y);
       // opaque to the optimiser: keep the packed fragment instead of recomputing it per block
       asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
       qf[qt][ks] = as_bf16x8(u);
     }
   }
-  __syncthreads();
-  // the blocks attended: the selection (ascending, ends with block i), or every block 0 .. i
-  int nsel = 0;
-  if (DENSE) nsel = (int)(i + 1);
-  else
-    while (nsel < topk && s_sel[nsel] >= 0) ++nsel;
-  auto blk = [&](int x) -> long { return DENSE ? (long)x : (long)s_sel[x]; };
 
   float m[PF_QT], lp[PF_QT];
   f32x4 minit[PF_QT];
@@ -178,39 +207,84 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   // block e run on VALU, then O^T += V^T P^T for block e. Blocks e+2 and e+3 are in flight.
   // The selection is ascending and always ends with the query's own block i, so the causal
   // diagonal block is the last one and is finished after the loop.
-#pragma unroll
-  for (int x = 0; x < 3; ++x)
-    if (x < nsel) dma_block(kc, vc, row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
   if (nsel > 2) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();  // blocks 0 and 1 landed
   __syncthreads();
 
   f32x4 SA[4][PF_QT], SB[4][PF_QT];
   scores<PF_QT>(lds[0][0], qf, minit, SA, l16);
+  // With 4 or more blocks, the gate rows of the output pass are copied into LDS during the last
+  // step: wave w's 32 rows (8 KB) into stage nsel % 4 (waves 0-3) or (nsel + 1) % 4 (waves 4-7),
+  // whose blocks were consumed before that step. Copy I = 4qt + dp, lane L: row qrow0 + 16qt +
+  // (L >> 1) % 16, 16-byte chunk 2dt + (L & 1) of dims, dt = 2dp + L / 32; the lanes of the
+  // output pass then read 512 contiguous bytes per (qt, dt).
+  const bool g_lds = !DENSE && nsel >= 4;
+  bf16_t* gtile = lds[(nsel + (wave >> 2)) & 3][0] + (wave & 3) * 4096;
+  auto gate_copy = [&]() {
+#pragma unroll
+    for (int I = 0; I < 8; ++I) {
+      const int qt = I >> 2, dt = 2 * (I & 3) + (lane >> 5), rr = (lane >> 1) & 15, c = 2 * dt + (lane & 1);
+      const long t = i * 64 + qrow0 + 16 * qt + rr - q0;
+      const long tc = t < n_q ? t : n_q - 1;
+      dma16(g + ((it.tok0 + tc) * Hq + h) * D + 8 * c, lds_addr_u32(gtile + I * 512));
+    }
+  };
   auto step = [&](int e, f32x4 (&Sc)[4][PF_QT], f32x4 (&Sn)[4][PF_QT]) {
     const bool more = e + 3 < nsel;
     if (more) dma_block(kc, vc, row_base, blk(e + 3), kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
     scores<PF_QT>(lds[(e + 1) & 3][0], qf, minit, Sn, l16);
     exp_pv<PF_QT>(lds[e & 3][1], Sc, Sn, OT, m, minit, lp, l16, lq, e == 0);
-    // block e+2 must have landed (only block e+3's copies may still be in flight)
-    if (more) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();
-    __syncthreads();
+    // block e+2 must have landed (only block e+3's copies may still be in flight); after the
+    // last step only the diagonal block is read, which the previous step's wait and barrier
+    // already cover, so the last step neither waits nor synchronises
+    if (DENSE || e < nsel - 2) {
+      if (more) wait_vmcnt<DMA_PER_WAVE>(); else wait_vmcnt<0>();
+      __syncthreads();
+    }
   };
   int e = 0;
-  for (; e + 2 <= nsel - 1; e += 2) {
-    step(e, SA, SB);
-    step(e + 1, SB, SA);
-  }
-  if (e < nsel - 1) {
-    step(e, SA, SB);
+  if constexpr (DENSE) {
+    for (; e + 2 <= nsel - 1; e += 2) {
+      step(e, SA, SB);
+      step(e + 1, SB, SA);
+    }
+    if (e < nsel - 1) {
+      step(e, SA, SB);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < PF_QT; ++qt) SA[kt][qt] = SB[kt][qt];
+        for (int qt = 0; qt < PF_QT; ++qt) SA[kt][qt] = SB[kt][qt];
+    }
+  } else {
+    // steps 0 .. nsel-3, then the last step nsel-2 with the gate copies issued first
+    const int last = nsel - 2;
+    for (; e + 2 <= last; e += 2) {
+      step(e, SA, SB);
+      step(e + 1, SB, SA);
+    }
+    if (e < last) {
+      step(e, SA, SB);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < PF_QT; ++qt) SA[kt][qt] = SB[kt][qt];
+      ++e;
+    }
+    if (e == last) {
+      if (g_lds) gate_copy();
+      step(e, SA, SB);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < PF_QT; ++qt) SA[kt][qt] = SB[kt][qt];
+    }
   }
   // diagonal block (index nsel-1); SB only receives the (unused) shift of a raised reference
   mask_diag<PF_QT>(SA, l16, lq, qrow0);
   exp_pv<PF_QT>(lds[(nsel - 1) & 3][1], SA, SB, OT, m, minit, lp, l16, lq, nsel == 1);
-  if (!head_ok) return;
+  if (!head_ok) {
+    if (g_lds) wait_vmcnt<0>();  // no copy into LDS outlives the wave
+    return;
+  }
 
   // ---- normalise, gate, store (lane: query qrow0 + 16qt + l16, dims 16dt + 4lq .. +3)
 #pragma unroll
@@ -222,14 +296,17 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
     if (t >= n_q) continue;
     const long base = ((it.tok0 + t) * Hq + h) * D;
+    if (g_lds) wait_vmcnt<0>();  // this wave's gate copies have landed
     // log2-domain log-sum-exp of the row's scaled scores (m is a score of the row, l >= 1)
     if (lse && lq == 0) lse[(it.tok0 + t) * Hq + h] = m[qt] + __log2f(l);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const long off = base + 16 * dt + 4 * lq;
-      const uint2 gv = *reinterpret_cast<const uint2*>(g + off);
-      const float g0 = __uint_as_float(gv.x << 16), g1 = __uint_as_float(gv.x & 0xffff0000u);
-      const float g2 = __uint_as_float(gv.y << 16), g3 = __uint_as_float(gv.y & 0xffff0000u);
+      const uint2 gw = g_lds ? *reinterpret_cast<const uint2*>(gtile + (4 * qt + (dt >> 1)) * 512 +
+                                                            8 * (32 * (dt & 1) + 2 * l16 + (lq >> 1)) + 4 * (lq & 1))
+                             : *reinterpret_cast<const uint2*>(g + off);
+      const float g0 = __uint_as_float(gw.x << 16), g1 = __uint_as_float(gw.x & 0xffff0000u);
+      const float g2 = __uint_as_float(gw.y << 16), g3 = __uint_as_float(gw.y & 0xffff0000u);
       uint2 o;
       o.x = pack_bf16x2(OT[dt][qt][0] * il * fast_sigmoid(g0), OT[dt][qt][1] * il * fast_sigmoid(g1));
       o.y = pack_bf16x2(OT[dt][qt][2] * il * fast_sigmoid(g2), OT[dt][qt][3] * il * fast_sigmoid(g3));
