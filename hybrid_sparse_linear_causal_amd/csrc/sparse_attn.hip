@@ -281,10 +281,10 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   // diagonal block (index nsel-1); SB only receives the (unused) shift of a raised reference
   mask_diag<PF_QT>(SA, l16, lq, qrow0);
   exp_pv<PF_QT>(lds[(nsel - 1) & 3][1], SA, SB, OT, m, minit, lp, l16, lq, nsel == 1);
-  if (!head_ok) {
-    if (g_lds) wait_vmcnt<0>();  // no copy into LDS outlives the wave
-    return;
-  }
+  // this wave's gate copies have landed (also where the wave stores nothing: no copy into LDS
+  // outlives the wave)
+  if (g_lds) wait_vmcnt<0>();
+  if (!head_ok) return;
 
   // ---- normalise, gate, store (lane: query qrow0 + 16qt + l16, dims 16dt + 4lq .. +3)
 #pragma unroll
@@ -296,7 +296,6 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     const long t = i * 64 + qrow0 + 16 * qt + l16 - q0;
     if (t >= n_q) continue;
     const long base = ((it.tok0 + t) * Hq + h) * D;
-    if (g_lds) wait_vmcnt<0>();  // this wave's gate copies have landed
     // log2-domain log-sum-exp of the row's scaled scores (m is a score of the row, l >= 1)
     if (lse && lq == 0) lse[(it.tok0 + t) * Hq + h] = m[qt] + __log2f(l);
 #pragma unroll

@@ -189,6 +189,7 @@ def test_kv_append_and_pool(S, B, N, Hq, Hkv, dtype):
     (1, 64 * 40 + 17, 8, 2, "bf16", 8, 2),
     (2, 64 * 23, 4, 1, "bf16", 6, 1),
     (1, 64 * 70, 16, 1, "bf16", 64, 2),   # top-k wider than every row: dense causal
+    (1, 64 * 20 + 33, 12, 2, "bf16", 8, 2),  # 6 heads per group: a head quad with 2 empty heads
 ])
 def test_sparse_prefill(S, B, N, Hq, Hkv, dtype, topk, n_local):
     d = 64 if dtype == "f32" else 128
