@@ -148,6 +148,17 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
     }
   }
   auto blk = [&](int x) -> long { return DENSE ? (long)x : (long)s_sel[x]; };
+  // block copies with scalar block addresses (K and V tiles both in the swzv layout); an entry
+  // past the cache (a malformed row) is read as the cache's last block
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const DmaLane dl = dma_lane_setup(wave_u);
+  const int last_blk = (int)((kv_len - 1) / 64), last_row = (int)((kv_len - 1) % 64);
+  auto copy_block = [&](int x, int s) {
+    int bk = DENSE ? x : __builtin_amdgcn_readfirstlane(s_sel[x]);
+    if (bk > last_blk) bk = last_blk;
+    const long off = (row_base + (long)bk * 64) * D;
+    dma_block_s(dl, kc + off, vc + off, bk == last_blk ? last_row : 63, lds[s][0], lds[s][1], wave_u);
+  };
   // the query-norm weights this lane applies, loaded before the copies are issued
   float qwv[4][8];
 #pragma unroll
@@ -157,7 +168,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   // the first three blocks' copies, issued before the query rows are normalised
 #pragma unroll
   for (int x = 0; x < 3; ++x)
-    if (x < nsel) dma_block(kc, vc, row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
+    if (x < nsel) copy_block(x, x);
 
   // ---- Q^T fragments (B operand: k = dim, n = query); normalised, scaled by scale*log2(e)
   bf16x8 qf[PF_QT][4];
@@ -211,7 +222,7 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   __syncthreads();
 
   f32x4 SA[4][PF_QT], SB[4][PF_QT];
-  scores<PF_QT>(lds[0][0], qf, minit, SA, l16);
+  scores<PF_QT, true>(lds[0][0], qf, minit, SA, l16);
   // With 4 or more blocks, the gate rows of the output pass are copied into LDS during the last
   // step: wave w's 32 rows (8 KB) into stage nsel % 4 (waves 0-3) or (nsel + 1) % 4 (waves 4-7),
   // whose blocks were consumed before that step. Copy I = 4qt + dp, lane L: row qrow0 + 16qt +
@@ -230,8 +241,8 @@ sparse_prefill_bf16_kernel(const bf16_t* __restrict__ q, const float* __restrict
   };
   auto step = [&](int e, f32x4 (&Sc)[4][PF_QT], f32x4 (&Sn)[4][PF_QT]) {
     const bool more = e + 3 < nsel;
-    if (more) dma_block(kc, vc, row_base, blk(e + 3), kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
-    scores<PF_QT>(lds[(e + 1) & 3][0], qf, minit, Sn, l16);
+    if (more) copy_block(e + 3, (e + 3) & 3);
+    scores<PF_QT, true>(lds[(e + 1) & 3][0], qf, minit, Sn, l16);
     exp_pv<PF_QT>(lds[e & 3][1], Sc, Sn, OT, m, minit, lp, l16, lq, e == 0);
     // block e+2 must have landed (only block e+3's copies may still be in flight); after the
     // last step only the diagonal block is read, which the previous step's wait and barrier

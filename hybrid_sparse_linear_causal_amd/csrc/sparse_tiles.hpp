@@ -41,6 +41,45 @@ __device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, lo
   }
 }
 
+// The same copy with the block's addresses kept in scalar registers: the lane's part of the
+// address is a 32-bit byte offset inside the block (saddr form of global_load_lds_dwordx4), and
+// both tiles use the swzv layout, so the K and V copies of a row share that offset. A lane's
+// offsets (rows 4I + lane/16 of pieces I = 2*wave and 2*wave+1, chunk positions
+// (lane % 16) ^ 2(row & 7)) are set up once by dma_lane_setup; per block only the clamp of rows
+// past the cache (lim = last valid row of the block, 0 <= lim <= 63) and the shift remain.
+// kb, vb: the block's first row in K and V; Ks, Vs: the stage's tiles; wave: the wave index as
+// a wave-uniform value.
+struct DmaLane {
+  int row[2];        // row of the block this lane copies for piece 2*wave + m
+  uint32_t chk[2];   // byte offset of the source chunk within the row
+};
+__device__ __forceinline__ DmaLane dma_lane_setup(int wave) {
+  const int lane = threadIdx.x & 63;
+  DmaLane d;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int row = 4 * (2 * wave + m) + (lane >> 4);
+    d.row[m] = row;
+    d.chk[m] = 16u * (uint32_t)((lane & 15) ^ (2 * (row & 7)));
+  }
+  return d;
+}
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_block_s(const DmaLane& d, const bf16_t* kb, const bf16_t* vb, int lim,
+                                            bf16_t* Ks, bf16_t* Vs, int wave) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int r = d.row[m] < lim ? d.row[m] : lim;
+    const uint32_t off = ((uint32_t)r << 8) + d.chk[m];
+    const int I = 2 * wave + m;
+    dma16s(kb, off, (uint32_t)(size_t)(Ks + I * 512));
+    dma16s(vb, off, (uint32_t)(size_t)(Vs + I * 512));
+  }
+}
+
 // A operand V^T (rows dv = 16*dt + l16, k = keys in the permuted order of the P^T fragments:
 // slots 0..3 = keys kb + 4*lq + e, slots 4..7 = keys kb + 16 + 4*lq + e) via two
 // transposing reads. Source lane (i = l16) points at key row kb(+16) + 4*lq + i/4, columns
