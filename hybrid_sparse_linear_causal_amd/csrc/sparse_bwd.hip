@@ -528,18 +528,28 @@ struct DkvLds {
 };
 
 // copies of one step: q~ and dO tiles in the swzv layout (16 pieces of 1 KB each, wave w moves
-// 4w .. 4w+3 of both) and, by wave 0, the 1 KB stats rows
+// 4w .. 4w+3 of both) and, by wave 0, the 1 KB stats rows. The step's tile base is a scalar
+// address (pad0: its first padded row); a lane adds its fixed byte offset loff[m] (row
+// 4I + lane/16 of piece I = 4w + m, the source chunk the swzv layout puts at position lane % 16),
+// so the copies take no vector address arithmetic. wave: the wave index as a uniform value.
+__device__ __forceinline__ void dkv_lane_offsets(int wave, uint32_t (&loff)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int row = 4 * (4 * wave + m) + (lane >> 4);
+    loff[m] = 2u * (uint32_t)(row * D + 8 * ((lane & 15) ^ (2 * (row & 7))));
+  }
+}
 __device__ __forceinline__ void dma_step(const bf16_t* qtb, const bf16_t* dob, const float* stb, long pad0,
-                                         DkvLds& L, int bufi) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                         const uint32_t (&loff)[4], DkvLds& L, int bufi, int wave) {
+  const int lane = threadIdx.x & 63;
+  const bf16_t* qb = qtb + pad0 * D;
+  const bf16_t* db = dob + pad0 * D;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int I = 4 * wave + m;
-    const int row = 4 * I + (lane >> 4);
-    const int ch = (lane & 15) ^ (2 * (row & 7));
-    const long off = (pad0 + row) * D + 8 * ch;
-    dma16(qtb + off, lds_addr_u32(L.qd[bufi][0] + I * 512));
-    dma16(dob + off, lds_addr_u32(L.qd[bufi][1] + I * 512));
+    dma16s(qb, loff[m], (uint32_t)(size_t)(L.qd[bufi][0] + I * 512));
+    dma16s(db, loff[m], (uint32_t)(size_t)(L.qd[bufi][1] + I * 512));
   }
   if (wave == 0) dma16(stb + pad0 * 4 + 4 * lane, lds_addr_u32(L.st[bufi]));
 }
@@ -581,10 +591,13 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
   __syncthreads();  // the list
   const int nl = L.n, nsteps = nl * G;
   auto pad_of = [&](int st) -> long {
-    const int r = L.list[st / G], hh = st % G;
+    const int r = __builtin_amdgcn_readfirstlane(L.list[st / G]), hh = st % G;
     return ((long)b * Hq + gk * G + hh) * nqb * 64 + (long)r * 64;
   };
-  if (nsteps > 0) dma_step(qtb, dob, stb, pad_of(0), L, 0);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t loff[4];
+  dkv_lane_offsets(wave_u, loff);
+  if (nsteps > 0) dma_step(qtb, dob, stb, pad_of(0), loff, L, 0, wave_u);
 
   const int kt = wave;  // key tile
   // this wave's K and V fragments (B operand: key 16kt + l16, dims 32ks + 8lq .. +7); rows past
@@ -608,7 +621,7 @@ sbwd_dkv_kernel(const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, co
     const int bi = st & 1;
     wait_vmcnt<0>();  // this step's copies have landed
     __syncthreads();  // visible to all; every wave is done with the other buffer
-    if (st + 1 < nsteps) dma_step(qtb, dob, stb, pad_of(st + 1), L, bi ^ 1);
+    if (st + 1 < nsteps) dma_step(qtb, dob, stb, pad_of(st + 1), loff, L, bi ^ 1, wave_u);
     const bf16_t* Qs = L.qd[bi][0];
     const bf16_t* Ds = L.qd[bi][1];
     const float* S4 = L.st[bi];
