@@ -122,7 +122,12 @@ sbwd_stats_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw, co
         *reinterpret_cast<uint4*>(qtb + (pad0 + qrow0 + 16 * qt + l16) * D + 32 * ks + 8 * lq) = u;
     }
   }
-  auto blk = [&](int x) -> long { return (long)s_sel[x]; };
+  // block copies by scalar addresses, K and V tiles both in the swzv layout
+  const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const DmaLane dl = dma_lane_setup(wave_u);
+  auto copy_block = [&](int x, int sg) {
+    dma_block_sel(dl, kc, vc, it.row_base, s_sel[x], kv_len, lds[sg][0], lds[sg][1], wave_u);
+  };
 
   float m[SB_QT], lp[SB_QT];
   f32x4 minit[SB_QT], OT[8][SB_QT];
@@ -139,15 +144,15 @@ sbwd_stats_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw, co
 
 #pragma unroll
   for (int x = 0; x < 3; ++x)
-    if (x < nsel) dma_block(kc, vc, it.row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
+    if (x < nsel) copy_block(x, x);
   if (nsel > 2) wait_vmcnt<2 * DMA_PER_WAVE>();
   else if (nsel > 1) wait_vmcnt<DMA_PER_WAVE>();
   else wait_vmcnt<0>();
   __syncthreads();
   auto step = [&](int e, bool diag) {
-    if (e + 3 < nsel) dma_block(kc, vc, it.row_base, blk(e + 3), kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
+    if (e + 3 < nsel) copy_block(e + 3, (e + 3) & 3);
     f32x4 ST[4][SB_QT], SN[4][SB_QT];
-    scores<SB_QT>(lds[e & 3][0], qf, minit, ST, l16);
+    scores<SB_QT, true>(lds[e & 3][0], qf, minit, ST, l16);
     if (diag) mask_diag<SB_QT>(ST, l16, lq, qrow0);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -328,18 +333,23 @@ sbwd_dq_kernel(const bf16_t* __restrict__ q, const float* __restrict__ qw, const
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int qt = 0; qt < SB_QT; ++qt) QT[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto blk = [&](int x) -> long { return (long)s_sel[x]; };
+  // block copies by scalar addresses, K and V tiles both in the swzv layout
+  const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const DmaLane dl = dma_lane_setup(wave_u);
+  auto copy_block = [&](int x, int sg) {
+    dma_block_sel(dl, kc, vc, it.row_base, s_sel[x], kv_len, lds[sg][0], lds[sg][1], wave_u);
+  };
 
 #pragma unroll
   for (int x = 0; x < 3; ++x)
-    if (x < nsel) dma_block<true>(kc, vc, it.row_base, blk(x), kv_len, lds[x][0], lds[x][1]);
+    if (x < nsel) copy_block(x, x);
   if (nsel > 2) wait_vmcnt<2 * DMA_PER_WAVE>();
   else if (nsel > 1) wait_vmcnt<DMA_PER_WAVE>();
   else wait_vmcnt<0>();
   __syncthreads();
   // K tiles in the swzv layout: read by rows for the scores and transposed for dq
   auto step = [&](int e, bool diag) {
-    if (e + 3 < nsel) dma_block<true>(kc, vc, it.row_base, blk(e + 3), kv_len, lds[(e + 3) & 3][0], lds[(e + 3) & 3][1]);
+    if (e + 3 < nsel) copy_block(e + 3, (e + 3) & 3);
     const bf16_t* Ks = lds[e & 3][0];
     const bf16_t* Vs = lds[e & 3][1];
     f32x4 ST[4][SB_QT], PT[4][SB_QT];

@@ -14,34 +14,17 @@ constexpr int SP_D = 128;  // head dim of the bf16 paths
 constexpr int TILE = 64 * SP_D;  // bf16 elements per 64-row tile
 constexpr int NSTAGE = 4;       // LDS ring depth (blocks resident or in flight)
 
-// V tiles use the swzv layout (transposing reads); K tiles use swz, or swzv where they are also
-// read transposed (template parameter KV of the DMA and the scores).
+// The staged K and V tiles use the swzv layout (V and, in the backward, K are read transposed;
+// row reads stay conflict-free in it); the scores read K in swzv (KV) or swz.
 
-// Issue the DMA of one 64-key block (K and V tiles, 16 KB each = 16 pieces of 1 KB) into a
-// stage. With 8 waves each wave moves pieces 2w and 2w+1 (rows 8w .. 8w+7) of both tiles:
+// One 64-key block (K and V tiles, 16 KB each = 16 pieces of 1 KB) is copied into a stage by
+// the 8 waves of a workgroup, wave w moving pieces 2w and 2w+1 (rows 8w .. 8w+7) of both tiles:
 // DMA_PER_WAVE instructions. Lane l of a piece fills chunk position l % 16 of row 4I + l / 16,
-// so it loads the source chunk that the tile's swizzle puts there. Rows at or beyond kv_len
-// are clamped to the last valid row: they are causally masked (K) or weighted 0 (V).
+// so it loads the source chunk that the tile's swizzle puts there. Rows at or beyond kv_len are
+// clamped to the last valid row: they are causally masked (K) or weighted 0 (V).
 constexpr int DMA_PER_WAVE = 4;
-template <bool KV = false>
-__device__ __forceinline__ void dma_block(const bf16_t* kc, const bf16_t* vc, long row_base,
-                                          long blk, long kv_len, bf16_t* Ks, bf16_t* Vs) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int I = 2 * wave + m;                 // 1 KB piece: rows 4I .. 4I+3
-    const int row = 4 * I + (lane >> 4);
-    const int chk = (lane & 15) ^ (KV ? 2 * (row & 7) : (row & 15));  // K source chunk stored here
-    const int chv = (lane & 15) ^ (2 * (row & 7));
-    long p = blk * 64 + row;
-    if (p >= kv_len) p = kv_len - 1;
-    const long off = (row_base + p) * SP_D;
-    dma16(kc + off + 8 * chk, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Ks + I * 512)));
-    dma16(vc + off + 8 * chv, __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(Vs + I * 512)));
-  }
-}
 
-// The same copy with the block's addresses kept in scalar registers: the lane's part of the
+// The copy keeps the block's addresses in scalar registers: the lane's part of the
 // address is a 32-bit byte offset inside the block (saddr form of global_load_lds_dwordx4), and
 // both tiles use the swzv layout, so the K and V copies of a row share that offset. A lane's
 // offsets (rows 4I + lane/16 of pieces I = 2*wave and 2*wave+1, chunk positions
@@ -78,6 +61,18 @@ __device__ __forceinline__ void dma_block_s(const DmaLane& d, const bf16_t* kb, 
     dma16s(kb, off, (uint32_t)(size_t)(Ks + I * 512));
     dma16s(vb, off, (uint32_t)(size_t)(Vs + I * 512));
   }
+}
+
+// dma_block_s of selected block blk of the cache rows starting at row_base (blk and the
+// arguments wave-uniform); an entry past the cache (a malformed selection) reads the cache's last
+// block, whose rows past kv_len repeat its last valid row
+__device__ __forceinline__ void dma_block_sel(const DmaLane& d, const bf16_t* kc, const bf16_t* vc, long row_base,
+                                              int blk, long kv_len, bf16_t* Ks, bf16_t* Vs, int wave) {
+  const int last_blk = (int)((kv_len - 1) / 64);
+  int bk = __builtin_amdgcn_readfirstlane(blk);
+  if (bk > last_blk) bk = last_blk;
+  const long off = (row_base + (long)bk * 64) * SP_D;
+  dma_block_s(d, kc + off, vc + off, bk == last_blk ? (int)((kv_len - 1) % 64) : 63, Ks, Vs, wave);
 }
 
 // A operand V^T (rows dv = 16*dt + l16, k = keys in the permuted order of the P^T fragments:
