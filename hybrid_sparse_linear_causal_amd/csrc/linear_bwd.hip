@@ -116,11 +116,35 @@ __device__ __forceinline__ long tok_of(bool rev, long u, int N) { return rev ? (
 
 // DMA of one chunk's tiles (64 rows x 256 B each, swizzled rows as swzv): wave w moves pieces
 // 2w, 2w+1 (rows 8w .. 8w+7) of each tile. Rows past the end are clamped to the last token in
-// order u (valid memory; the chunk kernel zeroes their B rows).
+// order u (valid memory; the chunk kernel zeroes their B rows). A whole chunk is addressed by a
+// scalar base (its lowest token) plus a fixed 32-bit byte offset per lane (saddr form of the
+// copy), so no vector address arithmetic is repeated per chunk; a partial chunk takes the
+// per-lane clamped addresses.
+// global -> LDS copy of 16 bytes per lane from a scalar base plus a 32-bit lane byte offset
+// (saddr form of global_load_lds_dwordx4); lds_addr wave-uniform
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 template <int NT>
 __device__ __forceinline__ void dma_tiles(const bf16_t* const (&src)[NT], long head_off, long tok_stride, long u0,
                                           int N, bool rev, bf16_t (*T)[CH * D]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (u0 + CH <= N) {
+    const long tok0 = rev ? (long)N - u0 - CH : u0;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int I = 2 * wave + m;
+      const int row = 4 * I + (lane >> 4);
+      const int ch = (lane & 15) ^ (2 * (row & 7));
+      const uint32_t off = 2u * (uint32_t)((rev ? CH - 1 - row : row) * tok_stride + 8 * ch);
+#pragma unroll
+      for (int x = 0; x < NT; ++x)
+        dma16s(src[x] + head_off + tok0 * tok_stride, off, (uint32_t)(size_t)(T[x] + I * 512));
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int I = 2 * wave + m;
